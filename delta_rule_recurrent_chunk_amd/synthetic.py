@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for the Kronecker delta rule mixer.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+draws inputs only; it holds none of the mixer's arithmetic.
+
+Recipe (fixed draw order from one ``numpy.random.Generator(PCG64(seed))``):
+  1. q, k, v ~ N(0, 1) of shape [B, T, H, d], each L2-normalised over d per
+     (b, t, h) -- the mixer receives normalised q, k, v (KronLSTM summary page,
+     onedev.kr, section "how it is used": short causal conv, SiLU, L2 norm).
+  2. x ~ N(mu, 1) of shape [B, T, H, dk].
+  3. a_log ~ U(-1, 1) of shape [H].
+  4. f = sigmoid(x) ** exp(a_log[h])  -- the forget gate is a sigmoid raised to
+     a learned positive per-head exponent (same section).
+  5. beta = beta_scale * sigmoid(N(0, 1)) of shape [B, T, H]; beta_scale = 2
+     gives the (0, 2) range of the state-tracking extension (same page,
+     section "premises and limits").
+  6. c = sigmoid(N(0, 1)) of shape [B, T, H].
+  7. dO ~ N(0, 1) of shape [B, T, H, dv] (only when requested).
+  8. S0 ~ N(0, s0_std^2) of shape [B, H, dv, dk] (only when s0_std is given).
+q, k, v, f (and dO) are then rounded to the workload's dtype with
+round-to-nearest-even; beta, c and S0 stay fp32.  Both the GPU library and
+the oracle consume the rounded values (the oracle upcasts them exactly).
+
+These seeded draws stand in for real activations: the pages measure on
+FineWeb-Edu language-model training, for which no data or weights exist here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str          # "fp32" or "bf16" for q, k, v, f, o (and dO, dq, ...)
+    mu: float = 3.0     # mean of the forget-gate pre-activation
+    beta_scale: float = 1.0
+    seed: int = 1000
+    backward: bool = False
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+WORKLOADS = {
+    # Tiny fp32 forward; the oracle finishes it in well under a second.
+    "tiny_fp32": Workload("tiny_fp32", 1, 256, 2, 32, 32, "fp32", seed=1000),
+    # One bf16 sequence at the 16-head, d=128 layer shape.
+    "single_seq": Workload("single_seq", 1, 2048, 16, 128, 128, "bf16", seed=1001),
+    # Training-step shape: 8 x 2048 = 16,384 tokens per step (headline).
+    "train_step": Workload("train_step", 8, 2048, 16, 128, 128, "bf16", seed=1002),
+    # Forward plus gate-aware backward.
+    "fwd_bwd": Workload("fwd_bwd", 4, 2048, 16, 128, 128, "bf16", seed=1003, backward=True),
+    # Long context, non-contractive erase gate in (0, 2), near-1 decay.
+    "long_ctx": Workload("long_ctx", 1, 32768, 16, 128, 128, "bf16", mu=5.0,
+                         beta_scale=2.0, seed=1004),
+}
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _l2n(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
+         s0_std=None, dST_std=None):
+    """Draw fp64 inputs (before dtype rounding).  Returns a dict."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(rng.standard_normal((B, T, H, dk)))
+    k = _l2n(rng.standard_normal((B, T, H, dk)))
+    v = _l2n(rng.standard_normal((B, T, H, dv)))
+    x = rng.normal(mu, 1.0, (B, T, H, dk))
+    a_log = rng.uniform(-1.0, 1.0, (H,))
+    f = _sigmoid(x) ** np.exp(a_log)[None, None, :, None]
+    beta = beta_scale * _sigmoid(rng.standard_normal((B, T, H)))
+    c = _sigmoid(rng.standard_normal((B, T, H)))
+    out = dict(q=q, k=k, v=v, f=f, beta=beta, c=c, S0=None, dO=None, dST=None)
+    if with_dO:
+        out["dO"] = rng.standard_normal((B, T, H, dv))
+    if s0_std is not None:
+        out["S0"] = rng.normal(0.0, s0_std, (B, H, dv, dk))
+    if dST_std is not None:
+        out["dST"] = rng.normal(0.0, dST_std, (B, H, dv, dk))
+    return out
+
+
+def draw_workload(w: Workload, with_dO=None, s0_std=None):
+    return draw(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, beta_scale=w.beta_scale,
+                with_dO=w.backward if with_dO is None else with_dO, s0_std=s0_std)
+
+
+def round_to(x, dtype: str):
+    """Round an fp64 array to ``dtype`` ("fp32" or "bf16", round-to-nearest-even)
+    and return the rounded values as fp64 (exact upcast)."""
+    if x is None:
+        return None
+    if dtype == "fp32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+        return t.to(torch.bfloat16).to(torch.float64).numpy()
+    raise ValueError(dtype)
+
+
+def rounded(inputs: dict, dtype: str) -> dict:
+    """Round the per-token tensors to ``dtype``; gates and states to fp32."""
+    out = {}
+    for key, val in inputs.items():
+        if val is None:
+            out[key] = None
+        elif key in ("q", "k", "v", "f", "dO"):
+            out[key] = round_to(val, dtype)
+        else:
+            out[key] = round_to(val, "fp32")
+    return out
