@@ -1,0 +1,158 @@
+"""MI355X (gfx950) Kronecker delta rule mixer -- thin Python binding.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libkrondelta.so`` through its C ABI (``include/kron_delta.h``).
+PyTorch supplies device memory and the current stream.  If the library is
+missing, every entry point raises; there is no CPU fallback.
+
+    o, S_T = fwd(q, k, v, f, beta, c, S0=None)
+    grads  = bwd(q, k, v, f, beta, c, S0, dO, dST=None)
+
+Shapes: q, k, f [B, T, H, d]; v [B, T, H, d]; beta, c [B, T, H] fp32;
+S0 / S_T [B, H, d, d] fp32 (S[i][j], i over values, j over keys).
+Dtypes: q, k, v, f (and o, dO, dq, ...) all bfloat16 or all float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkrondelta.so")
+
+KD_F32, KD_BF16 = 0, 1
+ABI_VERSION = 1
+EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
+            "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd")
+
+
+class KronDeltaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+class KdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkrondelta.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkrondelta.so is not built (run __graft_entry__.build() "
+                              "or python delta_rule_recurrent_chunk_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        dp = ctypes.POINTER(KdDesc)
+        L.kron_delta_abi_version.restype = i32
+        L.kron_delta_status_string.restype = ctypes.c_char_p
+        L.kron_delta_status_string.argtypes = [i32]
+        L.kron_delta_workspace_bytes.restype = sz
+        L.kron_delta_workspace_bytes.argtypes = [dp, i32]
+        L.kron_delta_fwd.restype = i32
+        L.kron_delta_fwd.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+        L.kron_delta_bwd.restype = i32
+        L.kron_delta_bwd.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+        if L.kron_delta_abi_version() != ABI_VERSION:
+            raise ImportError("libkrondelta.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kron_delta_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(torch, dt):
+    if dt == torch.bfloat16:
+        return KD_BF16
+    if dt == torch.float32:
+        return KD_F32
+    raise TypeError("q, k, v, f must be bfloat16 or float32, got %s" % dt)
+
+
+def _prep(torch, q, k, v, f, beta, c, S0):
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and f.is_cuda):
+        raise ValueError("inputs must be device tensors")
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v), ("f", f)):
+        if t.dtype != dt:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, dt))
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != (B, T, H, dk) or tuple(f.shape) != (B, T, H, dk) or tuple(v.shape) != (B, T, H, dv):
+        raise ValueError("q, k, f must be [B, T, H, dk] and v [B, T, H, dv]")
+    if tuple(beta.shape) != (B, T, H) or tuple(c.shape) != (B, T, H):
+        raise ValueError("beta and c must be [B, T, H]")
+    if beta.dtype != torch.float32 or c.dtype != torch.float32:
+        raise TypeError("beta and c must be float32")
+    if S0 is not None:
+        if tuple(S0.shape) != (B, H, dv, dk) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be float32 [B, H, dv, dk]")
+        S0 = S0.contiguous()
+    desc = KdDesc(B, T, H, dk, dv, _dtype_code(torch, dt))
+    return desc, q.contiguous(), k.contiguous(), v.contiguous(), f.contiguous(), \
+        beta.contiguous(), c.contiguous(), S0
+
+
+def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True):
+    """Chunkwise forward.  Returns (o, S_T); S_T is None if return_state=False."""
+    import torch
+    L = lib()
+    desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
+    o = torch.empty((desc.B, desc.T, desc.H, desc.dv), dtype=q.dtype, device=q.device)
+    ST = torch.empty((desc.B, desc.H, desc.dv, desc.dk), dtype=torch.float32,
+                     device=q.device) if return_state else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.kron_delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+                          _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), None, 0, ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_fwd")
+    return o, ST
+
+
+def workspace_bytes(B, T, H, d, dtype_code, with_backward=True) -> int:
+    desc = KdDesc(B, T, H, d, d, dtype_code)
+    return int(lib().kron_delta_workspace_bytes(ctypes.byref(desc), 1 if with_backward else 0))
+
+
+def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None):
+    """Gate-aware backward.  Returns a dict with dq, dk, dv, df, dbeta, dc, dS0."""
+    import torch
+    L = lib()
+    desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
+    if dO.dtype != q.dtype or tuple(dO.shape) != (desc.B, desc.T, desc.H, desc.dv):
+        raise ValueError("dO must match o's shape and dtype")
+    dO = dO.contiguous()
+    if dST is not None:
+        if tuple(dST.shape) != (desc.B, desc.H, desc.dv, desc.dk) or dST.dtype != torch.float32:
+            raise ValueError("dST must be float32 [B, H, dv, dk]")
+        dST = dST.contiguous()
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               df=torch.empty_like(f), dbeta=torch.empty_like(beta), dc=torch.empty_like(c),
+               dS0=torch.empty((desc.B, desc.H, desc.dv, desc.dk), dtype=torch.float32, device=dev)
+               if want_dS0 else None)
+    need = int(L.kron_delta_workspace_bytes(ctypes.byref(desc), 1))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = L.kron_delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+                          _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                          _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
+                          _ptr(out["dS0"]), _ptr(workspace), need, ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_bwd")
+    return out

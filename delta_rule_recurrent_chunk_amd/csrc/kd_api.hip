@@ -1,0 +1,149 @@
+// kd_api.hip -- the C ABI declared in include/kron_delta.h: argument checks,
+// workspace sizing and kernel dispatch on the caller's stream.  No
+// allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kron_delta.h"
+
+namespace kd {
+hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                      const float* beta, const float* c, const float* S0, void* o, float* ST,
+                      float* ckpt, int B, int T, int H, hipStream_t st);
+hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                      const float* beta, const float* c, const float* S0, const void* dO,
+                      const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
+                      float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st);
+size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H);
+}  // namespace kd
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+    Range r;
+    r.lo = (uintptr_t)p;
+    r.hi = r.lo + bytes;
+    return r;
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
+
+kd_status check_desc(const kd_desc* d) {
+    if (!d) return KD_ERR_NULL;
+    if (d->dtype != KD_F32 && d->dtype != KD_BF16) return KD_ERR_DTYPE;
+    if (d->B < 1 || d->H < 1 || d->T < 0) return KD_ERR_SHAPE;
+    if (d->dk != d->dv) return KD_ERR_SHAPE;
+    if (d->dk != 32 && d->dk != 64 && d->dk != 128) return KD_ERR_SHAPE;
+    if (d->dtype == KD_F32 && d->dk == 128) return KD_ERR_DTYPE;
+    if ((int64_t)d->B * (int64_t)d->H > (int64_t)INT32_MAX) return KD_ERR_SHAPE;
+    // kernels address one batch element's [T, H, d] tensor with 32-bit byte offsets
+    const int64_t es = d->dtype == KD_BF16 ? 2 : 4;
+    if ((int64_t)d->T * d->H * d->dk * es > (int64_t)INT32_MAX) return KD_ERR_SHAPE;
+    return KD_OK;
+}
+
+size_t esize(const kd_desc* d) { return d->dtype == KD_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int kron_delta_abi_version(void) { return KRON_DELTA_ABI_VERSION; }
+
+const char* kron_delta_status_string(int s) {
+    switch (s) {
+    case KD_OK: return "ok";
+    case KD_ERR_NULL: return "a required pointer is NULL";
+    case KD_ERR_SHAPE: return "unsupported shape (need B,H>=1, T>=0, dk==dv in {32,64,128})";
+    case KD_ERR_DTYPE: return "unsupported dtype (bf16: d in {32,64,128}; fp32: d in {32,64})";
+    case KD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KD_ERR_WORKSPACE: return "workspace missing or too small";
+    case KD_ERR_LAUNCH: return "kernel launch failed";
+    case KD_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+    }
+}
+
+size_t kron_delta_workspace_bytes(const kd_desc* d, int with_backward) {
+    if (check_desc(d) != KD_OK) return 0;
+    if (!with_backward) return 0;
+    return kd::bwd_workspace_bytes(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
+}
+
+kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const void* v,
+                         const void* f, const float* beta, const float* c, const float* S0,
+                         void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !f || !beta || !c || !o)) return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, f, beta, c, S0, o, ST};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
+                         range_of(beta, gb), range_of(c, gb), range_of(S0, S0 ? sb : 0)};
+    const Range outs[] = {range_of(o, ntok ? xb : 0), range_of(ST, ST ? sb : 0)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
+    if (ntok == 0 && !ST) return KD_OK;
+    hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
+                                  nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const void* v,
+                         const void* f, const float* beta, const float* c, const float* S0,
+                         const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                         void* df, float* dbeta, float* dc, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !f || !beta || !c || !dO || !dq || !dk || !dv || !df ||
+                     !dbeta || !dc))
+        return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    const size_t need = kron_delta_workspace_bytes(d, 1);
+    if (need > 0 && (!ws || ws_bytes < need)) return KD_ERR_WORKSPACE;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
+                         range_of(beta, gb), range_of(c, gb), range_of(S0, S0 ? sb : 0),
+                         range_of(dO, xb), range_of(dST, dST ? sb : 0)};
+    const Range outs[] = {range_of(dq, xb), range_of(dk, xb), range_of(dv, xb), range_of(df, xb),
+                          range_of(dbeta, gb), range_of(dc, gb), range_of(dS0, dS0 ? sb : 0),
+                          range_of(ws, need)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a)
+        for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
+            if (overlap(outs[a], outs[b])) return KD_ERR_ALIAS;
+    if (ntok == 0 && !dS0) return KD_OK;
+    hipError_t e = kd::launch_bwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, dO, dST,
+                                  dq, dk, dv, df, dbeta, dc, dS0, ws, d->B, d->T, d->H,
+                                  (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+/*
+ * kron_delta.h -- C ABI of the MI355X (gfx950) Kronecker delta rule library.
+ *
+ * The library computes the chunkwise-parallel forward pass (and the
+ * gate-aware backward pass) of the KronLSTM mixer's Kronecker delta rule.
+ * Per batch element b and head h it carries one state S in R^{dv x dk}; for
+ * every token t it applies
+ *     Sbar_t = S_{t-1} diag(f_t)                 (key-channel forget gate)
+ *     r_t    = v_t^T Sbar_t k_t                  (scalar association strength)
+ *     S_t    = Sbar_t + (c_t - beta_t r_t) v_t k_t^T
+ *     o_t    = S_t q_t
+ * Definition: onedev.kr paper summary "KronLSTM이 스칼라 보정으로 긴 문맥 선형
+ * 어텐션의 기억 간섭을 줄인다", sections "어떻게 동작하나" (the scalar correction
+ * of v^T S k toward a target along v k^T, erase by beta and write by c) and
+ * "어떻게 쓰나" (diagonal forget gate on the key dimension, applied from the
+ * right; per-head scalar beta and c; the matrix state is all that is carried).
+ * The chunkwise form follows the DeltaNet-style chunk-parallel training that
+ * the same page ("무엇과 다른가") says applies because the lifted transition is
+ * a generalised Householder matrix.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * All tensor arguments are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *    owned by the caller.  The library never allocates, frees or
+ *    synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    null stream) and the call returns without waiting for it.
+ *  * Layouts are contiguous, row-major:
+ *      q, k, f, dq, dk, df : [B, T, H, dk]      element type = desc->dtype
+ *      v, o, dO, dv        : [B, T, H, dv]      element type = desc->dtype
+ *      beta, c, dbeta, dc  : [B, T, H]          fp32
+ *      S0, ST, dST, dS0    : [B, H, dv, dk]     fp32, S[i][j] at i*dk + j
+ *  * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs.
+ *  * Supported shapes: B, H >= 1, T >= 0 (any length; a ragged last chunk is
+ *    handled), dk == dv == d with d in {32, 64, 128} for KD_BF16 and
+ *    d in {32, 64} for KD_F32.  B*H <= 2^31-1, and one batch element's
+ *    [T, H, d] tensor must span at most 2^31-1 bytes (T*H*d*elemsize).
+ *  * The state is always fp32.  Inputs f must lie in [0, 1].
+ *  * Argument checks run before any launch.  A failed check returns a
+ *    negative kd_status and enqueues nothing; outputs are untouched.
+ *    A failed launch returns KD_ERR_LAUNCH.
+ *  * The functions are stateless and thread-safe.
+ */
+#ifndef KRON_DELTA_H
+#define KRON_DELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KRON_DELTA_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KD_API __attribute__((visibility("default")))
+#else
+#define KD_API
+#endif
+
+typedef enum {
+    KD_F32 = 0,   /* q, k, v, f, o (and gradients) in IEEE fp32 */
+    KD_BF16 = 1   /* q, k, v, f, o (and gradients) in bfloat16  */
+} kd_dtype;
+
+typedef enum {
+    KD_OK = 0,
+    KD_ERR_NULL = -1,       /* a required pointer is NULL                 */
+    KD_ERR_SHAPE = -2,      /* unsupported B, T, H, dk, dv                */
+    KD_ERR_DTYPE = -3,      /* unknown dtype or dtype/shape combination   */
+    KD_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned           */
+    KD_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required    */
+    KD_ERR_LAUNCH = -6,     /* the HIP runtime rejected a kernel launch   */
+    KD_ERR_ALIAS = -7       /* an output overlaps an input                */
+} kd_status;
+
+typedef struct {
+    int32_t B;      /* batch size                  */
+    int32_t T;      /* sequence length             */
+    int32_t H;      /* heads                       */
+    int32_t dk;     /* key dimension               */
+    int32_t dv;     /* value dimension (== dk)     */
+    int32_t dtype;  /* kd_dtype                    */
+} kd_desc;
+
+/* ABI version of the loaded library (KRON_DELTA_ABI_VERSION). */
+KD_API int kron_delta_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+KD_API const char *kron_delta_status_string(int status);
+
+/*
+ * Device workspace, in bytes, that kron_delta_fwd (with_backward = 0) or
+ * kron_delta_bwd (with_backward = 1) needs for `desc`.  Returns 0 for an
+ * invalid descriptor as well as when no workspace is needed; the forward
+ * pass needs none.
+ */
+KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int with_backward);
+
+/*
+ * Forward pass.  Reads q, k, v, f, beta, c and the initial state S0 (NULL
+ * means S0 = 0); writes o and, when ST is non-NULL, the final state S_T.
+ * ws / ws_bytes are accepted for symmetry and may be NULL / 0.
+ */
+KD_API kd_status kron_delta_fwd(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         void *o, float *ST,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gate-aware backward pass: gradients of L = <dO, o> + <dST, S_T> with
+ * respect to q, k, v, f, beta, c and S0, where o and S_T are what
+ * kron_delta_fwd returns for the same inputs.  dST NULL means dS_T = 0;
+ * S0 NULL means S0 = 0; dS0 NULL means the gradient of S0 is not returned.
+ * Needs a workspace of kron_delta_workspace_bytes(desc, 1) bytes (holds the
+ * chunk-start states of a forward recomputation); its contents on entry are
+ * ignored and on exit are unspecified.
+ */
+KD_API kd_status kron_delta_bwd(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         const void *dO, const float *dST,
+                         void *dq, void *dk, void *dv, void *df,
+                         float *dbeta, float *dc, float *dS0,
+                         void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KRON_DELTA_H */

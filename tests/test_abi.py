@@ -1,0 +1,124 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library loads, exports every function include/kron_delta.h declares, and
+rejects bad arguments with the documented status codes before any launch
+(the pointers below are never dereferenced: every call fails its checks, or
+has nothing to compute, before touching the device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_recurrent_chunk_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kron_delta.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KD_API\s+[\w\s\*]+?\b(kron_delta_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kd.LIB_PATH):
+        from delta_rule_recurrent_chunk_amd import build
+        build.build()
+    return kd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(kd.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strings(L):
+    assert L.kron_delta_abi_version() == 1
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS, 12345):
+        assert isinstance(kd.status_string(s), str) and kd.status_string(s)
+
+
+def _desc(B=1, T=128, H=2, dk=64, dv=64, dtype=kd.KD_BF16):
+    return kd.KdDesc(B, T, H, dk, dv, dtype)
+
+
+# fake, 256-byte aligned, far-apart device addresses (never dereferenced)
+BASE = 0x7F0000000000
+STEP = 1 << 32
+
+
+def P(i, misalign=0):
+    return ctypes.c_void_p(BASE + i * STEP + misalign)
+
+
+def fwd(L, desc, ptrs=None, **over):
+    names = ["q", "k", "v", "f", "beta", "c", "S0", "o", "ST"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    if ptrs:
+        p.update(ptrs)
+    p.update(over)
+    d = ctypes.byref(desc) if desc is not None else None
+    return L.kron_delta_fwd(d, *[p[n] for n in names], None, 0, None)
+
+
+def bwd(L, desc, ws_bytes=None, **over):
+    names = ["q", "k", "v", "f", "beta", "c", "S0", "dO", "dST", "dq", "dk", "dv", "df",
+             "dbeta", "dc", "dS0"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    p["ws"] = P(40)
+    p.update(over)
+    need = L.kron_delta_workspace_bytes(ctypes.byref(desc), 1)
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.kron_delta_bwd(ctypes.byref(desc), *[p[n] for n in names], p["ws"], wsb, None)
+
+
+def test_fwd_argument_checks(L):
+    assert fwd(L, None) == NULL
+    assert fwd(L, _desc(dtype=7)) == DTYPE
+    assert fwd(L, _desc(B=0)) == SHAPE
+    assert fwd(L, _desc(H=0)) == SHAPE
+    assert fwd(L, _desc(T=-1)) == SHAPE
+    assert fwd(L, _desc(dk=64, dv=32)) == SHAPE
+    assert fwd(L, _desc(dk=48, dv=48)) == SHAPE
+    assert fwd(L, _desc(dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE
+    assert fwd(L, _desc(T=1 << 20, H=16, dk=128, dv=128)) == SHAPE   # > 2^31 bytes per batch element
+    assert fwd(L, _desc(), q=None) == NULL
+    assert fwd(L, _desc(), o=None) == NULL
+    assert fwd(L, _desc(), beta=None) == NULL
+    assert fwd(L, _desc(), k=P(1, misalign=8)) == ALIGN
+    assert fwd(L, _desc(), ST=P(8, misalign=4)) == ALIGN
+    assert fwd(L, _desc(), o=P(0)) == ALIAS          # o == q
+    assert fwd(L, _desc(), ST=P(6)) == ALIAS         # ST == S0
+    assert fwd(L, _desc(), ST=P(7)) == ALIAS         # ST == o
+    # nothing to compute: T = 0 and no final state requested
+    assert fwd(L, _desc(T=0), ST=None) == OK
+
+
+def test_bwd_argument_checks(L):
+    d = _desc()
+    assert L.kron_delta_workspace_bytes(ctypes.byref(d), 0) == 0
+    need = L.kron_delta_workspace_bytes(ctypes.byref(d), 1)
+    assert need >= 2 * 2 * 64 * 64 * 4   # one fp32 state per (b, h, chunk)
+    assert bwd(L, _desc(dtype=3)) == DTYPE
+    assert bwd(L, d, ws_bytes=need - 1) == WORKSPACE
+    assert bwd(L, d, ws=None) == WORKSPACE
+    assert bwd(L, d, dO=None) == NULL
+    assert bwd(L, d, dq=P(2)) == ALIAS               # dq == v
+    assert bwd(L, d, dS0=P(9)) == ALIAS              # dS0 == dq
+    assert bwd(L, d, ws=P(13)) == ALIAS              # workspace == dbeta (an output)
+    assert bwd(L, d, df=P(12, misalign=2)) == ALIGN
+    assert bwd(L, _desc(T=0), dS0=None) == OK
+
+
+def test_workspace_scales_with_chunks(L):
+    a = L.kron_delta_workspace_bytes(ctypes.byref(_desc(T=64)), 1)
+    b = L.kron_delta_workspace_bytes(ctypes.byref(_desc(T=65)), 1)
+    assert b == 2 * a
+    assert L.kron_delta_workspace_bytes(ctypes.byref(_desc(dk=48, dv=48)), 1) == 0
