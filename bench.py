@@ -1,0 +1,202 @@
+"""Benchmark of the chunkwise Kronecker delta rule forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train_step]
+
+A step is one kron_delta_fwd call over the whole workload (all B*H heads,
+all T tokens): decay products, Gram tiles, forward substitution, readout and
+state propagation all run inside that one kernel.  Inputs are seeded
+synthetic draws (see delta_rule_recurrent_chunk_amd/synthetic.py) that are
+resident in HBM before the timed region starts.  Prints one JSON line.
+
+The roofline entry prices the kernel's algorithmic HBM bytes per launch
+(q, k, v, f, beta, c read once, o and S_T written once) against the MI355X
+HBM3E peak of 8 TB/s, using the average launch duration measured with HIP
+events on the stream the kernel runs on.  The cpu_baseline entry times the
+fp64 oracle on the host cores on a bounded sample of the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "Kron-delta chunked fwd tokens/s (H=16,d=128) and % MFMA/HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kd_fwd_train_step_traffic.json")
+
+
+def algorithmic_bytes(w, esize, with_S0=False):
+    """HBM bytes one forward launch must move: every input once, every output once."""
+    ntok = w.B * w.T * w.H
+    b = 4 * ntok * w.dk * esize          # q, k, v, f
+    b += 2 * ntok * 4                    # beta, c (fp32)
+    b += ntok * w.dv * esize             # o
+    b += w.B * w.H * w.dv * w.dk * 4     # S_T (fp32)
+    if with_S0:
+        b += w.B * w.H * w.dv * w.dk * 4
+    return b
+
+
+def mfma_flops(w):
+    """MFMA flops of one launch as issued (full 16x16 tiles, including the
+    masked-out upper Gram tiles' partners): per (b, h, chunk) of C = 64 with
+    d = dk = dv: Grams 3 x 10 tiles x 2*16*16*d, state reads 2 x 2*C*d*d,
+    intra readout 2*C*C*d, state update 2*C*d*d."""
+    C = 64
+    d = w.dk
+    nch = (w.T + C - 1) // C
+    per = 3 * 10 * 2 * 16 * 16 * d + 2 * 2 * C * d * d + 2 * C * C * d + 2 * C * d * d
+    return w.B * w.H * nch * per
+
+
+def cpu_baseline(x_np, w, budget_s=12.0):
+    import numpy as np
+    import oracle
+    threads = oracle.num_threads()
+    done_tok = 0
+    t0 = time.perf_counter()
+    nb = 0
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        oracle.fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
+                   x_np["beta"][sl], x_np["c"][sl], None)
+        nb += 1
+        done_tok += w.T
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle forward on %d of %d sequences (T=%d, H=%d, d=%d), same seeded "
+                      "inputs, %.2f s wall" % (nb, w.B, w.T, w.H, w.dk, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="train_step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time launches after evicting the caches with a 1 GiB write")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (reference for HBM "
+                         "byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30}))
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Kronecker delta rule path here runs on a "
+              "single MI355X (heads would shard across GPUs with no exchange); use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import delta_rule_recurrent_chunk_amd as kd
+    from delta_rule_recurrent_chunk_amd import synthetic as sy
+
+    w = sy.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = sy.rounded(sy.draw_workload(w, with_dO=False), w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {n: torch.tensor(x[n], dtype=tdt if n in ("q", "k", "v", "f") else torch.float32,
+                         device=dev) for n in ("q", "k", "v", "f", "beta", "c")}
+    esize = 2 if w.dtype == "bf16" else 4
+
+    def step():
+        return kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the stream the binding launches on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps     # avg launch duration (events)
+    ms_per_step = wall * 1e3 / args.steps
+
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step * 1e-3)
+    abytes = algorithmic_bytes(w, esize)
+    achieved = abytes / (kernel_ms * 1e-3) / 1e9
+    flops = mfma_flops(w)
+    peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and args.workload == "train_step":
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        traffic = tr.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
+                "beta,c=sigmoid(N(0,1)))" % w.mu,
+        "config": {"workload": "%s: Kronecker delta rule chunked forward, B=%d T=%d H=%d "
+                               "dk=dv=%d, chunk 64, %s q/k/v/f, fp32 beta/c/state, S0=0"
+                               % (w.name, w.B, w.T, w.H, w.dk, w.dtype),
+                   "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kd_fwd_kernel<Bf16T,128>", "kernel_ms": kernel_ms,
+                     "algorithmic_bytes_per_launch": abytes,
+                     "mfma_tflops": flops / (kernel_ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (kernel_ms * 1e-3) / 1e12 / peak_tf},
+    }
+    if args.cold:
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for i in range(min(args.steps, 20)):
+            big.fill_(i & 255)
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b_))
+        cold_ms = float(np.median(times))
+        out["cold_cache"] = {"kernel_ms": cold_ms, "tokens_per_s": tokens / (cold_ms * 1e-3),
+                             "hbm_frac": abytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,6 +22,7 @@ namespace kd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;        // chunk length (tokens per chunk)
@@ -131,41 +132,49 @@ struct F32T {
     }
 };
 
-// Sixteen consecutive tokens of one channel, held in registers between the
-// global load and its use (the prefetch buffer).  bf16 values are packed two
-// per 32-bit register.
-template <class TR> struct Col16;
+// Eight consecutive tokens of two adjacent channels (j0 = even, j0 + 1) held
+// in registers between the global load and its use (the prefetch buffer).
+// One 32-bit load fetches both bf16 channels of a row.
+template <class TR> struct Pair8;
 
-template <> struct Col16<Bf16T> {
-    uint32_t w[SB / 2];
-    // p: wave-uniform base; element m at p[off + m*stride] (32-bit offsets);
-    // rows m >= nvalid read as `fill` (0 or 1, exact in bf16)
-    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int nvalid,
-                                         float fill) {
-        const uint16_t* p16 = reinterpret_cast<const uint16_t*>(p);
-        const uint32_t fb = __float_as_uint(fill) >> 16;
+template <> struct Pair8<Bf16T> {
+    uint32_t w[8];   // low half: channel j0, high half: channel j0 + 1
+    // p: wave-uniform base; row m at p[off + min(m, last)*stride] (32-bit
+    // element offsets, off even).  Loads are unconditional: rows past the
+    // sequence end re-read row `last` (in bounds) and are masked at use.
+    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int last) {
 #pragma unroll
-        for (int m = 0; m < SB / 2; ++m) {
-            const uint32_t lo = (2 * m < nvalid) ? (uint32_t)p16[off + (2 * m) * stride] : fb;
-            const uint32_t hi = (2 * m + 1 < nvalid) ? (uint32_t)p16[off + (2 * m + 1) * stride] : fb;
-            w[m] = lo | (hi << 16);
+        for (int m = 0; m < 8; ++m)
+            w[m] = *reinterpret_cast<const uint32_t*>(p + off + (uint32_t)(m < last ? m : last) * stride);
+    }
+    __device__ __forceinline__ float get(int m, int c) const {
+        return __uint_as_float(c ? (w[m] & 0xffff0000u) : (w[m] << 16));
+    }
+};
+
+template <> struct Pair8<F32T> {
+    float w[8][2];
+    __device__ __forceinline__ void load(const float* p, uint32_t off, uint32_t stride, int last) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float2 x = *reinterpret_cast<const float2*>(p + off + (uint32_t)(m < last ? m : last) * stride);
+            w[m][0] = x.x;
+            w[m][1] = x.y;
         }
     }
-    __device__ __forceinline__ float get(int tau) const {
-        const uint32_t x = w[tau >> 1];
-        return __uint_as_float((tau & 1) ? (x & 0xffff0000u) : (x << 16));
-    }
+    __device__ __forceinline__ float get(int m, int c) const { return w[m][c]; }
 };
 
-template <> struct Col16<F32T> {
-    float w[SB];
-    __device__ __forceinline__ void load(const float* p, uint32_t off, uint32_t stride, int nvalid,
-                                         float fill) {
-#pragma unroll
-        for (int m = 0; m < SB; ++m) w[m] = (m < nvalid) ? p[off + m * stride] : fill;
-    }
-    __device__ __forceinline__ float get(int tau) const { return w[tau]; }
-};
+// Store two adjacent channels' values (as the path's element type).
+__device__ __forceinline__ void st2(__bf16* p, float a, float b) {
+    bf16x2 x;
+    x[0] = (__bf16)a;
+    x[1] = (__bf16)b;
+    *reinterpret_cast<bf16x2*>(p) = x;
+}
+__device__ __forceinline__ void st2(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
 
 // Number of MFMA K-steps of each path that cover a contraction of length n.
 template <class TR, int N>

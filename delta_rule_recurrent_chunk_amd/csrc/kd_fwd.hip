@@ -41,6 +41,12 @@
 //    overlap the MFMA phases.
 #include "kd_device.h"
 
+// Phase markers: no-ops here; a profiling build may define them to record
+// timestamps at the phase boundaries of the chunk loop.
+#ifndef KD_PHASE_MARK
+#define KD_PHASE_MARK(chunk, id) ((void)0)
+#endif
+
 namespace kd {
 
 constexpr float kUnsafeFloor = 7.888609052210118e-31f;  // 2^-100
@@ -91,7 +97,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
-    const int I = tid / D, j = tid % D;          // prep ownership: sub-block I, channel j
+    // prep ownership: sub-block I, channel pair (j0, j0 + 1), half hf of the
+    // sub-block's 16 rows (rows 8hf .. 8hf + 7); the two halves of a channel
+    // pair sit in adjacent lanes.
+    const int I = tid / D, j0 = 2 * ((tid % D) >> 1), hf = tid & 1;
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     // Per batch element, every [T, H, D] tensor is addressed from a wave-uniform
     // base with 32-bit element offsets (the host checks T*H*D fits).
@@ -118,20 +127,22 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         for (int r = 0; r < 4; ++r)
             S[mt][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mt + 4 * g + r] : 0.f;
 
-    // ---- prefetch registers (this thread's column j, rows 16I..16I+15)
-    Col16<TR> rq, rk, rv, rf;
+    // ---- prefetch registers (channels j0, j0+1; rows 16I + 8hf .. +7)
+    Pair8<TR> rq, rk, rv, rf;
     float rbc = 0.f;
     auto load_chunk = [&](int n) {
-        const int t0 = n * CH + I * SB;
-        const int nvalid = T - t0;   // rows beyond the sequence read as q=k=v=0, f=1
-        const uint32_t off = (uint32_t)t0 * rs + hoff + j;
-        rq.load(qb, off, rs, nvalid, 0.f);
-        rk.load(kb, off, rs, nvalid, 0.f);
-        rv.load(vb, off, rs, nvalid, 0.f);
-        rf.load(fb, off, rs, nvalid, 1.f);
+        // Rows past the sequence end re-read the last row (in bounds) and are
+        // masked in the prep (q = k = v = 0, f = 1, beta = c = 0).
+        const int t0 = min(n * CH + SB * I + 8 * hf, T - 1);
+        const int last = min(7, T - 1 - t0);
+        const uint32_t off = (uint32_t)t0 * rs + hoff + j0;
+        rq.load(qb, off, rs, last);
+        rk.load(kb, off, rs, last);
+        rv.load(vb, off, rs, last);
+        rf.load(fb, off, rs, last);
         if (tid < 2 * CH) {
-            const int t = n * CH + (tid & (CH - 1));
-            rbc = t < T ? gsrc[(uint32_t)t * H + h] : 0.f;
+            const int t = min(n * CH + (tid & (CH - 1)), T - 1);
+            rbc = gsrc[(uint32_t)t * H + h];
         }
     };
     if (NC > 0) load_chunk(0);
@@ -146,15 +157,31 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 for (int r = 0; r < 4; ++r)
                     dst[(size_t)(16 * w + cl) * D + 16 * mt + 4 * g + r] = S[mt][r];
         }
+        KD_PHASE_MARK(n, 0);
         // ================= prep (a): decay products within the sub-block
-        float al[SB];
-        al[0] = rf.get(0);
+        const int nvalid = T - (n * CH + SB * I + 8 * hf);   // rows of this half inside the sequence
+        auto fget = [&](int m, int c) { return m < nvalid ? rf.get(m, c) : 1.f; };
+        float al[8][2];           // product of f from the sub-block start through the row
+        float P0[2], P1[2], bp[2];
+        bool unsafe[2];
 #pragma unroll
-        for (int tau = 1; tau < SB; ++tau) al[tau] = al[tau - 1] * rf.get(tau);
-        const float bp = al[SB - 1];
-        const bool unsafe = !(bp >= kUnsafeFloor);
-        sm.bprod[I][j] = bp;
-        if (unsafe) atomicOr(&sm.unsafe_mask, 1u << I);
+        for (int c = 0; c < 2; ++c) {
+            al[0][c] = fget(0, c);
+#pragma unroll
+            for (int m = 1; m < 8; ++m) al[m][c] = al[m - 1][c] * fget(m, c);
+            const float mine = al[7][c];
+            const float other = __shfl_xor(mine, 1, 64);
+            P0[c] = hf ? other : mine;     // product over rows 0..7 of the sub-block
+            P1[c] = hf ? mine : other;     // product over rows 8..15
+            bp[c] = P0[c] * P1[c];
+            if (hf) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) al[m][c] *= P0[c];
+            }
+            unsafe[c] = !(bp[c] >= kUnsafeFloor);
+        }
+        if (hf == 0) { sm.bprod[I][j0] = bp[0]; sm.bprod[I][j0 + 1] = bp[1]; }
+        if (unsafe[0] || unsafe[1]) atomicOr(&sm.unsafe_mask, 1u << I);
         // clear the diagonal tiles of M (scratch for the exact fallback)
         for (int x = tid; x < NSB * SB * SB; x += NT) {
             const int blk = x >> 8, e = x & 255;
@@ -162,73 +189,99 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         }
         lds_barrier();
 
+        KD_PHASE_MARK(n, 1);
         // ================= prep (b): operands into LDS
         {
-            float plt = 1.f, pgt = 1.f;
+            float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, om[2];
 #pragma unroll
             for (int I2 = 0; I2 < NSB; ++I2) {
-                const float x = sm.bprod[I2][j];
-                if (I2 < I) plt *= x;
-                if (I2 > I) pgt *= x;
-            }
-            sm.plt[I][j] = plt;
-            if (I == 0) sm.gam[j] = bp * pgt;
-            E kt[SB];
-            float om = 1.f;   // product of f after tau to the sub-block end
 #pragma unroll
-            for (int tau = SB - 1; tau >= 0; --tau) {
-                const int t = SB * I + tau;
-                const float kf = rk.get(tau), qf = rq.get(tau);
-                sm.Ka[t * LD + j] = TR::cvt(kf * al[tau]);
-                sm.Qa[t * LD + j] = TR::cvt(qf * al[tau]);
-                sm.Kw[t * LD + j] = TR::cvt(kf * om);
-                sm.Ki[t * LD + j] = unsafe ? TR::cvt(0.f) : TR::cvt(kf * __builtin_amdgcn_rcpf(al[tau]));
-                sm.V[t * LD + j] = TR::cvt(rv.get(tau));
-                kt[tau] = TR::cvt(kf * (om * pgt));
-                om *= rf.get(tau);
-            }
-            if constexpr (sizeof(E) == 2) {
-                bf16x8* dst = reinterpret_cast<bf16x8*>(&sm.KtT[j * LDT + SB * I]);
-                bf16x8 lo, hi;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { lo[e] = kt[e]; hi[e] = kt[8 + e]; }
-                dst[0] = lo; dst[1] = hi;
-            } else {
-                floatx4* dst = reinterpret_cast<floatx4*>(&sm.KtT[j * LDT + SB * I]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    floatx4 x = {kt[4 * e], kt[4 * e + 1], kt[4 * e + 2], kt[4 * e + 3]};
-                    dst[e] = x;
+                for (int c = 0; c < 2; ++c) {
+                    const float x = sm.bprod[I2][j0 + c];
+                    if (I2 < I) plt[c] *= x;
+                    if (I2 > I) pgt[c] *= x;
                 }
             }
-            if (unsafe) {
-                // Exact contributions of this key channel to the diagonal tile of
-                // sub-block I: G_K[t,s] (s<t) at M[t][s]; P[t,s] (s<t) at M[s][t];
-                // P[t,t] at M[t][t].  Its Ki column is zero, so the MFMA path
-                // leaves this channel out of those tiles.  Rare path: the column
-                // is re-read from global memory (rows past T read as k=q=0, f=1).
-                const int t0 = n * CH + SB * I;
-                const uint32_t off = (uint32_t)t0 * rs + hoff + j;
+            if (hf == 0) {
+                sm.plt[I][j0] = plt[0]; sm.plt[I][j0 + 1] = plt[1];
+                if (I == 0) { sm.gam[j0] = bp[0] * pgt[0]; sm.gam[j0 + 1] = bp[1] * pgt[1]; }
+            }
+            // om: product of f after the row to the sub-block end
+            om[0] = hf ? 1.f : P1[0];
+            om[1] = hf ? 1.f : P1[1];
+            float kt[2][8];
+#pragma unroll
+            for (int m = 7; m >= 0; --m) {
+                const int t = SB * I + 8 * hf + m;
+                const bool in = m < nvalid;
+                float kf[2], qf[2], vf[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    kf[c] = in ? rk.get(m, c) : 0.f;
+                    qf[c] = in ? rq.get(m, c) : 0.f;
+                    vf[c] = in ? rv.get(m, c) : 0.f;
+                }
+                st2(&sm.Ka[t * LD + j0], kf[0] * al[m][0], kf[1] * al[m][1]);
+                st2(&sm.Qa[t * LD + j0], qf[0] * al[m][0], qf[1] * al[m][1]);
+                st2(&sm.Kw[t * LD + j0], kf[0] * om[0], kf[1] * om[1]);
+                st2(&sm.Ki[t * LD + j0],
+                    unsafe[0] ? 0.f : kf[0] * __builtin_amdgcn_rcpf(al[m][0]),
+                    unsafe[1] ? 0.f : kf[1] * __builtin_amdgcn_rcpf(al[m][1]));
+                st2(&sm.V[t * LD + j0], vf[0], vf[1]);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    kt[c][m] = kf[c] * (om[c] * pgt[c]);
+                    om[c] *= fget(m, c);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                E* dst = &sm.KtT[(j0 + c) * LDT + SB * I + 8 * hf];
+                if constexpr (sizeof(E) == 2) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) x[m] = (__bf16)kt[c][m];
+                    *reinterpret_cast<bf16x8*>(dst) = x;
+                } else {
+                    reinterpret_cast<floatx4*>(dst)[0] = floatx4{kt[c][0], kt[c][1], kt[c][2], kt[c][3]};
+                    reinterpret_cast<floatx4*>(dst)[1] = floatx4{kt[c][4], kt[c][5], kt[c][6], kt[c][7]};
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (hf == 0 && unsafe[c]) {
+                    // Exact contributions of key channel j0 + c to the diagonal tile
+                    // of sub-block I: G_K[t,s] (s<t) at M[t][s]; P[t,s] (s<t) at
+                    // M[s][t]; P[t,t] at M[t][t].  Its Ki column is zero, so the
+                    // MFMA path leaves this channel out of those tiles.  Rare path:
+                    // the column is re-read from global memory.
+                    const int t0 = n * CH + SB * I;
+                    const uint32_t off = (uint32_t)t0 * rs + hoff + j0 + c;
 #pragma unroll 1
-                for (int s = 0; s < SB; ++s) {
-                    if (t0 + s >= T) break;
-                    const float ks_ = TR::tof(kb[off + s * rs]);
-                    atomicAdd(&sm.M[(SB * I + s) * LDM + SB * I + s], TR::tof(qb[off + s * rs]) * ks_);
-                    float prod = 1.f;
+                    for (int s = 0; s < SB; ++s) {
+                        if (t0 + s >= T) break;
+                        const float ks_ = TR::tof(kb[off + s * rs]);
+                        atomicAdd(&sm.M[(SB * I + s) * LDM + SB * I + s], TR::tof(qb[off + s * rs]) * ks_);
+                        float prod = 1.f;
 #pragma unroll 1
-                    for (int t = s + 1; t < SB && t0 + t < T; ++t) {
-                        prod *= TR::tof(fb[off + t * rs]);
-                        atomicAdd(&sm.M[(SB * I + t) * LDM + SB * I + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
-                        atomicAdd(&sm.M[(SB * I + s) * LDM + SB * I + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
+                        for (int t = s + 1; t < SB && t0 + t < T; ++t) {
+                            prod *= TR::tof(fb[off + t * rs]);
+                            atomicAdd(&sm.M[(SB * I + t) * LDM + SB * I + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
+                            atomicAdd(&sm.M[(SB * I + s) * LDM + SB * I + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
+                        }
                     }
                 }
             }
-            if (tid < CH) sm.beta[tid] = rbc;
-            else if (tid < 2 * CH) sm.c[tid - CH] = rbc;
+            if (tid < 2 * CH) {
+                const bool in = n * CH + (tid & (CH - 1)) < T;
+                if (tid < CH) sm.beta[tid] = in ? rbc : 0.f;
+                else sm.c[tid - CH] = in ? rbc : 0.f;
+            }
         }
         if (n + 1 < NC) load_chunk(n + 1);
         lds_barrier();
 
+        KD_PHASE_MARK(n, 2);
         // ================= Gram tiles: M and P
         const unsigned umask = sm.unsafe_mask;
         for (int tile = w; tile < 10; tile += NW) {
@@ -244,14 +297,14 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             const int gap = I_ - J_;
 #pragma unroll 2
             for (int ks = 0; ks < KD_; ++ks) {
-                Frag fb = TR::ld_nat(bK, ks, g);
+                Frag fbk = TR::ld_nat(bK, ks, g);
                 if (gap >= 2) {
-                    fb = TR::scale_nat(fb, sm.bprod[J_ + 1], ks, g);
-                    if (gap == 3) fb = TR::scale_nat(fb, sm.bprod[J_ + 2], ks, g);
+                    fbk = TR::scale_nat(fbk, sm.bprod[J_ + 1], ks, g);
+                    if (gap == 3) fbk = TR::scale_nat(fbk, sm.bprod[J_ + 2], ks, g);
                 }
                 const Frag fv_ = TR::ld_nat(bV, ks, g);
-                gk = TR::mma(TR::ld_nat(aK, ks, g), fb, gk);
-                pp = TR::mma(TR::ld_nat(aQ, ks, g), fb, pp);
+                gk = TR::mma(TR::ld_nat(aK, ks, g), fbk, gk);
+                pp = TR::mma(TR::ld_nat(aQ, ks, g), fbk, pp);
                 gv = TR::mma(TR::ld_nat(aV, ks, g), fv_, gv);
             }
             const int s_ = SB * J_ + cl;
@@ -274,6 +327,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             }
         }
 
+        KD_PHASE_MARK(n, 3);
         // ================= state reads: Y = Kbar S0^T, O = Qbar S0^T
         floatx4 Y[NSB], Oa[NSB];
 #pragma unroll
@@ -311,6 +365,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         }
         lds_barrier();
 
+        KD_PHASE_MARK(n, 4);
         // ================= forward substitution (I + M) u = c - beta r0
         if (w == 0) {
             const int t_ = lane;
@@ -333,6 +388,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         }
         lds_barrier();
 
+        KD_PHASE_MARK(n, 5);
         // ================= O += P (u * V); state update
         {
             Frag bW[KC_];
@@ -362,6 +418,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             }
         }
         lds_barrier();
+        KD_PHASE_MARK(n, 6);
     }
 
     if (ST) {
