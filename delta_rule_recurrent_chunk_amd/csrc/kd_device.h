@@ -23,6 +23,7 @@ namespace kd {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;        // chunk length (tokens per chunk)
@@ -37,6 +38,31 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Maximum over the 64 lanes of a wave of non-negative floats (compared as
+// their bit patterns), returned wave-uniform.  DPP quad/mirror steps reduce
+// each row of 16 lanes, then the four row maxima are read out as scalars.
+#define KD_DPP_UMAX(x, ctrl) max((x), (unsigned)__builtin_amdgcn_mov_dpp((int)(x), (ctrl), 0xf, 0xf, false))
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    unsigned x = __float_as_uint(v);
+    x = KD_DPP_UMAX(x, 0xB1);    // quad_perm [1,0,3,2]
+    x = KD_DPP_UMAX(x, 0x4E);    // quad_perm [2,3,0,1]
+    x = KD_DPP_UMAX(x, 0x141);   // row_half_mirror
+    x = KD_DPP_UMAX(x, 0x140);   // row_mirror
+    const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)x, 0);
+    const unsigned r1 = (unsigned)__builtin_amdgcn_readlane((int)x, 16);
+    const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)x, 32);
+    const unsigned r3 = (unsigned)__builtin_amdgcn_readlane((int)x, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+#undef KD_DPP_UMAX
+
+// 2^-e for the exponent e of x (x = m 2^e, 0.5 <= m < 1): scales x into
+// [0.5, 1).  Returns 1 for x == 0 (or non-finite x).
+__device__ __forceinline__ float pow2_scale(float x) {
+    if (!(x > 0.f) || !(x < 3.0e38f)) return 1.f;
+    return ldexpf(1.f, -__builtin_amdgcn_frexp_expf(x));
 }
 
 // ---------------------------------------------------------------- bf16 path
@@ -63,39 +89,52 @@ struct Bf16T {
         bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // B operand from accumulator tiles holding X[j][n] (j = 16mt + 4g + r),
-    // each K row j scaled by sc[j] (fp32, before rounding to bf16).
-    static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks, const float* sc, int g) {
-        const floatx4 s0 = *reinterpret_cast<const floatx4*>(sc + KS * ks + 4 * g);
-        const floatx4 s1 = *reinterpret_cast<const floatx4*>(sc + KS * ks + 16 + 4 * g);
-        const floatx4 a = acc[2 * ks] * s0;
-        const floatx4 b = acc[2 * ks + 1] * s1;
+    // B operand from accumulator tiles holding X[j][n] (j = 16mt + 4g + r):
+    // K-step ks takes tiles 2ks and 2ks+1, already in the "state" K order.
+    static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
+        const floatx4 a = acc[2 * ks];
+        const floatx4 b = acc[2 * ks + 1];
         Frag r;
         r[0] = cvt(a[0]); r[1] = cvt(a[1]); r[2] = cvt(a[2]); r[3] = cvt(a[3]);
         r[4] = cvt(b[0]); r[5] = cvt(b[1]); r[6] = cvt(b[2]); r[7] = cvt(b[3]);
         return r;
     }
-    // natural-order fragment scaled element-wise by sc[K] (K = 32ks + 8g + e)
-    static __device__ __forceinline__ Frag scale_nat(Frag x, const float* sc, int ks, int g) {
-        const floatx4 s0 = *reinterpret_cast<const floatx4*>(sc + KS * ks + 8 * g);
-        const floatx4 s1 = *reinterpret_cast<const floatx4*>(sc + KS * ks + 8 * g + 4);
-        Frag r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = cvt(tof(x[e]) * s0[e]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[4 + e] = cvt(tof(x[4 + e]) * s1[e]);
-        return r;
-    }
-    // natural-order fragment along K = token index t: value(t) = u[t] * col[t*ld]
-    static __device__ __forceinline__ Frag col_times(const E* col, int ld, const float* u, int ks, int g) {
+    // natural-order fragment along K = token index t from a row that is
+    // contiguous in t, each element scaled by u[t]
+    static __device__ __forceinline__ Frag row_times(const E* row, const float* u, int ks, int g) {
         const int t0 = KS * ks + 8 * g;
+        const Frag x = *reinterpret_cast<const Frag*>(row + t0);
         const floatx4 u0 = *reinterpret_cast<const floatx4*>(u + t0);
         const floatx4 u1 = *reinterpret_cast<const floatx4*>(u + t0 + 4);
         Frag r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = cvt(u0[e] * tof(col[(t0 + e) * ld]));
+        for (int e = 0; e < 4; ++e) r[e] = cvt(u0[e] * tof(x[e]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[4 + e] = cvt(u1[e] * tof(col[(t0 + 4 + e) * ld]));
+        for (int e = 0; e < 4; ++e) r[4 + e] = cvt(u1[e] * tof(x[4 + e]));
+        return r;
+    }
+
+    // State update operands in fp16 (11-bit mantissa; values pre-scaled by
+    // exact powers of two so they stay inside fp16's range).
+    typedef _Float16 H;
+    typedef halfx8 FragH;
+    static __device__ __forceinline__ floatx4 mma_h(FragH a, FragH b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ FragH ld_nat_h(const H* row, int ks, int g) {
+        return *reinterpret_cast<const FragH*>(row + KS * ks + 8 * g);
+    }
+    static __device__ __forceinline__ FragH row_times_h(const E* row, const float* u, float su,
+                                                        int ks, int g) {
+        const int t0 = KS * ks + 8 * g;
+        const Frag x = *reinterpret_cast<const Frag*>(row + t0);
+        const floatx4 u0 = *reinterpret_cast<const floatx4*>(u + t0);
+        const floatx4 u1 = *reinterpret_cast<const floatx4*>(u + t0 + 4);
+        FragH r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (_Float16)((u0[e] * su) * tof(x[e]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 + e] = (_Float16)((u1[e] * su) * tof(x[4 + e]));
         return r;
     }
 };
@@ -120,50 +159,119 @@ struct F32T {
     static __device__ __forceinline__ Frag ld_state(const E* row, int ks, int g) {
         return row[16 * (ks >> 2) + 4 * g + (ks & 3)];
     }
-    static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks, const float* sc, int g) {
-        return acc[ks >> 2][ks & 3] * sc[16 * (ks >> 2) + 4 * g + (ks & 3)];
+    static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
+        return acc[ks >> 2][ks & 3];
     }
-    static __device__ __forceinline__ Frag scale_nat(Frag x, const float* sc, int ks, int g) {
-        return x * sc[KS * ks + g];
-    }
-    static __device__ __forceinline__ Frag col_times(const E* col, int ld, const float* u, int ks, int g) {
+    static __device__ __forceinline__ Frag row_times(const E* row, const float* u, int ks, int g) {
         const int t = KS * ks + g;
-        return u[t] * col[t * ld];
+        return u[t] * row[t];
+    }
+    typedef float H;
+    typedef float FragH;
+    static __device__ __forceinline__ floatx4 mma_h(FragH a, FragH b, floatx4 c) { return mma(a, b, c); }
+    static __device__ __forceinline__ FragH ld_nat_h(const H* row, int ks, int g) { return ld_nat(row, ks, g); }
+    static __device__ __forceinline__ FragH row_times_h(const E* row, const float* u, float su,
+                                                        int ks, int g) {
+        const int t = KS * ks + g;
+        return (u[t] * su) * row[t];
     }
 };
 
-// Eight consecutive tokens of two adjacent channels (j0 = even, j0 + 1) held
-// in registers between the global load and its use (the prefetch buffer).
-// One 32-bit load fetches both bf16 channels of a row.
-template <class TR> struct Pair8;
+// Two consecutive tokens of eight adjacent channels (16-byte aligned group
+// ch0 .. ch0 + 7), held in registers between the global load and its use
+// (the prefetch buffer).  One 16-byte load per row for bf16.
+template <class TR> struct Row2x8;
 
-template <> struct Pair8<Bf16T> {
-    uint32_t w[8];   // low half: channel j0, high half: channel j0 + 1
-    // p: wave-uniform base; row m at p[off + min(m, last)*stride] (32-bit
-    // element offsets, off even).  Loads are unconditional: rows past the
-    // sequence end re-read row `last` (in bounds) and are masked at use.
-    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int last) {
+template <> struct Row2x8<Bf16T> {
+    uint4 w[2];   // row e, channels 2i (low half) and 2i + 1 (high half) in w[e][i]
+    // p: wave-uniform base; row e at element offset off_e (32-bit).
+    __device__ __forceinline__ void load(const __bf16* p, uint32_t off0, uint32_t off1) {
+        const char* base = reinterpret_cast<const char*>(p);
+        w[0] = *reinterpret_cast<const uint4*>(base + off0 * 2u);
+        w[1] = *reinterpret_cast<const uint4*>(base + off1 * 2u);
+    }
+    __device__ __forceinline__ uint32_t word(int e, int i) const {
+        return i == 0 ? w[e].x : i == 1 ? w[e].y : i == 2 ? w[e].z : w[e].w;
+    }
+    __device__ __forceinline__ float get(int e, int c) const {
+        const uint32_t x = word(e, c >> 1);
+        return __uint_as_float((c & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    // row e becomes `fill` (0 or 1; exact in bf16)
+    __device__ __forceinline__ void clear(int e, float fill) {
+        const uint32_t fb = __float_as_uint(fill) >> 16;
+        const uint32_t x = fb | (fb << 16);
+        w[e] = make_uint4(x, x, x, x);
+    }
+    __device__ __forceinline__ void store(__bf16* dst, int e) const {
+        *reinterpret_cast<uint4*>(dst) = w[e];
+    }
+};
+
+template <> struct Row2x8<F32T> {
+    floatx4 w[2][2];
+    __device__ __forceinline__ void load(const float* p, uint32_t off0, uint32_t off1) {
+        const char* base = reinterpret_cast<const char*>(p);
+        w[0][0] = *reinterpret_cast<const floatx4*>(base + off0 * 4u);
+        w[0][1] = *reinterpret_cast<const floatx4*>(base + off0 * 4u + 16u);
+        w[1][0] = *reinterpret_cast<const floatx4*>(base + off1 * 4u);
+        w[1][1] = *reinterpret_cast<const floatx4*>(base + off1 * 4u + 16u);
+    }
+    __device__ __forceinline__ float get(int e, int c) const { return w[e][c >> 2][c & 3]; }
+    __device__ __forceinline__ void clear(int e, float fill) {
+        w[e][0] = floatx4{fill, fill, fill, fill};
+        w[e][1] = w[e][0];
+    }
+    __device__ __forceinline__ void store(float* dst, int e) const {
+        reinterpret_cast<floatx4*>(dst)[0] = w[e][0];
+        reinterpret_cast<floatx4*>(dst)[1] = w[e][1];
+    }
+};
+
+// Products over the eight lanes l & 7 = 0..7 of each aligned 8-lane group:
+// inclusive prefix product of x in lane order (DPP row shifts, masked at the
+// group boundary).
+template <int S>
+__device__ __forceinline__ float dpp_row_shr(float x) {   // lane i <- lane i-S of its 16-lane row (1 if none)
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x),
+                                                      0x110 + S, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float group8_prefix_prod(float x, int r8) {
+    float y = dpp_row_shr<1>(x);
+    x = (r8 >= 1) ? x * y : x;
+    y = dpp_row_shr<2>(x);
+    x = (r8 >= 2) ? x * y : x;
+    y = dpp_row_shr<4>(x);
+    x = (r8 >= 4) ? x * y : x;
+    return x;
+}
+// Value of x in the previous lane of the 8-lane group (1 for the first lane).
+__device__ __forceinline__ float group8_shift1(float x, int r8) {
+    const float y = dpp_row_shr<1>(x);
+    return r8 >= 1 ? y : 1.f;
+}
+
+// Store eight values as one 16-byte row segment.
+__device__ __forceinline__ void st8v(__bf16* p, const float* x) {
+    bf16x8 r;
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            w[m] = *reinterpret_cast<const uint32_t*>(p + off + (uint32_t)(m < last ? m : last) * stride);
-    }
-    __device__ __forceinline__ float get(int m, int c) const {
-        return __uint_as_float(c ? (w[m] & 0xffff0000u) : (w[m] << 16));
-    }
-};
-
-template <> struct Pair8<F32T> {
-    float w[8][2];
-    __device__ __forceinline__ void load(const float* p, uint32_t off, uint32_t stride, int last) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float2 x = *reinterpret_cast<const float2*>(p + off + (uint32_t)(m < last ? m : last) * stride);
-            w[m][0] = x.x;
-            w[m][1] = x.y;
-        }
-    }
-    __device__ __forceinline__ float get(int m, int c) const { return w[m][c]; }
-};
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+    *reinterpret_cast<bf16x8*>(p) = r;
+}
+__device__ __forceinline__ void st8v(float* p, const float* x) {
+    reinterpret_cast<floatx4*>(p)[0] = floatx4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<floatx4*>(p)[1] = floatx4{x[4], x[5], x[6], x[7]};
+}
+// Store two consecutive values (a transposed-array entry pair).
+__device__ __forceinline__ void st2h(_Float16* p, float a, float b) {
+    _Float16 __attribute__((ext_vector_type(2))) x;
+    x[0] = (_Float16)a;
+    x[1] = (_Float16)b;
+    *reinterpret_cast<decltype(x)*>(p) = x;
+}
+__device__ __forceinline__ void st2h(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
 
 // Store two adjacent channels' values (as the path's element type).
 __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
@@ -174,6 +282,23 @@ __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
 }
 __device__ __forceinline__ void st2(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+// Store eight consecutive values (16 bytes of bf16 / 32 bytes of fp32).
+__device__ __forceinline__ void st8(__bf16* p, const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+    *reinterpret_cast<bf16x8*>(p) = r;
+}
+__device__ __forceinline__ void st8(_Float16* p, const float* x) {
+    halfx8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
+    *reinterpret_cast<halfx8*>(p) = r;
+}
+__device__ __forceinline__ void st8(float* p, const float* x) {
+    reinterpret_cast<floatx4*>(p)[0] = floatx4{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<floatx4*>(p)[1] = floatx4{x[4], x[5], x[6], x[7]};
 }
 
 // Number of MFMA K-steps of each path that cover a contraction of length n.
