@@ -273,6 +273,125 @@ __device__ __forceinline__ void st2h(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
 
+// Four consecutive tokens of eight adjacent channels (16-byte aligned group
+// ch0 .. ch0 + 7): the producer's prefetch buffer.  One 16-byte load per row
+// for bf16.
+template <class TR> struct Raw4x8;
+
+template <> struct Raw4x8<Bf16T> {
+    uint4 w[4];   // row e: channels 2i (low half) and 2i + 1 (high half) in word i
+    // p: wave-uniform base; row e at 32-bit element offset off + min(e, last)*stride.
+    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int last) {
+        const char* base = reinterpret_cast<const char*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = *reinterpret_cast<const uint4*>(base + (off + (uint32_t)(e < last ? e : last) * stride) * 2u);
+    }
+    __device__ __forceinline__ uint32_t word(int e, int i) const {
+        return i == 0 ? w[e].x : i == 1 ? w[e].y : i == 2 ? w[e].z : w[e].w;
+    }
+    __device__ __forceinline__ float get(int e, int c) const {
+        const uint32_t x = word(e, c >> 1);
+        return __uint_as_float((c & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    __device__ __forceinline__ void clear(int e, float fill) {
+        const uint32_t fb = __float_as_uint(fill) >> 16;
+        const uint32_t x = fb | (fb << 16);
+        w[e] = make_uint4(x, x, x, x);
+    }
+    __device__ __forceinline__ void store(__bf16* dst, int e) const {
+        *reinterpret_cast<uint4*>(dst) = w[e];
+    }
+};
+
+template <> struct Raw4x8<F32T> {
+    floatx4 w[4][2];
+    __device__ __forceinline__ void load(const float* p, uint32_t off, uint32_t stride, int last) {
+        const char* base = reinterpret_cast<const char*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t b = (off + (uint32_t)(e < last ? e : last) * stride) * 4u;
+            w[e][0] = *reinterpret_cast<const floatx4*>(base + b);
+            w[e][1] = *reinterpret_cast<const floatx4*>(base + b + 16u);
+        }
+    }
+    __device__ __forceinline__ float get(int e, int c) const { return w[e][c >> 2][c & 3]; }
+    __device__ __forceinline__ void clear(int e, float fill) {
+        w[e][0] = floatx4{fill, fill, fill, fill};
+        w[e][1] = w[e][0];
+    }
+    __device__ __forceinline__ void store(float* dst, int e) const {
+        reinterpret_cast<floatx4*>(dst)[0] = w[e][0];
+        reinterpret_cast<floatx4*>(dst)[1] = w[e][1];
+    }
+};
+
+// Four consecutive values of one channel, held from the producer's prep until
+// they are written as one 8-byte (bf16/fp16) or 16-byte (fp32) transposed
+// entry.
+template <class T> struct Col4;
+template <> struct Col4<__bf16> {
+    uint32_t w[2];
+    __device__ __forceinline__ void set(const float* x) {
+        bf16x2 a, b;
+        a[0] = (__bf16)x[0]; a[1] = (__bf16)x[1];
+        b[0] = (__bf16)x[2]; b[1] = (__bf16)x[3];
+        w[0] = __builtin_bit_cast(uint32_t, a);
+        w[1] = __builtin_bit_cast(uint32_t, b);
+    }
+    __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]); }
+};
+template <> struct Col4<_Float16> {
+    uint32_t w[2];
+    __device__ __forceinline__ void set(const float* x) {
+        _Float16 __attribute__((ext_vector_type(2))) a, b;
+        a[0] = (_Float16)x[0]; a[1] = (_Float16)x[1];
+        b[0] = (_Float16)x[2]; b[1] = (_Float16)x[3];
+        w[0] = __builtin_bit_cast(uint32_t, a);
+        w[1] = __builtin_bit_cast(uint32_t, b);
+    }
+    __device__ __forceinline__ void store(_Float16* p) const { *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]); }
+};
+template <> struct Col4<float> {
+    floatx4 w;
+    __device__ __forceinline__ void set(const float* x) { w = floatx4{x[0], x[1], x[2], x[3]}; }
+    __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<floatx4*>(p) = w; }
+};
+
+// Store four consecutive fp32 values in the path's element type.
+__device__ __forceinline__ void st4(__bf16* p, floatx4 x) {
+    bf16x4 r;
+    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+    *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void st4(float* p, floatx4 x) { *reinterpret_cast<floatx4*>(p) = x; }
+
+// Quad (4-lane group) scans of products, r4 = lane & 3.
+template <int CTRL>
+__device__ __forceinline__ float dpp_quad(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x),
+                                                      CTRL, 0xf, 0xf, false));
+}
+// exclusive prefix product (product over lanes r' < r4; 1 for r4 = 0) and the
+// exclusive suffix product (product over lanes r' > r4; 1 for r4 = 3)
+// Every DPP move is issued by all four lanes before any lane-dependent select:
+// a move placed under a condition becomes a branch, and a lane masked off by
+// that branch cannot be read.
+__device__ __forceinline__ void quad_excl_prod(float x, int r4, float& pre, float& suf) {
+    const float x1 = dpp_quad<0x90>(x);                  // quad_perm [0,0,1,2]
+    const float y1 = dpp_quad<0xF9>(x);                  // quad_perm [1,2,3,3]
+    const float a1 = (r4 >= 1) ? x * x1 : x;             // product of lanes r4-1 .. r4
+    const float b1 = (r4 <= 2) ? x * y1 : x;             // product of lanes r4 .. r4+1
+    const float x2 = dpp_quad<0x40>(a1);                 // quad_perm [0,0,0,1]
+    const float y2 = dpp_quad<0xFE>(b1);                 // quad_perm [2,3,3,3]
+    const float a2 = (r4 >= 2) ? a1 * x2 : a1;           // inclusive prefix
+    const float b2 = (r4 <= 1) ? b1 * y2 : b1;           // inclusive suffix
+    const float x3 = dpp_quad<0x90>(a2);
+    const float y3 = dpp_quad<0xF9>(b2);
+    pre = (r4 >= 1) ? x3 : 1.f;
+    suf = (r4 <= 2) ? y3 : 1.f;
+}
+
 // Store two adjacent channels' values (as the path's element type).
 __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
     bf16x2 x;

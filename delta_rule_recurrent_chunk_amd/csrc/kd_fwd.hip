@@ -19,29 +19,35 @@
 //     S_C = S0 diag(gamma_C) + (u * V)^T (K * gamma_C/gamma).
 //
 // MI355X design
-//  * One workgroup per (b, h); 4*d threads = d/16 waves; the chunk loop runs
-//    inside the kernel, so the fp32 state never leaves the chip.  The state is
-//    held TRANSPOSED (S^T, key index j as rows) as MFMA accumulators, wave w
-//    owning value columns i in [16w, 16w + 16).  In that orientation the
-//    accumulator registers are directly the B operand of both products that
-//    read the state (O_inter = Qbar S0^T and Y = Kbar S0^T), so the state needs
-//    no LDS round trip.
+//  * One workgroup per (b, h), 4*d threads = d/16 waves, chunk loop inside
+//    the kernel.  The waves split into two teams that run a software pipeline
+//    over chunks, so matrix-core work of one chunk overlaps the vector work of
+//    the next:
+//      consumers (waves 0 .. d/32-1) own the fp32 state, TRANSPOSED (S^T, key
+//        index j as rows) as MFMA accumulators, 32 value columns per wave.
+//        Accumulator registers are directly an MFMA operand of the state reads
+//        (Y^T = S Kbar^T, O^T = S Qbar^T), so the state never goes through LDS.
+//        They do the state reads, the forward substitution (one wave) and the
+//        readout and state update of chunk n.
+//      producers (the other half) load chunk n+1 from HBM, fold the decay into
+//        the operands and build its Gram tiles M, P on MFMA.
+//    Per iteration: stage A (consumer: state reads n | producer: transposed
+//    operands of n, decay scans of n+1) -- stage B (consumer: substitution n |
+//    producer: operands of n+1, loads of n+2) -- stage C (consumer: readout
+//    and update n | producer: Gram of n+1), one barrier after each stage.
 //  * Decay folding: Qbar = q*gamma, Kbar = k*gamma and Kc = k/gamma are the
-//    MFMA operands of every Gram tile and of the state reads (one operand set,
-//    no per-tile rescaling).  Kc needs gamma >= 2^-100; a key channel whose
-//    decay over the chunk falls below that has its Kc column zeroed and its
-//    Gram terms accumulated exactly by a scalar fallback, so every input in
-//    [0, 1] is handled exactly.  K * gamma_C/gamma is built from suffix
-//    products, which never divide.
-//  * Per chunk: prep (decay products, operands into LDS) -> Gram tiles and
-//    state reads (MFMA) -> forward substitution (one wave, lane t owns row t,
-//    readlane broadcast) -> O and state update (MFMA).  The next chunk's
-//    global loads are issued right after the prep so they overlap the MFMA
-//    phases; O leaves through LDS as full 16-byte row segments.
+//    MFMA operands of every Gram tile and of the state reads.  Kc needs
+//    gamma >= 2^-100; a key channel whose decay over the chunk falls below
+//    that has its Kc column zeroed and its Gram terms accumulated exactly by a
+//    scalar fallback, so every input in [0, 1] is handled exactly.
+//    K * gamma_C/gamma comes from suffix products and never divides.
+//  * Precision: Grams and state reads take bf16 operands; the rank-64 state
+//    update takes fp16 operands with exact power-of-two scales (max |k|,
+//    max |u| * max |v| per chunk), its accumulation is fp32.
 #include "kd_device.h"
 
 // Phase markers: no-ops here; a profiling build may define them to record
-// timestamps at the phase boundaries of the chunk loop.
+// timestamps at the stage boundaries of the chunk loop.
 #ifndef KD_PHASE_MARK
 #define KD_PHASE_MARK(chunk, id) ((void)0)
 #endif
@@ -53,28 +59,28 @@ constexpr float kSafeFloor = 7.888609052210118e-31f;  // 2^-100
 template <class TR, int D>
 struct FwdSmem {
     typedef typename TR::E E;
+    typedef typename TR::H Hh;
     static constexpr int LD = D + TR::PAD;     // row-major [CH][D] arrays
     static constexpr int LDT = CH + TR::PAD;   // transposed [D][CH] arrays
     static constexpr int LDM = CH + 4;         // fp32 M
     static constexpr int LDP = CH + TR::PAD;   // P
-    alignas(16) E Qb[CH * LD];     // q * gamma
+    static constexpr int NWC = D / 32;         // consumer waves
+    alignas(16) E Qb[CH * LD];     // q * gamma                     (chunk n+1 from stage B)
     alignas(16) E Kb[CH * LD];     // k * gamma
-    alignas(16) E Kc[CH * LD];     // k / gamma (0 for fallback channels); O staging after the Gram
+    alignas(16) E Kc[CH * LD];     // k / gamma, 0 for fallback channels
     alignas(16) E V[CH * LD];      // v
-    alignas(16) E VT[D * LDT];     // v^T
-    alignas(16) typename TR::H KtT[D * LDT];   // (k * gamma_C / gamma)^T * kscale (state-update precision)
+    alignas(16) E VT[D * LDT];     // v^T                           (chunk n from stage A)
+    alignas(16) Hh KtT[D * LDT];   // (k gamma_C / gamma)^T * kscale
     alignas(16) float M[CH * LDM]; // beta_t tril_{-1}(G_K * G_V); fallback scratch
-    alignas(16) E P[CH * LDP];     // tril_0 of the decayed Q K^T
-    alignas(16) float beta[CH];
-    alignas(16) float c[CH];
+    alignas(16) E P[2][CH * LDP];  // tril_0 of the decayed Q K^T, by chunk parity
+    alignas(16) float beta[2][CH];
+    alignas(16) float c[2][CH];
     alignas(16) float u[CH];
-    alignas(16) float r0p[D / 16][CH];
+    alignas(16) float r0p[NWC][CH];
     alignas(16) float bprod[NSB][D];   // product of f over each 16-token sub-block
-    alignas(16) float gam[D];          // gamma_C
-    unsigned unsafe_any;
-    unsigned kmax_bits;                // max |k| over the chunk (fp32 bits)
-    unsigned vmax_bits[2];             // max |v| over the chunk (fp32 bits), by chunk parity
-    unsigned umax_bits;                // max |u| over the chunk (fp32 bits)
+    alignas(16) float gam[2][D];       // gamma_C, by chunk parity
+    unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
+    unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
 template <class TR, int D>
@@ -86,25 +92,22 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     float* __restrict__ ckpt, int T, int H)
 {
     typedef typename TR::E E;
+    typedef typename TR::H Hh;
     typedef typename TR::Frag Frag;
+    typedef typename TR::FragH FragH;
     typedef FwdSmem<TR, D> SM;
     constexpr int NT = 4 * D;
-    constexpr int NW = D / 16;
-    constexpr int KD_ = D / TR::KS;   // K-steps over a d-long contraction
-    constexpr int KC_ = CH / TR::KS;  // K-steps over a chunk-long contraction
+    constexpr int NWC = SM::NWC;       // consumer waves (32 value columns each)
+    constexpr int NWP = D / 32;        // producer waves
+    constexpr int KD_ = D / TR::KS;    // K-steps over a d-long contraction
+    constexpr int KC_ = CH / TR::KS;   // K-steps over a chunk-long contraction
     constexpr int LD = SM::LD, LDT = SM::LDT, LDM = SM::LDM, LDP = SM::LDP;
-    constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
 
     __shared__ SM sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
-    // prep ownership: rows row0, row0 + 1 of the chunk and channels ch0 .. ch0+7;
-    // the eight row pairs of a 16-row sub-block sit in one aligned 8-lane group.
-    const int r8 = lane & 7;
-    const int qd = w * 8 + (lane >> 3);
-    const int I = qd / (D / 8), ch0 = 8 * (qd % (D / 8));
-    const int row0 = SB * I + 2 * r8;
+    const bool consumer = w < NWC;
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     // Per batch element, every [T, H, D] tensor is addressed from a wave-uniform
     // base with 32-bit element offsets (the host checks T*H*D fits).
@@ -115,371 +118,408 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const E* vb = v + bbase;
     const E* fb = f + bbase;
     E* ob = o ? o + bbase : nullptr;
-    const float* gsrc = (tid < CH ? beta : cc) + (size_t)b * T * H;
     const uint32_t hoff = (uint32_t)h * D;
     const int NC = (T + CH - 1) / CH;
 
-    // ---- one-time init
-    for (int x = tid; x < CH * LDP; x += NT) sm.P[x] = TR::cvt(0.f);
+    // ---- producer ownership: rows rb .. rb+3 of sub-block I, channels ch0 .. ch0+7;
+    // the four row quads of a (sub-block, channel group) are one lane quad.
+    const int ptid = tid - NWC * 64;
+    const int r4 = lane & 3;
+    const int pq = (w - NWC) * 16 + (lane >> 2);
+    const int I = pq / (D / 8), ch0 = 8 * (pq % (D / 8));
+    const int rb = SB * I + 4 * r4;
+    // ---- consumer ownership: value columns 32w .. 32w+31
+    const int i0 = 32 * w;
+
+    // ---- one-time init: the upper triangles of M and P are never written
+    for (int x = tid; x < 2 * CH * LDP; x += NT) (&sm.P[0][0])[x] = TR::cvt(0.f);
+    for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
     if (tid == 0) {
-        sm.unsafe_any = 0u; sm.kmax_bits = 0u; sm.umax_bits = 0u;
-        sm.vmax_bits[0] = 0u; sm.vmax_bits[1] = 0u;
+        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; sm.unsafe[s] = 0u; }
+        sm.umax = 0u;
     }
 
-    floatx4 S[D / 16];   // S^T[16mt + 4g + r][16w + cl]
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[mt][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mt + 4 * g + r] : 0.f;
-
-    // ---- prefetch registers (rows row0, row0 + 1; channels ch0 .. ch0 + 7)
-    Row2x8<TR> rq, rk, rv, rf;
-    float rbc = 0.f;
-    auto load_chunk = [&](int n) {
-        // Rows past the sequence end re-read the last row (in bounds) and are
-        // cleared in the prep (q = k = v = 0, f = 1, beta = c = 0).
-        const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
-        const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob2 = (uint32_t)tb * rs + hoff + ch0;
-        rq.load(qb, oa, ob2);
-        rk.load(kb, oa, ob2);
-        rv.load(vb, oa, ob2);
-        rf.load(fb, oa, ob2);
-        if (tid < 2 * CH) {
-            const int t = min(n * CH + (tid & (CH - 1)), T - 1);
-            rbc = gsrc[(uint32_t)t * H + h];
-        }
-    };
-    // Coalesced output of a staged O tile (rows in sm.Kc).
-    auto store_o = [&](int n) {
-        constexpr int VPR = D / EPV;   // 16-byte vectors per row
-        for (int x = tid; x < CH * VPR; x += NT) {
-            const int t = x / VPR, cv = x % VPR;
-            const int tg = n * CH + t;
-            if (tg < T)
-                *reinterpret_cast<uint4*>(ob + (uint32_t)tg * rs + hoff + cv * EPV) =
-                    *reinterpret_cast<const uint4*>(&sm.Kc[t * LD + cv * EPV]);
-        }
-    };
-    if (NC > 0) load_chunk(0);
     lds_barrier();
 
-    for (int n = 0; n < NC; ++n) {
-        if (ckpt) {   // chunk-start state, stored as S[i][j]
-            float* dst = ckpt + ((size_t)bh * NC + n) * D * D;
+    // Both teams run the same loop of barriers: one per stage plus two more in
+    // a stage C whose next chunk takes the exact fallback (the flag is read by
+    // every wave).  Each team's registers live only in its own loop.
+    if (consumer) {
+        floatx4 S[2][D / 16];   // S^T[16mj + 4g + r][i0 + 16nt + cl] in S[nt][mj]
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt)
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mj = 0; mj < D / 16; ++mj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    dst[(size_t)(16 * w + cl) * D + 16 * mt + 4 * g + r] = S[mt][r];
-        }
-        KD_PHASE_MARK(n, 0);
-        if (n > 0 && ob) store_o(n - 1);   // previous chunk's O, staged in Kc
-        // ================= prep (a): decay products within the sub-block
-        if (n * CH + CH > T) {   // ragged last chunk: clear rows past the end
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                if (n * CH + row0 + e >= T) {
-                    rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f);
-                }
-            if (tid < 2 * CH && n * CH + (tid & (CH - 1)) >= T) rbc = 0.f;
-        }
-        float incl[8], excl[8];   // products of f from the sub-block start through row0+1 / before row0
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            incl[c] = group8_prefix_prod(rf.get(0, c) * rf.get(1, c), r8);
-            excl[c] = group8_shift1(incl[c], r8);
-        }
-        if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);   // sub-block products
-        {   // chunk max |k| and |v|: exact power-of-two scales of the fp16
-            // state-update operands
-            float km = 0.f, vm = 0.f;
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    km = fmaxf(km, fabsf(rk.get(e, c)));
-                    vm = fmaxf(vm, fabsf(rv.get(e, c)));
-                }
-            km = wave_max_nonneg(km);
-            vm = wave_max_nonneg(vm);
-            if (lane == 0) {   // non-negative floats order like their bit patterns
-                atomicMax(&sm.kmax_bits, __float_as_uint(km));
-                atomicMax(&sm.vmax_bits[n & 1], __float_as_uint(vm));
-            }
-        }
-        // clear M: it doubles as the scratch of the exact fallback
-        for (int x = tid; x < CH * LDM / 4; x += NT)
-            reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-        lds_barrier();
+                    S[nt][mj][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] : 0.f;
 
-        KD_PHASE_MARK(n, 1);
-        // ================= prep (b): operands into LDS
-        float ksc;            // 2^-e scaling the chunk's max |k| into [0.5, 1)
-        unsigned unsafe = 0;  // bit c: channel ch0 + c decays below the floor in this chunk
-        {
-            float plt[8], gC[8];
+        for (int n = -1; n < NC; ++n) {
+            const int nn = n + 1;
+            // ======================================================= stage A
+            KD_PHASE_MARK(n, 0);
+            floatx4 Ot[2][NSB];   // O^T[i0 + 16mt + 4g + r][16tt + cl], lives to stage C
+            if (n >= 0) {
+                if (ckpt) {   // chunk-start state, stored as S[i][j]
+                    float* dst = ckpt + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; }
+                    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int I2 = 0; I2 < NSB; ++I2) {
+                        for (int mj = 0; mj < D / 16; ++mj)
 #pragma unroll
-                for (int c4 = 0; c4 < 2; ++c4) {
-                    const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
+                            for (int r = 0; r < 4; ++r)
+                                dst[(size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] = S[nt][mj][r];
+                }
+                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
+                floatx4 Yt[2][NSB];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gC[4 * c4 + e] *= x[e];
-                        if (I2 < I) plt[4 * c4 + e] *= x[e];
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) {
+                        Yt[mt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        Ot[mt][tt] = Yt[mt][tt];
+                    }
+#pragma unroll
+                for (int ks = 0; ks < KD_; ++ks) {
+                    const Frag a0 = TR::state_frag(S[0], ks);
+                    const Frag a1 = TR::state_frag(S[1], ks);
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) {
+                        const Frag bk = TR::ld_state(&sm.Kb[(SB * tt + cl) * LD], ks, g);
+                        const Frag bq = TR::ld_state(&sm.Qb[(SB * tt + cl) * LD], ks, g);
+                        Yt[0][tt] = TR::mma(a0, bk, Yt[0][tt]);
+                        Yt[1][tt] = TR::mma(a1, bk, Yt[1][tt]);
+                        Ot[0][tt] = TR::mma(a0, bq, Ot[0][tt]);
+                        Ot[1][tt] = TR::mma(a1, bq, Ot[1][tt]);
                     }
                 }
-            }
+                // partial r0[t] = sum over this wave's 32 value columns of Y[t,i] v[t,i]
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (!(gC[c] >= kSafeFloor)) unsafe |= 1u << c;
-            if (I == 0 && r8 == 0) st8v(&sm.gam[ch0], gC);
-            if (unsafe) atomicOr(&sm.unsafe_any, 1u);
-            ksc = pow2_scale(__uint_as_float(sm.kmax_bits));
-            float kt[2][8], vt[2][8];
+                for (int tt = 0; tt < NSB; ++tt) {
+                    float x = 0.f;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float qo[8], ko[8], co[8];
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const E* vr = &sm.V[(SB * tt + cl) * LD + i0 + 16 * mt + 4 * g];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float ga = plt[c] * (e == 0 ? excl[c] * rf.get(0, c) : incl[c]);
-                    const float kf = rk.get(e, c), qf = rq.get(e, c);
-                    const float kr = kf * __builtin_amdgcn_rcpf(ga);
-                    const bool un = (unsafe >> c) & 1u;
-                    qo[c] = qf * ga;
-                    ko[c] = kf * ga;
-                    co[c] = un ? 0.f : kr;
-                    kt[e][c] = un ? 0.f : kr * (gC[c] * ksc);   // fallback channels: filled in later
-                    vt[e][c] = rv.get(e, c);
+                        for (int r = 0; r < 4; ++r) x += Yt[mt][tt][r] * TR::tof(vr[r]);
+                    }
+                    x += __shfl_xor(x, 16, 64);
+                    x += __shfl_xor(x, 32, 64);
+                    if (g == 0) sm.r0p[w][SB * tt + cl] = x;
                 }
-                st8v(&sm.Qb[(row0 + e) * LD + ch0], qo);
-                st8v(&sm.Kb[(row0 + e) * LD + ch0], ko);
-                st8v(&sm.Kc[(row0 + e) * LD + ch0], co);
-                rv.store(&sm.V[(row0 + e) * LD + ch0], e);
             }
+            lds_barrier();
+            // ======================================================= stage B
+            KD_PHASE_MARK(n, 1);
+            if (n >= 0 && w == 0) {   // forward substitution (I + M) u = c - beta r0
+                const int t_ = lane;
+                float r0 = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                st2h(&sm.KtT[(ch0 + c) * LDT + row0], kt[0][c], kt[1][c]);
-                st2(&sm.VT[(ch0 + c) * LDT + row0], vt[0][c], vt[1][c]);
+                for (int ww = 0; ww < NWC; ++ww) r0 += sm.r0p[ww][t_];
+                float x = sm.c[n & 1][t_] - sm.beta[n & 1][t_] * r0;
+                float Mrow[CH];
+#pragma unroll
+                for (int s4 = 0; s4 < CH / 4; ++s4) {
+                    const floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t_ * LDM + 4 * s4]);
+                    Mrow[4 * s4] = m4[0]; Mrow[4 * s4 + 1] = m4[1]; Mrow[4 * s4 + 2] = m4[2]; Mrow[4 * s4 + 3] = m4[3];
+                }
+                // M is strictly lower triangular (zeros elsewhere), so the update
+                // needs no lane mask: lane t only changes while s < t.
+#pragma unroll
+                for (int s = 0; s < CH - 1; ++s) x = fmaf(-Mrow[s], readlane_f(x, s), x);
+                sm.u[t_] = x;
+                const float um = wave_max_nonneg(fabsf(x));
+                if (lane == 0) sm.umax = __float_as_uint(um);
             }
-            if (I == 0 && r8 == 0 && unsafe) {
-                // Exact Gram terms of a key channel whose chunk decay is below the
-                // floor (its Kc column is zero, so the MFMA tiles leave it out):
-                // G_K[t,s] (s<t) accumulates at M[t][s], P[t,s] (s<t) at M[s][t],
-                // P[t,t] at M[t][t].  Rare path: rows are re-read from global memory.
-                const int t0 = n * CH;
-#pragma unroll 1
-                for (int c = 0; c < 8; ++c) {
-                    if (!((unsafe >> c) & 1u)) continue;
-                    const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
-#pragma unroll 1
-                    for (int s = 0; s < CH && t0 + s < T; ++s) {
-                        const float ks_ = TR::tof(kb[off + s * rs]);
-                        atomicAdd(&sm.M[s * LDM + s], TR::tof(qb[off + s * rs]) * ks_);
-                        float prod = 1.f;
-#pragma unroll 1
-                        for (int t = s + 1; t < CH && t0 + t < T; ++t) {
-                            prod *= TR::tof(fb[off + t * rs]);
-                            atomicAdd(&sm.M[t * LDM + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
-                            atomicAdd(&sm.M[s * LDM + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
+            if (tid == 0 && n >= 0) {
+                // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
+                // the previous stage C, the latter's first writer runs in stage A(n+1)
+                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
+            }
+            lds_barrier();
+            // ======================================================= stage C
+            KD_PHASE_MARK(n, 2);
+            if (nn < NC && sm.unsafe[nn % 3] != 0u) {   // producers run the exact fallback
+                lds_barrier();
+                lds_barrier();
+            }
+            if (n >= 0) {   // readout and state update of chunk n
+                const float usc = pow2_scale(__uint_as_float(sm.umax) * __uint_as_float(sm.vmax[n % 3]));
+                const float ksc = pow2_scale(__uint_as_float(sm.kmax[n % 3]));
+                const float inv = 1.f / (usc * ksc);
+                // O^T += W^T P^T with W = u * V (bf16), then O leaves as 8-byte rows
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks) {
+                        const Frag wa = TR::row_times(&sm.VT[(i0 + 16 * mt + cl) * LDT], sm.u, ks, g);
+#pragma unroll
+                        for (int tt = 0; tt < NSB; ++tt)
+                            Ot[mt][tt] = TR::mma(wa, TR::ld_nat(&sm.P[n & 1][(SB * tt + cl) * LDP], ks, g), Ot[mt][tt]);
+                    }
+                }
+                if (ob) {
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) {
+                        const int t = n * CH + SB * tt + cl;
+                        if (t < T) {
+#pragma unroll
+                            for (int mt = 0; mt < 2; ++mt)
+                                st4(ob + (uint32_t)t * rs + hoff + i0 + 16 * mt + 4 * g, Ot[mt][tt]);
                         }
                     }
                 }
+                // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact powers of 2)
+                FragH wb[2][KC_];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks)
+                        wb[nt][ks] = TR::row_times_h(&sm.VT[(i0 + 16 * nt + cl) * LDT], sm.u, usc, ks, g);
+#pragma unroll
+                for (int mj = 0; mj < D / 16; ++mj) {
+                    const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc);
+                    S[0][mj] = S[0][mj] * gm;
+                    S[1][mj] = S[1][mj] * gm;
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks) {
+                        const FragH ak = TR::ld_nat_h(&sm.KtT[(16 * mj + cl) * LDT], ks, g);
+                        S[0][mj] = TR::mma_h(ak, wb[0][ks], S[0][mj]);
+                        S[1][mj] = TR::mma_h(ak, wb[1][ks], S[1][mj]);
+                    }
+                    S[0][mj] = S[0][mj] * inv;
+                    S[1][mj] = S[1][mj] * inv;
+                }
             }
-            if (tid < CH) sm.beta[tid] = rbc;
-            else if (tid < 2 * CH) sm.c[tid - CH] = rbc;
+            lds_barrier();
         }
-        lds_barrier();
+        if (ST) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int mj = 0; mj < D / 16; ++mj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] = S[nt][mj][r];
+        }
+    } else {
+        Raw4x8<TR> rq, rk, rv, rf;          // raw rows of the chunk being prepared
+        float rb_beta = 0.f, rb_c = 0.f;    // beta_t, c_t for t = ptid (ptid < CH)
+        float apre[4][8], asuf[4][8];       // within-thread prefix (incl.) / suffix (excl.) products of f
+        float qpre[8], qsuf[8];             // products over the lane quad's earlier / later rows
+        Col4<E> keep_v[8];                  // v and K-tilde of the prepared chunk, written
+        Col4<Hh> keep_kt[8];                //   transposed in the following stage A
+        unsigned pmask = 0;                 // fallback channels (bit c: ch0 + c) of the prepared chunk
+        auto load_chunk = [&](int n) {
+            // Rows past the sequence end re-read the last row (in bounds) and are
+            // cleared before use (q = k = v = 0, f = 1, beta = c = 0).
+            const int t0 = min(n * CH + rb, T - 1);
+            const int last = min(3, T - 1 - t0);
+            const uint32_t off = (uint32_t)t0 * rs + hoff + ch0;
+            rq.load(qb, off, rs, last);
+            rk.load(kb, off, rs, last);
+            rv.load(vb, off, rs, last);
+            rf.load(fb, off, rs, last);
+            if (ptid < CH) {
+                const int t = min(n * CH + ptid, T - 1);
+                const size_t gi = ((size_t)b * T + t) * H + h;
+                rb_beta = beta[gi];
+                rb_c = cc[gi];
+            }
+        };
+        if (NC > 0) load_chunk(0);
 
-        KD_PHASE_MARK(n, 2);
-        // ================= Gram tiles: M and P
-        const bool fallback = sm.unsafe_any != 0u;
-        if (I == 0 && r8 == 0 && unsafe) {
-            // K-tilde of the fallback channels by suffix products (no division);
-            // read only after two more barriers.
-            const int t0 = n * CH;
+        for (int n = -1; n < NC; ++n) {
+            const int nn = n + 1;             // chunk the producers prepare
+            const bool prod_on = nn < NC;
+            // ======================================================= stage A
+            if (n >= 0) {   // transposed operands of chunk n
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    keep_v[c].store(&sm.VT[(ch0 + c) * LDT + rb]);
+                    keep_kt[c].store(&sm.KtT[(ch0 + c) * LDT + rb]);
+                }
+            }
+            if (prod_on) {   // decay scans of chunk nn
+                if (nn * CH + CH > T) {   // ragged last chunk: clear rows past the end
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (nn * CH + rb + e >= T) {
+                            rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f);
+                        }
+                    if (ptid < CH && nn * CH + ptid >= T) { rb_beta = 0.f; rb_c = 0.f; }
+                }
+                float tot[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    apre[0][c] = rf.get(0, c);
+#pragma unroll
+                    for (int e = 1; e < 4; ++e) apre[e][c] = apre[e - 1][c] * rf.get(e, c);
+                    asuf[3][c] = 1.f;
+#pragma unroll
+                    for (int e = 2; e >= 0; --e) asuf[e][c] = asuf[e + 1][c] * rf.get(e + 1, c);
+                    tot[c] = apre[3][c];
+                    quad_excl_prod(tot[c], r4, qpre[c], qsuf[c]);
+                }
+                if (r4 == 3) {
+                    float sb[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) sb[c] = qpre[c] * tot[c];
+                    st8v(&sm.bprod[I][ch0], sb);   // sub-block products
+                }
+                float km = 0.f, vm = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        km = fmaxf(km, fabsf(rk.get(e, c)));
+                        vm = fmaxf(vm, fabsf(rv.get(e, c)));
+                    }
+                km = wave_max_nonneg(km);
+                vm = wave_max_nonneg(vm);
+                if (lane == 0) {   // non-negative floats order like their bit patterns
+                    atomicMax(&sm.kmax[nn % 3], __float_as_uint(km));
+                    atomicMax(&sm.vmax[nn % 3], __float_as_uint(vm));
+                }
+                if (ptid < CH) {
+                    sm.beta[nn & 1][ptid] = rb_beta;
+                    sm.c[nn & 1][ptid] = rb_c;
+                }
+            }
+            lds_barrier();
+            // ======================================================= stage B
+            if (prod_on) {   // operands of chunk nn into LDS
+                float plt[8], pgt[8], gC[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) { plt[c] = 1.f; pgt[c] = 1.f; }
+#pragma unroll
+                for (int I2 = 0; I2 < NSB; ++I2) {
+#pragma unroll
+                    for (int c4 = 0; c4 < 2; ++c4) {
+                        const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (I2 < I) plt[4 * c4 + e] *= x[e];
+                            if (I2 > I) pgt[4 * c4 + e] *= x[e];
+                        }
+                    }
+                }
+                pmask = 0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    // gamma_C = (earlier sub-blocks) (this sub-block) (later ones)
+                    gC[c] = plt[c] * (qpre[c] * apre[3][c] * qsuf[c]) * pgt[c];
+                    if (!(gC[c] >= kSafeFloor)) pmask |= 1u << c;
+                }
+                if (I == 0 && r4 == 0) st8v(&sm.gam[nn & 1][ch0], gC);
+                if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
+                const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
+                float vcol[8][4], kcol[8][4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float qo[8], ko[8], co[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const float ga = plt[c] * qpre[c] * apre[e][c];           // gamma at row rb+e
+                        const float om = asuf[e][c] * qsuf[c] * pgt[c];           // gamma_C / gamma
+                        const float kf = rk.get(e, c), qf = rq.get(e, c);
+                        qo[c] = qf * ga;
+                        ko[c] = kf * ga;
+                        co[c] = ((pmask >> c) & 1u) ? 0.f : kf * __builtin_amdgcn_rcpf(ga);
+                        kcol[c][e] = (kf * ksc) * om;
+                        vcol[c][e] = rv.get(e, c);
+                    }
+                    st8v(&sm.Qb[(rb + e) * LD + ch0], qo);
+                    st8v(&sm.Kb[(rb + e) * LD + ch0], ko);
+                    st8v(&sm.Kc[(rb + e) * LD + ch0], co);
+                    rv.store(&sm.V[(rb + e) * LD + ch0], e);
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    keep_v[c].set(vcol[c]);
+                    keep_kt[c].set(kcol[c]);
+                }
+                if (nn + 1 < NC) load_chunk(nn + 1);
+            }
+            lds_barrier();
+            // ======================================================= stage C
+            const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
+            if (fallback) {
+                // Exact Gram terms of key channels of chunk nn whose decay is below
+                // the floor (their Kc columns are zero, so the MFMA tiles leave them
+                // out): G_K[t,s] (s<t) accumulates at M[t][s], P[t,s] (s<t) at
+                // M[s][t], P[t,t] at M[t][t].  Rare path: rows are re-read from
+                // global memory.
+                for (int x = ptid; x < CH * LDM / 4; x += NT - NWC * 64)
+                    reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+                lds_barrier();
+                if (I == 0 && r4 == 0 && pmask) {
+                    const int t0 = nn * CH;
 #pragma unroll 1
-            for (int c = 0; c < 8; ++c) {
-                if (!((unsafe >> c) & 1u)) continue;
-                const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
-                float suf = 1.f;
+                    for (int c = 0; c < 8; ++c) {
+                        if (!((pmask >> c) & 1u)) continue;
+                        const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
 #pragma unroll 1
-                for (int t = CH - 1; t >= 0; --t) {
-                    if (t0 + t < T) {
-                        sm.KtT[(ch0 + c) * LDT + t] = (typename TR::H)(TR::tof(kb[off + t * rs]) * ksc * suf);
-                        suf *= TR::tof(fb[off + t * rs]);
+                        for (int s = 0; s < CH && t0 + s < T; ++s) {
+                            const float ks_ = TR::tof(kb[off + s * rs]);
+                            atomicAdd(&sm.M[s * LDM + s], TR::tof(qb[off + s * rs]) * ks_);
+                            float prod = 1.f;
+#pragma unroll 1
+                            for (int t = s + 1; t < CH && t0 + t < T; ++t) {
+                                prod *= TR::tof(fb[off + t * rs]);
+                                atomicAdd(&sm.M[t * LDM + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
+                                atomicAdd(&sm.M[s * LDM + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
+                            }
+                        }
+                    }
+                }
+                lds_barrier();
+            }
+            if (prod_on) {   // Gram tiles of chunk nn: M and P
+                for (int tile = w - NWC; tile < 10; tile += NWP) {
+                    // lower-triangular tile list (I_, J_), I_ >= J_
+                    const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+                    const int J_ = tile - (I_ * (I_ + 1)) / 2;
+                    floatx4 gk = {0.f, 0.f, 0.f, 0.f}, pp = gk, gv = gk;
+                    const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
+                    const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
+                    const E* aV = &sm.V[(SB * I_ + cl) * LD];
+                    const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
+                    const E* bV = &sm.V[(SB * J_ + cl) * LD];
+#pragma unroll
+                    for (int ks = 0; ks < KD_; ++ks) {
+                        const Frag fk = TR::ld_nat(bK, ks, g);
+                        gk = TR::mma(TR::ld_nat(aK, ks, g), fk, gk);
+                        pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, pp);
+                        gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), gv);
+                    }
+                    const int s_ = SB * J_ + cl;
+                    if (fallback) {
+                        float ck[4], cp[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t_ = SB * I_ + 4 * g + r;
+                            ck[r] = (s_ < t_) ? sm.M[t_ * LDM + s_] : 0.f;
+                            cp[r] = (s_ <= t_) ? sm.M[s_ * LDM + t_] : 0.f;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            gk[r] += ck[r];
+                            pp[r] += cp[r];
+                            const int t_ = SB * I_ + 4 * g + r;
+                            if (I_ != J_) sm.M[s_ * LDM + t_] = 0.f;   // mirror upper tile back to zero
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t_ = SB * I_ + 4 * g + r;
+                        sm.M[t_ * LDM + s_] = (s_ < t_) ? sm.beta[nn & 1][t_] * gk[r] * gv[r] : 0.f;
+                        sm.P[nn & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
                     }
                 }
             }
+            lds_barrier();
         }
-        // Reset the other parity's max |v|: its last reader (the previous chunk's
-        // update) finished before the prep barriers, its next writer (the next
-        // chunk's prep) comes after this chunk's closing barrier.
-        if (tid == 0) sm.vmax_bits[(n + 1) & 1] = 0u;
-        for (int tile = w; tile < 10; tile += NW) {
-            // lower-triangular tile list (I_, J_), I_ >= J_
-            const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-            const int J_ = tile - (I_ * (I_ + 1)) / 2;
-            floatx4 gk = {0.f, 0.f, 0.f, 0.f}, pp = gk, gv = gk;
-            const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
-            const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
-            const E* aV = &sm.V[(SB * I_ + cl) * LD];
-            const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
-            const E* bV = &sm.V[(SB * J_ + cl) * LD];
-#pragma unroll
-            for (int ks = 0; ks < KD_; ++ks) {
-                const Frag fk = TR::ld_nat(bK, ks, g);
-                gk = TR::mma(TR::ld_nat(aK, ks, g), fk, gk);
-                pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, pp);
-                gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), gv);
-            }
-            const int s_ = SB * J_ + cl;
-            if (fallback) {
-                float ck[4], cp[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t_ = SB * I_ + 4 * g + r;
-                    ck[r] = (s_ < t_) ? sm.M[t_ * LDM + s_] : 0.f;
-                    cp[r] = (s_ <= t_) ? sm.M[s_ * LDM + t_] : 0.f;
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    gk[r] += ck[r];
-                    pp[r] += cp[r];
-                    const int t_ = SB * I_ + 4 * g + r;
-                    if (I_ != J_) sm.M[s_ * LDM + t_] = 0.f;   // mirror upper tile back to zero
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t_ = SB * I_ + 4 * g + r;
-                sm.M[t_ * LDM + s_] = (s_ < t_) ? sm.beta[t_] * gk[r] * gv[r] : 0.f;
-                sm.P[t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
-            }
-        }
-
-        KD_PHASE_MARK(n, 3);
-        // ================= state reads: Y = Kbar S0^T, O = Qbar S0^T
-        floatx4 Y[NSB], Oa[NSB];
-#pragma unroll
-        for (int I_ = 0; I_ < NSB; ++I_) { Y[I_] = floatx4{0.f, 0.f, 0.f, 0.f}; Oa[I_] = Y[I_]; }
-#pragma unroll
-        for (int ks = 0; ks < KD_; ++ks) {
-            const Frag bS = TR::state_frag(S, ks);
-#pragma unroll
-            for (int I_ = 0; I_ < NSB; ++I_) {
-                Y[I_] = TR::mma(TR::ld_state(&sm.Kb[(SB * I_ + cl) * LD], ks, g), bS, Y[I_]);
-                Oa[I_] = TR::mma(TR::ld_state(&sm.Qb[(SB * I_ + cl) * LD], ks, g), bS, Oa[I_]);
-            }
-        }
-        // partial r0[t] = sum over this wave's 16 value columns of Y[t,i] v[t,i]
-        {
-            float x[16];
-#pragma unroll
-            for (int I_ = 0; I_ < NSB; ++I_)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[4 * I_ + r] = Y[I_][r] * TR::tof(sm.V[(SB * I_ + 4 * g + r) * LD + 16 * w + cl]);
-            // butterfly reduce-scatter over the 16 lanes of a row group: lane cl
-            // ends with the full sum of entry cl.
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) {
-                const bool up = (cl & m) != 0;
-#pragma unroll
-                for (int e = 0; e < m; ++e) {
-                    const float send = up ? x[e] : x[e + m];
-                    const float keep = up ? x[e + m] : x[e];
-                    x[e] = keep + __shfl_xor(send, m, 64);
-                }
-            }
-            sm.r0p[w][SB * (cl >> 2) + 4 * g + (cl & 3)] = x[0];
-        }
-        lds_barrier();
-
-        KD_PHASE_MARK(n, 4);
-        // ================= forward substitution (I + M) u = c - beta r0
-        // The next chunk's loads are issued where each wave is otherwise idle:
-        // waves 1.. while wave 0 solves, wave 0 right after.  Issue stalls
-        // while HBM drains the requests then cost no compute time.
-        if (w != 0 && n + 1 < NC) load_chunk(n + 1);
-        if (w == 0) {
-            const int t_ = lane;
-            float r0 = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) r0 += sm.r0p[ww][t_];
-            float x = sm.c[t_] - sm.beta[t_] * r0;
-            float Mrow[CH];
-#pragma unroll
-            for (int s4 = 0; s4 < CH / 4; ++s4) {
-                const floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t_ * LDM + 4 * s4]);
-                Mrow[4 * s4] = m4[0]; Mrow[4 * s4 + 1] = m4[1]; Mrow[4 * s4 + 2] = m4[2]; Mrow[4 * s4 + 3] = m4[3];
-            }
-            // M is strictly lower triangular (zeros elsewhere), so the update
-            // needs no lane mask: lane t only changes while s < t.
-#pragma unroll
-            for (int s = 0; s < CH - 1; ++s) x = fmaf(-Mrow[s], readlane_f(x, s), x);
-            sm.u[t_] = x;
-            const float um = wave_max_nonneg(fabsf(x));
-            if (lane == 0) {
-                sm.umax_bits = __float_as_uint(um);
-                // all reads of these flags for this chunk are done (prep b, Gram)
-                sm.unsafe_any = 0u;
-                sm.kmax_bits = 0u;
-            }
-            if (n + 1 < NC) load_chunk(n + 1);
-        }
-        lds_barrier();
-
-        KD_PHASE_MARK(n, 5);
-        // ================= O += P (u * V); state update
-        {
-            // Scales of the fp16 state-update operands (exact powers of two).
-            const float usc = pow2_scale(__uint_as_float(sm.umax_bits) * __uint_as_float(sm.vmax_bits[n & 1]));
-            const float inv = 1.f / (usc * ksc);
-            Frag bW[KC_];
-#pragma unroll
-            for (int ks = 0; ks < KC_; ++ks) bW[ks] = TR::row_times(&sm.VT[(16 * w + cl) * LDT], sm.u, ks, g);
-#pragma unroll
-            for (int I_ = 0; I_ < NSB; ++I_)
-#pragma unroll
-                for (int ks = 0; ks < KC_; ++ks)
-                    Oa[I_] = TR::mma(TR::ld_nat(&sm.P[(SB * I_ + cl) * LDP], ks, g), bW[ks], Oa[I_]);
-            if (ob) {   // stage O in the (now free) Kc array
-#pragma unroll
-                for (int I_ = 0; I_ < NSB; ++I_)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sm.Kc[(SB * I_ + 4 * g + r) * LD + 16 * w + cl] = TR::cvt(Oa[I_][r]);
-            }
-            typename TR::FragH hW[KC_];
-#pragma unroll
-            for (int ks = 0; ks < KC_; ++ks)
-                hW[ks] = TR::row_times_h(&sm.VT[(16 * w + cl) * LDT], sm.u, usc, ks, g);
-            // S <- (S diag(gamma_C) * s + K~'^T W') / s with s = usc * ksc
-#pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[16 * mt + 4 * g]);
-                S[mt] = S[mt] * (gm * (usc * ksc));
-#pragma unroll
-                for (int ks = 0; ks < KC_; ++ks)
-                    S[mt] = TR::mma_h(TR::ld_nat_h(&sm.KtT[(16 * mt + cl) * LDT], ks, g), hW[ks], S[mt]);
-                S[mt] = S[mt] * inv;
-            }
-        }
-        lds_barrier();
-        KD_PHASE_MARK(n, 6);
-    }
-    if (NC > 0 && ob) store_o(NC - 1);
-
-    if (ST) {
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ST[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mt + 4 * g + r] = S[mt][r];
     }
 }
 
