@@ -131,6 +131,13 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     // ---- consumer ownership: value columns 32w .. 32w+31
     const int i0 = 32 * w;
 
+    if (NC == 0) {   // empty sequence: S_T = S0
+        if (ST)
+            for (int x = tid; x < D * D; x += NT)
+                ST[(size_t)bh * D * D + x] = S0 ? S0[(size_t)bh * D * D + x] : 0.f;
+        return;
+    }
+
     // ---- one-time init: the upper triangles of M and P are never written
     for (int x = tid; x < 2 * CH * LDP; x += NT) (&sm.P[0][0])[x] = TR::cvt(0.f);
     for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     if (g == 0) sm.r0p[w][SB * tt + cl] = x;
                 }
             }
+            KD_PHASE_MARK(n, 3);
             lds_barrier();
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
@@ -236,6 +244,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 // the previous stage C, the latter's first writer runs in stage A(n+1)
                 sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
             }
+            KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
@@ -291,6 +300,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     S[1][mj] = S[1][mj] * inv;
                 }
             }
+            KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
         if (ST) {
@@ -305,7 +315,6 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     } else {
         Raw4x8<TR> rq, rk, rv, rf;          // raw rows of the chunk being prepared
         float rb_beta = 0.f, rb_c = 0.f;    // beta_t, c_t for t = ptid (ptid < CH)
-        float apre[4][8], asuf[4][8];       // within-thread prefix (incl.) / suffix (excl.) products of f
         float qpre[8], qsuf[8];             // products over the lane quad's earlier / later rows
         Col4<E> keep_v[8];                  // v and K-tilde of the prepared chunk, written
         Col4<Hh> keep_kt[8];                //   transposed in the following stage A
@@ -320,19 +329,21 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             rk.load(kb, off, rs, last);
             rv.load(vb, off, rs, last);
             rf.load(fb, off, rs, last);
-            if (ptid < CH) {
-                const int t = min(n * CH + ptid, T - 1);
-                const size_t gi = ((size_t)b * T + t) * H + h;
-                rb_beta = beta[gi];
-                rb_c = cc[gi];
-            }
+            // every lane loads (lanes past the first wave re-read its tokens), so
+            // the prefetch registers are never merged with older values: a merge
+            // makes the compiler copy them and wait for the loads right away
+            const int t = min(n * CH + (ptid & (CH - 1)), T - 1);
+            const uint32_t gi = ((uint32_t)t * H + h);
+            rb_beta = beta[(size_t)b * T * H + gi];
+            rb_c = cc[(size_t)b * T * H + gi];
         };
-        if (NC > 0) load_chunk(0);
+        load_chunk(0);
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
             const bool prod_on = nn < NC;
             // ======================================================= stage A
+            KD_PHASE_MARK(n, 0);
             if (n >= 0) {   // transposed operands of chunk n
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
@@ -352,13 +363,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 float tot[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    apre[0][c] = rf.get(0, c);
-#pragma unroll
-                    for (int e = 1; e < 4; ++e) apre[e][c] = apre[e - 1][c] * rf.get(e, c);
-                    asuf[3][c] = 1.f;
-#pragma unroll
-                    for (int e = 2; e >= 0; --e) asuf[e][c] = asuf[e + 1][c] * rf.get(e + 1, c);
-                    tot[c] = apre[3][c];
+                    tot[c] = (rf.get(0, c) * rf.get(1, c)) * (rf.get(2, c) * rf.get(3, c));
                     quad_excl_prod(tot[c], r4, qpre[c], qsuf[c]);
                 }
                 if (r4 == 3) {
@@ -386,8 +391,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     sm.c[nn & 1][ptid] = rb_c;
                 }
             }
+            KD_PHASE_MARK(n, 3);
             lds_barrier();
             // ======================================================= stage B
+            KD_PHASE_MARK(n, 1);
             if (prod_on) {   // operands of chunk nn into LDS
                 float plt[8], pgt[8], gC[8];
 #pragma unroll
@@ -403,6 +410,18 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                             if (I2 > I) pgt[4 * c4 + e] *= x[e];
                         }
                     }
+                }
+                // within-thread products of f over this thread's four rows:
+                // apre[e] over rows 0..e, asuf[e] over rows e+1..3
+                float apre[4][8], asuf[4][8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    apre[0][c] = rf.get(0, c);
+#pragma unroll
+                    for (int e = 1; e < 4; ++e) apre[e][c] = apre[e - 1][c] * rf.get(e, c);
+                    asuf[3][c] = 1.f;
+#pragma unroll
+                    for (int e = 2; e >= 0; --e) asuf[e][c] = asuf[e + 1][c] * rf.get(e + 1, c);
                 }
                 pmask = 0;
 #pragma unroll
@@ -439,10 +458,13 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     keep_v[c].set(vcol[c]);
                     keep_kt[c].set(kcol[c]);
                 }
-                if (nn + 1 < NC) load_chunk(nn + 1);
             }
+            // unconditional, clamped to the last chunk (see load_chunk)
+            load_chunk(min(nn + 1, NC - 1));
+            KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
+            KD_PHASE_MARK(n, 2);
             const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
             if (fallback) {
                 // Exact Gram terms of key channels of chunk nn whose decay is below
@@ -518,6 +540,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     }
                 }
             }
+            KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
     }
