@@ -29,7 +29,40 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "Kron-delta chunked fwd tokens/s (H=16,d=128) and % MFMA/HBM roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kd_fwd_train_step_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kd_fwd_train_step_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "delta_rule_recurrent_chunk_amd", "csrc", n)
+                  for n in ("kd_fwd.hip", "kd_device.h")]
+COPY_ELEMS = 1 << 28     # calibration copy: 2^28 fp32 = 1 GiB read and 1 GiB written
+
+
+def kernel_source_hash():
+    """sha256 over the forward kernel's sources, to tell whether stored counter
+    figures still describe the kernel that runs."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(w, esize, with_S0=False):
@@ -87,18 +120,20 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time launches after evicting the caches with a 1 GiB write")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain 1 GiB device-to-device copy (reference for HBM "
-                         "byte counters) and exit")
+                    help="run only a plain elementwise copy kernel (1 GiB read, 1 GiB written; "
+                         "the reference for the HBM byte counters) three times and exit")
     args = ap.parse_args()
 
     if args.copy_calibration:
         import torch
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        src = torch.empty(COPY_ELEMS, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30}))
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # one elementwise kernel per call
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": COPY_ELEMS * 4,
+                          "copy_bytes_written_per_launch": COPY_ELEMS * 4}))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,11 +182,7 @@ def main():
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
     flops = mfma_flops(w)
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE) and args.workload == "train_step":
-        with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
-        traffic = tr.get("hbm_bytes_per_launch")
+    traffic = stored_traffic() if args.workload == "train_step" else None
 
     out = {
         "metric": METRIC,
