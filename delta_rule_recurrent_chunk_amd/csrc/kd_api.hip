@@ -10,7 +10,7 @@
 namespace kd {
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      float* ckpt, int B, int T, int H, hipStream_t st);
+                      void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st);
 hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, const void* dO,
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
@@ -104,7 +104,7 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
     hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
-                                  nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+                                  nullptr, nullptr, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 
@@ -115,6 +115,8 @@ kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const v
                          size_t ws_bytes, void* stream) {
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
+    // the chunk-local backward kernel holds its fp32 operands in LDS only up to d = 32
+    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
     const size_t gb = ntok * sizeof(float);

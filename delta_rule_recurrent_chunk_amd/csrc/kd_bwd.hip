@@ -1,18 +1,827 @@
-// kd_bwd.hip -- gate-aware chunkwise backward (placeholder until the kernel lands).
+// kd_bwd.hip -- gate-aware chunkwise backward of the Kronecker delta rule, gfx950.
+//
+// Reverse mode of the chunked forward (the forward kernel's header gives the
+// chunk algebra; the pages are the onedev.kr KronLSTM summary, sections
+// "어떻게 동작하나" and "어떻게 쓰나", and the aitrends.kr Gated DeltaNet-2
+// summary, sections "방법론" steps 3-4 and "핵심 기여", which names a
+// gate-aware backward through the WY form).  Per chunk, with dS the gradient
+// of the state leaving the chunk and drho = (I + M)^{-T} du:
+//   du   = rowsum((P^T dO + Kt dS^T) * V)            (Kt = K gamma_C / gamma)
+//   dS0  = dS diag(gamma_C) + dO^T Qbar + V^T diag(dr0) Kbar,  dr0 = -beta * drho
+//   dM   = -drho u^T (strictly lower), dGK = beta dM * GV, dGV = beta dM * GK
+//   dV   = diag(u) (P^T dO + Kt dS^T) + (dGV + dGV^T) V + diag(dr0) Kbar S0^T
+//   dKbar = dGK Kc + diag(dr0) V S0,   dKc = dGK^T Kbar + dP^T Qbar,
+//   dQbar = dO S0 + dP Kc,   dKt = W dS,   dP = tril_0(dO W^T),  W = u * V
+//   dbeta = -r0 drho + rowsum(dM * GK * GV),   dc = drho
+// and the decay enters through g = d/d(log gamma):
+//   g_t = dQbar Qbar + dKbar Kbar - dKc Kc - dKt Kt,
+//   g_C = gamma_C colsum(dS * S0) + sum_t dKt Kt,
+//   d log f_s = sum_{t >= s} g_t + g_C,   df = d log f / f.
+//
+// Three launches on the caller's stream:
+//   1. the forward kernel with checkpoints: per chunk the entering state (in
+//      the input dtype, as S[i][j] and S^T[j][i]) and u, r0;
+//   2. kd_bwd_state_kernel: one workgroup per (b, h), chunks in reverse, the
+//      fp32 dS^T held as MFMA accumulators (the mirror of the forward state):
+//      state read, back substitution, rank-128 update; stores dS and drho;
+//   3. kd_bwd_chunk_kernel: one workgroup per (b, h, chunk), all chunks in
+//      parallel: every local gradient.
+// A chunk with a key channel whose decay over the chunk falls below 2^-100
+// (the forward's exact-fallback case, which includes f = 0) is not handled
+// here: all its gradients are NaN, and so is every gradient that depends on
+// it through the state gradient (dk, dv, df, dbeta, dc of the earlier chunks
+// of that (b, h), and dS0); dq of the earlier chunks does not and stays exact.
 #include "kd_device.h"
 
 namespace kd {
 
-size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H) {
-    (void)bf16;
+hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                      const float* beta, const float* c, const float* S0, void* o, float* ST,
+                      void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st);
+
+// Workspace: [S0 checkpoints | u, r0 | dS per chunk | drho], 256-byte aligned parts.
+struct BwdWs {
+    size_t s0, ur, ds, rho, total;
+};
+static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     const size_t nc = (size_t)(T + CH - 1) / CH;
-    return (size_t)B * H * nc * d * d * sizeof(float);
+    const size_t units = (size_t)B * H * nc;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    BwdWs w;
+    w.s0 = 0;
+    w.ur = up(units * 2 * d * d * esz);
+    w.ds = w.ur + up(units * 2 * CH * sizeof(float));
+    w.rho = w.ds + up(units * 2 * d * d * esz);
+    w.total = w.rho + up(units * CH * sizeof(float));
+    return w;
 }
 
-hipError_t launch_bwd(int, int, const void*, const void*, const void*, const void*, const float*,
-                      const float*, const float*, const void*, const float*, void*, void*, void*,
-                      void*, float*, float*, float*, void*, int, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H) {
+    return bwd_ws_layout(bf16 ? 2 : 4, d, B, T, H).total;
+}
+
+// Common prep of both backward kernels: thread owns rows row0, row0 + 1 of the
+// chunk and channels ch0 .. ch0 + 7 (the eight row pairs of a 16-row
+// sub-block sit in one aligned 8-lane group).
+struct PrepIdx {
+    int r8, I, ch0, row0;
+    __device__ PrepIdx(int tid, int D) {
+        const int lane = tid & 63, w = tid >> 6;
+        r8 = lane & 7;
+        const int qd = w * 8 + (lane >> 3);
+        I = qd / (D / 8);
+        ch0 = 8 * (qd % (D / 8));
+        row0 = SB * I + 2 * r8;
+    }
+};
+
+// ======================================================================
+// Serial dS recurrence
+// ======================================================================
+template <class TR, int D>
+struct BwdStateSmem {
+    typedef typename TR::E E;
+    static constexpr int LD = D + TR::PAD;     // [CH][D] row-major operands
+    static constexpr int LDT = CH + TR::PAD;   // [D][CH] transposed operands
+    static constexpr int LDM = CH + 4;         // fp32 M
+    static constexpr int LDP = CH + TR::PAD;
+    static constexpr int NW = D / 16;
+    static constexpr size_t KCB = (size_t)CH * LD * sizeof(E);
+    static constexpr size_t MB = (size_t)CH * LDM * sizeof(float);
+    alignas(16) E Qb[CH * LD];                        // q gamma for the Gram, then K-tilde
+    alignas(16) E Kb[CH * LD];                        // k gamma
+    alignas(16) unsigned char KcM[KCB > MB ? KCB : MB];   // k / gamma for the Gram, then M (fp32)
+    alignas(16) E V[CH * LD];
+    alignas(16) E VT[D * LDT];                        // v^T
+    alignas(16) E OT[D * LDT];                        // dO^T
+    alignas(16) E QT[D * LDT];                        // (q gamma)^T
+    alignas(16) E KT[D * LDT];                        // (k gamma)^T
+    alignas(16) E PT[CH * LDP];                       // PT[s][t] = P[t][s]
+    alignas(16) float beta[CH];
+    alignas(16) float dr0[CH];
+    alignas(16) float dup[NW][CH];                    // partial du per wave
+    alignas(16) float bprod[NSB][D];
+    alignas(16) float gam[D];
+    unsigned unsafe_any;
+};
+
+template <class TR, int D>
+__global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
+    const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
+    const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
+    const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const float* __restrict__ dST, typename TR::E* __restrict__ wsdS, float* __restrict__ wsrho,
+    float* __restrict__ dS0, int T, int H)
+{
+    typedef typename TR::E E;
+    typedef typename TR::Frag Frag;
+    typedef BwdStateSmem<TR, D> SM;
+    constexpr int NT = 4 * D;
+    constexpr int NW = SM::NW;
+    constexpr int KD_ = D / TR::KS;
+    constexpr int KC_ = CH / TR::KS;
+    constexpr int LD = SM::LD, LDT = SM::LDT, LDM = SM::LDM, LDP = SM::LDP;
+    constexpr int NTPW = (10 + NW - 1) / NW;   // Gram tiles per wave
+
+    __shared__ SM sm;
+    E* Kc = reinterpret_cast<E*>(sm.KcM);
+    float* Mf = reinterpret_cast<float*>(sm.KcM);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
+    const PrepIdx pi(tid, D);
+    const int r8 = pi.r8, I = pi.I, ch0 = pi.ch0, row0 = pi.row0;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const uint32_t rs = (uint32_t)H * D;
+    const size_t bbase = (size_t)b * T * H * D;
+    const uint32_t hoff = (uint32_t)h * D;
+    const int NC = (T + CH - 1) / CH;
+
+    floatx4 dSt[D / 16];   // dS^T[16mj + 4g + r][16w + cl] = dS[16w + cl][16mj + 4g + r]
+#pragma unroll
+    for (int mj = 0; mj < D / 16; ++mj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dSt[mj][r] = dST ? dST[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g + r] : 0.f;
+
+    if (NC > 0) {
+        for (int x = tid; x < CH * LDP; x += NT) sm.PT[x] = TR::cvt(0.f);   // upper part stays zero
+        if (tid == 0) sm.unsafe_any = 0u;
+        lds_barrier();
+    }
+
+    for (int n = NC - 1; n >= 0; --n) {
+        // gradient of the state leaving chunk n, for the chunk-local kernel
+        {
+            E* dst = wsdS + ((size_t)bh * NC + n) * 2 * D * D;
+#pragma unroll
+            for (int mj = 0; mj < D / 16; ++mj) {
+                const int i = 16 * w + cl, j = 16 * mj + 4 * g;
+                st4(dst + i * D + j, dSt[mj]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[D * D + (j + r) * D + i] = TR::cvt(dSt[mj][r]);
+            }
+        }
+        // ---------------- prep (a): rows, decay products within the sub-block
+        Row2x8<TR> rq, rk, rv, rf, ro;
+        float rbeta = 0.f;
+        {
+            const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
+            const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
+            rq.load(q + bbase, oa, ob);
+            rk.load(k + bbase, oa, ob);
+            rv.load(v + bbase, oa, ob);
+            rf.load(f + bbase, oa, ob);
+            ro.load(dO + bbase, oa, ob);
+            const int t = min(n * CH + (tid & (CH - 1)), T - 1);
+            rbeta = beta[((size_t)b * T + t) * H + h];
+            if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    if (n * CH + row0 + e >= T) {
+                        rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f); ro.clear(e, 0.f);
+                    }
+                if (n * CH + (tid & (CH - 1)) >= T) rbeta = 0.f;
+            }
+        }
+        float incl[8], excl[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            incl[c] = group8_prefix_prod(rf.get(0, c) * rf.get(1, c), r8);
+            excl[c] = group8_shift1(incl[c], r8);
+        }
+        if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
+        if (tid < CH) sm.beta[tid] = rbeta;
+        lds_barrier();
+
+        // ---------------- prep (b): operands
+        float kt[2][8];   // K-tilde rows, written once the Gram has read Qb
+        {
+            float plt[8], gC[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; }
+#pragma unroll
+            for (int I2 = 0; I2 < NSB; ++I2)
+#pragma unroll
+                for (int c4 = 0; c4 < 2; ++c4) {
+                    const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gC[4 * c4 + e] *= x[e];
+                        if (I2 < I) plt[4 * c4 + e] *= x[e];
+                    }
+                }
+            unsigned unsafe = 0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (!(gC[c] >= kSafeFloor)) unsafe |= 1u << c;
+            if (I == 0 && r8 == 0) st8v(&sm.gam[ch0], gC);
+            if (unsafe) atomicOr(&sm.unsafe_any, 1u);
+            float qo[2][8], ko[2][8];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                float co[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float ga = plt[c] * (e == 0 ? excl[c] * rf.get(0, c) : incl[c]);
+                    const float kf = rk.get(e, c);
+                    const bool un = (unsafe >> c) & 1u;
+                    const float kr = kf * __builtin_amdgcn_rcpf(ga);
+                    qo[e][c] = rq.get(e, c) * ga;
+                    ko[e][c] = kf * ga;
+                    co[c] = un ? 0.f : kr;
+                    kt[e][c] = un ? 0.f : kr * gC[c];
+                }
+                st8v(&sm.Qb[(row0 + e) * LD + ch0], qo[e]);
+                st8v(&sm.Kb[(row0 + e) * LD + ch0], ko[e]);
+                st8v(&Kc[(row0 + e) * LD + ch0], co);
+                rv.store(&sm.V[(row0 + e) * LD + ch0], e);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                st2(&sm.VT[(ch0 + c) * LDT + row0], rv.get(0, c), rv.get(1, c));
+                st2(&sm.OT[(ch0 + c) * LDT + row0], ro.get(0, c), ro.get(1, c));
+                st2(&sm.QT[(ch0 + c) * LDT + row0], qo[0][c], qo[1][c]);
+                st2(&sm.KT[(ch0 + c) * LDT + row0], ko[0][c], ko[1][c]);
+            }
+        }
+        lds_barrier();
+
+        // ---------------- Gram tiles M, P (kept in registers until every wave is done)
+        floatx4 mv[NTPW], pv[NTPW];
+#pragma unroll
+        for (int it = 0; it < NTPW; ++it) {
+            const int tile = w + it * NW;
+            if (tile < 10) {
+                const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+                const int J_ = tile - (I_ * (I_ + 1)) / 2;
+                floatx4 gk = {0.f, 0.f, 0.f, 0.f}, pp = gk, gv = gk;
+#pragma unroll
+                for (int ks = 0; ks < KD_; ++ks) {
+                    const Frag fk = TR::ld_nat(&Kc[(SB * J_ + cl) * LD], ks, g);
+                    gk = TR::mma(TR::ld_nat(&sm.Kb[(SB * I_ + cl) * LD], ks, g), fk, gk);
+                    pp = TR::mma(TR::ld_nat(&sm.Qb[(SB * I_ + cl) * LD], ks, g), fk, pp);
+                    gv = TR::mma(TR::ld_nat(&sm.V[(SB * I_ + cl) * LD], ks, g),
+                                 TR::ld_nat(&sm.V[(SB * J_ + cl) * LD], ks, g), gv);
+                }
+                const int s_ = SB * J_ + cl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = SB * I_ + 4 * g + r;
+                    mv[it][r] = (s_ < t_) ? sm.beta[t_] * gk[r] * gv[r] : 0.f;
+                    pv[it][r] = (s_ <= t_) ? pp[r] : 0.f;
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < NTPW; ++it) {
+            const int tile = w + it * NW;
+            if (tile < 10) {
+                const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+                const int J_ = tile - (I_ * (I_ + 1)) / 2;
+                const int s_ = SB * J_ + cl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = SB * I_ + 4 * g + r;
+                    Mf[t_ * LDM + s_] = mv[it][r];
+                }
+                st4(&sm.PT[s_ * LDP + SB * I_ + 4 * g], pv[it]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) st8v(&sm.Qb[(row0 + e) * LD + ch0], kt[e]);   // K-tilde rows
+        lds_barrier();
+
+        // ---------------- state read: dW = Kt dS^T + P^T dO (rows t, this wave's 16 columns i)
+        floatx4 dW[NSB];
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt) dW[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD_; ++ks) {
+            const Frag bS = TR::state_frag(dSt, ks);
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt)
+                dW[tt] = TR::mma(TR::ld_state(&sm.Qb[(SB * tt + cl) * LD], ks, g), bS, dW[tt]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KC_; ++ks) {
+            const Frag bO = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt)
+                dW[tt] = TR::mma(TR::ld_nat(&sm.PT[(SB * tt + cl) * LDP], ks, g), bO, dW[tt]);
+        }
+        {   // partial du[t] over this wave's 16 value columns
+            float x[16];
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[4 * tt + r] = dW[tt][r] * TR::tof(sm.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) {
+                const bool up = (cl & m) != 0;
+#pragma unroll
+                for (int e = 0; e < m; ++e) {
+                    const float send = up ? x[e] : x[e + m];
+                    const float keep = up ? x[e + m] : x[e];
+                    x[e] = keep + __shfl_xor(send, m, 64);
+                }
+            }
+            sm.dup[w][SB * (cl >> 2) + 4 * g + (cl & 3)] = x[0];
+        }
+        lds_barrier();
+
+        // ---------------- back substitution (I + M)^T drho = du
+        if (w == 0) {
+            const int t_ = lane;
+            float x = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) x += sm.dup[ww][t_];
+            float Mcol[CH];
+#pragma unroll
+            for (int s = 0; s < CH; ++s) Mcol[s] = Mf[s * LDM + t_];
+            // lane t takes the finished drho_s of every later row s; M above the
+            // diagonal is not cleared, hence the mask
+#pragma unroll
+            for (int s = CH - 1; s >= 1; --s) {
+                const float xs = readlane_f(x, s);
+                const float y = fmaf(-Mcol[s], xs, x);
+                x = (t_ < s) ? y : x;
+            }
+            if (sm.unsafe_any) x = __builtin_nanf("");
+            wsrho[((size_t)bh * NC + n) * CH + t_] = x;
+            sm.dr0[t_] = -sm.beta[t_] * x;
+        }
+        lds_barrier();
+
+        // ---------------- dS <- dS diag(gamma_C) + dO^T Qbar + V^T diag(dr0) Kbar
+        if (tid == 0) sm.unsafe_any = 0u;   // read for the last time above
+        {
+            Frag bO[KC_], bR[KC_];
+#pragma unroll
+            for (int ks = 0; ks < KC_; ++ks) {
+                bO[ks] = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
+                bR[ks] = TR::row_times(&sm.VT[(16 * w + cl) * LDT], sm.dr0, ks, g);
+            }
+#pragma unroll
+            for (int mj = 0; mj < D / 16; ++mj) {
+                const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[16 * mj + 4 * g]);
+                dSt[mj] = dSt[mj] * gm;
+#pragma unroll
+                for (int ks = 0; ks < KC_; ++ks) {
+                    dSt[mj] = TR::mma(TR::ld_nat(&sm.QT[(16 * mj + cl) * LDT], ks, g), bO[ks], dSt[mj]);
+                    dSt[mj] = TR::mma(TR::ld_nat(&sm.KT[(16 * mj + cl) * LDT], ks, g), bR[ks], dSt[mj]);
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    if (dS0) {
+#pragma unroll
+        for (int mj = 0; mj < D / 16; ++mj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dS0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g + r] = dSt[mj][r];
+    }
+}
+
+// ======================================================================
+// Chunk-local gradients, every chunk in parallel
+// ======================================================================
+template <class TR, int D>
+struct BwdChunkSmem {
+    typedef typename TR::E E;
+    static constexpr int LD = D + TR::PAD;     // [CH][D] operands
+    static constexpr int LDP = CH + TR::PAD;   // [CH][CH] matrices
+    static constexpr int LDF = D + 4;          // fp32 staging of the results
+    static constexpr size_t ROWB = (size_t)CH * LD * sizeof(E);
+    static constexpr size_t SQB = (size_t)CH * LDP * sizeof(E);
+    static constexpr size_t OPB = 5 * ROWB + 6 * SQB;
+    static constexpr size_t STB = 4 * (size_t)CH * LDF * sizeof(float);
+    // operands (Qb, Kb, Kc, V, dO, then P, dGK hi/lo, dP hi/lo, Gsym); later the staging
+    alignas(16) unsigned char big[OPB > STB ? OPB : STB];
+    alignas(16) float gam[D];          // gamma_C
+    alignas(16) float beta[CH];
+    alignas(16) float u[CH];
+    alignas(16) float r0[CH];
+    alignas(16) float drho[CH];
+    alignas(16) float dr0[CH];
+    alignas(16) float dbp[NSB][CH];    // dbeta partial of row t from column block J (J <= t / 16)
+    alignas(16) float bprod[NSB][D];
+    alignas(16) float gC2[D];          // sum_i dS[i][j] S0[i][j]
+    alignas(16) float gsub[NSB][D];    // sub-block sums of g
+    alignas(16) float hsub[NSB][D];    // sub-block sums of dKt * Kt
+    unsigned unsafe_any;
+};
+
+template <class TR, int D>
+__global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
+    const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
+    const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
+    const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const typename TR::E* __restrict__ ckptS, const float* __restrict__ ckptU,
+    const typename TR::E* __restrict__ wsdS, const float* __restrict__ wsrho,
+    typename TR::E* __restrict__ dq, typename TR::E* __restrict__ dk,
+    typename TR::E* __restrict__ dv, typename TR::E* __restrict__ df,
+    float* __restrict__ dbeta, float* __restrict__ dc, int T, int H)
+{
+    typedef typename TR::E E;
+    typedef typename TR::Frag Frag;
+    typedef BwdChunkSmem<TR, D> SM;
+    constexpr int NT = 4 * D;
+    constexpr int NW = D / 16;
+    constexpr int KD_ = D / TR::KS;
+    constexpr int KC_ = CH / TR::KS;
+    constexpr int LD = SM::LD, LDP = SM::LDP, LDF = SM::LDF;
+
+    __shared__ SM sm;
+    E* Qb = reinterpret_cast<E*>(sm.big);
+    E* Kb = Qb + CH * LD;
+    E* Kc = Kb + CH * LD;
+    E* Vs = Kc + CH * LD;
+    E* Do = Vs + CH * LD;
+    E* P = Do + CH * LD;
+    E* dGK = P + CH * LDP;     // hi part (bf16) ...
+    E* dGKl = dGK + CH * LDP;  // ... and the rest
+    E* dP = dGKl + CH * LDP;
+    E* dPl = dP + CH * LDP;
+    E* Gs = dPl + CH * LDP;
+    float* stQ = reinterpret_cast<float*>(sm.big);
+    float* stK = stQ + CH * LDF;
+    float* stC = stK + CH * LDF;
+    float* stT = stC + CH * LDF;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
+    const PrepIdx pi(tid, D);
+    const int r8 = pi.r8, I = pi.I, ch0 = pi.ch0, row0 = pi.row0;
+    const int NC = (T + CH - 1) / CH;
+    const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
+    const int b = bh / H, h = bh % H;
+    const uint32_t rs = (uint32_t)H * D;
+    const size_t bbase = (size_t)b * T * H * D;
+    const uint32_t hoff = (uint32_t)h * D;
+    const size_t unit = (size_t)bh * NC + n;
+
+    // ---------------- prep (a)
+    Row2x8<TR> rq, rk, rv, rf, ro;
+    const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
+    const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
+    rq.load(q + bbase, oa, ob);
+    rk.load(k + bbase, oa, ob);
+    rv.load(v + bbase, oa, ob);
+    rf.load(f + bbase, oa, ob);
+    ro.load(dO + bbase, oa, ob);
+    if (tid < CH) {
+        const bool valid = n * CH + tid < T;
+        const int t = min(n * CH + tid, T - 1);
+        sm.beta[tid] = valid ? beta[((size_t)b * T + t) * H + h] : 0.f;
+        sm.u[tid] = valid ? ckptU[unit * 2 * CH + tid] : 0.f;
+        sm.r0[tid] = valid ? ckptU[unit * 2 * CH + CH + tid] : 0.f;
+        sm.drho[tid] = valid ? wsrho[unit * CH + tid] : 0.f;
+    }
+    if (n * CH + CH > T) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            if (n * CH + row0 + e >= T) {
+                rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f); ro.clear(e, 0.f);
+            }
+    }
+    // the upper triangles of P, dGK, dP (hi and lo) are never written
+    for (int x = tid; x < 5 * CH * LDP; x += NT) P[x] = TR::cvt(0.f);
+    if (tid == 0) sm.unsafe_any = 0u;
+    float incl[8], excl[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        incl[c] = group8_prefix_prod(rf.get(0, c) * rf.get(1, c), r8);
+        excl[c] = group8_shift1(incl[c], r8);
+    }
+    if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
+    lds_barrier();
+
+    // ---------------- prep (b): operands; gamma and gamma_C stay in registers
+    float ga[2][8], gC[8];
+    {
+        float plt[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; }
+#pragma unroll
+        for (int I2 = 0; I2 < NSB; ++I2)
+#pragma unroll
+            for (int c4 = 0; c4 < 2; ++c4) {
+                const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gC[4 * c4 + e] *= x[e];
+                    if (I2 < I) plt[4 * c4 + e] *= x[e];
+                }
+            }
+        unsigned unsafe = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (!(gC[c] >= kSafeFloor)) unsafe |= 1u << c;
+        if (unsafe) atomicOr(&sm.unsafe_any, 1u);
+        if (I == 0 && r8 == 0) st8v(&sm.gam[ch0], gC);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float qo[8], ko[8], co[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                ga[e][c] = plt[c] * (e == 0 ? excl[c] * rf.get(0, c) : incl[c]);
+                const float kf = rk.get(e, c);
+                const bool un = (unsafe >> c) & 1u;
+                const float kr = kf * __builtin_amdgcn_rcpf(ga[e][c]);
+                qo[c] = rq.get(e, c) * ga[e][c];
+                ko[c] = kf * ga[e][c];
+                co[c] = un ? 0.f : kr;
+            }
+            st8v(&Qb[(row0 + e) * LD + ch0], qo);
+            st8v(&Kb[(row0 + e) * LD + ch0], ko);
+            st8v(&Kc[(row0 + e) * LD + ch0], co);
+            rv.store(&Vs[(row0 + e) * LD + ch0], e);
+            ro.store(&Do[(row0 + e) * LD + ch0], e);
+        }
+    }
+    if (tid < CH) sm.dr0[tid] = -sm.beta[tid] * sm.drho[tid];
+    lds_barrier();
+
+    // ---------------- C x C tiles: P, dP, dGK, dGV (+ its transpose), dbeta
+    for (int tile = w; tile < 10; tile += NW) {
+        const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+        const int J_ = tile - (I_ * (I_ + 1)) / 2;
+        const int s_ = SB * J_ + cl;
+        floatx4 gk = {0.f, 0.f, 0.f, 0.f}, gv = gk, pp = gk, dp = gk;
+        const float us = sm.u[s_];
+#pragma unroll
+        for (int ks = 0; ks < KD_; ++ks) {
+            const Frag fk = TR::ld_nat(&Kc[(SB * J_ + cl) * LD], ks, g);
+            const Frag fv = TR::ld_nat(&Vs[(SB * J_ + cl) * LD], ks, g);
+            gk = TR::mma(TR::ld_nat(&Kb[(SB * I_ + cl) * LD], ks, g), fk, gk);
+            pp = TR::mma(TR::ld_nat(&Qb[(SB * I_ + cl) * LD], ks, g), fk, pp);
+            gv = TR::mma(TR::ld_nat(&Vs[(SB * I_ + cl) * LD], ks, g), fv, gv);
+            dp = TR::mma(TR::ld_nat(&Do[(SB * I_ + cl) * LD], ks, g), TR::scale(fv, us), dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t_ = SB * I_ + 4 * g + r;
+            const bool low = s_ < t_, inc = s_ <= t_;
+            const float dM = low ? -sm.drho[t_] * us : 0.f;
+            const float bt = sm.beta[t_];
+            const float dgv = bt * dM * gk[r];
+            P[t_ * LDP + s_] = TR::cvt(inc ? pp[r] : 0.f);
+            const float dpv = inc ? dp[r] : 0.f, dgkv = bt * dM * gv[r];
+            const E dph = TR::cvt(dpv), dgkh = TR::cvt(dgkv);
+            dP[t_ * LDP + s_] = dph;
+            dPl[t_ * LDP + s_] = TR::lo_part(dpv, dph);
+            dGK[t_ * LDP + s_] = dgkh;
+            dGKl[t_ * LDP + s_] = TR::lo_part(dgkv, dgkh);
+            if (low) {
+                Gs[t_ * LDP + s_] = TR::cvt(dgv);
+                Gs[s_ * LDP + t_] = TR::cvt(dgv);
+            } else if (s_ == t_) {
+                Gs[t_ * LDP + t_] = TR::cvt(0.f);
+            }
+            float db = dM * gk[r] * gv[r];
+            db += __shfl_xor(db, 1, 64);
+            db += __shfl_xor(db, 2, 64);
+            db += __shfl_xor(db, 4, 64);
+            db += __shfl_xor(db, 8, 64);
+            if (cl == 0) sm.dbp[J_][t_] = db;
+        }
+    }
+    const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
+    const E* S0n = ckptS + unit * 2 * D * D;   // S0[i][j]
+    const E* S0T = S0n + D * D;                // S0^T[j][i]
+    const E* dSn = wsdS + unit * 2 * D * D;    // dS[i][j]
+    const E* dSTn = dSn + D * D;               // dS^T[j][i]
+    {   // colsum(dS * S0) for column jc: lane group g takes a quarter of i
+        float acc = 0.f;
+#pragma unroll 8
+        for (int x = 0; x < D / 4; ++x) {
+            const int i = g * (D / 4) + x;
+            acc += TR::tof(S0T[jc * D + i]) * TR::tof(dSTn[jc * D + i]);
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (g == 0) sm.gC2[jc] = acc;
+    }
+    lds_barrier();
+
+    // ---------------- C x D results, this wave's 16 columns, all 64 rows
+    floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB], aV[NSB];
+#pragma unroll
+    for (int tt = 0; tt < NSB; ++tt) {
+        aQ[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt]; aV[tt] = aQ[tt];
+    }
+    // contractions over a d-long index: B operands straight from global memory
+#pragma unroll
+    for (int ks = 0; ks < KD_; ++ks) {
+        const Frag b_s0t = TR::ld_nat(S0T + jc * D, ks, g);    // B[i][j] = S0[i][j]
+        const Frag b_dst = TR::ld_nat(dSTn + jc * D, ks, g);   // B[i][j] = dS[i][j]
+        const Frag b_ds = TR::ld_nat(dSn + jc * D, ks, g);     // B[j][i] = dS[i][j]
+        const Frag b_s0 = TR::ld_nat(S0n + jc * D, ks, g);     // B[j][i] = S0[i][j]
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt) {
+            const int tr = SB * tt + cl;
+            const float sr = sm.dr0[tr], su = sm.u[tr];
+            const Frag a_v = TR::ld_nat(&Vs[tr * LD], ks, g);
+            aQ[tt] = TR::mma(TR::ld_nat(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);    // dO S0
+            aK[tt] = TR::mma(TR::scale(a_v, sr), b_s0t, aK[tt]);                  // dr0 (V S0)
+            aT[tt] = TR::mma(TR::scale(a_v, su), b_dst, aT[tt]);                  // W dS
+            // u (Kt dS^T) with Kt = Kc gamma_C formed in the fragment
+            aV[tt] = TR::mma(TR::scale_k(TR::ld_nat(&Kc[tr * LD], ks, g), su, sm.gam, ks, g), b_ds, aV[tt]);
+            aV[tt] = TR::mma(TR::scale(TR::ld_nat(&Kb[tr * LD], ks, g), sr), b_s0, aV[tt]);   // dr0 (Kbar S0^T)
+        }
+    }
+    // contractions over the chunk: transposed operands read in place
+#pragma unroll
+    for (int ks = 0; ks < KC_; ++ks) {
+        const Frag b_kc = TR::ld_col(&Kc[jc], LD, ks, g);   // B[s][j] = Kc[s][j]
+        const Frag b_kb = TR::ld_col(&Kb[jc], LD, ks, g);   // B[t][j] = Kbar[t][j]
+        const Frag b_qb = TR::ld_col(&Qb[jc], LD, ks, g);   // B[t][j] = Qbar[t][j]
+        const Frag b_v = TR::ld_col(&Vs[jc], LD, ks, g);    // B[s][i] = V[s][i]
+        const Frag b_do = TR::ld_col(&Do[jc], LD, ks, g);   // B[t][i] = dO[t][i]
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt) {
+            const int tr = SB * tt + cl;
+            // dP and dGK enter as hi + lo (their bf16 rounding would dominate the
+            // error of dq and df)
+            aQ[tt] = TR::mma(TR::ld_nat(&dP[tr * LDP], ks, g), b_kc, aQ[tt]);            // dP Kc
+            aK[tt] = TR::mma(TR::ld_nat(&dGK[tr * LDP], ks, g), b_kc, aK[tt]);           // dGK Kc
+            aC[tt] = TR::mma(TR::ld_col(&dGK[tr], LDP, ks, g), b_kb, aC[tt]);            // dGK^T Kbar
+            aC[tt] = TR::mma(TR::ld_col(&dP[tr], LDP, ks, g), b_qb, aC[tt]);             // dP^T Qbar
+            if (TR::SPLIT) {
+                aQ[tt] = TR::mma(TR::ld_nat(&dPl[tr * LDP], ks, g), b_kc, aQ[tt]);
+                aK[tt] = TR::mma(TR::ld_nat(&dGKl[tr * LDP], ks, g), b_kc, aK[tt]);
+                aC[tt] = TR::mma(TR::ld_col(&dGKl[tr], LDP, ks, g), b_kb, aC[tt]);
+                aC[tt] = TR::mma(TR::ld_col(&dPl[tr], LDP, ks, g), b_qb, aC[tt]);
+            }
+            aV[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aV[tt]);             // (dGV + dGV^T) V
+            aV[tt] = TR::mma(TR::scale(TR::ld_col(&P[tr], LDP, ks, g), sm.u[tr]), b_do, aV[tt]);   // u (P^T dO)
+        }
+    }
+    lds_barrier();   // every operand read is done: the staging reuses the space
+#pragma unroll
+    for (int tt = 0; tt < NSB; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = SB * tt + 4 * g + r;
+            stQ[row * LDF + jc] = aQ[tt][r];
+            stK[row * LDF + jc] = aK[tt][r];
+            stC[row * LDF + jc] = aC[tt][r];
+            stT[row * LDF + jc] = aT[tt][r];
+        }
+    lds_barrier();
+
+    // ---------------- elementwise: dq, dk, and the decay gradient (prep layout)
+    const bool poison = sm.unsafe_any != 0u;
+    float dqv[2][8], dkv[2][8], suf0[8], suf1[8], totg[8], toth[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float gg[2], hh[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int idx = (row0 + e) * LDF + ch0 + c;
+            const float dQ = stQ[idx], dKb = stK[idx], dKc = stC[idx], dKt = stT[idx];
+            const float gm = ga[e][c], rg = __builtin_amdgcn_rcpf(gm);
+            const float qf = rq.get(e, c), kf = rk.get(e, c);
+            // Qbar, Kbar, Kc exactly as the MFMA products saw them (same fp32
+            // arithmetic as the prep, same rounding): each Gram pair (t, s)
+            // then enters g_t and g_s with equal and opposite values, and the
+            // suffix sums below cancel it exactly.  Kt enters no product whose
+            // result feeds g, so it is taken exact.
+            const float kr = kf * rg;
+            const float Qbar = TR::tof(TR::cvt(qf * gm)), Kbar = TR::tof(TR::cvt(kf * gm));
+            const float Kcv = TR::tof(TR::cvt(kr)), Ktv = kr * gC[c];
+            dqv[e][c] = dQ * gm;
+            dkv[e][c] = dKb * gm + dKc * rg + dKt * (gC[c] * rg);
+            gg[e] = dQ * Qbar + dKb * Kbar - dKc * Kcv - dKt * Ktv;
+            hh[e] = dKt * Ktv;
+        }
+        const float pair = gg[0] + gg[1];
+        const float inc = group8_suffix_sum(pair, r8);
+        const float nxt = group8_next1(inc, r8);
+        toth[c] = group8_suffix_sum(hh[0] + hh[1], r8);
+        totg[c] = inc;
+        suf1[c] = nxt + gg[1];
+        suf0[c] = suf1[c] + gg[0];
+    }
+    if (r8 == 0) {
+        st8v(&sm.gsub[I][ch0], totg);
+        st8v(&sm.hsub[I][ch0], toth);
+    }
+    lds_barrier();
+    {
+        float dfv[2][8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float later = 0.f, htot = 0.f;
+#pragma unroll
+            for (int I2 = 0; I2 < NSB; ++I2) {
+                if (I2 > I) later += sm.gsub[I2][ch0 + c];
+                htot += sm.hsub[I2][ch0 + c];
+            }
+            const float base = later + gC[c] * sm.gC2[ch0 + c] + htot;
+            dfv[0][c] = (suf0[c] + base) / rf.get(0, c);
+            dfv[1][c] = (suf1[c] + base) / rf.get(1, c);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int t = n * CH + row0 + e;
+            if (t < T) {
+                if (poison) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        dqv[e][c] = __builtin_nanf("");
+                        dkv[e][c] = dqv[e][c];
+                        dfv[e][c] = dqv[e][c];
+                    }
+                }
+                const uint32_t off = (uint32_t)t * rs + hoff + ch0;
+                st8v(dq + bbase + off, dqv[e]);
+                st8v(dk + bbase + off, dkv[e]);
+                st8v(df + bbase + off, dfv[e]);
+            }
+        }
+    }
+    lds_barrier();   // staging reads done before dV reuses it
+#pragma unroll
+    for (int tt = 0; tt < NSB; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stQ[(SB * tt + 4 * g + r) * LDF + jc] = aV[tt][r];
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int t = n * CH + row0 + e;
+        if (t < T) {
+            float x[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = poison ? __builtin_nanf("") : stQ[(row0 + e) * LDF + ch0 + c];
+            st8v(dv + bbase + (uint32_t)t * rs + hoff + ch0, x);
+        }
+    }
+    if (tid < CH && n * CH + tid < T) {
+        const size_t gi = ((size_t)b * T + n * CH + tid) * H + h;
+        float db = -sm.r0[tid] * sm.drho[tid];
+        for (int J = 0; J <= tid / SB; ++J) db += sm.dbp[J][tid];   // fixed order: bitwise reproducible
+        dbeta[gi] = poison ? __builtin_nanf("") : db;
+        dc[gi] = poison ? __builtin_nanf("") : sm.drho[tid];
+    }
+}
+
+// --------------------------------------------------------------- launchers
+template <class TR, int D>
+static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* f,
+                               const float* beta, const float* c, const float* S0, const void* dO,
+                               const float* dST, void* dq, void* dk, void* dv, void* df,
+                               float* dbeta, float* dc, float* dS0, void* ws, int B, int T, int H,
+                               hipStream_t st)
+{
+    typedef typename TR::E E;
+    const BwdWs L = bwd_ws_layout(sizeof(E), D, B, T, H);
+    char* wb = static_cast<char*>(ws);
+    E* ckS = reinterpret_cast<E*>(wb + L.s0);
+    float* ckU = reinterpret_cast<float*>(wb + L.ur);
+    E* wdS = reinterpret_cast<E*>(wb + L.ds);
+    float* wrho = reinterpret_cast<float*>(wb + L.rho);
+    const int NC = (T + CH - 1) / CH;
+    if (NC > 0) {
+        hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr,
+                                  ckS, ckU, B, T, H, st);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO, dST,
+                       wdS, wrho, dS0, T, H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || NC == 0) return e;
+    hipLaunchKernelGGL((kd_bwd_chunk_kernel<TR, D>), dim3((unsigned)(B * H * NC)), dim3(4 * D), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
+                       (const E*)ckS, (const float*)ckU, (const E*)wdS, (const float*)wrho,
+                       (E*)dq, (E*)dk, (E*)dv, (E*)df, dbeta, dc, T, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                      const float* beta, const float* c, const float* S0, const void* dO,
+                      const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
+                      float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st)
+{
+#define KD_BWD_ARGS q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, B, T, H, st
+    if (bf16) {
+        switch (d) {
+        case 32: return launch_bwd_t<Bf16T, 32>(KD_BWD_ARGS);
+        case 64: return launch_bwd_t<Bf16T, 64>(KD_BWD_ARGS);
+        case 128: return launch_bwd_t<Bf16T, 128>(KD_BWD_ARGS);
+        }
+    } else if (d == 32) {
+        return launch_bwd_t<F32T, 32>(KD_BWD_ARGS);
+    }
+#undef KD_BWD_ARGS
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kd

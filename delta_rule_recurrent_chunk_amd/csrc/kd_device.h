@@ -27,6 +27,9 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;        // chunk length (tokens per chunk)
+// Decay operands are referenced to the chunk start and divide by gamma; a key
+// channel whose decay over a chunk falls below this floor is treated apart.
+constexpr float kSafeFloor = 7.888609052210118e-31f;  // 2^-100
 constexpr int SB = 16;        // sub-block edge = MFMA tile edge
 constexpr int NSB = CH / SB;  // sub-blocks per chunk
 
@@ -99,6 +102,36 @@ struct Bf16T {
         r[4] = cvt(b[0]); r[5] = cvt(b[1]); r[6] = cvt(b[2]); r[7] = cvt(b[3]);
         return r;
     }
+    // natural-order fragment from a column: K = 32ks + 8g + e at col[K * ld]
+    // (a transposed operand read in place, one element per load)
+    static __device__ __forceinline__ Frag ld_col(const E* col, int ld, int ks, int g) {
+        const E* p = col + (KS * ks + 8 * g) * ld;
+        Frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = p[e * ld];
+        return r;
+    }
+    // every element times s (one row or column of an operand scaled)
+    static __device__ __forceinline__ Frag scale(Frag x, float s) {
+        Frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = cvt(tof(x[e]) * s);
+        return r;
+    }
+    // element e times s * sv[K] for the fragment's K = 32ks + 8g + e
+    static __device__ __forceinline__ Frag scale_k(Frag x, float s, const float* sv, int ks, int g) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(sv + KS * ks + 8 * g);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(sv + KS * ks + 8 * g + 4);
+        Frag r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = cvt(tof(x[e]) * (s * a[e]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 + e] = cvt(tof(x[4 + e]) * (s * b[e]));
+        return r;
+    }
+    // operands that need more than bf16 precision are stored as hi + lo
+    static constexpr bool SPLIT = true;
+    static __device__ __forceinline__ E lo_part(float x, E hi) { return cvt(x - tof(hi)); }
     // natural-order fragment along K = token index t from a row that is
     // contiguous in t, each element scaled by u[t]
     static __device__ __forceinline__ Frag row_times(const E* row, const float* u, int ks, int g) {
@@ -162,6 +195,15 @@ struct F32T {
     static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
         return acc[ks >> 2][ks & 3];
     }
+    static __device__ __forceinline__ Frag ld_col(const E* col, int ld, int ks, int g) {
+        return col[(KS * ks + g) * ld];
+    }
+    static __device__ __forceinline__ Frag scale(Frag x, float s) { return x * s; }
+    static __device__ __forceinline__ Frag scale_k(Frag x, float s, const float* sv, int ks, int g) {
+        return x * (s * sv[KS * ks + g]);
+    }
+    static constexpr bool SPLIT = false;
+    static __device__ __forceinline__ E lo_part(float, E) { return 0.f; }
     static __device__ __forceinline__ Frag row_times(const E* row, const float* u, int ks, int g) {
         const int t = KS * ks + g;
         return u[t] * row[t];
@@ -249,6 +291,27 @@ __device__ __forceinline__ float group8_prefix_prod(float x, int r8) {
 __device__ __forceinline__ float group8_shift1(float x, int r8) {
     const float y = dpp_row_shr<1>(x);
     return r8 >= 1 ? y : 1.f;
+}
+// Sums over the same 8-lane groups in reverse lane order.  Every DPP move is
+// issued by all lanes before the lane-dependent select.
+template <int S>
+__device__ __forceinline__ float dpp_row_shl0(float x) {   // lane i <- lane i+S of its 16-lane row (0 if none)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + S, 0xf, 0xf, false));
+}
+// inclusive suffix sum: lanes r8 .. 7 of the group
+__device__ __forceinline__ float group8_suffix_sum(float x, int r8) {
+    float y = dpp_row_shl0<1>(x);
+    x = (r8 <= 6) ? x + y : x;
+    y = dpp_row_shl0<2>(x);
+    x = (r8 <= 5) ? x + y : x;
+    y = dpp_row_shl0<4>(x);
+    x = (r8 <= 3) ? x + y : x;
+    return x;
+}
+// value of x in the next lane of the group (0 for the last lane)
+__device__ __forceinline__ float group8_next1(float x, int r8) {
+    const float y = dpp_row_shl0<1>(x);
+    return r8 <= 6 ? y : 0.f;
 }
 
 // Store eight values as one 16-byte row segment.

@@ -54,8 +54,6 @@
 
 namespace kd {
 
-constexpr float kSafeFloor = 7.888609052210118e-31f;  // 2^-100
-
 template <class TR, int D>
 struct FwdSmem {
     typedef typename TR::E E;
@@ -89,7 +87,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, typename TR::E* __restrict__ o, float* __restrict__ ST,
-    float* __restrict__ ckpt, int T, int H)
+    typename TR::E* __restrict__ ckptS, float* __restrict__ ckptU, int T, int H)
 {
     typedef typename TR::E E;
     typedef typename TR::H Hh;
@@ -167,15 +165,17 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             KD_PHASE_MARK(n, 0);
             floatx4 Ot[2][NSB];   // O^T[i0 + 16mt + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
-                if (ckpt) {   // chunk-start state, stored as S[i][j]
-                    float* dst = ckpt + ((size_t)bh * NC + n) * D * D;
+                if (ckptS) {   // chunk-start state for the backward: S[i][j], then S^T[j][i]
+                    E* dst = ckptS + ((size_t)bh * NC + n) * 2 * D * D;
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                        for (int mj = 0; mj < D / 16; ++mj)
+                        for (int mj = 0; mj < D / 16; ++mj) {
+                            const int i = i0 + 16 * nt + cl, j = 16 * mj + 4 * g;
+                            st4(dst + i * D + j, S[nt][mj]);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                dst[(size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] = S[nt][mj][r];
+                            for (int r = 0; r < 4; ++r) dst[D * D + (j + r) * D + i] = TR::cvt(S[nt][mj][r]);
+                        }
                 }
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
                 floatx4 Yt[2][NSB];
@@ -236,6 +236,11 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
                 for (int s = 0; s < CH - 1; ++s) x = fmaf(-Mrow[s], readlane_f(x, s), x);
                 sm.u[t_] = x;
+                if (ckptU) {   // u and r0 of the chunk for the backward
+                    float* du = ckptU + ((size_t)bh * NC + n) * 2 * CH;
+                    du[t_] = x;
+                    du[CH + t_] = r0;
+                }
                 const float um = wave_max_nonneg(fabsf(x));
                 if (lane == 0) sm.umax = __float_as_uint(um);
             }
@@ -550,31 +555,34 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 template <class TR, int D>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* f,
                                const float* beta, const float* c, const float* S0, void* o,
-                               float* ST, float* ckpt, int B, int T, int H, hipStream_t st)
+                               float* ST, void* ckptS, float* ckptU, int B, int T, int H,
+                               hipStream_t st)
 {
     typedef typename TR::E E;
     hipLaunchKernelGGL((kd_fwd_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                       ckpt, T, H);
+                       (E*)ckptS, ckptU, T, H);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      float* ckpt, int B, int T, int H, hipStream_t st)
+                      void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st)
 {
+#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ckptS, ckptU, B, T, H, st
     if (bf16) {
         switch (d) {
-        case 32: return launch_fwd_t<Bf16T, 32>(q, k, v, f, beta, c, S0, o, ST, ckpt, B, T, H, st);
-        case 64: return launch_fwd_t<Bf16T, 64>(q, k, v, f, beta, c, S0, o, ST, ckpt, B, T, H, st);
-        case 128: return launch_fwd_t<Bf16T, 128>(q, k, v, f, beta, c, S0, o, ST, ckpt, B, T, H, st);
+        case 32: return launch_fwd_t<Bf16T, 32>(KD_FWD_ARGS);
+        case 64: return launch_fwd_t<Bf16T, 64>(KD_FWD_ARGS);
+        case 128: return launch_fwd_t<Bf16T, 128>(KD_FWD_ARGS);
         }
     } else {
         switch (d) {
-        case 32: return launch_fwd_t<F32T, 32>(q, k, v, f, beta, c, S0, o, ST, ckpt, B, T, H, st);
-        case 64: return launch_fwd_t<F32T, 64>(q, k, v, f, beta, c, S0, o, ST, ckpt, B, T, H, st);
+        case 32: return launch_fwd_t<F32T, 32>(KD_FWD_ARGS);
+        case 64: return launch_fwd_t<F32T, 64>(KD_FWD_ARGS);
         }
     }
+#undef KD_FWD_ARGS
     return hipErrorInvalidValue;
 }
 

@@ -113,9 +113,22 @@ KD_API kd_status kron_delta_fwd(const kd_desc *desc,
  * respect to q, k, v, f, beta, c and S0, where o and S_T are what
  * kron_delta_fwd returns for the same inputs.  dST NULL means dS_T = 0;
  * S0 NULL means S0 = 0; dS0 NULL means the gradient of S0 is not returned.
- * Needs a workspace of kron_delta_workspace_bytes(desc, 1) bytes (holds the
- * chunk-start states of a forward recomputation); its contents on entry are
- * ignored and on exit are unspecified.
+ * Needs a workspace of kron_delta_workspace_bytes(desc, 1) bytes: it holds,
+ * per 64-token chunk, the entering state and the WY targets of a forward
+ * recomputation and the state gradient of the reverse sweep (about
+ * 4 * d * d * sizeof(element) bytes per chunk and head); its contents on
+ * entry are ignored and on exit are unspecified.
+ * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv = 32
+ * (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
+ * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2
+ * summary, section "핵심 기여" (gate-aware backward pass), applied to the rule
+ * of the onedev.kr KronLSTM summary, section "어떻게 동작하나".
+ * Limitation: a chunk in which some key channel decays below 2^-100 over
+ * the chunk (for instance f = 0) is not differentiated: all its gradients are
+ * NaN, and so are those that depend on it through the state gradient (dk,
+ * dv, df, dbeta, dc of the earlier chunks of the same (b, h), and dS0); dq of
+ * the earlier chunks does not depend on it and stays exact.
+ * Enqueued on `stream` as three kernels; no allocation, no synchronisation.
  */
 KD_API kd_status kron_delta_bwd(const kd_desc *desc,
                          const void *q, const void *k, const void *v, const void *f,
