@@ -77,6 +77,17 @@ def algorithmic_bytes(w, esize, with_S0=False):
     return b
 
 
+def algorithmic_bytes_fwd_bwd(w, esize):
+    """HBM bytes of one forward + backward step: the forward's inputs and o; the
+    backward's inputs (q, k, v, f, beta, c, dO) and outputs (dq, dk, dv, df,
+    dbeta, dc, dS0).  Checkpoints are the implementation's, not counted."""
+    ntok = w.B * w.T * w.H
+    fwd = algorithmic_bytes(w, esize) - w.B * w.H * w.dv * w.dk * 4   # no S_T in this step
+    bwd = 5 * ntok * w.dk * esize + 2 * ntok * 4 + 4 * ntok * w.dk * esize + 2 * ntok * 4
+    bwd += w.B * w.H * w.dv * w.dk * 4
+    return fwd + bwd
+
+
 def mfma_flops(w):
     """MFMA flops of one launch as issued (full 16x16 tiles, including the
     masked-out upper Gram tiles' partners): per (b, h, chunk) of C = 64 with
@@ -100,14 +111,18 @@ def cpu_baseline(x_np, w, budget_s=12.0):
         sl = slice(b, b + 1)
         oracle.fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
                    x_np["beta"][sl], x_np["c"][sl], None)
+        if w.backward:
+            oracle.bwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
+                       x_np["beta"][sl], x_np["c"][sl], None, x_np["dO"][sl])
         nb += 1
         done_tok += w.T
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": done_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 oracle forward on %d of %d sequences (T=%d, H=%d, d=%d), same seeded "
-                      "inputs, %.2f s wall" % (nb, w.B, w.T, w.H, w.dk, dt)}
+            "sample": "fp64 oracle %s on %d of %d sequences (T=%d, H=%d, d=%d), same seeded "
+                      "inputs, %.2f s wall" % ("forward + backward" if w.backward else "forward",
+                                               nb, w.B, w.T, w.H, w.dk, dt)}
 
 
 def main():
@@ -149,14 +164,25 @@ def main():
 
     w = sy.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    x = sy.rounded(sy.draw_workload(w, with_dO=False), w.dtype)
+    x = sy.rounded(sy.draw_workload(w), w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = {n: torch.tensor(x[n], dtype=tdt if n in ("q", "k", "v", "f") else torch.float32,
                          device=dev) for n in ("q", "k", "v", "f", "beta", "c")}
     esize = 2 if w.dtype == "bf16" else 4
 
-    def step():
-        return kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
+    if w.backward:   # a step is the forward plus the gate-aware backward
+        t["dO"] = torch.tensor(x["dO"], dtype=tdt, device=dev)
+        ws = torch.empty(max(kd.workspace_bytes(w.B, w.T, w.H, w.dk, 1 if w.dtype == "bf16" else 0,
+                                                 with_backward=True), 16),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
+            return kd.bwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None, t["dO"],
+                          workspace=ws)
+    else:
+        def step():
+            return kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
 
     for _ in range(args.warmup):
         step()
@@ -178,14 +204,15 @@ def main():
 
     tokens = w.B * w.T
     value = tokens / (ms_per_step * 1e-3)
-    abytes = algorithmic_bytes(w, esize)
+    abytes = algorithmic_bytes_fwd_bwd(w, esize) if w.backward else algorithmic_bytes(w, esize)
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
     flops = mfma_flops(w)
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
     traffic = stored_traffic() if args.workload == "train_step" else None
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not w.backward else
+        "Kron-delta chunked fwd+bwd tokens/s (H=16,d=128) and % HBM roofline",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -198,17 +225,22 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
                 "beta,c=sigmoid(N(0,1)))" % w.mu,
-        "config": {"workload": "%s: Kronecker delta rule chunked forward, B=%d T=%d H=%d "
+        "config": {"workload": "%s: Kronecker delta rule chunked %s, B=%d T=%d H=%d "
                                "dk=dv=%d, chunk 64, %s q/k/v/f, fp32 beta/c/state, S0=0"
-                               % (w.name, w.B, w.T, w.H, w.dk, w.dtype),
+                               % (w.name, "forward + gate-aware backward" if w.backward else "forward",
+                                  w.B, w.T, w.H, w.dk, w.dtype),
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_fwd_kernel<Bf16T,128>", "kernel_ms": kernel_ms,
+                     "kernel": "kd_fwd_kernel<Bf16T,128>" if not w.backward else
+                     "kd_fwd_kernel + kd_fwd_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
+                     "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,
-                     "mfma_tflops": flops / (kernel_ms * 1e-3) / 1e12,
-                     "mfma_frac": flops / (kernel_ms * 1e-3) / 1e12 / peak_tf},
+                     },
     }
+    if not w.backward:
+        out["roofline"]["mfma_tflops"] = flops / (kernel_ms * 1e-3) / 1e12
+        out["roofline"]["mfma_frac"] = flops / (kernel_ms * 1e-3) / 1e12 / peak_tf
     if args.cold:
         big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         times = []

@@ -20,7 +20,7 @@
 //
 // Three launches on the caller's stream:
 //   1. the forward kernel with checkpoints: per chunk the entering state (in
-//      the input dtype, as S[i][j] and S^T[j][i]) and u, r0;
+//      the input dtype, S[i][j]) and u, r0;
 //   2. kd_bwd_state_kernel: one workgroup per (b, h), chunks in reverse, the
 //      fp32 dS^T held as MFMA accumulators (the mirror of the forward state):
 //      state read, back substitution, rank-128 update; stores dS and drho;
@@ -49,9 +49,9 @@ static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     BwdWs w;
     w.s0 = 0;
-    w.ur = up(units * 2 * d * d * esz);
+    w.ur = up(units * d * d * esz);
     w.ds = w.ur + up(units * 2 * CH * sizeof(float));
-    w.rho = w.ds + up(units * 2 * d * d * esz);
+    w.rho = w.ds + up(units * d * d * esz);
     w.total = w.rho + up(units * CH * sizeof(float));
     return w;
 }
@@ -151,16 +151,12 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     }
 
     for (int n = NC - 1; n >= 0; --n) {
-        // gradient of the state leaving chunk n, for the chunk-local kernel
+        // gradient of the state leaving chunk n, dS[i][j], for the chunk-local kernel
         {
-            E* dst = wsdS + ((size_t)bh * NC + n) * 2 * D * D;
+            E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj) {
-                const int i = 16 * w + cl, j = 16 * mj + 4 * g;
-                st4(dst + i * D + j, dSt[mj]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[D * D + (j + r) * D + i] = TR::cvt(dSt[mj][r]);
-            }
+            for (int mj = 0; mj < D / 16; ++mj)
+                st4(dst + ((uint32_t)(16 * w + cl) * D + 16 * mj + 4 * g), dSt[mj]);
         }
         // ---------------- prep (a): rows, decay products within the sub-block
         Row2x8<TR> rq, rk, rv, rf, ro;
@@ -592,16 +588,14 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
         }
     }
     const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
-    const E* S0n = ckptS + unit * 2 * D * D;   // S0[i][j]
-    const E* S0T = S0n + D * D;                // S0^T[j][i]
-    const E* dSn = wsdS + unit * 2 * D * D;    // dS[i][j]
-    const E* dSTn = dSn + D * D;               // dS^T[j][i]
+    const E* S0n = ckptS + unit * D * D;   // S0[i][j]
+    const E* dSn = wsdS + unit * D * D;    // dS[i][j]
     {   // colsum(dS * S0) for column jc: lane group g takes a quarter of i
         float acc = 0.f;
 #pragma unroll 8
         for (int x = 0; x < D / 4; ++x) {
             const int i = g * (D / 4) + x;
-            acc += TR::tof(S0T[jc * D + i]) * TR::tof(dSTn[jc * D + i]);
+            acc += TR::tof(S0n[i * D + jc]) * TR::tof(dSn[i * D + jc]);
         }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
@@ -617,10 +611,11 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
         aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt]; aV[tt] = aQ[tt];
     }
     // contractions over a d-long index: B operands straight from global memory
+    // (L2), columns of S0 and dS read element by element
 #pragma unroll
     for (int ks = 0; ks < KD_; ++ks) {
-        const Frag b_s0t = TR::ld_nat(S0T + jc * D, ks, g);    // B[i][j] = S0[i][j]
-        const Frag b_dst = TR::ld_nat(dSTn + jc * D, ks, g);   // B[i][j] = dS[i][j]
+        const Frag b_s0t = TR::ld_col(S0n + jc, D, ks, g);     // B[i][j] = S0[i][j]
+        const Frag b_dst = TR::ld_col(dSn + jc, D, ks, g);     // B[i][j] = dS[i][j]
         const Frag b_ds = TR::ld_nat(dSn + jc * D, ks, g);     // B[j][i] = dS[i][j]
         const Frag b_s0 = TR::ld_nat(S0n + jc * D, ks, g);     // B[j][i] = S0[i][j]
 #pragma unroll

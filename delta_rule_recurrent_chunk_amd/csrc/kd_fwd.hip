@@ -81,7 +81,10 @@ struct FwdSmem {
     unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
-template <class TR, int D>
+// CKPT: also store, per chunk, the entering state (S[i][j], in the input
+// dtype) and the WY targets u and r0, for the backward.  A separate
+// instantiation, so the plain forward carries none of its registers.
+template <class TR, int D, bool CKPT>
 __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
@@ -165,17 +168,13 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             KD_PHASE_MARK(n, 0);
             floatx4 Ot[2][NSB];   // O^T[i0 + 16mt + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
-                if (ckptS) {   // chunk-start state for the backward: S[i][j], then S^T[j][i]
-                    E* dst = ckptS + ((size_t)bh * NC + n) * 2 * D * D;
+                if (CKPT) {   // chunk-start state for the backward, S[i][j]
+                    E* dst = ckptS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                        for (int mj = 0; mj < D / 16; ++mj) {
-                            const int i = i0 + 16 * nt + cl, j = 16 * mj + 4 * g;
-                            st4(dst + i * D + j, S[nt][mj]);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) dst[D * D + (j + r) * D + i] = TR::cvt(S[nt][mj][r]);
-                        }
+                        for (int mj = 0; mj < D / 16; ++mj)
+                            st4(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
                 }
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
                 floatx4 Yt[2][NSB];
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
                 for (int s = 0; s < CH - 1; ++s) x = fmaf(-Mrow[s], readlane_f(x, s), x);
                 sm.u[t_] = x;
-                if (ckptU) {   // u and r0 of the chunk for the backward
+                if (CKPT) {   // u and r0 of the chunk for the backward
                     float* du = ckptU + ((size_t)bh * NC + n) * 2 * CH;
                     du[t_] = x;
                     du[CH + t_] = r0;
@@ -559,9 +558,14 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
                                hipStream_t st)
 {
     typedef typename TR::E E;
-    hipLaunchKernelGGL((kd_fwd_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                       (E*)ckptS, ckptU, T, H);
+    if (ckptS)
+        hipLaunchKernelGGL((kd_fwd_kernel<TR, D, true>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
+                           (E*)ckptS, ckptU, T, H);
+    else
+        hipLaunchKernelGGL((kd_fwd_kernel<TR, D, false>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
+                           (E*)nullptr, (float*)nullptr, T, H);
     return hipGetLastError();
 }
 
