@@ -170,6 +170,22 @@ struct Bf16T {
         for (int e = 0; e < 4; ++e) r[4 + e] = (_Float16)((u1[e] * su) * tof(x[4 + e]));
         return r;
     }
+    // the same for two rows sharing one scaled slice of u
+    static __device__ __forceinline__ void rows_times_h2(const E* row0, const E* row1, const float* u,
+                                                         float su, int ks, int g, FragH& r0, FragH& r1) {
+        const int t0 = KS * ks + 8 * g;
+        const Frag x0 = *reinterpret_cast<const Frag*>(row0 + t0);
+        const Frag x1 = *reinterpret_cast<const Frag*>(row1 + t0);
+        const floatx4 u0 = *reinterpret_cast<const floatx4*>(u + t0) * su;
+        const floatx4 u1 = *reinterpret_cast<const floatx4*>(u + t0 + 4) * su;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r0[e] = (_Float16)(u0[e] * tof(x0[e]));
+            r1[e] = (_Float16)(u0[e] * tof(x1[e]));
+            r0[4 + e] = (_Float16)(u1[e] * tof(x0[4 + e]));
+            r1[4 + e] = (_Float16)(u1[e] * tof(x1[4 + e]));
+        }
+    }
 };
 
 // ---------------------------------------------------------------- fp32 path
@@ -216,6 +232,13 @@ struct F32T {
                                                         int ks, int g) {
         const int t = KS * ks + g;
         return (u[t] * su) * row[t];
+    }
+    static __device__ __forceinline__ void rows_times_h2(const E* row0, const E* row1, const float* u,
+                                                         float su, int ks, int g, FragH& r0, FragH& r1) {
+        const int t = KS * ks + g;
+        const float us = u[t] * su;
+        r0 = us * row0[t];
+        r1 = us * row1[t];
     }
 };
 
@@ -389,6 +412,124 @@ template <> struct Raw4x8<F32T> {
     }
 };
 
+// Sixteen consecutive tokens (one sub-block) of two adjacent channels ch0,
+// ch0 + 1: the producer's prefetch buffer.  One 4-byte load per row for bf16
+// (8-byte for fp32); the lanes of a wave cover adjacent channel pairs, so every
+// load instruction reads whole rows.
+template <class TR> struct Raw16x2;
+
+template <> struct Raw16x2<Bf16T> {
+    uint32_t w[16];   // row e: channel ch0 in the low half, ch0 + 1 in the high half
+    // p: wave-uniform base; row e at 32-bit element offset off + min(e, last)*stride.
+    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int last) {
+        const char* base = reinterpret_cast<const char*>(p);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            w[e] = *reinterpret_cast<const uint32_t*>(base + (off + (uint32_t)(e < last ? e : last) * stride) * 2u);
+    }
+    __device__ __forceinline__ float get(int e, int cc) const {
+        return __uint_as_float(cc ? (w[e] & 0xffff0000u) : (w[e] << 16));
+    }
+    __device__ __forceinline__ void clear(int e, float fill) {
+        const uint32_t fb = __float_as_uint(fill) >> 16;
+        w[e] = fb | (fb << 16);
+    }
+    __device__ __forceinline__ void store(__bf16* dst, int e) const { *reinterpret_cast<uint32_t*>(dst) = w[e]; }
+    // max |x| over the 32 values
+    __device__ __forceinline__ float absmax() const {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)   // bf16 magnitudes order like unsigned integers
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[e] & 0x7fff7fffu));
+        const uint32_t hi = m[0] > m[1] ? m[0] : m[1];
+        return __uint_as_float(hi << 16);
+    }
+};
+
+template <> struct Raw16x2<F32T> {
+    float2 w[16];
+    __device__ __forceinline__ void load(const float* p, uint32_t off, uint32_t stride, int last) {
+        const char* base = reinterpret_cast<const char*>(p);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            w[e] = *reinterpret_cast<const float2*>(base + (off + (uint32_t)(e < last ? e : last) * stride) * 4u);
+    }
+    __device__ __forceinline__ float get(int e, int cc) const { return cc ? w[e].y : w[e].x; }
+    __device__ __forceinline__ void clear(int e, float fill) { w[e] = make_float2(fill, fill); }
+    __device__ __forceinline__ void store(float* dst, int e) const { *reinterpret_cast<float2*>(dst) = w[e]; }
+    __device__ __forceinline__ float absmax() const {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fmaxf(fabsf(w[e].x), fabsf(w[e].y)));
+        return m;
+    }
+};
+
+// Sixteen consecutive tokens of one channel, kept from the producer's prep
+// until they are written as one transposed entry (32 bytes for bf16 and fp16,
+// 64 bytes for fp32).
+template <class T> struct Col16;
+template <> struct Col16<__bf16> {
+    uint32_t w[8];
+    __device__ __forceinline__ void set_raw(const Raw16x2<Bf16T>& r, int cc) {
+        const uint32_t sel = cc ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = __builtin_amdgcn_perm(r.w[2 * k + 1], r.w[2 * k], sel);
+    }
+    __device__ __forceinline__ void store(__bf16* p) const {
+        reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+};
+template <> struct Col16<_Float16> {
+    uint32_t w[8];
+    __device__ __forceinline__ void set_pair(int k, float a, float b) {
+        _Float16 __attribute__((ext_vector_type(2))) x;
+        x[0] = (_Float16)a;
+        x[1] = (_Float16)b;
+        w[k] = __builtin_bit_cast(uint32_t, x);
+    }
+    __device__ __forceinline__ void store(_Float16* p) const {
+        reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+};
+template <> struct Col16<float> {
+    float w[16];
+    __device__ __forceinline__ void set_raw(const Raw16x2<F32T>& r, int cc) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[e] = r.get(e, cc);
+    }
+    __device__ __forceinline__ void set_pair(int k, float a, float b) { w[2 * k] = a; w[2 * k + 1] = b; }
+    __device__ __forceinline__ void store(float* p) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            reinterpret_cast<floatx4*>(p)[k] = floatx4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    }
+};
+
+// max |x| over the 32 values of four raw rows, as a float.
+__device__ __forceinline__ float raw_absmax(const Raw4x8<Bf16T>& r) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // bf16 magnitudes order like unsigned integers
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, r.word(e, i) & 0x7fff7fffu));
+    const uint32_t hi = m[0] > m[1] ? m[0] : m[1];
+    return __uint_as_float(hi << 16);
+}
+__device__ __forceinline__ float raw_absmax(const Raw4x8<F32T>& r) {
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(r.get(e, c)));
+    return m;
+}
+
 // Four consecutive values of one channel, held from the producer's prep until
 // they are written as one 8-byte (bf16/fp16) or 16-byte (fp32) transposed
 // entry.
@@ -403,6 +544,12 @@ template <> struct Col4<__bf16> {
         w[1] = __builtin_bit_cast(uint32_t, b);
     }
     __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]); }
+    // channel c of four raw rows, taken as 16-bit halves of the loaded words
+    __device__ __forceinline__ void set_raw(const Raw4x8<Bf16T>& r, int c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        w[0] = __builtin_amdgcn_perm(r.word(1, c >> 1), r.word(0, c >> 1), sel);
+        w[1] = __builtin_amdgcn_perm(r.word(3, c >> 1), r.word(2, c >> 1), sel);
+    }
 };
 template <> struct Col4<_Float16> {
     uint32_t w[2];
@@ -418,6 +565,9 @@ template <> struct Col4<_Float16> {
 template <> struct Col4<float> {
     floatx4 w;
     __device__ __forceinline__ void set(const float* x) { w = floatx4{x[0], x[1], x[2], x[3]}; }
+    __device__ __forceinline__ void set_raw(const Raw4x8<F32T>& r, int c) {
+        w = floatx4{r.get(0, c), r.get(1, c), r.get(2, c), r.get(3, c)};
+    }
     __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<floatx4*>(p) = w; }
 };
 
@@ -432,8 +582,8 @@ __device__ __forceinline__ void st4(float* p, floatx4 x) { *reinterpret_cast<flo
 // Quad (4-lane group) scans of products, r4 = lane & 3.
 template <int CTRL>
 __device__ __forceinline__ float dpp_quad(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x),
-                                                      CTRL, 0xf, 0xf, false));
+    // a quad permutation always has a source lane, so no "old" value is needed
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 // exclusive prefix product (product over lanes r' < r4; 1 for r4 = 0) and the
 // exclusive suffix product (product over lanes r' > r4; 1 for r4 = 3)

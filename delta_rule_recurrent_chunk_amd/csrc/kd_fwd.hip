@@ -122,13 +122,13 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const uint32_t hoff = (uint32_t)h * D;
     const int NC = (T + CH - 1) / CH;
 
-    // ---- producer ownership: rows rb .. rb+3 of sub-block I, channels ch0 .. ch0+7;
-    // the four row quads of a (sub-block, channel group) are one lane quad.
+    // ---- producer ownership: the 16 rows rb .. rb+15 of sub-block I and the two
+    // channels ch0, ch0 + 1 (the decay scans stay inside the lane); at d = 128
+    // each producer wave owns one whole sub-block, so I is wave-uniform.
     const int ptid = tid - NWC * 64;
-    const int r4 = lane & 3;
-    const int pq = (w - NWC) * 16 + (lane >> 2);
-    const int I = pq / (D / 8), ch0 = 8 * (pq % (D / 8));
-    const int rb = SB * I + 4 * r4;
+    const int I = (D == 128) ? __builtin_amdgcn_readfirstlane(w - NWC) : ptid / (D / 2);
+    const int ch0 = 2 * (ptid % (D / 2));
+    const int rb = SB * I;
     // ---- consumer ownership: value columns 32w .. 32w+31
     const int i0 = 32 * w;
 
@@ -179,24 +179,18 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
                 floatx4 Yt[2][NSB];
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) {
-                        Yt[mt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                        Ot[mt][tt] = Yt[mt][tt];
-                    }
-#pragma unroll
                 for (int ks = 0; ks < KD_; ++ks) {
                     const Frag a0 = TR::state_frag(S[0], ks);
                     const Frag a1 = TR::state_frag(S[1], ks);
+                    const floatx4 z = {0.f, 0.f, 0.f, 0.f};   // first K-step: inline-zero accumulator
 #pragma unroll
                     for (int tt = 0; tt < NSB; ++tt) {
                         const Frag bk = TR::ld_state(&sm.Kb[(SB * tt + cl) * LD], ks, g);
                         const Frag bq = TR::ld_state(&sm.Qb[(SB * tt + cl) * LD], ks, g);
-                        Yt[0][tt] = TR::mma(a0, bk, Yt[0][tt]);
-                        Yt[1][tt] = TR::mma(a1, bk, Yt[1][tt]);
-                        Ot[0][tt] = TR::mma(a0, bq, Ot[0][tt]);
-                        Ot[1][tt] = TR::mma(a1, bq, Ot[1][tt]);
+                        Yt[0][tt] = TR::mma(a0, bk, ks ? Yt[0][tt] : z);
+                        Yt[1][tt] = TR::mma(a1, bk, ks ? Yt[1][tt] : z);
+                        Ot[0][tt] = TR::mma(a0, bq, ks ? Ot[0][tt] : z);
+                        Ot[1][tt] = TR::mma(a1, bq, ks ? Ot[1][tt] : z);
                     }
                 }
                 // partial r0[t] = sum over this wave's 32 value columns of Y[t,i] v[t,i]
@@ -285,10 +279,9 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact powers of 2)
                 FragH wb[2][KC_];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int ks = 0; ks < KC_; ++ks)
-                        wb[nt][ks] = TR::row_times_h(&sm.VT[(i0 + 16 * nt + cl) * LDT], sm.u, usc, ks, g);
+                for (int ks = 0; ks < KC_; ++ks)
+                    TR::rows_times_h2(&sm.VT[(i0 + cl) * LDT], &sm.VT[(i0 + 16 + cl) * LDT], sm.u, usc,
+                                      ks, g, wb[0][ks], wb[1][ks]);
 #pragma unroll
                 for (int mj = 0; mj < D / 16; ++mj) {
                     const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc);
@@ -317,17 +310,17 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                         ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] = S[nt][mj][r];
         }
     } else {
-        Raw4x8<TR> rq, rk, rv, rf;          // raw rows of the chunk being prepared
+        Raw16x2<TR> rq, rk, rv, rf;         // raw rows of the chunk being prepared
         float rb_beta = 0.f, rb_c = 0.f;    // beta_t, c_t for t = ptid (ptid < CH)
-        float qpre[8], qsuf[8];             // products over the lane quad's earlier / later rows
-        Col4<E> keep_v[8];                  // v and K-tilde of the prepared chunk, written
-        Col4<Hh> keep_kt[8];                //   transposed in the following stage A
-        unsigned pmask = 0;                 // fallback channels (bit c: ch0 + c) of the prepared chunk
+        float tot[2];                       // product of f over the sub-block, per channel
+        Col16<E> keep_v[2];                 // v and K-tilde of the prepared chunk, written
+        Col16<Hh> keep_kt[2];               //   transposed in the following stage A
+        unsigned pmask = 0;                 // fallback channels (bit cc: ch0 + cc) of the prepared chunk
         auto load_chunk = [&](int n) {
             // Rows past the sequence end re-read the last row (in bounds) and are
             // cleared before use (q = k = v = 0, f = 1, beta = c = 0).
             const int t0 = min(n * CH + rb, T - 1);
-            const int last = min(3, T - 1 - t0);
+            const int last = min(SB - 1, T - 1 - t0);
             const uint32_t off = (uint32_t)t0 * rs + hoff + ch0;
             rq.load(qb, off, rs, last);
             rk.load(kb, off, rs, last);
@@ -350,42 +343,30 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             KD_PHASE_MARK(n, 0);
             if (n >= 0) {   // transposed operands of chunk n
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    keep_v[c].store(&sm.VT[(ch0 + c) * LDT + rb]);
-                    keep_kt[c].store(&sm.KtT[(ch0 + c) * LDT + rb]);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    keep_v[c2].store(&sm.VT[(ch0 + c2) * LDT + rb]);
+                    keep_kt[c2].store(&sm.KtT[(ch0 + c2) * LDT + rb]);
                 }
             }
-            if (prod_on) {   // decay scans of chunk nn
+            if (prod_on) {   // decay products of chunk nn
                 if (nn * CH + CH > T) {   // ragged last chunk: clear rows past the end
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < SB; ++e)
                         if (nn * CH + rb + e >= T) {
                             rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f);
                         }
                     if (ptid < CH && nn * CH + ptid >= T) { rb_beta = 0.f; rb_c = 0.f; }
                 }
-                float tot[8];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    tot[c] = (rf.get(0, c) * rf.get(1, c)) * (rf.get(2, c) * rf.get(3, c));
-                    quad_excl_prod(tot[c], r4, qpre[c], qsuf[c]);
+                for (int c2 = 0; c2 < 2; ++c2) {   // pairwise tree over the 16 rows
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = rf.get(2 * e, c2) * rf.get(2 * e + 1, c2);
+                    tot[c2] = ((x[0] * x[1]) * (x[2] * x[3])) * ((x[4] * x[5]) * (x[6] * x[7]));
                 }
-                if (r4 == 3) {
-                    float sb[8];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) sb[c] = qpre[c] * tot[c];
-                    st8v(&sm.bprod[I][ch0], sb);   // sub-block products
-                }
-                float km = 0.f, vm = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        km = fmaxf(km, fabsf(rk.get(e, c)));
-                        vm = fmaxf(vm, fabsf(rv.get(e, c)));
-                    }
-                km = wave_max_nonneg(km);
-                vm = wave_max_nonneg(vm);
+                st2(&sm.bprod[I][ch0], tot[0], tot[1]);   // sub-block products
+                const float km = wave_max_nonneg(rk.absmax());
+                const float vm = wave_max_nonneg(rv.absmax());
                 if (lane == 0) {   // non-negative floats order like their bit patterns
                     atomicMax(&sm.kmax[nn % 3], __float_as_uint(km));
                     atomicMax(&sm.vmax[nn % 3], __float_as_uint(vm));
@@ -400,68 +381,59 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
             if (prod_on) {   // operands of chunk nn into LDS
-                float plt[8], pgt[8], gC[8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) { plt[c] = 1.f; pgt[c] = 1.f; }
+                // gamma before the sub-block (plt), after it (pgt), over the chunk
+                float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, gC[2], rgC[2];
 #pragma unroll
                 for (int I2 = 0; I2 < NSB; ++I2) {
-#pragma unroll
-                    for (int c4 = 0; c4 < 2; ++c4) {
-                        const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (I2 < I) plt[4 * c4 + e] *= x[e];
-                            if (I2 > I) pgt[4 * c4 + e] *= x[e];
-                        }
-                    }
-                }
-                // within-thread products of f over this thread's four rows:
-                // apre[e] over rows 0..e, asuf[e] over rows e+1..3
-                float apre[4][8], asuf[4][8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    apre[0][c] = rf.get(0, c);
-#pragma unroll
-                    for (int e = 1; e < 4; ++e) apre[e][c] = apre[e - 1][c] * rf.get(e, c);
-                    asuf[3][c] = 1.f;
-#pragma unroll
-                    for (int e = 2; e >= 0; --e) asuf[e][c] = asuf[e + 1][c] * rf.get(e + 1, c);
+                    const float2 x = *reinterpret_cast<const float2*>(&sm.bprod[I2][ch0]);
+                    if (I2 < I) { plt[0] *= x.x; plt[1] *= x.y; }
+                    if (I2 > I) { pgt[0] *= x.x; pgt[1] *= x.y; }
                 }
                 pmask = 0;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    // gamma_C = (earlier sub-blocks) (this sub-block) (later ones)
-                    gC[c] = plt[c] * (qpre[c] * apre[3][c] * qsuf[c]) * pgt[c];
-                    if (!(gC[c] >= kSafeFloor)) pmask |= 1u << c;
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    gC[c2] = (plt[c2] * tot[c2]) * pgt[c2];
+                    // fallback channels get a zero Kc column (their Gram terms are
+                    // added exactly below)
+                    const bool un = !(gC[c2] >= kSafeFloor);
+                    if (un) pmask |= 1u << c2;
+                    rgC[c2] = un ? 0.f : __builtin_amdgcn_rcpf(gC[c2]);
                 }
-                if (I == 0 && r4 == 0) st8v(&sm.gam[nn & 1][ch0], gC);
+                if (I == 0) st2(&sm.gam[nn & 1][ch0], gC[0], gC[1]);
                 if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
                 const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
-                float vcol[8][4], kcol[8][4];
+                // gamma_C / gamma at each row: suffix products within the sub-block
+                float om[SB][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float qo[8], ko[8], co[8];
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    om[SB - 1][c2] = pgt[c2];
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float ga = plt[c] * qpre[c] * apre[e][c];           // gamma at row rb+e
-                        const float om = asuf[e][c] * qsuf[c] * pgt[c];           // gamma_C / gamma
-                        const float kf = rk.get(e, c), qf = rq.get(e, c);
-                        qo[c] = qf * ga;
-                        ko[c] = kf * ga;
-                        co[c] = ((pmask >> c) & 1u) ? 0.f : kf * __builtin_amdgcn_rcpf(ga);
-                        kcol[c][e] = (kf * ksc) * om;
-                        vcol[c][e] = rv.get(e, c);
+                    for (int e = SB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * rf.get(e + 1, c2);
+                }
+                float ga[2] = {plt[0], plt[1]};   // gamma at the current row (running prefix)
+                float kprev[2] = {0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    float qo[2], ko[2], co[2];
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        ga[c2] *= rf.get(e, c2);
+                        const float kf = rk.get(e, c2), qf = rq.get(e, c2);
+                        const float kt = kf * om[e][c2];          // K-tilde
+                        qo[c2] = qf * ga[c2];
+                        ko[c2] = kf * ga[c2];
+                        // k / gamma = K-tilde / gamma_C (no reciprocal per element)
+                        co[c2] = kt * rgC[c2];
+                        if (e & 1) keep_kt[c2].set_pair(e >> 1, kprev[c2], kt * ksc);
+                        else kprev[c2] = kt * ksc;
                     }
-                    st8v(&sm.Qb[(rb + e) * LD + ch0], qo);
-                    st8v(&sm.Kb[(rb + e) * LD + ch0], ko);
-                    st8v(&sm.Kc[(rb + e) * LD + ch0], co);
+                    st2(&sm.Qb[(rb + e) * LD + ch0], qo[0], qo[1]);
+                    st2(&sm.Kb[(rb + e) * LD + ch0], ko[0], ko[1]);
+                    st2(&sm.Kc[(rb + e) * LD + ch0], co[0], co[1]);
                     rv.store(&sm.V[(rb + e) * LD + ch0], e);
                 }
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    keep_v[c].set(vcol[c]);
-                    keep_kt[c].set(kcol[c]);
-                }
+                for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
             }
             // unconditional, clamped to the last chunk (see load_chunk)
             load_chunk(min(nn + 1, NC - 1));
@@ -479,10 +451,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 for (int x = ptid; x < CH * LDM / 4; x += NT - NWC * 64)
                     reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
                 lds_barrier();
-                if (I == 0 && r4 == 0 && pmask) {
+                if (I == 0 && pmask) {
                     const int t0 = nn * CH;
 #pragma unroll 1
-                    for (int c = 0; c < 8; ++c) {
+                    for (int c = 0; c < 2; ++c) {
                         if (!((pmask >> c) & 1u)) continue;
                         const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
 #pragma unroll 1
@@ -506,7 +478,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     // lower-triangular tile list (I_, J_), I_ >= J_
                     const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
                     const int J_ = tile - (I_ * (I_ + 1)) / 2;
-                    floatx4 gk = {0.f, 0.f, 0.f, 0.f}, pp = gk, gv = gk;
+                    floatx4 gk, pp, gv;
                     const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
                     const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
                     const E* aV = &sm.V[(SB * I_ + cl) * LD];
@@ -514,10 +486,11 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     const E* bV = &sm.V[(SB * J_ + cl) * LD];
 #pragma unroll
                     for (int ks = 0; ks < KD_; ++ks) {
+                        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
                         const Frag fk = TR::ld_nat(bK, ks, g);
-                        gk = TR::mma(TR::ld_nat(aK, ks, g), fk, gk);
-                        pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, pp);
-                        gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), gv);
+                        gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
+                        pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
+                        gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
                     }
                     const int s_ = SB * J_ + cl;
                     if (fallback) {
