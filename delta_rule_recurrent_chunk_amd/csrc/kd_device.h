@@ -92,6 +92,18 @@ struct Bf16T {
         bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // Column order of the forward's row-major LDS operands: inside every block
+    // of 32 columns, column j goes to 8*((j % 16) / 4) + 4*((j / 16) % 2) + j % 4,
+    // so the "state" K slice of lane group g is one contiguous 16-byte run.
+    // Contractions over j (the Gram tiles) read both operands in this order,
+    // which leaves their sums unchanged.
+    static __device__ __forceinline__ int pcol(int j) {
+        return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
+    }
+    // state-order fragment from a row stored in pcol order
+    static __device__ __forceinline__ Frag ld_state_p(const E* row, int ks, int g) {
+        return *reinterpret_cast<const Frag*>(row + KS * ks + 8 * g);
+    }
     // B operand from accumulator tiles holding X[j][n] (j = 16mt + 4g + r):
     // K-step ks takes tiles 2ks and 2ks+1, already in the "state" K order.
     static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
@@ -208,6 +220,9 @@ struct F32T {
     static __device__ __forceinline__ Frag ld_state(const E* row, int ks, int g) {
         return row[16 * (ks >> 2) + 4 * g + (ks & 3)];
     }
+    // fp32 fragments are single elements: no column permutation
+    static __device__ __forceinline__ int pcol(int j) { return j; }
+    static __device__ __forceinline__ Frag ld_state_p(const E* row, int ks, int g) { return ld_state(row, ks, g); }
     static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
         return acc[ks >> 2][ks & 3];
     }

@@ -63,6 +63,7 @@ struct FwdSmem {
     static constexpr int LDM = CH + 4;         // fp32 M
     static constexpr int LDP = CH + TR::PAD;   // P
     static constexpr int NWC = D / 32;         // consumer waves
+    // row-major [CH][LD] operands, columns in TR::pcol order
     alignas(16) E Qb[CH * LD];     // q * gamma                     (chunk n+1 from stage B)
     alignas(16) E Kb[CH * LD];     // k * gamma
     alignas(16) E Kc[CH * LD];     // k / gamma, 0 for fallback channels
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const int ptid = tid - NWC * 64;
     const int I = (D == 128) ? __builtin_amdgcn_readfirstlane(w - NWC) : ptid / (D / 2);
     const int ch0 = 2 * (ptid % (D / 2));
+    const int pc0 = TR::pcol(ch0);   // ch0 and ch0 + 1 stay adjacent under pcol
     const int rb = SB * I;
     // ---- consumer ownership: value columns 32w .. 32w+31
     const int i0 = 32 * w;
@@ -185,8 +187,8 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     const floatx4 z = {0.f, 0.f, 0.f, 0.f};   // first K-step: inline-zero accumulator
 #pragma unroll
                     for (int tt = 0; tt < NSB; ++tt) {
-                        const Frag bk = TR::ld_state(&sm.Kb[(SB * tt + cl) * LD], ks, g);
-                        const Frag bq = TR::ld_state(&sm.Qb[(SB * tt + cl) * LD], ks, g);
+                        const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
+                        const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
                         Yt[0][tt] = TR::mma(a0, bk, ks ? Yt[0][tt] : z);
                         Yt[1][tt] = TR::mma(a1, bk, ks ? Yt[1][tt] : z);
                         Ot[0][tt] = TR::mma(a0, bq, ks ? Ot[0][tt] : z);
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     float x = 0.f;
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) {
-                        const E* vr = &sm.V[(SB * tt + cl) * LD + i0 + 16 * mt + 4 * g];
+                        const E* vr = &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 16 * mt + 4 * g)];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) x += Yt[mt][tt][r] * TR::tof(vr[r]);
                     }
@@ -427,10 +429,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                         if (e & 1) keep_kt[c2].set_pair(e >> 1, kprev[c2], kt * ksc);
                         else kprev[c2] = kt * ksc;
                     }
-                    st2(&sm.Qb[(rb + e) * LD + ch0], qo[0], qo[1]);
-                    st2(&sm.Kb[(rb + e) * LD + ch0], ko[0], ko[1]);
-                    st2(&sm.Kc[(rb + e) * LD + ch0], co[0], co[1]);
-                    rv.store(&sm.V[(rb + e) * LD + ch0], e);
+                    st2(&sm.Qb[(rb + e) * LD + pc0], qo[0], qo[1]);
+                    st2(&sm.Kb[(rb + e) * LD + pc0], ko[0], ko[1]);
+                    st2(&sm.Kc[(rb + e) * LD + pc0], co[0], co[1]);
+                    rv.store(&sm.V[(rb + e) * LD + pc0], e);
                 }
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
