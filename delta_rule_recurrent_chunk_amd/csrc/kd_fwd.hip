@@ -318,25 +318,32 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         Col16<E> keep_v[2];                 // v and K-tilde of the prepared chunk, written
         Col16<Hh> keep_kt[2];               //   transposed in the following stage A
         unsigned pmask = 0;                 // fallback channels (bit cc: ch0 + cc) of the prepared chunk
-        auto load_chunk = [&](int n) {
-            // Rows past the sequence end re-read the last row (in bounds) and are
-            // cleared before use (q = k = v = 0, f = 1, beta = c = 0).
+        // Rows past the sequence end re-read the last row (in bounds) and are
+        // cleared before use (q = k = v = 0, f = 1, beta = c = 0).  Every load
+        // is unconditional (clamped to the last chunk), so the prefetch
+        // registers are never merged with older values: a merge makes the
+        // compiler copy them and wait for the loads right away.
+        auto row_off = [&](int n, int& last) {
             const int t0 = min(n * CH + rb, T - 1);
-            const int last = min(SB - 1, T - 1 - t0);
-            const uint32_t off = (uint32_t)t0 * rs + hoff + ch0;
+            last = min(SB - 1, T - 1 - t0);
+            return (uint32_t)t0 * rs + hoff + ch0;
+        };
+        auto load_q = [&](int n) {   // with beta and c (lanes past the first wave re-read its tokens)
+            int last;
+            const uint32_t off = row_off(n, last);
             rq.load(qb, off, rs, last);
-            rk.load(kb, off, rs, last);
-            rv.load(vb, off, rs, last);
-            rf.load(fb, off, rs, last);
-            // every lane loads (lanes past the first wave re-read its tokens), so
-            // the prefetch registers are never merged with older values: a merge
-            // makes the compiler copy them and wait for the loads right away
             const int t = min(n * CH + (ptid & (CH - 1)), T - 1);
             const uint32_t gi = ((uint32_t)t * H + h);
             rb_beta = beta[(size_t)b * T * H + gi];
             rb_c = cc[(size_t)b * T * H + gi];
         };
-        load_chunk(0);
+        auto load_k = [&](int n) { int last; const uint32_t off = row_off(n, last); rk.load(kb, off, rs, last); };
+        auto load_v = [&](int n) { int last; const uint32_t off = row_off(n, last); rv.load(vb, off, rs, last); };
+        auto load_f = [&](int n) { int last; const uint32_t off = row_off(n, last); rf.load(fb, off, rs, last); };
+        load_q(0);
+        load_k(0);
+        load_v(0);
+        load_f(0);
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
@@ -437,8 +444,11 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
             }
-            // unconditional, clamped to the last chunk (see load_chunk)
-            load_chunk(min(nn + 1, NC - 1));
+            // Prefetch of chunk nn + 1, spread over the end of this stage and the
+            // Gram of the next: when every workgroup requested its whole chunk at
+            // once, the issuing wave stalled until HBM drained the burst.
+            const int npf = min(nn + 1, NC - 1);
+            load_q(npf);
             KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
@@ -475,8 +485,12 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 }
                 lds_barrier();
             }
-            if (prod_on) {   // Gram tiles of chunk nn: M and P
-                for (int tile = w - NWC; tile < 10; tile += NWP) {
+            load_k(npf);
+            constexpr int NTPW = (10 + NWP - 1) / NWP;   // Gram tiles per producer wave (at most)
+#pragma unroll
+            for (int it = 0; it < NTPW; ++it) {   // Gram tiles of chunk nn: M and P
+                const int tile = w - NWC + it * NWP;
+                if (prod_on && tile < 10) {
                     // lower-triangular tile list (I_, J_), I_ >= J_
                     const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
                     const int J_ = tile - (I_ * (I_ + 1)) / 2;
@@ -518,6 +532,9 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                         sm.P[nn & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
                     }
                 }
+                // (it is a compile-time constant in each unrolled copy: no branch)
+                if (it == 0) load_v(npf);
+                if (it == 1) load_f(npf);
             }
             KD_PHASE_MARK(n, 5);
             lds_barrier();
