@@ -44,6 +44,8 @@
 //  * Precision: Grams and state reads take bf16 operands; the rank-64 state
 //    update takes fp16 operands with exact power-of-two scales (max |k|,
 //    max |u| * max |v| per chunk), its accumulation is fp32.
+#include <type_traits>
+
 #include "kd_device.h"
 
 // Phase markers: no-ops here; a profiling build may define them to record
@@ -347,17 +349,76 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         load_k(0);
         load_v(0);
         load_f(0);
+        // One lower-triangular 16 x 16 tile (I_ >= J_) of M (DO_M) and / or P
+        // (DO_P) for chunk ch, whose operands are in LDS.  The M part writes
+        // only the strictly lower entries of M; the diagonal and the upper
+        // triangle stay zero, except after the exact fallback, whose P terms
+        // sit there: the P part reads them and clears each entry it read.  The
+        // two parts never touch the same entry, so they may run on different
+        // waves in any order.
+        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch, bool fbk) {
+            constexpr bool DO_M = decltype(do_m)::value, DO_P = decltype(do_p)::value;
+            const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int J_ = tile - (I_ * (I_ + 1)) / 2;
+            floatx4 gk, pp, gv;
+            const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
+            const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
+            const E* aV = &sm.V[(SB * I_ + cl) * LD];
+            const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
+            const E* bV = &sm.V[(SB * J_ + cl) * LD];
+#pragma unroll
+            for (int ks = 0; ks < KD_; ++ks) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                const Frag fk = TR::ld_nat(bK, ks, g);
+                if (DO_M) gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
+                if (DO_P) pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
+                if (DO_M) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
+            }
+            const int s_ = SB * J_ + cl;
+            if (fbk) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = SB * I_ + 4 * g + r;
+                    if (DO_M && s_ < t_) gk[r] += sm.M[t_ * LDM + s_];
+                    if (DO_P && s_ <= t_) {
+                        pp[r] += sm.M[s_ * LDM + t_];
+                        sm.M[s_ * LDM + t_] = 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t_ = SB * I_ + 4 * g + r;
+                if (DO_M && s_ < t_) sm.M[t_ * LDM + s_] = sm.beta[ch & 1][t_] * gk[r] * gv[r];
+                if (DO_P) sm.P[ch & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
+            }
+        };
+        typedef std::integral_constant<bool, true> kYes;
+        typedef std::integral_constant<bool, false> kNo;
+        // Gram tiles per producer wave.  At d = 128 tiles 8 and 9 wait for the
+        // next stage A, where the producers have slack (their M entries are
+        // first read by the forward substitution of stage B, their P entries by
+        // the readout of stage C), split over the four producer waves: the M
+        // parts on the first two, the P parts on the other two.
+        constexpr int NTPW = (10 + NWP - 1) / NWP;
+        constexpr int NTPW_C = (D == 128) ? 2 : NTPW;
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
             const bool prod_on = nn < NC;
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
-            if (n >= 0) {   // transposed operands of chunk n
+            if (n >= 0) {   // transposed operands of chunk n, and its remaining Gram tiles
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
                     keep_v[c2].store(&sm.VT[(ch0 + c2) * LDT + rb]);
                     keep_kt[c2].store(&sm.KtT[(ch0 + c2) * LDT + rb]);
+                }
+                if (D == 128) {
+                    const int pw = w - NWC;   // producer wave 0..3
+                    const bool fbk = sm.unsafe[n % 3] != 0u;
+                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n, fbk);
+                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n, fbk);
                 }
             }
             if (prod_on) {   // decay products of chunk nn
@@ -489,52 +550,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 lds_barrier();
             }
             load_k(npf);
-            constexpr int NTPW = (10 + NWP - 1) / NWP;   // Gram tiles per producer wave (at most)
 #pragma unroll
-            for (int it = 0; it < NTPW; ++it) {   // Gram tiles of chunk nn: M and P
+            for (int it = 0; it < NTPW_C; ++it) {   // Gram tiles of chunk nn: M and P
                 const int tile = w - NWC + it * NWP;
-                if (prod_on && tile < 10) {
-                    // lower-triangular tile list (I_, J_), I_ >= J_
-                    const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-                    const int J_ = tile - (I_ * (I_ + 1)) / 2;
-                    floatx4 gk, pp, gv;
-                    const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
-                    const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
-                    const E* aV = &sm.V[(SB * I_ + cl) * LD];
-                    const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
-                    const E* bV = &sm.V[(SB * J_ + cl) * LD];
-#pragma unroll
-                    for (int ks = 0; ks < KD_; ++ks) {
-                        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                        const Frag fk = TR::ld_nat(bK, ks, g);
-                        gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
-                        pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
-                        gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
-                    }
-                    const int s_ = SB * J_ + cl;
-                    if (fallback) {
-                        float ck[4], cp[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t_ = SB * I_ + 4 * g + r;
-                            ck[r] = (s_ < t_) ? sm.M[t_ * LDM + s_] : 0.f;
-                            cp[r] = (s_ <= t_) ? sm.M[s_ * LDM + t_] : 0.f;
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            gk[r] += ck[r];
-                            pp[r] += cp[r];
-                            const int t_ = SB * I_ + 4 * g + r;
-                            if (I_ != J_) sm.M[s_ * LDM + t_] = 0.f;   // mirror upper tile back to zero
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t_ = SB * I_ + 4 * g + r;
-                        sm.M[t_ * LDM + s_] = (s_ < t_) ? sm.beta[nn & 1][t_] * gk[r] * gv[r] : 0.f;
-                        sm.P[nn & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
-                    }
-                }
+                if (prod_on && tile < 10) gram_tile(kYes(), kYes(), tile, nn, fallback);
                 // (it is a compile-time constant in each unrolled copy: no branch)
                 if (it == 0) load_v(npf);
                 if (it == 1) load_f(npf);
