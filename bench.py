@@ -31,7 +31,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "Kron-delta chunked fwd tokens/s (H=16,d=128) and % MFMA/HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kd_fwd_train_step_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "delta_rule_recurrent_chunk_amd", "csrc", n)
-                  for n in ("kd_fwd.hip", "kd_device.h")]
+                  for n in ("kd_fwd.hip", "kd_fwd16.hip", "kd_device.h")]
 COPY_ELEMS = 1 << 28     # calibration copy: 2^28 fp32 = 1 GiB read and 1 GiB written
 
 

@@ -524,6 +524,60 @@ template <> struct Col16<float> {
     }
 };
 
+// Eight consecutive tokens of two adjacent channels ch0, ch0 + 1 (bf16): one
+// 4-byte load per row, so a wave whose lanes cover adjacent channel pairs
+// reads whole rows.
+struct Raw8x2 {
+    uint32_t w[8];   // row e: channel ch0 in the low half, ch0 + 1 in the high half
+    // p: wave-uniform base; row e at 32-bit element offset off + min(e, last)*stride.
+    __device__ __forceinline__ void load(const __bf16* p, uint32_t off, uint32_t stride, int last) {
+        const char* base = reinterpret_cast<const char*>(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            w[e] = *reinterpret_cast<const uint32_t*>(base + (off + (uint32_t)(e < last ? e : last) * stride) * 2u);
+    }
+    __device__ __forceinline__ float get(int e, int cc) const {
+        return __uint_as_float(cc ? (w[e] & 0xffff0000u) : (w[e] << 16));
+    }
+    __device__ __forceinline__ void clear(int e, float fill) {
+        const uint32_t fb = __float_as_uint(fill) >> 16;
+        w[e] = fb | (fb << 16);
+    }
+    __device__ __forceinline__ void store(__bf16* dst, int e) const { *reinterpret_cast<uint32_t*>(dst) = w[e]; }
+    // max |x| over the 16 values
+    __device__ __forceinline__ float absmax() const {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)   // bf16 magnitudes order like unsigned integers
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[e] & 0x7fff7fffu));
+        const uint32_t hi = m[0] > m[1] ? m[0] : m[1];
+        return __uint_as_float(hi << 16);
+    }
+};
+
+// Eight consecutive tokens of one channel (16 bytes), written as one
+// transposed entry.
+struct Col8 {
+    uint32_t w[4];
+    // channel cc of raw rows, taken as 16-bit halves of the loaded words
+    __device__ __forceinline__ void set_raw(const Raw8x2& r, int cc) {
+        const uint32_t sel = cc ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = __builtin_amdgcn_perm(r.w[2 * k + 1], r.w[2 * k], sel);
+    }
+    // tokens 2k, 2k + 1 as fp16
+    __device__ __forceinline__ void set_pair_h(int k, float a, float b) {
+        _Float16 __attribute__((ext_vector_type(2))) x;
+        x[0] = (_Float16)a;
+        x[1] = (_Float16)b;
+        w[k] = __builtin_bit_cast(uint32_t, x);
+    }
+    __device__ __forceinline__ void store(void* p) const {
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+
 // max |x| over the 32 values of four raw rows, as a float.
 __device__ __forceinline__ float raw_absmax(const Raw4x8<Bf16T>& r) {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));

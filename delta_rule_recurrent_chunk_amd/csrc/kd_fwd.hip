@@ -583,6 +583,10 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, cons
     return hipGetLastError();
 }
 
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
+                        const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
+                        int B, int T, int H, hipStream_t st);
+
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
                       void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st)
@@ -592,7 +596,7 @@ hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void*
         switch (d) {
         case 32: return launch_fwd_t<Bf16T, 32>(KD_FWD_ARGS);
         case 64: return launch_fwd_t<Bf16T, 64>(KD_FWD_ARGS);
-        case 128: return launch_fwd_t<Bf16T, 128>(KD_FWD_ARGS);
+        case 128: return launch_fwd16(KD_FWD_ARGS);   // sixteen-wave kernel (kd_fwd16.hip)
         }
     } else {
         switch (d) {

@@ -1,0 +1,490 @@
+// kd_fwd16.hip -- chunkwise forward for bf16 inputs at d = 128, sixteen waves
+// per (b, h).
+//
+// Same method, chunk algebra and software pipeline as the generic forward
+// kernel (kd_fwd.hip; onedev.kr KronLSTM summary, sections "어떻게 동작하나"
+// and "어떻게 쓰나"; aitrends.kr Gated DeltaNet-2 summary, section "방법론"
+// steps 3-4): per chunk n,
+//     (I + M) u = c - beta * r0,  r0_t = v_t^T S0 Kbar_t,
+//     O = Qbar S0^T + P (u * V),  S_C = S0 diag(gamma_C) + (u * V)^T Ktilde.
+// What changes is the split of the work: each role has eight waves, so every
+// SIMD holds two consumer and two producer waves (128 registers each) and
+// one wave's LDS, matrix-core or dependency wait is covered by the others.
+//   consumers (waves 0..7): 16 value columns of the fp32 state each, held
+//     transposed as MFMA accumulators (S^T[j][i], key index j as rows);
+//     state reads, the forward substitution (wave 0), readout and update.
+//   producers (waves 8..15): 8 rows of the chunk being prepared each, two
+//     adjacent key channels per lane; decay products, operands, Gram tiles.
+// Stage A: state reads of n | transposed operands of n, decay products of n+1.
+// Stage B: substitution of n | operands of n+1, first prefetch of n+2.
+// Stage C: readout and update of n | Gram tiles of n+1, rest of the prefetch.
+#include <type_traits>
+
+#include "kd_device.h"
+
+namespace kd {
+
+namespace f16w {
+constexpr int D = 128;
+constexpr int NT = 1024;
+constexpr int NWC = 8;            // consumer waves
+constexpr int NWP = 8;            // producer waves
+constexpr int RB = CH / NWP;      // rows per producer wave
+constexpr int LD = D + 16;        // row-major [CH][D] operands (columns in pcol order)
+constexpr int LDT = CH + 8;       // transposed [D][CH] operands
+constexpr int LDM = CH + 4;       // fp32 M
+constexpr int LDP = CH + 8;       // P
+}  // namespace f16w
+
+struct Fwd16Smem {
+    alignas(16) __bf16 Qb[CH * f16w::LD];       // q * gamma
+    alignas(16) __bf16 Kb[CH * f16w::LD];       // k * gamma
+    alignas(16) __bf16 Kc[CH * f16w::LD];       // k / gamma (0 for fallback channels)
+    alignas(16) __bf16 V[CH * f16w::LD];        // v
+    alignas(16) __bf16 VT[f16w::D * f16w::LDT];     // v^T
+    alignas(16) _Float16 KtT[f16w::D * f16w::LDT];  // (k gamma_C / gamma)^T * kscale
+    alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V); fallback scratch
+    alignas(16) __bf16 P[2][CH * f16w::LDP];    // tril_0 of the decayed Q K^T, by chunk parity
+    alignas(16) float beta[2][CH];
+    alignas(16) float c[2][CH];
+    alignas(16) float u[CH];
+    alignas(16) float r0p[f16w::NWC][CH];
+    alignas(16) float bprod[f16w::NWP][f16w::D];   // product of f over each 8-row block
+    alignas(16) float gam[2][f16w::D];             // gamma_C, by chunk parity
+    unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
+    unsigned umax;                          // max |u| of the current chunk (bits)
+};
+
+// CKPT: also store, per chunk, the entering state (S[i][j], bf16) and u, r0.
+template <bool CKPT>
+__global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
+    const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
+    __bf16* __restrict__ ckptS, float* __restrict__ ckptU, int T, int H)
+{
+    using namespace f16w;
+    typedef Bf16T TR;
+    typedef __bf16 E;
+    typedef TR::Frag Frag;
+    typedef TR::FragH FragH;
+    constexpr int KD_ = D / TR::KS;    // K-steps over d
+    constexpr int KC_ = CH / TR::KS;   // K-steps over a chunk
+
+    __shared__ Fwd16Smem sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool consumer = w < NWC;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    // per batch element, [T, H, D] tensors are addressed from a wave-uniform
+    // base with 32-bit element offsets (the host checks T*H*D fits)
+    const uint32_t rs = (uint32_t)H * D;
+    const size_t bbase = (size_t)b * T * H * D;
+    const E* qb = q + bbase;
+    const E* kb = k + bbase;
+    const E* vb = v + bbase;
+    const E* fb = f + bbase;
+    E* ob = o ? o + bbase : nullptr;
+    const uint32_t hoff = (uint32_t)h * D;
+    const int NC = (T + CH - 1) / CH;
+
+    if (NC == 0) {   // empty sequence: S_T = S0
+        if (ST)
+            for (int x = tid; x < D * D; x += NT)
+                ST[(size_t)bh * D * D + x] = S0 ? S0[(size_t)bh * D * D + x] : 0.f;
+        return;
+    }
+
+    // one-time init: the upper triangles of M and P are never written
+    for (int x = tid; x < 2 * CH * LDP; x += NT) (&sm.P[0][0])[x] = TR::cvt(0.f);
+    for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
+    if (tid == 0) {
+        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; sm.unsafe[s] = 0u; }
+        sm.umax = 0u;
+    }
+    lds_barrier();
+
+    // Both teams run the same sequence of barriers (three per chunk, two more
+    // in a stage C whose next chunk takes the exact fallback).
+    if (consumer) {
+        const int i0 = 16 * w;   // value columns i0 .. i0 + 15
+        const uint32_t o_lane = (uint32_t)cl * rs + hoff + i0 + 4 * g;
+        floatx4 S[D / 16];       // S^T[16mj + 4g + r][i0 + cl] in S[mj][r]
+#pragma unroll
+        for (int mj = 0; mj < D / 16; ++mj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[mj][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] : 0.f;
+
+        for (int n = -1; n < NC; ++n) {
+            const int nn = n + 1;
+            // ======================================================= stage A
+            floatx4 Ot[NSB];   // O^T[i0 + 4g + r][16tt + cl], lives to stage C
+            if (n >= 0) {
+                if (CKPT) {
+                    E* dst = ckptS + ((size_t)bh * NC + n) * D * D;
+#pragma unroll
+                    for (int mj = 0; mj < D / 16; ++mj)
+                        st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj]);
+                }
+                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index, N = token)
+                floatx4 Yt[NSB];
+#pragma unroll
+                for (int ks = 0; ks < KD_; ++ks) {
+                    const Frag a = TR::state_frag(S, ks);
+                    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) {
+                        const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
+                        const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
+                        Yt[tt] = TR::mma(a, bk, ks ? Yt[tt] : z);
+                        Ot[tt] = TR::mma(a, bq, ks ? Ot[tt] : z);
+                    }
+                }
+                // partial r0[t] over this wave's 16 value columns
+#pragma unroll
+                for (int tt = 0; tt < NSB; ++tt) {
+                    // value columns i0 + 4g .. i0 + 4g + 3 are adjacent under pcol
+                    const bf16x4 vr = *reinterpret_cast<const bf16x4*>(
+                        &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 4 * g)]);
+                    float x = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x += Yt[tt][r] * TR::tof(vr[r]);
+                    x += __shfl_xor(x, 16, 64);
+                    x += __shfl_xor(x, 32, 64);
+                    if (g == 0) sm.r0p[w][SB * tt + cl] = x;
+                }
+            }
+            lds_barrier();
+            // ======================================================= stage B
+            if (n >= 0 && w == 0) {   // forward substitution (I + M) u = c - beta r0
+                const int t_ = lane;
+                float r0 = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NWC; ++ww) r0 += sm.r0p[ww][t_];
+                float x = sm.c[n & 1][t_] - sm.beta[n & 1][t_] * r0;
+                // M is strictly lower triangular (zeros elsewhere): lane t only
+                // changes while s < t, no mask needed
+#pragma unroll
+                for (int sb = 0; sb < CH / 16; ++sb) {
+                    float Mrow[16];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t_ * LDM + 16 * sb + 4 * s4]);
+                        Mrow[4 * s4] = m4[0]; Mrow[4 * s4 + 1] = m4[1];
+                        Mrow[4 * s4 + 2] = m4[2]; Mrow[4 * s4 + 3] = m4[3];
+                    }
+#pragma unroll
+                    for (int s = 0; s < 16; ++s)
+                        if (16 * sb + s < CH - 1) x = fmaf(-Mrow[s], readlane_f(x, 16 * sb + s), x);
+                }
+                sm.u[t_] = x;
+                if (CKPT) {
+                    float* du = ckptU + ((size_t)bh * NC + n) * 2 * CH;
+                    du[t_] = x;
+                    du[CH + t_] = r0;
+                }
+                const float um = wave_max_nonneg(fabsf(x));
+                if (lane == 0) sm.umax = __float_as_uint(um);
+            }
+            if (tid == 0 && n >= 0) {
+                // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
+                // the previous stage C, the latter's first writer runs in stage A(n+1)
+                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
+            }
+            lds_barrier();
+            // ======================================================= stage C
+            if (nn < NC && sm.unsafe[nn % 3] != 0u) {   // producers run the exact fallback
+                lds_barrier();
+                lds_barrier();
+            }
+            if (n >= 0) {
+                const float usc = pow2_scale(__uint_as_float(sm.umax) * __uint_as_float(sm.vmax[n % 3]));
+                const float ksc = pow2_scale(__uint_as_float(sm.kmax[n % 3]));
+                const float inv = 1.f / (usc * ksc);
+                // O^T += W^T P^T with W = u * V
+#pragma unroll
+                for (int ks = 0; ks < KC_; ++ks) {
+                    const Frag wa = TR::row_times(&sm.VT[(i0 + cl) * LDT], sm.u, ks, g);
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt)
+                        Ot[tt] = TR::mma(wa, TR::ld_nat(&sm.P[n & 1][(SB * tt + cl) * LDP], ks, g), Ot[tt]);
+                }
+                if (ob) {
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) {
+                        // row offset = scalar part + this lane's part (one register
+                        // across the loop instead of one per tt)
+                        const uint32_t srow = __builtin_amdgcn_readfirstlane((uint32_t)(n * CH + SB * tt) * rs);
+                        if (n * CH + SB * tt + cl < T) st4(ob + (srow + o_lane), Ot[tt]);
+                    }
+                }
+                // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact powers of 2)
+                FragH wb[KC_];
+#pragma unroll
+                for (int ks = 0; ks < KC_; ++ks) wb[ks] = TR::row_times_h(&sm.VT[(i0 + cl) * LDT], sm.u, usc, ks, g);
+#pragma unroll
+                for (int mj = 0; mj < D / 16; ++mj) {
+                    const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc);
+                    S[mj] = S[mj] * gm;
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks)
+                        S[mj] = TR::mma_h(TR::ld_nat_h(&sm.KtT[(16 * mj + cl) * LDT], ks, g), wb[ks], S[mj]);
+                    S[mj] = S[mj] * inv;
+                }
+            }
+            lds_barrier();
+        }
+        if (ST) {
+#pragma unroll
+            for (int mj = 0; mj < D / 16; ++mj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] = S[mj][r];
+        }
+    } else {
+        const int pw = w - NWC;          // producer wave 0..7 (wave-uniform)
+        const int rb = RB * pw;          // rows rb .. rb + 7 of the chunk
+        const int ch0 = 2 * lane;        // channels ch0, ch0 + 1
+        const int pc0 = TR::pcol(ch0);   // adjacent under pcol
+        Raw8x2 rq, rk, rv, rf;           // raw rows of the chunk being prepared
+        float rb_beta = 0.f, rb_c = 0.f; // beta_t, c_t for t = lane (used by wave 0)
+        float tot[2];                    // product of f over the 8 rows, per channel
+        Col8 keep_v[2], keep_kt[2];      // v and K-tilde of the prepared chunk, written
+                                         //   transposed in the following stage A
+        unsigned pmask = 0;              // fallback channels (bit cc: ch0 + cc)
+        // Rows past the sequence end re-read the last row (in bounds) and are
+        // cleared before use.  Loads are unconditional (clamped to the last
+        // chunk) so the prefetch registers never merge with older values.
+        auto row_off = [&](int n, int& last) {
+            const int t0 = min(n * CH + rb, T - 1);
+            last = min(RB - 1, T - 1 - t0);
+            return (uint32_t)t0 * rs + hoff + ch0;
+        };
+        auto load_q = [&](int n) {
+            int last;
+            const uint32_t off = row_off(n, last);
+            rq.load(qb, off, rs, last);
+            const int t = min(n * CH + lane, T - 1);
+            const uint32_t gi = (uint32_t)t * H + h;
+            rb_beta = beta[(size_t)b * T * H + gi];
+            rb_c = cc[(size_t)b * T * H + gi];
+        };
+        auto load_k = [&](int n) { int last; const uint32_t off = row_off(n, last); rk.load(kb, off, rs, last); };
+        auto load_v = [&](int n) { int last; const uint32_t off = row_off(n, last); rv.load(vb, off, rs, last); };
+        auto load_f = [&](int n) { int last; const uint32_t off = row_off(n, last); rf.load(fb, off, rs, last); };
+        load_q(0);
+        load_k(0);
+        load_v(0);
+        load_f(0);
+        // One lower-triangular 16 x 16 tile (I_ >= J_) of M (DO_M) and / or P
+        // (DO_P) for chunk ch.  The M part writes only the strictly lower
+        // entries of M; after the exact fallback, whose P terms sit on and
+        // above the diagonal of M, the P part reads and clears them.  The two
+        // parts never touch the same entry.
+        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch, bool fbk) {
+            constexpr bool DO_M = decltype(do_m)::value, DO_P = decltype(do_p)::value;
+            const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int J_ = tile - (I_ * (I_ + 1)) / 2;
+            floatx4 gk, pp, gv;
+            const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
+            const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
+            const E* aV = &sm.V[(SB * I_ + cl) * LD];
+            const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
+            const E* bV = &sm.V[(SB * J_ + cl) * LD];
+#pragma unroll
+            for (int ks = 0; ks < KD_; ++ks) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                const Frag fk = TR::ld_nat(bK, ks, g);
+                if (DO_M) gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
+                if (DO_P) pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
+                if (DO_M) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
+            }
+            const int s_ = SB * J_ + cl;
+            if (fbk) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = SB * I_ + 4 * g + r;
+                    if (DO_M && s_ < t_) gk[r] += sm.M[t_ * LDM + s_];
+                    if (DO_P && s_ <= t_) {
+                        pp[r] += sm.M[s_ * LDM + t_];
+                        sm.M[s_ * LDM + t_] = 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t_ = SB * I_ + 4 * g + r;
+                if (DO_M && s_ < t_) sm.M[t_ * LDM + s_] = sm.beta[ch & 1][t_] * gk[r] * gv[r];
+                if (DO_P) sm.P[ch & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
+            }
+        };
+        typedef std::integral_constant<bool, true> kYes;
+        typedef std::integral_constant<bool, false> kNo;
+
+        for (int n = -1; n < NC; ++n) {
+            const int nn = n + 1;             // chunk the producers prepare
+            const bool prod_on = nn < NC;
+            // ======================================================= stage A
+            if (n >= 0) {   // transposed operands of chunk n and its last two Gram tiles
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    keep_v[c2].store(&sm.VT[(ch0 + c2) * LDT + rb]);
+                    keep_kt[c2].store(&sm.KtT[(ch0 + c2) * LDT + rb]);
+                }
+                // tiles 8 and 9 (rows 48..63) are first read by the substitution
+                // (M) and the readout (P) of chunk n: their M and P parts run
+                // here on producer waves 0..3, one SIMD each
+                if (pw < 4) {
+                    const bool fbk = sm.unsafe[n % 3] != 0u;
+                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n, fbk);
+                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n, fbk);
+                }
+            }
+            if (prod_on) {   // decay products of chunk nn
+                if (nn * CH + CH > T) {   // ragged last chunk: clear rows past the end
+#pragma unroll
+                    for (int e = 0; e < RB; ++e)
+                        if (nn * CH + rb + e >= T) {
+                            rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f);
+                        }
+                    if (nn * CH + lane >= T) { rb_beta = 0.f; rb_c = 0.f; }
+                }
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {   // pairwise tree over the 8 rows
+                    const float x0 = rf.get(0, c2) * rf.get(1, c2), x1 = rf.get(2, c2) * rf.get(3, c2);
+                    const float x2 = rf.get(4, c2) * rf.get(5, c2), x3 = rf.get(6, c2) * rf.get(7, c2);
+                    tot[c2] = (x0 * x1) * (x2 * x3);
+                }
+                st2(&sm.bprod[pw][ch0], tot[0], tot[1]);
+                const float km = wave_max_nonneg(rk.absmax());
+                const float vm = wave_max_nonneg(rv.absmax());
+                if (lane == 0) {   // non-negative floats order like their bit patterns
+                    atomicMax(&sm.kmax[nn % 3], __float_as_uint(km));
+                    atomicMax(&sm.vmax[nn % 3], __float_as_uint(vm));
+                }
+                if (pw == 0) {
+                    sm.beta[nn & 1][lane] = rb_beta;
+                    sm.c[nn & 1][lane] = rb_c;
+                }
+            }
+            lds_barrier();
+            // ======================================================= stage B
+            if (prod_on) {   // operands of chunk nn into LDS
+                // gamma before this block (plt), after it (pgt), and over the chunk
+                // (gC, multiplied in one fixed order so every wave agrees on it)
+                float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, gC[2] = {1.f, 1.f}, rgC[2];
+#pragma unroll
+                for (int p = 0; p < NWP; ++p) {
+                    const float2 x = *reinterpret_cast<const float2*>(&sm.bprod[p][ch0]);
+                    gC[0] *= x.x; gC[1] *= x.y;
+                    if (p < pw) { plt[0] *= x.x; plt[1] *= x.y; }
+                    if (p > pw) { pgt[0] *= x.x; pgt[1] *= x.y; }
+                }
+                pmask = 0;
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    // fallback channels get a zero Kc column (their Gram terms are
+                    // added exactly in stage C)
+                    const bool un = !(gC[c2] >= kSafeFloor);
+                    if (un) pmask |= 1u << c2;
+                    rgC[c2] = un ? 0.f : __builtin_amdgcn_rcpf(gC[c2]);
+                }
+                if (pw == 0) st2(&sm.gam[nn & 1][ch0], gC[0], gC[1]);
+                if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
+                const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
+                // gamma_C / gamma at each row: suffix products within the block
+                float om[RB][2];
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    om[RB - 1][c2] = pgt[c2];
+#pragma unroll
+                    for (int e = RB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * rf.get(e + 1, c2);
+                }
+                float ga[2] = {plt[0], plt[1]};   // gamma at the current row
+                float kprev[2] = {0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < RB; ++e) {
+                    float qo[2], ko[2], co[2];
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        ga[c2] *= rf.get(e, c2);
+                        const float kf = rk.get(e, c2), qf = rq.get(e, c2);
+                        const float kt = kf * om[e][c2];   // K-tilde
+                        qo[c2] = qf * ga[c2];
+                        ko[c2] = kf * ga[c2];
+                        co[c2] = kt * rgC[c2];             // k / gamma = K-tilde / gamma_C
+                        if (e & 1) keep_kt[c2].set_pair_h(e >> 1, kprev[c2], kt * ksc);
+                        else kprev[c2] = kt * ksc;
+                    }
+                    st2(&sm.Qb[(rb + e) * LD + pc0], qo[0], qo[1]);
+                    st2(&sm.Kb[(rb + e) * LD + pc0], ko[0], ko[1]);
+                    st2(&sm.Kc[(rb + e) * LD + pc0], co[0], co[1]);
+                    rv.store(&sm.V[(rb + e) * LD + pc0], e);
+                }
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
+            }
+            const int npf = min(nn + 1, NC - 1);   // prefetch of chunk nn + 1
+            load_q(npf);
+            lds_barrier();
+            // ======================================================= stage C
+            const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
+            if (fallback) {
+                // Exact Gram terms of the key channels of chunk nn whose decay is
+                // below the floor: G_K[t,s] (s<t) accumulates at M[t][s], P[t,s]
+                // (s<t) at M[s][t], P[t,t] at M[t][t].  Rare path: rows are
+                // re-read from global memory.
+                for (int x = tid - NWC * 64; x < CH * LDM / 4; x += NWP * 64)
+                    reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+                lds_barrier();
+                if (pw == 0 && pmask) {
+                    const int t0 = nn * CH;
+#pragma unroll 1
+                    for (int c = 0; c < 2; ++c) {
+                        if (!((pmask >> c) & 1u)) continue;
+                        const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
+#pragma unroll 1
+                        for (int s = 0; s < CH && t0 + s < T; ++s) {
+                            const float ks_ = TR::tof(kb[off + s * rs]);
+                            atomicAdd(&sm.M[s * LDM + s], TR::tof(qb[off + s * rs]) * ks_);
+                            float prod = 1.f;
+#pragma unroll 1
+                            for (int t = s + 1; t < CH && t0 + t < T; ++t) {
+                                prod *= TR::tof(fb[off + t * rs]);
+                                atomicAdd(&sm.M[t * LDM + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
+                                atomicAdd(&sm.M[s * LDM + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
+                            }
+                        }
+                    }
+                }
+                lds_barrier();
+            }
+            load_k(npf);
+            if (prod_on) gram_tile(kYes(), kYes(), pw, nn, fallback);   // tiles 0..7
+            load_v(npf);
+            load_f(npf);
+            lds_barrier();
+        }
+    }
+}
+
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
+                        const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
+                        int B, int T, int H, hipStream_t st)
+{
+    typedef __bf16 E;
+    if (ckptS)
+        hipLaunchKernelGGL(kd_fwd16_kernel<true>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
+                           (E*)ckptS, ckptU, T, H);
+    else
+        hipLaunchKernelGGL(kd_fwd16_kernel<false>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
+                           (E*)nullptr, (float*)nullptr, T, H);
+    return hipGetLastError();
+}
+
+}  // namespace kd
