@@ -232,8 +232,8 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_fwd_kernel<Bf16T,128>" if not w.backward else
-                     "kd_fwd_kernel + kd_fwd_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
+                     "kernel": "kd_fwd16_kernel<false>" if not w.backward else
+                     "kd_fwd16_kernel + kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,
                      },

@@ -182,6 +182,22 @@ struct Bf16T {
         for (int e = 0; e < 4; ++e) r[4 + e] = (_Float16)((u1[e] * su) * tof(x[4 + e]));
         return r;
     }
+    // row_times (bf16) and row_times_h (fp16, u scaled by su) from one read of
+    // the row and of u
+    static __device__ __forceinline__ void row_times_both(const E* row, const float* u, float su, int ks,
+                                                          int g, Frag& wa, FragH& wb) {
+        const int t0 = KS * ks + 8 * g;
+        const Frag x = *reinterpret_cast<const Frag*>(row + t0);
+        const floatx4 u0 = *reinterpret_cast<const floatx4*>(u + t0);
+        const floatx4 u1 = *reinterpret_cast<const floatx4*>(u + t0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wa[e] = cvt(u0[e] * tof(x[e]));
+            wa[4 + e] = cvt(u1[e] * tof(x[4 + e]));
+            wb[e] = (_Float16)((u0[e] * su) * tof(x[e]));
+            wb[4 + e] = (_Float16)((u1[e] * su) * tof(x[4 + e]));
+        }
+    }
     // the same for two rows sharing one scaled slice of u
     static __device__ __forceinline__ void rows_times_h2(const E* row0, const E* row1, const float* u,
                                                          float su, int ks, int g, FragH& r0, FragH& r1) {

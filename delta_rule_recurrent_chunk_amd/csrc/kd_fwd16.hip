@@ -22,6 +22,12 @@
 
 #include "kd_device.h"
 
+// Phase markers: no-ops here; a profiling build may define them to record
+// timestamps at the stage boundaries of the chunk loop.
+#ifndef KD_PHASE_MARK
+#define KD_PHASE_MARK(chunk, id) ((void)0)
+#endif
+
 namespace kd {
 
 namespace f16w {
@@ -34,6 +40,7 @@ constexpr int LD = D + 16;        // row-major [CH][D] operands (columns in pcol
 constexpr int LDT = CH + 8;       // transposed [D][CH] operands
 constexpr int LDM = CH + 4;       // fp32 M
 constexpr int LDP = CH + 8;       // P
+constexpr int LDR = 4 * NWC + 4;  // r0 partials per token (row stride 36: conflict-free stores)
 }  // namespace f16w
 
 struct Fwd16Smem {
@@ -48,7 +55,7 @@ struct Fwd16Smem {
     alignas(16) float beta[2][CH];
     alignas(16) float c[2][CH];
     alignas(16) float u[CH];
-    alignas(16) float r0p[f16w::NWC][CH];
+    alignas(16) float r0q[CH * f16w::LDR];     // r0 partials: [t][4 * wave + lane group]
     alignas(16) float bprod[f16w::NWP][f16w::D];   // product of f over each 8-row block
     alignas(16) float gam[2][f16w::D];             // gamma_C, by chunk parity
     unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
@@ -121,6 +128,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;
             // ======================================================= stage A
+            KD_PHASE_MARK(n, 0);
             floatx4 Ot[NSB];   // O^T[i0 + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
                 if (CKPT) {
@@ -129,41 +137,63 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int mj = 0; mj < D / 16; ++mj)
                         st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj]);
                 }
-                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index, N = token)
-                floatx4 Yt[NSB];
+                // Y^T = S Kbar^T, then O^T = S Qbar^T (M = value index, N = token).
+                // The B fragments of the next K-step are loaded before the MFMAs
+                // of this one.
+                auto state_pass = [&](const E* op, floatx4* acc) {
+                    Frag bc[NSB];
 #pragma unroll
-                for (int ks = 0; ks < KD_; ++ks) {
-                    const Frag a = TR::state_frag(S, ks);
-                    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                    for (int tt = 0; tt < NSB; ++tt) bc[tt] = TR::ld_state_p(&op[(SB * tt + cl) * LD], 0, g);
+#pragma unroll
+                    for (int ks = 0; ks < KD_; ++ks) {
+                        Frag bn[NSB];
+                        if (ks + 1 < KD_) {
+#pragma unroll
+                            for (int tt = 0; tt < NSB; ++tt) bn[tt] = TR::ld_state_p(&op[(SB * tt + cl) * LD], ks + 1, g);
+                        }
+                        const Frag a = TR::state_frag(S, ks);
+                        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int tt = 0; tt < NSB; ++tt) acc[tt] = TR::mma(a, bc[tt], ks ? acc[tt] : z);
+                        if (ks + 1 < KD_) {
+#pragma unroll
+                            for (int tt = 0; tt < NSB; ++tt) bc[tt] = bn[tt];
+                        }
+                    }
+                };
+                {
+                    floatx4 Yt[NSB];
+                    state_pass(sm.Kb, Yt);
+                    // partial r0[t] over value columns i0 + 4g .. i0 + 4g + 3 (adjacent
+                    // under pcol); the substitution wave adds the 32 partials of t
 #pragma unroll
                     for (int tt = 0; tt < NSB; ++tt) {
-                        const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
-                        const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
-                        Yt[tt] = TR::mma(a, bk, ks ? Yt[tt] : z);
-                        Ot[tt] = TR::mma(a, bq, ks ? Ot[tt] : z);
+                        const bf16x4 vr = *reinterpret_cast<const bf16x4*>(
+                            &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 4 * g)]);
+                        float x = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x += Yt[tt][r] * TR::tof(vr[r]);
+                        sm.r0q[(SB * tt + cl) * LDR + 4 * w + g] = x;
                     }
                 }
-                // partial r0[t] over this wave's 16 value columns
-#pragma unroll
-                for (int tt = 0; tt < NSB; ++tt) {
-                    // value columns i0 + 4g .. i0 + 4g + 3 are adjacent under pcol
-                    const bf16x4 vr = *reinterpret_cast<const bf16x4*>(
-                        &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 4 * g)]);
-                    float x = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) x += Yt[tt][r] * TR::tof(vr[r]);
-                    x += __shfl_xor(x, 16, 64);
-                    x += __shfl_xor(x, 32, 64);
-                    if (g == 0) sm.r0p[w][SB * tt + cl] = x;
-                }
+                state_pass(sm.Qb, Ot);
             }
+            KD_PHASE_MARK(n, 3);
             lds_barrier();
             // ======================================================= stage B
+            KD_PHASE_MARK(n, 1);
             if (n >= 0 && w == 0) {   // forward substitution (I + M) u = c - beta r0
                 const int t_ = lane;
-                float r0 = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < NWC; ++ww) r0 += sm.r0p[ww][t_];
+                __builtin_amdgcn_s_setprio(3);   // the chain every other wave waits for
+                float r0;
+                {
+                    const floatx4* pr = reinterpret_cast<const floatx4*>(&sm.r0q[t_ * LDR]);
+                    floatx4 a = pr[0] + pr[4], b = pr[1] + pr[5];
+                    a += pr[2] + pr[6];
+                    b += pr[3] + pr[7];
+                    a += b;
+                    r0 = (a[0] + a[1]) + (a[2] + a[3]);
+                }
                 float x = sm.c[n & 1][t_] - sm.beta[n & 1][t_] * r0;
                 // M is strictly lower triangular (zeros elsewhere): lane t only
                 // changes while s < t, no mask needed
@@ -188,14 +218,17 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
                 const float um = wave_max_nonneg(fabsf(x));
                 if (lane == 0) sm.umax = __float_as_uint(um);
+                __builtin_amdgcn_s_setprio(0);
             }
             if (tid == 0 && n >= 0) {
                 // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
                 // the previous stage C, the latter's first writer runs in stage A(n+1)
                 sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
             }
+            KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
+            KD_PHASE_MARK(n, 2);
             if (nn < NC && sm.unsafe[nn % 3] != 0u) {   // producers run the exact fallback
                 lds_barrier();
                 lds_barrier();
@@ -204,13 +237,20 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 const float usc = pow2_scale(__uint_as_float(sm.umax) * __uint_as_float(sm.vmax[n % 3]));
                 const float ksc = pow2_scale(__uint_as_float(sm.kmax[n % 3]));
                 const float inv = 1.f / (usc * ksc);
-                // O^T += W^T P^T with W = u * V
+                // W = u * V of this wave's value columns: bf16 for the readout,
+                // fp16 scaled by usc for the update
+                Frag wa[KC_];
+                FragH wb[KC_];
+#pragma unroll
+                for (int ks = 0; ks < KC_; ++ks) TR::row_times_both(&sm.VT[(i0 + cl) * LDT], sm.u, usc, ks, g, wa[ks], wb[ks]);
+                // O^T += W^T P^T (the P fragments of a K-step loaded together)
 #pragma unroll
                 for (int ks = 0; ks < KC_; ++ks) {
-                    const Frag wa = TR::row_times(&sm.VT[(i0 + cl) * LDT], sm.u, ks, g);
+                    Frag pf[NSB];
 #pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt)
-                        Ot[tt] = TR::mma(wa, TR::ld_nat(&sm.P[n & 1][(SB * tt + cl) * LDP], ks, g), Ot[tt]);
+                    for (int tt = 0; tt < NSB; ++tt) pf[tt] = TR::ld_nat(&sm.P[n & 1][(SB * tt + cl) * LDP], ks, g);
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) Ot[tt] = TR::mma(wa[ks], pf[tt], Ot[tt]);
                 }
                 if (ob) {
 #pragma unroll
@@ -221,20 +261,24 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                         if (n * CH + SB * tt + cl < T) st4(ob + (srow + o_lane), Ot[tt]);
                     }
                 }
-                // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact powers of 2)
-                FragH wb[KC_];
+                // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact
+                // powers of 2); K-steps outermost, so consecutive MFMAs go to
+                // different accumulators
 #pragma unroll
-                for (int ks = 0; ks < KC_; ++ks) wb[ks] = TR::row_times_h(&sm.VT[(i0 + cl) * LDT], sm.u, usc, ks, g);
+                for (int mj = 0; mj < D / 16; ++mj)
+                    S[mj] = S[mj] * (*reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc));
 #pragma unroll
-                for (int mj = 0; mj < D / 16; ++mj) {
-                    const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc);
-                    S[mj] = S[mj] * gm;
+                for (int ks = 0; ks < KC_; ++ks) {
+                    FragH ak[D / 16];
 #pragma unroll
-                    for (int ks = 0; ks < KC_; ++ks)
-                        S[mj] = TR::mma_h(TR::ld_nat_h(&sm.KtT[(16 * mj + cl) * LDT], ks, g), wb[ks], S[mj]);
-                    S[mj] = S[mj] * inv;
+                    for (int mj = 0; mj < D / 16; ++mj) ak[mj] = TR::ld_nat_h(&sm.KtT[(16 * mj + cl) * LDT], ks, g);
+#pragma unroll
+                    for (int mj = 0; mj < D / 16; ++mj) S[mj] = TR::mma_h(ak[mj], wb[ks], S[mj]);
                 }
+#pragma unroll
+                for (int mj = 0; mj < D / 16; ++mj) S[mj] = S[mj] * inv;
             }
+            KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
         if (ST) {
@@ -294,13 +338,26 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             const E* aV = &sm.V[(SB * I_ + cl) * LD];
             const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
             const E* bV = &sm.V[(SB * J_ + cl) * LD];
+            // operands of one K-step; those of the next are loaded before the
+            // MFMAs of the current one
+            struct GF { Frag k, a, q, v, w; };
+            auto ldg = [&](int ks) {
+                GF r;
+                r.k = TR::ld_nat(bK, ks, g);
+                if (DO_M) { r.a = TR::ld_nat(aK, ks, g); r.v = TR::ld_nat(aV, ks, g); r.w = TR::ld_nat(bV, ks, g); }
+                if (DO_P) r.q = TR::ld_nat(aQ, ks, g);
+                return r;
+            };
+            GF cur = ldg(0);
 #pragma unroll
             for (int ks = 0; ks < KD_; ++ks) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                const Frag fk = TR::ld_nat(bK, ks, g);
-                if (DO_M) gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
-                if (DO_P) pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
-                if (DO_M) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
+                GF nxt;
+                if (ks + 1 < KD_) nxt = ldg(ks + 1);
+                if (DO_M) gk = TR::mma(cur.a, cur.k, ks ? gk : z);
+                if (DO_P) pp = TR::mma(cur.q, cur.k, ks ? pp : z);
+                if (DO_M) gv = TR::mma(cur.v, cur.w, ks ? gv : z);
+                if (ks + 1 < KD_) cur = nxt;
             }
             const int s_ = SB * J_ + cl;
             if (fbk) {
@@ -328,6 +385,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             const int nn = n + 1;             // chunk the producers prepare
             const bool prod_on = nn < NC;
             // ======================================================= stage A
+            KD_PHASE_MARK(n, 0);
             if (n >= 0) {   // transposed operands of chunk n and its last two Gram tiles
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
@@ -370,18 +428,38 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     sm.c[nn & 1][lane] = rb_c;
                 }
             }
+            KD_PHASE_MARK(n, 3);
             lds_barrier();
             // ======================================================= stage B
+            KD_PHASE_MARK(n, 1);
             if (prod_on) {   // operands of chunk nn into LDS
                 // gamma before this block (plt), after it (pgt), and over the chunk
-                // (gC, multiplied in one fixed order so every wave agrees on it)
+                // (gC, multiplied in one fixed order so every wave agrees on it).
+                // pw is wave-uniform: one straight-line case per value.
                 float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, gC[2] = {1.f, 1.f}, rgC[2];
+                {
+                    float2 xb[NWP];
 #pragma unroll
-                for (int p = 0; p < NWP; ++p) {
-                    const float2 x = *reinterpret_cast<const float2*>(&sm.bprod[p][ch0]);
-                    gC[0] *= x.x; gC[1] *= x.y;
-                    if (p < pw) { plt[0] *= x.x; plt[1] *= x.y; }
-                    if (p > pw) { pgt[0] *= x.x; pgt[1] *= x.y; }
+                    for (int p = 0; p < NWP; ++p) xb[p] = *reinterpret_cast<const float2*>(&sm.bprod[p][ch0]);
+                    auto prods = [&](auto pw_c) {
+                        constexpr int PW = decltype(pw_c)::value;
+#pragma unroll
+                        for (int p = 0; p < NWP; ++p) {
+                            gC[0] *= xb[p].x; gC[1] *= xb[p].y;
+                            if (p < PW) { plt[0] *= xb[p].x; plt[1] *= xb[p].y; }
+                            if (p > PW) { pgt[0] *= xb[p].x; pgt[1] *= xb[p].y; }
+                        }
+                    };
+                    switch (pw) {
+                    case 0: prods(std::integral_constant<int, 0>()); break;
+                    case 1: prods(std::integral_constant<int, 1>()); break;
+                    case 2: prods(std::integral_constant<int, 2>()); break;
+                    case 3: prods(std::integral_constant<int, 3>()); break;
+                    case 4: prods(std::integral_constant<int, 4>()); break;
+                    case 5: prods(std::integral_constant<int, 5>()); break;
+                    case 6: prods(std::integral_constant<int, 6>()); break;
+                    default: prods(std::integral_constant<int, 7>()); break;
+                    }
                 }
                 pmask = 0;
 #pragma unroll
@@ -394,12 +472,16 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
                 if (pw == 0) st2(&sm.gam[nn & 1][ch0], gC[0], gC[1]);
                 if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
+                // K-tilde is kept scaled by ksc (a power of 2) for the fp16 update;
+                // Kc = K-tilde / gamma_C takes 1 / ksc back through rgC
                 const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
-                // gamma_C / gamma at each row: suffix products within the block
+                const float iksc = 1.f / ksc;
+                // ksc * gamma_C / gamma at each row: suffix products within the block
                 float om[RB][2];
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
-                    om[RB - 1][c2] = pgt[c2];
+                    rgC[c2] *= iksc;
+                    om[RB - 1][c2] = pgt[c2] * ksc;
 #pragma unroll
                     for (int e = RB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * rf.get(e + 1, c2);
                 }
@@ -412,12 +494,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int c2 = 0; c2 < 2; ++c2) {
                         ga[c2] *= rf.get(e, c2);
                         const float kf = rk.get(e, c2), qf = rq.get(e, c2);
-                        const float kt = kf * om[e][c2];   // K-tilde
+                        const float kt = kf * om[e][c2];   // K-tilde * ksc
                         qo[c2] = qf * ga[c2];
                         ko[c2] = kf * ga[c2];
                         co[c2] = kt * rgC[c2];             // k / gamma = K-tilde / gamma_C
-                        if (e & 1) keep_kt[c2].set_pair_h(e >> 1, kprev[c2], kt * ksc);
-                        else kprev[c2] = kt * ksc;
+                        if (e & 1) keep_kt[c2].set_pair_h(e >> 1, kprev[c2], kt);
+                        else kprev[c2] = kt;
                     }
                     st2(&sm.Qb[(rb + e) * LD + pc0], qo[0], qo[1]);
                     st2(&sm.Kb[(rb + e) * LD + pc0], ko[0], ko[1]);
@@ -429,8 +511,10 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             }
             const int npf = min(nn + 1, NC - 1);   // prefetch of chunk nn + 1
             load_q(npf);
+            KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
+            KD_PHASE_MARK(n, 2);
             const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
             if (fallback) {
                 // Exact Gram terms of the key channels of chunk nn whose decay is
@@ -466,6 +550,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (prod_on) gram_tile(kYes(), kYes(), pw, nn, fallback);   // tiles 0..7
             load_v(npf);
             load_f(npf);
+            KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
     }
