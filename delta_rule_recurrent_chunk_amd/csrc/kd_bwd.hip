@@ -20,10 +20,12 @@
 //
 // Three launches on the caller's stream:
 //   1. the forward kernel with checkpoints: per chunk the entering state (in
-//      the input dtype, S[i][j]) and u, r0;
+//      the input dtype, S[i][j]), u, r0, and the chunk's M and P;
 //   2. kd_bwd_state_kernel: one workgroup per (b, h), chunks in reverse, the
 //      fp32 dS^T held as MFMA accumulators (the mirror of the forward state):
-//      state read, back substitution, rank-128 update; stores dS and drho;
+//      state read, back substitution, rank-128 update; stores dS and drho.
+//      M and P come from the forward, and each chunk's inputs are loaded
+//      while the previous chunk is processed;
 //   3. kd_bwd_chunk_kernel: one workgroup per (b, h, chunk), all chunks in
 //      parallel: every local gradient.
 // A chunk with a key channel whose decay over the chunk falls below 2^-100
@@ -37,11 +39,13 @@ namespace kd {
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st);
+                      void* ckptS, float* ckptU, float* ckptM, void* ckptP, int B, int T, int H,
+                      hipStream_t st);
 
-// Workspace: [S0 checkpoints | u, r0 | dS per chunk | drho], 256-byte aligned parts.
+// Workspace: [S0 checkpoints | u, r0 | dS per chunk | drho | M | P], 256-byte
+// aligned parts (per chunk: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4, CH*CH*e bytes).
 struct BwdWs {
-    size_t s0, ur, ds, rho, total;
+    size_t s0, ur, ds, rho, mm, pp, total;
 };
 static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     const size_t nc = (size_t)(T + CH - 1) / CH;
@@ -52,7 +56,9 @@ static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     w.ur = up(units * d * d * esz);
     w.ds = w.ur + up(units * 2 * CH * sizeof(float));
     w.rho = w.ds + up(units * d * d * esz);
-    w.total = w.rho + up(units * CH * sizeof(float));
+    w.mm = w.rho + up(units * CH * sizeof(float));
+    w.pp = w.mm + up(units * CH * CH * sizeof(float));
+    w.total = w.pp + up(units * CH * CH * esz);
     return w;
 }
 
@@ -86,17 +92,14 @@ struct BwdStateSmem {
     static constexpr int LDM = CH + 4;         // fp32 M
     static constexpr int LDP = CH + TR::PAD;
     static constexpr int NW = D / 16;
-    static constexpr size_t KCB = (size_t)CH * LD * sizeof(E);
-    static constexpr size_t MB = (size_t)CH * LDM * sizeof(float);
-    alignas(16) E Qb[CH * LD];                        // q gamma for the Gram, then K-tilde
-    alignas(16) E Kb[CH * LD];                        // k gamma
-    alignas(16) unsigned char KcM[KCB > MB ? KCB : MB];   // k / gamma for the Gram, then M (fp32)
+    alignas(16) E Kt[CH * LD];                        // K-tilde rows
     alignas(16) E V[CH * LD];
     alignas(16) E VT[D * LDT];                        // v^T
     alignas(16) E OT[D * LDT];                        // dO^T
     alignas(16) E QT[D * LDT];                        // (q gamma)^T
     alignas(16) E KT[D * LDT];                        // (k gamma)^T
     alignas(16) E PT[CH * LDP];                       // PT[s][t] = P[t][s]
+    alignas(16) float M[CH * LDM];                    // M of the chunk (strictly lower)
     alignas(16) float beta[CH];
     alignas(16) float dr0[CH];
     alignas(16) float dup[NW][CH];                    // partial du per wave
@@ -105,27 +108,41 @@ struct BwdStateSmem {
     unsigned unsafe_any;
 };
 
+// One chunk's inputs as held in registers between its prefetch and its prep:
+// two rows x eight channels of q, k, v, f, dO per thread, beta of one token,
+// and a slice of the chunk's M and P from the forward.
+template <class TR, int D>
+struct BwdStateRegs {
+    typedef typename TR::E E;
+    static constexpr int MV = CH * CH / (4 * 4 * D);             // float4 of M per thread
+    static constexpr int PV = CH * CH * sizeof(E) / (16 * 4 * D);  // 16-byte slices of P per thread
+    Row2x8<TR> q, k, v, f, o;
+    float beta;
+    floatx4 m[MV];
+    uint4 p[PV];
+};
+
 template <class TR, int D>
 __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const float* __restrict__ ckM, const typename TR::E* __restrict__ ckP,
     const float* __restrict__ dST, typename TR::E* __restrict__ wsdS, float* __restrict__ wsrho,
     float* __restrict__ dS0, int T, int H)
 {
     typedef typename TR::E E;
     typedef typename TR::Frag Frag;
     typedef BwdStateSmem<TR, D> SM;
+    typedef BwdStateRegs<TR, D> RG;
     constexpr int NT = 4 * D;
     constexpr int NW = SM::NW;
     constexpr int KD_ = D / TR::KS;
     constexpr int KC_ = CH / TR::KS;
     constexpr int LD = SM::LD, LDT = SM::LDT, LDM = SM::LDM, LDP = SM::LDP;
-    constexpr int NTPW = (10 + NW - 1) / NW;   // Gram tiles per wave
+    constexpr int EPV = 16 / sizeof(E);   // P elements per 16-byte slice
 
     __shared__ SM sm;
-    E* Kc = reinterpret_cast<E*>(sm.KcM);
-    float* Mf = reinterpret_cast<float*>(sm.KcM);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
@@ -144,10 +161,29 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
         for (int r = 0; r < 4; ++r)
             dSt[mj][r] = dST ? dST[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g + r] : 0.f;
 
+    // Loads of chunk n into registers; unconditional (n is clamped by the
+    // caller, rows past the end re-read the last row and are cleared in the
+    // prep), so the next chunk's loads stay in flight across the current one.
+    RG cur;
+    auto load_chunk = [&](int n) {
+        const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
+        const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
+        cur.q.load(q + bbase, oa, ob);
+        cur.k.load(k + bbase, oa, ob);
+        cur.v.load(v + bbase, oa, ob);
+        cur.f.load(f + bbase, oa, ob);
+        cur.o.load(dO + bbase, oa, ob);
+        cur.beta = beta[((size_t)b * T + min(n * CH + (tid & (CH - 1)), T - 1)) * H + h];
+        const float* mg = ckM + ((size_t)bh * NC + n) * CH * CH;
+        const E* pg = ckP + ((size_t)bh * NC + n) * CH * CH;
+#pragma unroll
+        for (int i = 0; i < RG::MV; ++i) cur.m[i] = reinterpret_cast<const floatx4*>(mg)[tid + NT * i];
+#pragma unroll
+        for (int i = 0; i < RG::PV; ++i) cur.p[i] = reinterpret_cast<const uint4*>(pg)[tid + NT * i];
+    };
     if (NC > 0) {
-        for (int x = tid; x < CH * LDP; x += NT) sm.PT[x] = TR::cvt(0.f);   // upper part stays zero
         if (tid == 0) sm.unsafe_any = 0u;
-        lds_barrier();
+        load_chunk(NC - 1);
     }
 
     for (int n = NC - 1; n >= 0; --n) {
@@ -158,40 +194,39 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
             for (int mj = 0; mj < D / 16; ++mj)
                 st4(dst + ((uint32_t)(16 * w + cl) * D + 16 * mj + 4 * g), dSt[mj]);
         }
-        // ---------------- prep (a): rows, decay products within the sub-block
-        Row2x8<TR> rq, rk, rv, rf, ro;
-        float rbeta = 0.f;
-        {
-            const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
-            const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
-            rq.load(q + bbase, oa, ob);
-            rk.load(k + bbase, oa, ob);
-            rv.load(v + bbase, oa, ob);
-            rf.load(f + bbase, oa, ob);
-            ro.load(dO + bbase, oa, ob);
-            const int t = min(n * CH + (tid & (CH - 1)), T - 1);
-            rbeta = beta[((size_t)b * T + t) * H + h];
-            if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
+        // ---------------- prep (a): decay products within the sub-block; M and P
+        if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
 #pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    if (n * CH + row0 + e >= T) {
-                        rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f); ro.clear(e, 0.f);
-                    }
-                if (n * CH + (tid & (CH - 1)) >= T) rbeta = 0.f;
-            }
+            for (int e = 0; e < 2; ++e)
+                if (n * CH + row0 + e >= T) {
+                    cur.q.clear(e, 0.f); cur.k.clear(e, 0.f); cur.v.clear(e, 0.f); cur.f.clear(e, 1.f);
+                    cur.o.clear(e, 0.f);
+                }
+            if (n * CH + (tid & (CH - 1)) >= T) cur.beta = 0.f;
         }
         float incl[8], excl[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            incl[c] = group8_prefix_prod(rf.get(0, c) * rf.get(1, c), r8);
+            incl[c] = group8_prefix_prod(cur.f.get(0, c) * cur.f.get(1, c), r8);
             excl[c] = group8_shift1(incl[c], r8);
         }
         if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
-        if (tid < CH) sm.beta[tid] = rbeta;
+        if (tid < CH) sm.beta[tid] = cur.beta;
+#pragma unroll
+        for (int i = 0; i < RG::MV; ++i) {
+            const int x = tid + NT * i, t = x / (CH / 4), s4 = x % (CH / 4);
+            *reinterpret_cast<floatx4*>(&sm.M[t * LDM + 4 * s4]) = cur.m[i];
+        }
+#pragma unroll
+        for (int i = 0; i < RG::PV; ++i) {   // transposed: PT[s][t] = P[t][s]
+            const int x = tid + NT * i, t = x / (CH / EPV), s0 = EPV * (x % (CH / EPV));
+            const E* pe = reinterpret_cast<const E*>(&cur.p[i]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) sm.PT[(s0 + e) * LDP + t] = pe[e];
+        }
         lds_barrier();
 
         // ---------------- prep (b): operands
-        float kt[2][8];   // K-tilde rows, written once the Gram has read Qb
         {
             float plt[8], gC[8];
 #pragma unroll
@@ -216,77 +251,28 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
             float qo[2][8], ko[2][8];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                float co[8];
+                float kt[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const float ga = plt[c] * (e == 0 ? excl[c] * rf.get(0, c) : incl[c]);
-                    const float kf = rk.get(e, c);
+                    const float ga = plt[c] * (e == 0 ? excl[c] * cur.f.get(0, c) : incl[c]);
+                    const float kf = cur.k.get(e, c);
                     const bool un = (unsafe >> c) & 1u;
-                    const float kr = kf * __builtin_amdgcn_rcpf(ga);
-                    qo[e][c] = rq.get(e, c) * ga;
+                    qo[e][c] = cur.q.get(e, c) * ga;
                     ko[e][c] = kf * ga;
-                    co[c] = un ? 0.f : kr;
-                    kt[e][c] = un ? 0.f : kr * gC[c];
+                    kt[c] = un ? 0.f : kf * __builtin_amdgcn_rcpf(ga) * gC[c];   // K-tilde
                 }
-                st8v(&sm.Qb[(row0 + e) * LD + ch0], qo[e]);
-                st8v(&sm.Kb[(row0 + e) * LD + ch0], ko[e]);
-                st8v(&Kc[(row0 + e) * LD + ch0], co);
-                rv.store(&sm.V[(row0 + e) * LD + ch0], e);
+                st8v(&sm.Kt[(row0 + e) * LD + ch0], kt);
+                cur.v.store(&sm.V[(row0 + e) * LD + ch0], e);
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                st2(&sm.VT[(ch0 + c) * LDT + row0], rv.get(0, c), rv.get(1, c));
-                st2(&sm.OT[(ch0 + c) * LDT + row0], ro.get(0, c), ro.get(1, c));
+                st2(&sm.VT[(ch0 + c) * LDT + row0], cur.v.get(0, c), cur.v.get(1, c));
+                st2(&sm.OT[(ch0 + c) * LDT + row0], cur.o.get(0, c), cur.o.get(1, c));
                 st2(&sm.QT[(ch0 + c) * LDT + row0], qo[0][c], qo[1][c]);
                 st2(&sm.KT[(ch0 + c) * LDT + row0], ko[0][c], ko[1][c]);
             }
         }
-        lds_barrier();
-
-        // ---------------- Gram tiles M, P (kept in registers until every wave is done)
-        floatx4 mv[NTPW], pv[NTPW];
-#pragma unroll
-        for (int it = 0; it < NTPW; ++it) {
-            const int tile = w + it * NW;
-            if (tile < 10) {
-                const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-                const int J_ = tile - (I_ * (I_ + 1)) / 2;
-                floatx4 gk = {0.f, 0.f, 0.f, 0.f}, pp = gk, gv = gk;
-#pragma unroll
-                for (int ks = 0; ks < KD_; ++ks) {
-                    const Frag fk = TR::ld_nat(&Kc[(SB * J_ + cl) * LD], ks, g);
-                    gk = TR::mma(TR::ld_nat(&sm.Kb[(SB * I_ + cl) * LD], ks, g), fk, gk);
-                    pp = TR::mma(TR::ld_nat(&sm.Qb[(SB * I_ + cl) * LD], ks, g), fk, pp);
-                    gv = TR::mma(TR::ld_nat(&sm.V[(SB * I_ + cl) * LD], ks, g),
-                                 TR::ld_nat(&sm.V[(SB * J_ + cl) * LD], ks, g), gv);
-                }
-                const int s_ = SB * J_ + cl;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t_ = SB * I_ + 4 * g + r;
-                    mv[it][r] = (s_ < t_) ? sm.beta[t_] * gk[r] * gv[r] : 0.f;
-                    pv[it][r] = (s_ <= t_) ? pp[r] : 0.f;
-                }
-            }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int it = 0; it < NTPW; ++it) {
-            const int tile = w + it * NW;
-            if (tile < 10) {
-                const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-                const int J_ = tile - (I_ * (I_ + 1)) / 2;
-                const int s_ = SB * J_ + cl;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t_ = SB * I_ + 4 * g + r;
-                    Mf[t_ * LDM + s_] = mv[it][r];
-                }
-                st4(&sm.PT[s_ * LDP + SB * I_ + 4 * g], pv[it]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) st8v(&sm.Qb[(row0 + e) * LD + ch0], kt[e]);   // K-tilde rows
+        load_chunk(max(n - 1, 0));   // the next chunk's loads run under this one
         lds_barrier();
 
         // ---------------- state read: dW = Kt dS^T + P^T dO (rows t, this wave's 16 columns i)
@@ -298,7 +284,7 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
             const Frag bS = TR::state_frag(dSt, ks);
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt)
-                dW[tt] = TR::mma(TR::ld_state(&sm.Qb[(SB * tt + cl) * LD], ks, g), bS, dW[tt]);
+                dW[tt] = TR::mma(TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], ks, g), bS, dW[tt]);
         }
 #pragma unroll
         for (int ks = 0; ks < KC_; ++ks) {
@@ -336,13 +322,12 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
             for (int ww = 0; ww < NW; ++ww) x += sm.dup[ww][t_];
             float Mcol[CH];
 #pragma unroll
-            for (int s = 0; s < CH; ++s) Mcol[s] = Mf[s * LDM + t_];
-            // lane t takes the finished drho_s of every later row s; M above the
-            // diagonal is not cleared, hence the mask
+            for (int s = 0; s < CH; ++s) Mcol[s] = sm.M[s * LDM + t_];
+            // lane t takes the finished drho_s of every later row s; the mask
+            // keeps a non-finite drho_s of an earlier row out of lane t
 #pragma unroll
             for (int s = CH - 1; s >= 1; --s) {
-                const float xs = readlane_f(x, s);
-                const float y = fmaf(-Mcol[s], xs, x);
+                const float y = fmaf(-Mcol[s], readlane_f(x, s), x);
                 x = (t_ < s) ? y : x;
             }
             if (sm.unsafe_any) x = __builtin_nanf("");
@@ -361,15 +346,15 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
                 bR[ks] = TR::row_times(&sm.VT[(16 * w + cl) * LDT], sm.dr0, ks, g);
             }
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj) {
-                const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[16 * mj + 4 * g]);
-                dSt[mj] = dSt[mj] * gm;
+            for (int mj = 0; mj < D / 16; ++mj)
+                dSt[mj] = dSt[mj] * *reinterpret_cast<const floatx4*>(&sm.gam[16 * mj + 4 * g]);
 #pragma unroll
-                for (int ks = 0; ks < KC_; ++ks) {
+            for (int ks = 0; ks < KC_; ++ks)
+#pragma unroll
+                for (int mj = 0; mj < D / 16; ++mj) {
                     dSt[mj] = TR::mma(TR::ld_nat(&sm.QT[(16 * mj + cl) * LDT], ks, g), bO[ks], dSt[mj]);
                     dSt[mj] = TR::mma(TR::ld_nat(&sm.KT[(16 * mj + cl) * LDT], ks, g), bR[ks], dSt[mj]);
                 }
-            }
         }
         lds_barrier();
     }
@@ -782,15 +767,17 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     float* ckU = reinterpret_cast<float*>(wb + L.ur);
     E* wdS = reinterpret_cast<E*>(wb + L.ds);
     float* wrho = reinterpret_cast<float*>(wb + L.rho);
+    float* ckM = reinterpret_cast<float*>(wb + L.mm);
+    E* ckP = reinterpret_cast<E*>(wb + L.pp);
     const int NC = (T + CH - 1) / CH;
     if (NC > 0) {
         hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr,
-                                  ckS, ckU, B, T, H, st);
+                                  ckS, ckU, ckM, ckP, B, T, H, st);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO, dST,
-                       wdS, wrho, dS0, T, H);
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
+                       (const float*)ckM, (const E*)ckP, dST, wdS, wrho, dS0, T, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NC == 0) return e;
     hipLaunchKernelGGL((kd_bwd_chunk_kernel<TR, D>), dim3((unsigned)(B * H * NC)), dim3(4 * D), 0, st,

@@ -88,7 +88,8 @@ struct FwdSmem {
 };
 
 // CKPT: also store, per chunk, the entering state (S[i][j], in the input
-// dtype) and the WY targets u and r0, for the backward.  A separate
+// dtype), the WY targets u and r0, and M (fp32) and P (input dtype) as
+// [CH][CH] row-major, for the backward.  A separate
 // instantiation, so the plain forward carries none of its registers.
 template <class TR, int D, bool CKPT>
 __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, typename TR::E* __restrict__ o, float* __restrict__ ST,
-    typename TR::E* __restrict__ ckptS, float* __restrict__ ckptU, int T, int H)
+    typename TR::E* __restrict__ ckptS, float* __restrict__ ckptU, float* __restrict__ ckptM,
+    typename TR::E* __restrict__ ckptP, int T, int H)
 {
     typedef typename TR::E E;
     typedef typename TR::H Hh;
@@ -243,6 +245,23 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 }
                 const float um = wave_max_nonneg(fabsf(x));
                 if (lane == 0) sm.umax = __float_as_uint(um);
+            }
+            if (CKPT && n >= 0) {
+                // M and P of chunk n are complete and nobody writes them in this
+                // stage: the consumer waves copy them out ([CH][CH] row-major)
+                constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte move
+                float* dm = ckptM + ((size_t)bh * NC + n) * CH * CH;
+                E* dp = ckptP + ((size_t)bh * NC + n) * CH * CH;
+                for (int x = tid; x < CH * CH / 4; x += NWC * 64) {
+                    const int t = x / (CH / 4), s4 = x % (CH / 4);
+                    *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
+                        *reinterpret_cast<const floatx4*>(&sm.M[t * LDM + 4 * s4]);
+                }
+                for (int x = tid; x < CH * CH / EPV; x += NWC * 64) {
+                    const int t = x / (CH / EPV), sv = x % (CH / EPV);
+                    *reinterpret_cast<uint4*>(dp + t * CH + EPV * sv) =
+                        *reinterpret_cast<const uint4*>(&sm.P[n & 1][t * LDP + EPV * sv]);
+                }
             }
             if (tid == 0 && n >= 0) {
                 // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
@@ -568,30 +587,31 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 template <class TR, int D>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* f,
                                const float* beta, const float* c, const float* S0, void* o,
-                               float* ST, void* ckptS, float* ckptU, int B, int T, int H,
-                               hipStream_t st)
+                               float* ST, void* ckptS, float* ckptU, float* ckptM, void* ckptP,
+                               int B, int T, int H, hipStream_t st)
 {
     typedef typename TR::E E;
     if (ckptS)
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, true>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)ckptS, ckptU, T, H);
+                           (E*)ckptS, ckptU, ckptM, (E*)ckptP, T, H);
     else
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, false>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)nullptr, (float*)nullptr, T, H);
+                           (E*)nullptr, (float*)nullptr, (float*)nullptr, (E*)nullptr, T, H);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
                         const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
-                        int B, int T, int H, hipStream_t st);
+                        float* ckptM, void* ckptP, int B, int T, int H, hipStream_t st);
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      void* ckptS, float* ckptU, int B, int T, int H, hipStream_t st)
+                      void* ckptS, float* ckptU, float* ckptM, void* ckptP, int B, int T, int H,
+                      hipStream_t st)
 {
-#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ckptS, ckptU, B, T, H, st
+#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ckptS, ckptU, ckptM, ckptP, B, T, H, st
     if (bf16) {
         switch (d) {
         case 32: return launch_fwd_t<Bf16T, 32>(KD_FWD_ARGS);

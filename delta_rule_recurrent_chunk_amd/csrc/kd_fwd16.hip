@@ -62,13 +62,15 @@ struct Fwd16Smem {
     unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
-// CKPT: also store, per chunk, the entering state (S[i][j], bf16) and u, r0.
+// CKPT: also store, per chunk, the entering state (S[i][j], bf16), u and r0,
+// and the chunk's M (fp32) and P (bf16), both [CH][CH] row-major.
 template <bool CKPT>
 __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
-    __bf16* __restrict__ ckptS, float* __restrict__ ckptU, int T, int H)
+    __bf16* __restrict__ ckptS, float* __restrict__ ckptU, float* __restrict__ ckptM,
+    __bf16* __restrict__ ckptP, int T, int H)
 {
     using namespace f16w;
     typedef Bf16T TR;
@@ -219,6 +221,23 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 const float um = wave_max_nonneg(fabsf(x));
                 if (lane == 0) sm.umax = __float_as_uint(um);
                 __builtin_amdgcn_s_setprio(0);
+            }
+            if (CKPT && n >= 0 && w >= 1) {
+                // M and P of chunk n are complete (their last tiles ran in stage
+                // A) and nobody writes them in this stage: the idle consumer waves
+                // copy them out
+                float* dm = ckptM + ((size_t)bh * NC + n) * CH * CH;
+                E* dp = ckptP + ((size_t)bh * NC + n) * CH * CH;
+                for (int x = tid - 64; x < CH * CH / 4; x += (NWC - 1) * 64) {
+                    const int t = x >> 4, s4 = x & 15;
+                    *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
+                        *reinterpret_cast<const floatx4*>(&sm.M[t * LDM + 4 * s4]);
+                }
+                for (int x = tid - 64; x < CH * CH / 8; x += (NWC - 1) * 64) {
+                    const int t = x >> 3, s8 = x & 7;
+                    *reinterpret_cast<uint4*>(dp + t * CH + 8 * s8) =
+                        *reinterpret_cast<const uint4*>(&sm.P[n & 1][t * LDP + 8 * s8]);
+                }
             }
             if (tid == 0 && n >= 0) {
                 // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
@@ -558,17 +577,17 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
                         const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
-                        int B, int T, int H, hipStream_t st)
+                        float* ckptM, void* ckptP, int B, int T, int H, hipStream_t st)
 {
     typedef __bf16 E;
     if (ckptS)
         hipLaunchKernelGGL(kd_fwd16_kernel<true>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)ckptS, ckptU, T, H);
+                           (E*)ckptS, ckptU, ckptM, (E*)ckptP, T, H);
     else
         hipLaunchKernelGGL(kd_fwd16_kernel<false>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)nullptr, (float*)nullptr, T, H);
+                           (E*)nullptr, (float*)nullptr, (float*)nullptr, (E*)nullptr, T, H);
     return hipGetLastError();
 }
 
