@@ -164,15 +164,28 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     // Loads of chunk n into registers; unconditional (n is clamped by the
     // caller, rows past the end re-read the last row and are cleared in the
     // prep), so the next chunk's loads stay in flight across the current one.
+    // The loads of the next chunk are issued in three parts over the stages
+    // that follow the prep, so no wave issues the whole chunk at once.
     RG cur;
-    auto load_chunk = [&](int n) {
+    auto row_offs = [&](int n, uint32_t& oa, uint32_t& ob) {
         const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
-        const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
+        oa = (uint32_t)ta * rs + hoff + ch0;
+        ob = (uint32_t)tb * rs + hoff + ch0;
+    };
+    auto load_part1 = [&](int n) {
+        uint32_t oa, ob;
+        row_offs(n, oa, ob);
         cur.q.load(q + bbase, oa, ob);
         cur.k.load(k + bbase, oa, ob);
-        cur.v.load(v + bbase, oa, ob);
         cur.f.load(f + bbase, oa, ob);
+    };
+    auto load_part2 = [&](int n) {
+        uint32_t oa, ob;
+        row_offs(n, oa, ob);
+        cur.v.load(v + bbase, oa, ob);
         cur.o.load(dO + bbase, oa, ob);
+    };
+    auto load_part3 = [&](int n) {
         cur.beta = beta[((size_t)b * T + min(n * CH + (tid & (CH - 1)), T - 1)) * H + h];
         const float* mg = ckM + ((size_t)bh * NC + n) * CH * CH;
         const E* pg = ckP + ((size_t)bh * NC + n) * CH * CH;
@@ -183,17 +196,20 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     };
     if (NC > 0) {
         if (tid == 0) sm.unsafe_any = 0u;
-        load_chunk(NC - 1);
+        load_part1(NC - 1);
+        load_part2(NC - 1);
+        load_part3(NC - 1);
     }
 
-    for (int n = NC - 1; n >= 0; --n) {
-        // gradient of the state leaving chunk n, dS[i][j], for the chunk-local kernel
-        {
-            E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
+    // gradient of the state leaving chunk n, dS[i][j], for the chunk-local kernel
+    auto store_dS = [&](int n) {
+        E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj)
-                st4(dst + ((uint32_t)(16 * w + cl) * D + 16 * mj + 4 * g), dSt[mj]);
-        }
+        for (int mj = 0; mj < D / 16; ++mj)
+            st4(dst + ((uint32_t)(16 * w + cl) * D + 16 * mj + 4 * g), dSt[mj]);
+    };
+
+    for (int n = NC - 1; n >= 0; --n) {
         // ---------------- prep (a): decay products within the sub-block; M and P
         if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
 #pragma unroll
@@ -272,49 +288,63 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
                 st2(&sm.KT[(ch0 + c) * LDT + row0], ko[0][c], ko[1][c]);
             }
         }
-        load_chunk(max(n - 1, 0));   // the next chunk's loads run under this one
+        const int npf = max(n - 1, 0);   // the next chunk's loads run under this one
+        load_part1(npf);
         lds_barrier();
 
         // ---------------- state read: dW = Kt dS^T + P^T dO (rows t, this wave's 16 columns i)
         floatx4 dW[NSB];
+        {
+            Frag ac[NSB];
 #pragma unroll
-        for (int tt = 0; tt < NSB; ++tt) dW[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < NSB; ++tt) ac[tt] = TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], 0, g);
 #pragma unroll
-        for (int ks = 0; ks < KD_; ++ks) {
-            const Frag bS = TR::state_frag(dSt, ks);
+            for (int ks = 0; ks < KD_; ++ks) {
+                Frag an[NSB];
+                if (ks + 1 < KD_) {
 #pragma unroll
-            for (int tt = 0; tt < NSB; ++tt)
-                dW[tt] = TR::mma(TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], ks, g), bS, dW[tt]);
+                    for (int tt = 0; tt < NSB; ++tt) an[tt] = TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], ks + 1, g);
+                }
+                const Frag bS = TR::state_frag(dSt, ks);
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int tt = 0; tt < NSB; ++tt) dW[tt] = TR::mma(ac[tt], bS, ks ? dW[tt] : z);
+                if (ks + 1 < KD_) {
+#pragma unroll
+                    for (int tt = 0; tt < NSB; ++tt) ac[tt] = an[tt];
+                }
+            }
         }
 #pragma unroll
         for (int ks = 0; ks < KC_; ++ks) {
             const Frag bO = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
+            Frag ap[NSB];
 #pragma unroll
-            for (int tt = 0; tt < NSB; ++tt)
-                dW[tt] = TR::mma(TR::ld_nat(&sm.PT[(SB * tt + cl) * LDP], ks, g), bO, dW[tt]);
+            for (int tt = 0; tt < NSB; ++tt) ap[tt] = TR::ld_nat(&sm.PT[(SB * tt + cl) * LDP], ks, g);
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt) dW[tt] = TR::mma(ap[tt], bO, dW[tt]);
         }
-        {   // partial du[t] over this wave's 16 value columns
+        load_part2(npf);
+        {   // partial du[t] over this wave's 16 value columns: transpose-reduce
+            // over the 16 lanes of a row with DPP partners (row mirror, half-row
+            // mirror, quad swaps), after which lane cl holds element cl
             float x[16];
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     x[4 * tt + r] = dW[tt][r] * TR::tof(sm.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) {
-                const bool up = (cl & m) != 0;
-#pragma unroll
-                for (int e = 0; e < m; ++e) {
-                    const float send = up ? x[e] : x[e + m];
-                    const float keep = up ? x[e + m] : x[e];
-                    x[e] = keep + __shfl_xor(send, m, 64);
-                }
-            }
+            row16_reduce_step<8>(x, cl);
+            row16_reduce_step<4>(x, cl);
+            row16_reduce_step<2>(x, cl);
+            row16_reduce_step<1>(x, cl);
             sm.dup[w][SB * (cl >> 2) + 4 * g + (cl & 3)] = x[0];
         }
         lds_barrier();
 
-        // ---------------- back substitution (I + M)^T drho = du
+        // ---------------- back substitution (I + M)^T drho = du; every wave
+        // then stores dS and issues the rest of the next chunk's loads (the
+        // others while wave 0 solves)
         if (w == 0) {
             const int t_ = lane;
             float x = 0.f;
@@ -334,6 +364,8 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
             wsrho[((size_t)bh * NC + n) * CH + t_] = x;
             sm.dr0[t_] = -sm.beta[t_] * x;
         }
+        store_dS(n);
+        load_part3(npf);
         lds_barrier();
 
         // ---------------- dS <- dS diag(gamma_C) + dO^T Qbar + V^T diag(dr0) Kbar

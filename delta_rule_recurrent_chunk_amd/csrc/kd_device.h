@@ -690,6 +690,25 @@ __device__ __forceinline__ void quad_excl_prod(float x, int r4, float& pre, floa
     suf = (r4 <= 2) ? y3 : 1.f;
 }
 
+// One step of a transpose-reduce over the 16 lanes of a DPP row: x[0 .. 2M)
+// of every lane are summed in pairs with a partner lane whose bit M of the
+// row index differs, and each lane keeps the half selected by that bit (the
+// partner comes from a mirror or quad swap, so it need not be lane ^ M: it
+// only has to share the bits above M).  After the steps M = 8, 4, 2, 1,
+// lane l of the row holds the row's sum of element l in x[0].  The DPP moves
+// run on every lane; only the selects depend on the lane.
+template <int M>
+__device__ __forceinline__ void row16_reduce_step(float* x, int cl) {
+    constexpr int CTRL = M == 8 ? 0x140 : M == 4 ? 0x141 : M == 2 ? 0x4E : 0xB1;
+    const bool up = (cl & M) != 0;
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+        const float send = up ? x[e] : x[e + M];
+        const float keep = up ? x[e + M] : x[e];
+        x[e] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+    }
+}
+
 // Store two adjacent channels' values (as the path's element type).
 __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
     bf16x2 x;
