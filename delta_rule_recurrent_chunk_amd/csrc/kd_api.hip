@@ -8,10 +8,10 @@
 #include "kron_delta.h"
 
 namespace kd {
+struct FwdCkpt;
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      void* ckptS, float* ckptU, float* ckptM, void* ckptP, int B, int T, int H,
-                      hipStream_t st);
+                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st);
 hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, const void* dO,
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
@@ -105,7 +105,7 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
     hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
-                                  nullptr, nullptr, nullptr, nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+                                  nullptr, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

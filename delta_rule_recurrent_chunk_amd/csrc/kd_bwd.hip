@@ -33,17 +33,19 @@
 // here: all its gradients are NaN, and so is every gradient that depends on
 // it through the state gradient (dk, dv, df, dbeta, dc of the earlier chunks
 // of that (b, h), and dS0); dq of the earlier chunks does not and stays exact.
+#include <type_traits>
+
 #include "kd_device.h"
 
 namespace kd {
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      void* ckptS, float* ckptU, float* ckptM, void* ckptP, int B, int T, int H,
-                      hipStream_t st);
+                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st);
 
-// Workspace: [S0 checkpoints | u, r0 | dS per chunk | drho | M | P], 256-byte
-// aligned parts (per chunk: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4, CH*CH*e bytes).
+// Workspace: [S0 | u, r0 | dS | drho | M | P] per (b, h, chunk) unit,
+// 256-byte aligned parts (per unit: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4,
+// CH*CH*e bytes).
 struct BwdWs {
     size_t s0, ur, ds, rho, mm, pp, total;
 };
@@ -479,13 +481,52 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     const size_t unit = (size_t)bh * NC + n;
 
     // ---------------- prep (a)
-    Row2x8<TR> rq, rk, rv, rf, ro;
+    // q, k, f and the decay factors are needed again by the elementwise stage
+    // at the end; they are re-read there (L2) rather than held in registers
+    // through the contractions.
     const int ta = min(n * CH + row0, T - 1), tb = min(n * CH + row0 + 1, T - 1);
     const uint32_t oa = (uint32_t)ta * rs + hoff + ch0, ob = (uint32_t)tb * rs + hoff + ch0;
-    rq.load(q + bbase, oa, ob);
-    rk.load(k + bbase, oa, ob);
+    const bool ragged = n * CH + CH > T;
+    auto load_qkf = [&](Row2x8<TR>& rq_, Row2x8<TR>& rk_, Row2x8<TR>& rf_) {
+        rq_.load(q + bbase, oa, ob);
+        rk_.load(k + bbase, oa, ob);
+        rf_.load(f + bbase, oa, ob);
+    };
+    auto clear_qkf = [&](Row2x8<TR>& rq_, Row2x8<TR>& rk_, Row2x8<TR>& rf_) {
+        if (ragged) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                if (n * CH + row0 + e >= T) { rq_.clear(e, 0.f); rk_.clear(e, 0.f); rf_.clear(e, 1.f); }
+        }
+    };
+    // gamma at this thread's two rows and gamma_C, from f and the sub-block
+    // products in sm.bprod (the same arithmetic every time it is called)
+    auto gammas = [&](const Row2x8<TR>& rf_, float (&ga_)[2][8], float (&gC_)[8]) {
+        float plt[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC_[c] = 1.f; }
+#pragma unroll
+        for (int I2 = 0; I2 < NSB; ++I2)
+#pragma unroll
+            for (int c4 = 0; c4 < 2; ++c4) {
+                const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gC_[4 * c4 + e] *= x[e];
+                    if (I2 < I) plt[4 * c4 + e] *= x[e];
+                }
+            }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float incl = group8_prefix_prod(rf_.get(0, c) * rf_.get(1, c), r8);
+            const float excl = group8_shift1(incl, r8);
+            ga_[0][c] = plt[c] * (excl * rf_.get(0, c));
+            ga_[1][c] = plt[c] * incl;
+        }
+    };
+    Row2x8<TR> pq, pk, rv, pf, ro;   // prep copies of q, k, f
+    load_qkf(pq, pk, pf);
     rv.load(v + bbase, oa, ob);
-    rf.load(f + bbase, oa, ob);
     ro.load(dO + bbase, oa, ob);
     if (tid < CH) {
         const bool valid = n * CH + tid < T;
@@ -495,42 +536,28 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
         sm.r0[tid] = valid ? ckptU[unit * 2 * CH + CH + tid] : 0.f;
         sm.drho[tid] = valid ? wsrho[unit * CH + tid] : 0.f;
     }
-    if (n * CH + CH > T) {
+    clear_qkf(pq, pk, pf);
+    if (ragged) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            if (n * CH + row0 + e >= T) {
-                rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f); rf.clear(e, 1.f); ro.clear(e, 0.f);
-            }
+            if (n * CH + row0 + e >= T) { rv.clear(e, 0.f); ro.clear(e, 0.f); }
     }
     // the upper triangles of P, dGK, dP (hi and lo) are never written
-    for (int x = tid; x < 5 * CH * LDP; x += NT) P[x] = TR::cvt(0.f);
+    for (int x = tid; x < 5 * CH * LDP * (int)sizeof(E) / 16; x += NT)
+        reinterpret_cast<uint4*>(P)[x] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) sm.unsafe_any = 0u;
-    float incl[8], excl[8];
+    {
+        float incl[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        incl[c] = group8_prefix_prod(rf.get(0, c) * rf.get(1, c), r8);
-        excl[c] = group8_shift1(incl[c], r8);
+        for (int c = 0; c < 8; ++c) incl[c] = group8_prefix_prod(pf.get(0, c) * pf.get(1, c), r8);
+        if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
     }
-    if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
     lds_barrier();
 
-    // ---------------- prep (b): operands; gamma and gamma_C stay in registers
-    float ga[2][8], gC[8];
+    // ---------------- prep (b): operands
     {
-        float plt[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; }
-#pragma unroll
-        for (int I2 = 0; I2 < NSB; ++I2)
-#pragma unroll
-            for (int c4 = 0; c4 < 2; ++c4) {
-                const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gC[4 * c4 + e] *= x[e];
-                    if (I2 < I) plt[4 * c4 + e] *= x[e];
-                }
-            }
+        float ga[2][8], gC[8];
+        gammas(pf, ga, gC);
         unsigned unsafe = 0;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -542,11 +569,10 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
             float qo[8], ko[8], co[8];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                ga[e][c] = plt[c] * (e == 0 ? excl[c] * rf.get(0, c) : incl[c]);
-                const float kf = rk.get(e, c);
+                const float kf = pk.get(e, c);
                 const bool un = (unsafe >> c) & 1u;
                 const float kr = kf * __builtin_amdgcn_rcpf(ga[e][c]);
-                qo[c] = rq.get(e, c) * ga[e][c];
+                qo[c] = pq.get(e, c) * ga[e][c];
                 ko[c] = kf * ga[e][c];
                 co[c] = un ? 0.f : kr;
             }
@@ -574,8 +600,9 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
             gk = TR::mma(TR::ld_nat(&Kb[(SB * I_ + cl) * LD], ks, g), fk, gk);
             pp = TR::mma(TR::ld_nat(&Qb[(SB * I_ + cl) * LD], ks, g), fk, pp);
             gv = TR::mma(TR::ld_nat(&Vs[(SB * I_ + cl) * LD], ks, g), fv, gv);
-            dp = TR::mma(TR::ld_nat(&Do[(SB * I_ + cl) * LD], ks, g), TR::scale(fv, us), dp);
+            dp = TR::mma(TR::ld_nat(&Do[(SB * I_ + cl) * LD], ks, g), fv, dp);
         }
+        dp = dp * us;   // dP[t][s] = u_s (dO V^T)[t][s]: column s = this lane's
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t_ = SB * I_ + 4 * g + r;
@@ -607,9 +634,8 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
     const E* S0n = ckptS + unit * D * D;   // S0[i][j]
     const E* dSn = wsdS + unit * D * D;    // dS[i][j]
-    {   // colsum(dS * S0) for column jc: lane group g takes a quarter of i
+    if (!std::is_same<TR, Bf16T>::value) {   // colsum(dS * S0) for column jc (bf16: below)
         float acc = 0.f;
-#pragma unroll 8
         for (int x = 0; x < D / 4; ++x) {
             const int i = g * (D / 4) + x;
             acc += TR::tof(S0n[i * D + jc]) * TR::tof(dSn[i * D + jc]);
@@ -621,32 +647,60 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     lds_barrier();
 
     // ---------------- C x D results, this wave's 16 columns, all 64 rows
-    floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB], aV[NSB];
+    // Scalings by u[t] or dr0[t] of the output row t are applied to the
+    // accumulators, not to the operands: aK and aT start as V S0 and V dS, and
+    // dV is accumulated in two parts, aVu = Kt dS^T + P^T dO (times u) and
+    // aVr = dr0 (Kbar S0^T) + (dGV + dGV^T) V.  The key-channel scaling of
+    // Kt = Kc gamma_C goes on the dS fragment, once per K-step.
+    floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB], aVu[NSB], aVr[NSB];
 #pragma unroll
     for (int tt = 0; tt < NSB; ++tt) {
         aQ[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt]; aV[tt] = aQ[tt];
+        aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt]; aVu[tt] = aQ[tt]; aVr[tt] = aQ[tt];
     }
-    // contractions over a d-long index: B operands straight from global memory
-    // (L2), columns of S0 and dS read element by element
+    // contractions over a d-long index, B operands from the state checkpoints
+    // in global memory (L2): rows directly, columns through col_frag (whose
+    // tiles also give colsum(dS * S0) for bf16)
+    {
+        const Frag csel = TR::col_sel(16 * w, g, cl);
+        float gc2 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KD_; ++ks) {
-        const Frag b_s0t = TR::ld_col(S0n + jc, D, ks, g);     // B[i][j] = S0[i][j]
-        const Frag b_dst = TR::ld_col(dSn + jc, D, ks, g);     // B[i][j] = dS[i][j]
-        const Frag b_ds = TR::ld_nat(dSn + jc * D, ks, g);     // B[j][i] = dS[i][j]
-        const Frag b_s0 = TR::ld_nat(S0n + jc * D, ks, g);     // B[j][i] = S0[i][j]
+        for (int ks = 0; ks < KD_; ++ks) {
+            floatx4 ts[2], td[2];
+            const Frag b_s0t = TR::col_frag(S0n, D, ks, 16 * w, csel, g, cl, ts);   // B[i][j] = S0[i][j]
+            const Frag b_dst = TR::col_frag(dSn, D, ks, 16 * w, csel, g, cl, td);   // B[i][j] = dS[i][j]
+            if (std::is_same<TR, Bf16T>::value) {
 #pragma unroll
-        for (int tt = 0; tt < NSB; ++tt) {
-            const int tr = SB * tt + cl;
-            const float sr = sm.dr0[tr], su = sm.u[tr];
-            const Frag a_v = TR::ld_nat(&Vs[tr * LD], ks, g);
-            aQ[tt] = TR::mma(TR::ld_nat(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);    // dO S0
-            aK[tt] = TR::mma(TR::scale(a_v, sr), b_s0t, aK[tt]);                  // dr0 (V S0)
-            aT[tt] = TR::mma(TR::scale(a_v, su), b_dst, aT[tt]);                  // W dS
-            // u (Kt dS^T) with Kt = Kc gamma_C formed in the fragment
-            aV[tt] = TR::mma(TR::scale_k(TR::ld_nat(&Kc[tr * LD], ks, g), su, sm.gam, ks, g), b_ds, aV[tt]);
-            aV[tt] = TR::mma(TR::scale(TR::ld_nat(&Kb[tr * LD], ks, g), sr), b_s0, aV[tt]);   // dr0 (Kbar S0^T)
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gc2 += ts[hh][r] * td[hh][r];
+            }
+            const Frag b_dsg = TR::scale_k(TR::ld_nat(dSn + jc * D, ks, g), 1.f, sm.gam, ks, g);   // B[j][i] = dS[i][j] gamma_C[j]
+            const Frag b_s0 = TR::ld_nat(S0n + jc * D, ks, g);     // B[j][i] = S0[i][j]
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt) {
+                const int tr = SB * tt + cl;
+                const Frag a_v = TR::ld_colmatch(&Vs[tr * LD], ks, g);
+                aQ[tt] = TR::mma(TR::ld_colmatch(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);   // dO S0
+                aK[tt] = TR::mma(a_v, b_s0t, aK[tt]);                                      // V S0
+                aT[tt] = TR::mma(a_v, b_dst, aT[tt]);                                      // V dS
+                aVu[tt] = TR::mma(TR::ld_nat(&Kc[tr * LD], ks, g), b_dsg, aVu[tt]);       // Kt dS^T
+                aVr[tt] = TR::mma(TR::ld_nat(&Kb[tr * LD], ks, g), b_s0, aVr[tt]);        // Kbar S0^T
+            }
         }
+        if (std::is_same<TR, Bf16T>::value) {
+            gc2 += __shfl_xor(gc2, 16, 64);
+            gc2 += __shfl_xor(gc2, 32, 64);
+            if (g == 0) sm.gC2[jc] = gc2;
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NSB; ++tt) {
+        const floatx4 r0v = *reinterpret_cast<const floatx4*>(&sm.dr0[SB * tt + 4 * g]);
+        const floatx4 uv = *reinterpret_cast<const floatx4*>(&sm.u[SB * tt + 4 * g]);
+        aK[tt] = aK[tt] * r0v;    // dr0 (V S0)
+        aT[tt] = aT[tt] * uv;     // W dS
+        aVr[tt] = aVr[tt] * r0v;  // dr0 (Kbar S0^T)
     }
     // contractions over the chunk: transposed operands read in place
 #pragma unroll
@@ -671,10 +725,17 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
                 aC[tt] = TR::mma(TR::ld_col(&dGKl[tr], LDP, ks, g), b_kb, aC[tt]);
                 aC[tt] = TR::mma(TR::ld_col(&dPl[tr], LDP, ks, g), b_qb, aC[tt]);
             }
-            aV[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aV[tt]);             // (dGV + dGV^T) V
-            aV[tt] = TR::mma(TR::scale(TR::ld_col(&P[tr], LDP, ks, g), sm.u[tr]), b_do, aV[tt]);   // u (P^T dO)
+            aVr[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aVr[tt]);           // (dGV + dGV^T) V
+            aVu[tt] = TR::mma(TR::ld_col(&P[tr], LDP, ks, g), b_do, aVu[tt]);            // P^T dO
         }
     }
+    floatx4 aV[NSB];   // dV = u (Kt dS^T + P^T dO) + aVr
+#pragma unroll
+    for (int tt = 0; tt < NSB; ++tt)
+        aV[tt] = aVu[tt] * *reinterpret_cast<const floatx4*>(&sm.u[SB * tt + 4 * g]) + aVr[tt];
+    // q, k, f again for the elementwise stage (in flight during the staging)
+    Row2x8<TR> rq, rk, rf;
+    load_qkf(rq, rk, rf);
     lds_barrier();   // every operand read is done: the staging reuses the space
 #pragma unroll
     for (int tt = 0; tt < NSB; ++tt)
@@ -689,6 +750,9 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     lds_barrier();
 
     // ---------------- elementwise: dq, dk, and the decay gradient (prep layout)
+    clear_qkf(rq, rk, rf);
+    float ga[2][8], gC[8];
+    gammas(rf, ga, gC);   // bitwise the values the prep used
     const bool poison = sm.unsafe_any != 0u;
     float dqv[2][8], dkv[2][8], suf0[8], suf1[8], totg[8], toth[8];
 #pragma unroll
@@ -795,26 +859,27 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     typedef typename TR::E E;
     const BwdWs L = bwd_ws_layout(sizeof(E), D, B, T, H);
     char* wb = static_cast<char*>(ws);
-    E* ckS = reinterpret_cast<E*>(wb + L.s0);
-    float* ckU = reinterpret_cast<float*>(wb + L.ur);
+    FwdCkpt ck;
+    ck.S = wb + L.s0;
+    ck.U = reinterpret_cast<float*>(wb + L.ur);
+    ck.M = reinterpret_cast<float*>(wb + L.mm);
+    ck.P = wb + L.pp;
     E* wdS = reinterpret_cast<E*>(wb + L.ds);
     float* wrho = reinterpret_cast<float*>(wb + L.rho);
-    float* ckM = reinterpret_cast<float*>(wb + L.mm);
-    E* ckP = reinterpret_cast<E*>(wb + L.pp);
     const int NC = (T + CH - 1) / CH;
     if (NC > 0) {
-        hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr,
-                                  ckS, ckU, ckM, ckP, B, T, H, st);
+        hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr, &ck,
+                                  B, T, H, st);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
-                       (const float*)ckM, (const E*)ckP, dST, wdS, wrho, dS0, T, H);
+                       (const float*)ck.M, (const E*)ck.P, dST, wdS, wrho, dS0, T, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NC == 0) return e;
     hipLaunchKernelGGL((kd_bwd_chunk_kernel<TR, D>), dim3((unsigned)(B * H * NC)), dim3(4 * D), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
-                       (const E*)ckS, (const float*)ckU, (const E*)wdS, (const float*)wrho,
+                       (const E*)ck.S, (const float*)ck.U, (const E*)wdS, (const float*)wrho,
                        (E*)dq, (E*)dk, (E*)dv, (E*)df, dbeta, dc, T, H);
     return hipGetLastError();
 }

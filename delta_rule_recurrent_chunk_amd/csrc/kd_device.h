@@ -123,6 +123,28 @@ struct Bf16T {
         for (int e = 0; e < 8; ++e) r[e] = p[e * ld];
         return r;
     }
+    // Column fragments of a row-major matrix without strided loads: B operand
+    // with K = rows 32ks .. 32ks + 31 (in the "state" order) and N = columns
+    // c0 + cl (c0 a multiple of 16).  Two rows-by-16 tiles pass through the
+    // matrix core against a 0/1 selection of the 16 columns (one term per
+    // output, so the values are exact); tiles[hh] receives them as
+    // accumulators (rows 32ks + 16hh + 4g + r of column c0 + cl).
+    static __device__ __forceinline__ Frag col_sel(int c0, int g, int cl) {
+        Frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = cvt(8 * g + e == (c0 & 31) + cl ? 1.f : 0.f);
+        return r;
+    }
+    static __device__ __forceinline__ Frag col_frag(const E* m, int ld, int ks, int c0, Frag sel,
+                                                    int g, int cl, floatx4* tiles) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            tiles[hh] = mma(ld_nat(m + (uint32_t)(KS * ks + 16 * hh + cl) * ld + (c0 & ~31), 0, g), sel,
+                            floatx4{0.f, 0.f, 0.f, 0.f});
+        return state_frag(tiles, 0);
+    }
+    // A operand along the same K order as col_frag (rows of the contraction)
+    static __device__ __forceinline__ Frag ld_colmatch(const E* row, int ks, int g) { return ld_state(row, ks, g); }
     // every element times s (one row or column of an operand scaled)
     static __device__ __forceinline__ Frag scale(Frag x, float s) {
         Frag r;
@@ -245,6 +267,13 @@ struct F32T {
     static __device__ __forceinline__ Frag ld_col(const E* col, int ld, int ks, int g) {
         return col[(KS * ks + g) * ld];
     }
+    // fp32: one element per lane and K-step, read in place
+    static __device__ __forceinline__ Frag col_sel(int, int, int) { return 0.f; }
+    static __device__ __forceinline__ Frag col_frag(const E* m, int ld, int ks, int c0, Frag, int g, int cl,
+                                                    floatx4*) {
+        return m[(uint32_t)(KS * ks + g) * ld + c0 + cl];
+    }
+    static __device__ __forceinline__ Frag ld_colmatch(const E* row, int ks, int g) { return ld_nat(row, ks, g); }
     static __device__ __forceinline__ Frag scale(Frag x, float s) { return x * s; }
     static __device__ __forceinline__ Frag scale_k(Frag x, float s, const float* sv, int ks, int g) {
         return x * (s * sv[KS * ks + g]);
@@ -719,6 +748,18 @@ __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
 __device__ __forceinline__ void st2(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
+// Load eight consecutive values (16-byte aligned) as fp32.
+__device__ __forceinline__ void ld8f(const __bf16* p, float* x) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void ld8f(const float* p, float* x) {
+    const floatx4 a = reinterpret_cast<const floatx4*>(p)[0], b = reinterpret_cast<const floatx4*>(p)[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+
 // Store eight consecutive values (16 bytes of bf16 / 32 bytes of fp32).
 __device__ __forceinline__ void st8(__bf16* p, const float* x) {
     bf16x8 r;
@@ -736,6 +777,15 @@ __device__ __forceinline__ void st8(float* p, const float* x) {
     reinterpret_cast<floatx4*>(p)[0] = floatx4{x[0], x[1], x[2], x[3]};
     reinterpret_cast<floatx4*>(p)[1] = floatx4{x[4], x[5], x[6], x[7]};
 }
+
+// Per-chunk records that the checkpointing forward leaves for the backward,
+// each an array over (b, h, chunk) units in that order.
+struct FwdCkpt {
+    void* S;    // entering state S[i][j], input dtype, d*d per unit
+    float* U;   // u, then r0: 2*CH fp32 per unit
+    float* M;   // M, [CH][CH] fp32 per unit
+    void* P;    // P, [CH][CH] input dtype per unit
+};
 
 // Number of MFMA K-steps of each path that cover a contraction of length n.
 template <class TR, int N>

@@ -87,9 +87,9 @@ struct FwdSmem {
     unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
-// CKPT: also store, per chunk, the entering state (S[i][j], in the input
-// dtype), the WY targets u and r0, and M (fp32) and P (input dtype) as
-// [CH][CH] row-major, for the backward.  A separate
+// CKPT: also store, per chunk, the records of FwdCkpt for the backward: the
+// entering state (input dtype), the WY targets u and r0,
+// and M (fp32) and P (input dtype) as [CH][CH] row-major.  A separate
 // instantiation, so the plain forward carries none of its registers.
 template <class TR, int D, bool CKPT>
 __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
@@ -97,8 +97,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, typename TR::E* __restrict__ o, float* __restrict__ ST,
-    typename TR::E* __restrict__ ckptS, float* __restrict__ ckptU, float* __restrict__ ckptM,
-    typename TR::E* __restrict__ ckptP, int T, int H)
+    FwdCkpt ck, int T, int H)
 {
     typedef typename TR::E E;
     typedef typename TR::H Hh;
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             floatx4 Ot[2][NSB];   // O^T[i0 + 16mt + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
                 if (CKPT) {   // chunk-start state for the backward, S[i][j]
-                    E* dst = ckptS + ((size_t)bh * NC + n) * D * D;
+                    E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 for (int s = 0; s < CH - 1; ++s) x = fmaf(-Mrow[s], readlane_f(x, s), x);
                 sm.u[t_] = x;
                 if (CKPT) {   // u and r0 of the chunk for the backward
-                    float* du = ckptU + ((size_t)bh * NC + n) * 2 * CH;
+                    float* du = ck.U + ((size_t)bh * NC + n) * 2 * CH;
                     du[t_] = x;
                     du[CH + t_] = r0;
                 }
@@ -250,8 +249,8 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 // M and P of chunk n are complete and nobody writes them in this
                 // stage: the consumer waves copy them out ([CH][CH] row-major)
                 constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte move
-                float* dm = ckptM + ((size_t)bh * NC + n) * CH * CH;
-                E* dp = ckptP + ((size_t)bh * NC + n) * CH * CH;
+                float* dm = ck.M + ((size_t)bh * NC + n) * CH * CH;
+                E* dp = static_cast<E*>(ck.P) + ((size_t)bh * NC + n) * CH * CH;
                 for (int x = tid; x < CH * CH / 4; x += NWC * 64) {
                     const int t = x / (CH / 4), s4 = x % (CH / 4);
                     *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
@@ -587,31 +586,30 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 template <class TR, int D>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* f,
                                const float* beta, const float* c, const float* S0, void* o,
-                               float* ST, void* ckptS, float* ckptU, float* ckptM, void* ckptP,
-                               int B, int T, int H, hipStream_t st)
+                               float* ST, const FwdCkpt* ck, int B, int T, int H, hipStream_t st)
 {
     typedef typename TR::E E;
-    if (ckptS)
+    if (ck)
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, true>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)ckptS, ckptU, ckptM, (E*)ckptP, T, H);
+                           *ck, T, H);
     else
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, false>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)nullptr, (float*)nullptr, (float*)nullptr, (E*)nullptr, T, H);
+                           FwdCkpt{}, T, H);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
-                        const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
-                        float* ckptM, void* ckptP, int B, int T, int H, hipStream_t st);
+                        const float* c, const float* S0, void* o, float* ST, const FwdCkpt* ck,
+                        int B, int T, int H, hipStream_t st);
 
+// ck: the checkpoint records to fill (the backward's recompute), or null.
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      void* ckptS, float* ckptU, float* ckptM, void* ckptP, int B, int T, int H,
-                      hipStream_t st)
+                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st)
 {
-#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ckptS, ckptU, ckptM, ckptP, B, T, H, st
+#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ck, B, T, H, st
     if (bf16) {
         switch (d) {
         case 32: return launch_fwd_t<Bf16T, 32>(KD_FWD_ARGS);

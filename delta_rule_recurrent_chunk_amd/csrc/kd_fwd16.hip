@@ -62,15 +62,14 @@ struct Fwd16Smem {
     unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
-// CKPT: also store, per chunk, the entering state (S[i][j], bf16), u and r0,
-// and the chunk's M (fp32) and P (bf16), both [CH][CH] row-major.
+// CKPT: also store, per chunk, the records of FwdCkpt: the entering state
+// (bf16), u and r0, and the chunk's M and P.
 template <bool CKPT>
 __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
-    __bf16* __restrict__ ckptS, float* __restrict__ ckptU, float* __restrict__ ckptM,
-    __bf16* __restrict__ ckptP, int T, int H)
+    FwdCkpt ck, int T, int H)
 {
     using namespace f16w;
     typedef Bf16T TR;
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             floatx4 Ot[NSB];   // O^T[i0 + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
                 if (CKPT) {
-                    E* dst = ckptS + ((size_t)bh * NC + n) * D * D;
+                    E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
                     for (int mj = 0; mj < D / 16; ++mj)
                         st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj]);
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
                 sm.u[t_] = x;
                 if (CKPT) {
-                    float* du = ckptU + ((size_t)bh * NC + n) * 2 * CH;
+                    float* du = ck.U + ((size_t)bh * NC + n) * 2 * CH;
                     du[t_] = x;
                     du[CH + t_] = r0;
                 }
@@ -226,8 +225,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 // M and P of chunk n are complete (their last tiles ran in stage
                 // A) and nobody writes them in this stage: the idle consumer waves
                 // copy them out
-                float* dm = ckptM + ((size_t)bh * NC + n) * CH * CH;
-                E* dp = ckptP + ((size_t)bh * NC + n) * CH * CH;
+                float* dm = ck.M + ((size_t)bh * NC + n) * CH * CH;
+                E* dp = static_cast<E*>(ck.P) + ((size_t)bh * NC + n) * CH * CH;
                 for (int x = tid - 64; x < CH * CH / 4; x += (NWC - 1) * 64) {
                     const int t = x >> 4, s4 = x & 15;
                     *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
@@ -576,18 +575,18 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 }
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
-                        const float* c, const float* S0, void* o, float* ST, void* ckptS, float* ckptU,
-                        float* ckptM, void* ckptP, int B, int T, int H, hipStream_t st)
+                        const float* c, const float* S0, void* o, float* ST, const FwdCkpt* ck,
+                        int B, int T, int H, hipStream_t st)
 {
     typedef __bf16 E;
-    if (ckptS)
+    if (ck)
         hipLaunchKernelGGL(kd_fwd16_kernel<true>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)ckptS, ckptU, ckptM, (E*)ckptP, T, H);
+                           *ck, T, H);
     else
         hipLaunchKernelGGL(kd_fwd16_kernel<false>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           (E*)nullptr, (float*)nullptr, (float*)nullptr, (E*)nullptr, T, H);
+                           FwdCkpt{}, T, H);
     return hipGetLastError();
 }
 
