@@ -88,6 +88,13 @@ def algorithmic_bytes_fwd_bwd(w, esize):
     return fwd + bwd
 
 
+def algorithmic_bytes_decode(w, esize):
+    """HBM bytes of one decode call: the carried fp32 state read and written
+    once, every token input once, o once."""
+    ntok = w.B * w.T * w.H
+    return 2 * w.B * w.H * w.dv * w.dk * 4 + 4 * ntok * w.dk * esize + 2 * ntok * 4 + ntok * w.dv * esize
+
+
 def mfma_flops(w):
     """MFMA flops of one launch as issued (full 16x16 tiles, including the
     masked-out upper Gram tiles' partners): per (b, h, chunk) of C = 64 with
@@ -114,7 +121,8 @@ def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
         for b in range(w.B):
             sl = slice(b, b + 1)
             oracle.fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
-                       x_np["beta"][sl], x_np["c"][sl], None)
+                       x_np["beta"][sl], x_np["c"][sl],
+                       x_np["S0"][sl] if x_np.get("S0") is not None else None)
             if w.backward:
                 oracle.bwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
                            x_np["beta"][sl], x_np["c"][sl], None, x_np["dO"][sl])
@@ -177,7 +185,12 @@ def main():
                          device=dev) for n in ("q", "k", "v", "f", "beta", "c")}
     esize = 2 if w.dtype == "bf16" else 4
 
-    if w.backward:   # a step is the forward plus the gate-aware backward
+    if w.decode:     # a step is one decode call, the state updated in place
+        t["S"] = torch.tensor(x["S0"], dtype=torch.float32, device=dev)
+
+        def step():
+            return kd.decode(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S"])
+    elif w.backward:   # a step is the forward plus the gate-aware backward
         t["dO"] = torch.tensor(x["dO"], dtype=tdt, device=dev)
         ws = torch.empty(max(kd.workspace_bytes(w.B, w.T, w.H, w.dk, 1 if w.dtype == "bf16" else 0,
                                                  with_backward=True), 16),
@@ -211,15 +224,17 @@ def main():
 
     tokens = w.B * w.T
     value = tokens / (ms_per_step * 1e-3)
-    abytes = algorithmic_bytes_fwd_bwd(w, esize) if w.backward else algorithmic_bytes(w, esize)
+    abytes = (algorithmic_bytes_decode(w, esize) if w.decode else
+              algorithmic_bytes_fwd_bwd(w, esize) if w.backward else algorithmic_bytes(w, esize))
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
     flops = mfma_flops(w)
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
     traffic = stored_traffic() if args.workload == "train_step" else None
 
     out = {
-        "metric": METRIC if not w.backward else
-        "Kron-delta chunked fwd+bwd tokens/s (H=16,d=128) and % HBM roofline",
+        "metric": ("Kron-delta decode tokens/s (H=16,d=128) and % HBM roofline" if w.decode else
+                   "Kron-delta chunked fwd+bwd tokens/s (H=16,d=128) and % HBM roofline"
+                   if w.backward else METRIC),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -232,20 +247,25 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
                 "beta,c=sigmoid(N(0,1)))" % w.mu,
-        "config": {"workload": "%s: Kronecker delta rule chunked %s, B=%d T=%d H=%d "
-                               "dk=dv=%d, chunk 64, %s q/k/v/f, fp32 beta/c/state, S0=0"
-                               % (w.name, "forward + gate-aware backward" if w.backward else "forward",
-                                  w.B, w.T, w.H, w.dk, w.dtype),
+        "config": {"workload": ("%s: Kronecker delta rule decode (token by token on the carried "
+                                "state, updated in place), B=%d T=%d H=%d dk=dv=%d, %s q/k/v/f, "
+                                "fp32 beta/c/state, S ~ N(0, 0.1^2)"
+                                % (w.name, w.B, w.T, w.H, w.dk, w.dtype)) if w.decode else
+                               ("%s: Kronecker delta rule chunked %s, B=%d T=%d H=%d "
+                                "dk=dv=%d, chunk 64, %s q/k/v/f, fp32 beta/c/state, S0=0"
+                                % (w.name, "forward + gate-aware backward" if w.backward else "forward",
+                                   w.B, w.T, w.H, w.dk, w.dtype)),
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_fwd16_kernel<false>" if not w.backward else
+                     "kernel": "kd_decode_kernel<bf16,128>" if w.decode else
+                     "kd_fwd16_kernel<false>" if not w.backward else
                      "kd_fwd16_kernel + kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,
                      },
     }
-    if not w.backward:
+    if not w.backward and not w.decode:
         out["roofline"]["mfma_tflops"] = flops / (kernel_ms * 1e-3) / 1e12
         out["roofline"]["mfma_frac"] = flops / (kernel_ms * 1e-3) / 1e12 / peak_tf
     if args.cold:

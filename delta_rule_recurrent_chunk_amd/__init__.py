@@ -7,6 +7,7 @@ missing, every entry point raises; there is no CPU fallback.
 
     o, S_T = fwd(q, k, v, f, beta, c, S0=None)
     grads  = bwd(q, k, v, f, beta, c, S0, dO, dST=None)
+    o      = decode(q, k, v, f, beta, c, S)        (S updated in place)
 
 Shapes: q, k, f [B, T, H, d]; v [B, T, H, d]; beta, c [B, T, H] fp32;
 S0 / S_T [B, H, d, d] fp32 (S[i][j], i over values, j over keys).
@@ -23,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libkrondelta.so")
 KD_F32, KD_BF16 = 0, 1
 ABI_VERSION = 1
 EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
-            "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd")
+            "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
+            "kron_delta_decode")
 
 
 class KronDeltaError(RuntimeError):
@@ -59,6 +61,8 @@ def lib():
         L.kron_delta_fwd.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
         L.kron_delta_bwd.restype = i32
         L.kron_delta_bwd.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+        L.kron_delta_decode.restype = i32
+        L.kron_delta_decode.argtypes = [dp] + [vp] * 9 + [vp]
         if L.kron_delta_abi_version() != ABI_VERSION:
             raise ImportError("libkrondelta.so ABI version mismatch")
         _lib = L
@@ -121,6 +125,28 @@ def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True):
     if st != 0:
         raise KronDeltaError(st, "kron_delta_fwd")
     return o, ST
+
+
+def decode(q, k, v, f, beta, c, S, *, S_out=None):
+    """Token-by-token recurrence on a carried state (serving).  q, k, v, f are
+    [B, T, H, d] for the T new tokens (typically T = 1); S [B, H, d, d] fp32 is
+    the state before them.  Returns o; the state after the last token goes to
+    S_out, or into S itself (in place) when S_out is None."""
+    import torch
+    L = lib()
+    desc, q, k, v, f, beta, c, S = _prep(torch, q, k, v, f, beta, c, S)
+    if S is None:
+        raise ValueError("decode needs the carried state S")
+    out = S if S_out is None else S_out
+    if tuple(out.shape) != tuple(S.shape) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("S_out must be a contiguous float32 tensor shaped like S")
+    o = torch.empty((desc.B, desc.T, desc.H, desc.dv), dtype=q.dtype, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.kron_delta_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+                             _ptr(c), _ptr(S), _ptr(o), _ptr(out), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_decode")
+    return o
 
 
 def workspace_bytes(B, T, H, d, dtype_code, with_backward=True) -> int:

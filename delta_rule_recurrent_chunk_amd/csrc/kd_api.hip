@@ -17,6 +17,9 @@ hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void*
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
                       float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st);
 size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H);
+hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                         const float* beta, const float* c, const float* S_in, void* o, float* S_out,
+                         int B, int T, int H, hipStream_t st);
 }  // namespace kd
 
 namespace {
@@ -39,13 +42,14 @@ bool overlap(Range a, Range b) {
 
 bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
 
-kd_status check_desc(const kd_desc* d) {
+// fp32_d128: whether the entry point supports fp32 at d = 128 (decode only)
+kd_status check_desc(const kd_desc* d, bool fp32_d128 = false) {
     if (!d) return KD_ERR_NULL;
     if (d->dtype != KD_F32 && d->dtype != KD_BF16) return KD_ERR_DTYPE;
     if (d->B < 1 || d->H < 1 || d->T < 0) return KD_ERR_SHAPE;
     if (d->dk != d->dv) return KD_ERR_SHAPE;
     if (d->dk != 32 && d->dk != 64 && d->dk != 128) return KD_ERR_SHAPE;
-    if (d->dtype == KD_F32 && d->dk == 128) return KD_ERR_DTYPE;
+    if (d->dtype == KD_F32 && d->dk == 128 && !fp32_d128) return KD_ERR_DTYPE;
     if ((int64_t)d->B * (int64_t)d->H > (int64_t)INT32_MAX) return KD_ERR_SHAPE;
     // kernels address one batch element's [T, H, d] tensor with 32-bit byte offsets
     const int64_t es = d->dtype == KD_BF16 ? 2 : 4;
@@ -106,6 +110,35 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
     if (ntok == 0 && !ST) return KD_OK;
     hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
                                   nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+kd_status kron_delta_decode(const kd_desc* d, const void* q, const void* k, const void* v,
+                            const void* f, const float* beta, const float* c, const float* S_in,
+                            void* o, float* S_out, void* stream) {
+    kd_status st = check_desc(d, true);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (!S_out) return KD_ERR_NULL;
+    if (ntok > 0 && (!q || !k || !v || !f || !beta || !c || !o)) return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, f, beta, c, S_in, o, S_out};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    // S_out may be S_in itself (update in place); any other overlap is rejected
+    const bool inplace = S_in != nullptr && S_in == S_out;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
+                         range_of(beta, gb), range_of(c, gb), range_of(inplace ? nullptr : S_in, sb)};
+    const Range outs[] = {range_of(o, ntok ? xb : 0), range_of(S_out, sb)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
+    if (inplace && (overlap(outs[0], range_of(S_in, sb)))) return KD_ERR_ALIAS;
+    hipError_t e = kd::launch_decode(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S_in, o, S_out,
+                                     d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

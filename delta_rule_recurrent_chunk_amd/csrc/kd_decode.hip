@@ -1,0 +1,125 @@
+// kd_decode.hip -- token-by-token recurrence on a carried state (serving), gfx950.
+//
+// For each (b, h) and each of the T tokens, in order (onedev.kr KronLSTM
+// summary, sections "어떻게 동작하나" and "어떻게 쓰나"):
+//     Sbar = S diag(f_t);  r = v_t^T Sbar k_t;  S = Sbar + (c_t - beta_t r) v_t k_t^T;
+//     o_t = S q_t = Sbar q_t + (c_t - beta_t r) v_t (k_t . q_t).
+// No chunking: T is small in decoding (typically 1), and the state (d x d
+// fp32) is the only large operand, so the kernel is bound by reading and
+// writing it once per call.
+//
+// One workgroup of 256 threads per (b, h).  The state lives in registers for
+// the whole call: thread t owns row i = t / TPR of S and a contiguous run of
+// CPT = d*d / 256 columns (TPR = 256 / d threads per row), read and written as
+// 16-byte vectors so each row's threads cover it with whole cache lines.
+#include "kd_device.h"
+
+namespace kd {
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void kd_decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ f,
+    const float* __restrict__ beta, const float* __restrict__ cc, const float* S_in,
+    E* __restrict__ o, float* S_out, int T, int H)
+{
+    constexpr int NT = 256;
+    constexpr int TPR = NT / D;          // threads per state row
+    constexpr int CPT = D / TPR;         // columns per thread
+    constexpr int NV = CPT / 4;          // float4 per thread
+    __shared__ float sq[D], sk[D], sf[D], sv[D];
+    __shared__ float red[2][NT / 64];    // per-wave partials of r and k.q
+    __shared__ float bc[2];              // beta_t, c_t
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int i = tid / TPR, j0 = (tid % TPR) * CPT;   // row and first column
+
+    floatx4 S[NV];
+    const size_t sbase = (size_t)bh * D * D + (size_t)i * D + j0;
+#pragma unroll
+    for (int x = 0; x < NV; ++x)
+        S[x] = S_in ? *reinterpret_cast<const floatx4*>(S_in + sbase + 4 * x) : floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int t = 0; t < T; ++t) {
+        const size_t row = ((size_t)b * T + t) * H + h;   // token (b, t, h)
+        if (tid < D) {
+            sq[tid] = (float)q[row * D + tid];
+            sk[tid] = (float)k[row * D + tid];
+            sf[tid] = (float)f[row * D + tid];
+            sv[tid] = (float)v[row * D + tid];
+        }
+        if (tid == 0) { bc[0] = beta[row]; bc[1] = cc[row]; }
+        __syncthreads();
+        // Sbar = S diag(f); partial y = Sbar k and z = Sbar q over this thread's columns
+        float y = 0.f, z = 0.f;
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * x + e;
+                const float sb = S[x][e] * sf[j];
+                S[x][e] = sb;
+                y = fmaf(sb, sk[j], y);
+                z = fmaf(sb, sq[j], z);
+            }
+        }
+        // whole-row sums over the TPR threads of the row (adjacent lanes)
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) {
+            y += __shfl_xor(y, m, 64);
+            z += __shfl_xor(z, m, 64);
+        }
+        // r = sum_i v_i y_i and k.q, each counted once (row leaders, lanes < D)
+        float pr = (tid % TPR == 0) ? sv[i] * y : 0.f;
+        float pk = (tid < D) ? sk[tid] * sq[tid] : 0.f;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            pr += __shfl_xor(pr, m, 64);
+            pk += __shfl_xor(pk, m, 64);
+        }
+        if (lane == 0) { red[0][w] = pr; red[1][w] = pk; }
+        __syncthreads();
+        float r = 0.f, kq = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NT / 64; ++ww) { r += red[0][ww]; kq += red[1][ww]; }
+        const float a = bc[1] - bc[0] * r;
+        // S = Sbar + a v k^T;  o = Sbar q + a v (k.q)
+        const float av = a * sv[i];
+#pragma unroll
+        for (int x = 0; x < NV; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[x][e] = fmaf(av, sk[j0 + 4 * x + e], S[x][e]);
+        if (tid % TPR == 0) o[row * D + i] = (E)(z + av * kq);
+        __syncthreads();   // the token vectors and partials are reused
+    }
+#pragma unroll
+    for (int x = 0; x < NV; ++x) *reinterpret_cast<floatx4*>(S_out + sbase + 4 * x) = S[x];
+}
+
+hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                         const float* beta, const float* c, const float* S_in, void* o, float* S_out,
+                         int B, int T, int H, hipStream_t st)
+{
+#define KD_DEC(E, D)                                                                                     \
+    hipLaunchKernelGGL((kd_decode_kernel<E, D>), dim3((unsigned)(B * H)), dim3(256), 0, st, (const E*)q,  \
+                       (const E*)k, (const E*)v, (const E*)f, beta, c, S_in, (E*)o, S_out, T, H)
+    if (bf16) {
+        switch (d) {
+        case 32: KD_DEC(__bf16, 32); break;
+        case 64: KD_DEC(__bf16, 64); break;
+        case 128: KD_DEC(__bf16, 128); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+        case 32: KD_DEC(float, 32); break;
+        case 64: KD_DEC(float, 64); break;
+        case 128: KD_DEC(float, 128); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
+#undef KD_DEC
+    return hipGetLastError();
+}
+
+}  // namespace kd

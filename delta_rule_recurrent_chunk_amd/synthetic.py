@@ -44,6 +44,7 @@ class Workload:
     beta_scale: float = 1.0
     seed: int = 1000
     backward: bool = False
+    decode: bool = False   # token-by-token on a carried state (S0 drawn, N(0, 0.1^2))
 
     @property
     def tokens(self) -> int:
@@ -62,6 +63,8 @@ WORKLOADS = {
     # Long context, non-contractive erase gate in (0, 2), near-1 decay.
     "long_ctx": Workload("long_ctx", 1, 32768, 16, 128, 128, "bf16", mu=5.0,
                          beta_scale=2.0, seed=1004),
+    # Serving: one new token for each of 32 sequences on their carried states.
+    "decode_step": Workload("decode_step", 32, 1, 16, 128, 128, "bf16", seed=1005, decode=True),
 }
 
 
@@ -96,6 +99,8 @@ def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
 
 
 def draw_workload(w: Workload, with_dO=None, s0_std=None):
+    if s0_std is None and w.decode:
+        s0_std = 0.1
     return draw(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, beta_scale=w.beta_scale,
                 with_dO=w.backward if with_dO is None else with_dO, s0_std=s0_std)
 

@@ -109,15 +109,33 @@ KD_API kd_status kron_delta_fwd(const kd_desc *desc,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Decode: the recurrence applied token by token to a carried state, for
+ * serving (one step is the definition above, taken directly, without the
+ * chunked form).  desc->T is the number of new tokens per (b, h) (any T >= 0;
+ * typically 1), with q, k, v, f, beta, c laid out as for kron_delta_fwd.
+ * S_in [B, H, dv, dk] fp32 is the state before the first new token (NULL
+ * means 0); S_out receives the state after the last one and may be the same
+ * buffer as S_in (the state is then updated in place; any other overlap of
+ * an output with an input is KD_ERR_ALIAS).  o [B, T, H, dv] in the input
+ * dtype.  Supports bf16 and fp32 with dk = dv in {32, 64, 128}.  One kernel,
+ * one workgroup per (b, h); the state is read and written once per call.
+ */
+KD_API kd_status kron_delta_decode(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S_in,
+                         void *o, float *S_out, void *stream);
+
+/*
  * Gate-aware backward pass: gradients of L = <dO, o> + <dST, S_T> with
  * respect to q, k, v, f, beta, c and S0, where o and S_T are what
  * kron_delta_fwd returns for the same inputs.  dST NULL means dS_T = 0;
  * S0 NULL means S0 = 0; dS0 NULL means the gradient of S0 is not returned.
  * Needs a workspace of kron_delta_workspace_bytes(desc, 1) bytes: it holds,
- * per 64-token chunk, the entering state and the WY targets of a forward
- * recomputation and the state gradient of the reverse sweep (about
- * 4 * d * d * sizeof(element) bytes per chunk and head); its contents on
- * entry are ignored and on exit are unspecified.
+ * per 64-token chunk and head, the entering state, the WY targets and the
+ * chunk matrices M and P of a forward recomputation, and the state gradient
+ * of the reverse sweep (about 2*d*d*e + 64*64*(4 + e) + 768 bytes, e the
+ * element size); its contents on entry are ignored and on exit are
+ * unspecified.
  * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv = 32
  * (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
  * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2

@@ -122,3 +122,28 @@ def test_workspace_scales_with_chunks(L):
     b = L.kron_delta_workspace_bytes(ctypes.byref(_desc(T=65)), 1)
     assert b == 2 * a
     assert L.kron_delta_workspace_bytes(ctypes.byref(_desc(dk=48, dv=48)), 1) == 0
+
+
+def decode(L, desc, **over):
+    names = ["q", "k", "v", "f", "beta", "c", "S_in", "o", "S_out"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    p.update(over)
+    d = ctypes.byref(desc) if desc is not None else None
+    return L.kron_delta_decode(d, *[p[n] for n in names], None)
+
+
+def test_decode_argument_checks(L):
+    # every case fails its checks before a launch
+    assert decode(L, None) == NULL
+    assert decode(L, _desc(T=1, dtype=5)) == DTYPE
+    assert decode(L, _desc(T=1, dk=48, dv=48)) == SHAPE
+    assert decode(L, _desc(T=-1)) == SHAPE
+    assert decode(L, _desc(T=1), S_out=None) == NULL
+    assert decode(L, _desc(T=1), q=None) == NULL
+    assert decode(L, _desc(T=1), beta=None) == NULL
+    assert decode(L, _desc(T=1), v=P(2, misalign=4)) == ALIGN
+    assert decode(L, _desc(T=1), S_out=P(8, misalign=8)) == ALIGN
+    assert decode(L, _desc(T=1), o=P(0)) == ALIAS            # o == q
+    assert decode(L, _desc(T=1), S_out=P(1)) == ALIAS        # S_out == k
+    assert decode(L, _desc(T=1), S_out=P(7)) == ALIAS        # S_out == o
+    assert decode(L, _desc(T=1), o=P(6)) == ALIAS            # o == S_in
