@@ -8,6 +8,7 @@ missing, every entry point raises; there is no CPU fallback.
     o, S_T = fwd(q, k, v, f, beta, c, S0=None)
     grads  = bwd(q, k, v, f, beta, c, S0, dO, dST=None)
     o      = decode(q, k, v, f, beta, c, S)        (S updated in place)
+    o, S_T = fwd_varlen(q, k, v, f, beta, c, cu_seqlens, S0=None)   (packed sequences)
 
 Shapes: q, k, f [B, T, H, d]; v [B, T, H, d]; beta, c [B, T, H] fp32;
 S0 / S_T [B, H, d, d] fp32 (S[i][j], i over values, j over keys).
@@ -25,7 +26,7 @@ KD_F32, KD_BF16 = 0, 1
 ABI_VERSION = 1
 EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
-            "kron_delta_decode")
+            "kron_delta_decode", "kron_delta_fwd_varlen")
 
 
 class KronDeltaError(RuntimeError):
@@ -62,6 +63,8 @@ def lib():
         L.kron_delta_bwd.restype = i32
         L.kron_delta_bwd.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
         L.kron_delta_decode.restype = i32
+        L.kron_delta_fwd_varlen.restype = i32
+        L.kron_delta_fwd_varlen.argtypes = [dp, vp] + [vp] * 9 + [vp]
         L.kron_delta_decode.argtypes = [dp] + [vp] * 9 + [vp]
         if L.kron_delta_abi_version() != ABI_VERSION:
             raise ImportError("libkrondelta.so ABI version mismatch")
@@ -124,6 +127,41 @@ def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True):
                           _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), None, 0, ctypes.c_void_p(stream))
     if st != 0:
         raise KronDeltaError(st, "kron_delta_fwd")
+    return o, ST
+
+
+def fwd_varlen(q, k, v, f, beta, c, cu_seqlens, S0=None, *, return_state=True):
+    """Forward over packed sequences: q, k, f [T, H, dk], v [T, H, dv], beta, c
+    [T, H] (all sequences concatenated along T); cu_seqlens int32 [N + 1] on
+    the device.  Returns (o [T, H, dv], S_T [N, H, dv, dk] or None)."""
+    import torch
+    L = lib()
+    if q.dim() != 3:
+        raise ValueError("packed q must be [T, H, d]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be an int32 device vector [N + 1]")
+    N = cu_seqlens.numel() - 1
+    if N < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    S0b = None
+    if S0 is not None:
+        S0b = S0
+    desc, q4, k4, v4, f4, b4, c4, _ = _prep(torch, q[None], k[None], v[None], f[None], beta[None],
+                                            c[None], None)
+    T, H, dk, dv = desc.T, desc.H, desc.dk, desc.dv
+    desc = KdDesc(N, T, H, dk, dv, desc.dtype)
+    if S0b is not None:
+        if tuple(S0b.shape) != (N, H, dv, dk) or S0b.dtype != torch.float32:
+            raise ValueError("S0 must be float32 [N, H, dv, dk]")
+        S0b = S0b.contiguous()
+    cu = cu_seqlens.contiguous()
+    o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    ST = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device) if return_state else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.kron_delta_fwd_varlen(ctypes.byref(desc), _ptr(cu), _ptr(q4), _ptr(k4), _ptr(v4), _ptr(f4),
+                                 _ptr(b4), _ptr(c4), _ptr(S0b), _ptr(o), _ptr(ST), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_fwd_varlen")
     return o, ST
 
 

@@ -11,7 +11,7 @@ namespace kd {
 struct FwdCkpt;
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st);
+                      const FwdCkpt* ck, const int* cu, int B, int T, int H, hipStream_t st);
 hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, const void* dO,
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
@@ -109,7 +109,36 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
     hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
-                                  nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+                                  nullptr, nullptr, d->B, d->T, d->H, (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+kd_status kron_delta_fwd_varlen(const kd_desc* d, const int32_t* cu_seqlens, const void* q,
+                                const void* k, const void* v, const void* f, const float* beta,
+                                const float* c, const float* S0, void* o, float* ST, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    if (!cu_seqlens) return KD_ERR_NULL;
+    if (((uintptr_t)cu_seqlens & 3u) != 0) return KD_ERR_ALIGN;
+    const size_t ntok = (size_t)d->T * d->H;   // all sequences packed along T
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !f || !beta || !c || !o)) return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, f, beta, c, S0, o, ST};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
+                         range_of(beta, gb), range_of(c, gb), range_of(S0, S0 ? sb : 0),
+                         range_of(cu_seqlens, (size_t)(d->B + 1) * sizeof(int32_t))};
+    const Range outs[] = {range_of(o, ntok ? xb : 0), range_of(ST, ST ? sb : 0)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
+    if (ntok == 0 && !ST) return KD_OK;
+    hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
+                                  nullptr, cu_seqlens, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

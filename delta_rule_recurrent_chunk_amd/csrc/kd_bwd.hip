@@ -41,7 +41,7 @@ namespace kd {
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st);
+                      const FwdCkpt* ck, const int* cu, int B, int T, int H, hipStream_t st);
 
 // Workspace: [S0 | u, r0 | dS | drho | M | P] per (b, h, chunk) unit,
 // 256-byte aligned parts (per unit: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4,
@@ -869,7 +869,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     const int NC = (T + CH - 1) / CH;
     if (NC > 0) {
         hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr, &ck,
-                                  B, T, H, st);
+                                  nullptr, B, T, H, st);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, typename TR::E* __restrict__ o, float* __restrict__ ST,
-    FwdCkpt ck, int T, int H)
+    FwdCkpt ck, const int* __restrict__ cu, int T_, int H)
 {
     typedef typename TR::E E;
     typedef typename TR::H Hh;
@@ -120,7 +120,15 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     // Per batch element, every [T, H, D] tensor is addressed from a wave-uniform
     // base with 32-bit element offsets (the host checks T*H*D fits).
     const uint32_t rs = (uint32_t)H * D;         // token stride (elements)
-    const size_t bbase = (size_t)b * T * H * D;
+    // Batch element b holds tokens tok0 .. tok0 + T - 1: T_ tokens each, or,
+    // for packed sequences, those between the offsets cu[b] and cu[b + 1]
+    // (clamped to [0, T_], so bad offsets cannot reach outside the tensors).
+    int tok0 = b * T_, T = T_;
+    if (cu) {
+        tok0 = min(max(cu[b], 0), T_);
+        T = min(max(cu[b + 1], tok0), T_) - tok0;
+    }
+    const size_t bbase = (size_t)tok0 * H * D;
     const E* qb = q + bbase;
     const E* kb = k + bbase;
     const E* vb = v + bbase;
@@ -357,8 +365,8 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             rq.load(qb, off, rs, last);
             const int t = min(n * CH + (ptid & (CH - 1)), T - 1);
             const uint32_t gi = ((uint32_t)t * H + h);
-            rb_beta = beta[(size_t)b * T * H + gi];
-            rb_c = cc[(size_t)b * T * H + gi];
+            rb_beta = beta[(size_t)tok0 * H + gi];
+            rb_c = cc[(size_t)tok0 * H + gi];
         };
         auto load_k = [&](int n) { int last; const uint32_t off = row_off(n, last); rk.load(kb, off, rs, last); };
         auto load_v = [&](int n) { int last; const uint32_t off = row_off(n, last); rv.load(vb, off, rs, last); };
@@ -586,30 +594,33 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 template <class TR, int D>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* f,
                                const float* beta, const float* c, const float* S0, void* o,
-                               float* ST, const FwdCkpt* ck, int B, int T, int H, hipStream_t st)
+                               float* ST, const FwdCkpt* ck, const int* cu, int B, int T, int H,
+                               hipStream_t st)
 {
     typedef typename TR::E E;
     if (ck)
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, true>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           *ck, T, H);
+                           *ck, (const int*)nullptr, T, H);
     else
         hipLaunchKernelGGL((kd_fwd_kernel<TR, D, false>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           FwdCkpt{}, T, H);
+                           FwdCkpt{}, cu, T, H);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
                         const float* c, const float* S0, void* o, float* ST, const FwdCkpt* ck,
-                        int B, int T, int H, hipStream_t st);
+                        const int* cu, int B, int T, int H, hipStream_t st);
 
 // ck: the checkpoint records to fill (the backward's recompute), or null.
+// cu: null, or the B + 1 token offsets of packed sequences (T = total tokens;
+// not combined with ck).
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
-                      const FwdCkpt* ck, int B, int T, int H, hipStream_t st)
+                      const FwdCkpt* ck, const int* cu, int B, int T, int H, hipStream_t st)
 {
-#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ck, B, T, H, st
+#define KD_FWD_ARGS q, k, v, f, beta, c, S0, o, ST, ck, cu, B, T, H, st
     if (bf16) {
         switch (d) {
         case 32: return launch_fwd_t<Bf16T, 32>(KD_FWD_ARGS);

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
-    FwdCkpt ck, int T, int H)
+    FwdCkpt ck, const int* __restrict__ cu, int T_, int H)
 {
     using namespace f16w;
     typedef Bf16T TR;
@@ -89,7 +89,15 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     // per batch element, [T, H, D] tensors are addressed from a wave-uniform
     // base with 32-bit element offsets (the host checks T*H*D fits)
     const uint32_t rs = (uint32_t)H * D;
-    const size_t bbase = (size_t)b * T * H * D;
+    // Batch element b holds tokens tok0 .. tok0 + T - 1: T_ tokens each, or,
+    // for packed sequences, those between the offsets cu[b] and cu[b + 1]
+    // (clamped to [0, T_], so bad offsets cannot reach outside the tensors).
+    int tok0 = b * T_, T = T_;
+    if (cu) {
+        tok0 = min(max(cu[b], 0), T_);
+        T = min(max(cu[b + 1], tok0), T_) - tok0;
+    }
+    const size_t bbase = (size_t)tok0 * H * D;
     const E* qb = q + bbase;
     const E* kb = k + bbase;
     const E* vb = v + bbase;
@@ -331,8 +339,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             rq.load(qb, off, rs, last);
             const int t = min(n * CH + lane, T - 1);
             const uint32_t gi = (uint32_t)t * H + h;
-            rb_beta = beta[(size_t)b * T * H + gi];
-            rb_c = cc[(size_t)b * T * H + gi];
+            rb_beta = beta[(size_t)tok0 * H + gi];
+            rb_c = cc[(size_t)tok0 * H + gi];
         };
         auto load_k = [&](int n) { int last; const uint32_t off = row_off(n, last); rk.load(kb, off, rs, last); };
         auto load_v = [&](int n) { int last; const uint32_t off = row_off(n, last); rv.load(vb, off, rs, last); };
@@ -576,17 +584,17 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* f, const float* beta,
                         const float* c, const float* S0, void* o, float* ST, const FwdCkpt* ck,
-                        int B, int T, int H, hipStream_t st)
+                        const int* cu, int B, int T, int H, hipStream_t st)
 {
     typedef __bf16 E;
     if (ck)
         hipLaunchKernelGGL(kd_fwd16_kernel<true>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           *ck, T, H);
+                           *ck, (const int*)nullptr, T, H);
     else
         hipLaunchKernelGGL(kd_fwd16_kernel<false>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           FwdCkpt{}, T, H);
+                           FwdCkpt{}, cu, T, H);
     return hipGetLastError();
 }
 

@@ -109,6 +109,25 @@ KD_API kd_status kron_delta_fwd(const kd_desc *desc,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Forward pass over packed variable-length sequences.  desc->B is the number
+ * of sequences N and desc->T the total number of tokens; sequence s holds
+ * tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed tensors
+ *     q, k, f : [T, H, dk]    v, o : [T, H, dv]    beta, c : [T, H]
+ * and has its own state: S0 and ST are [N, H, dv, dk] (S0 NULL means 0; ST
+ * NULL skips it).  cu_seqlens is a DEVICE array of N + 1 int32 offsets,
+ * non-decreasing from 0 to T (4-byte aligned); it is read on the device,
+ * where offsets outside [0, T] are clamped into it (a sequence then covers
+ * fewer tokens; memory outside the tensors is never touched).  Tokens not
+ * covered by any sequence leave o unwritten.  Same definition, shapes and
+ * precision as kron_delta_fwd; the sequences are processed independently, so
+ * the result for each equals kron_delta_fwd on that sequence alone.
+ */
+KD_API kd_status kron_delta_fwd_varlen(const kd_desc *desc, const int32_t *cu_seqlens,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         void *o, float *ST, void *stream);
+
+/*
  * Decode: the recurrence applied token by token to a carried state, for
  * serving (one step is the definition above, taken directly, without the
  * chunked form).  desc->T is the number of new tokens per (b, h) (any T >= 0;

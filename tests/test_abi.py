@@ -147,3 +147,24 @@ def test_decode_argument_checks(L):
     assert decode(L, _desc(T=1), S_out=P(1)) == ALIAS        # S_out == k
     assert decode(L, _desc(T=1), S_out=P(7)) == ALIAS        # S_out == o
     assert decode(L, _desc(T=1), o=P(6)) == ALIAS            # o == S_in
+
+
+def fwd_varlen(L, desc, **over):
+    names = ["cu", "q", "k", "v", "f", "beta", "c", "S0", "o", "ST"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    p.update(over)
+    d = ctypes.byref(desc) if desc is not None else None
+    return L.kron_delta_fwd_varlen(d, *[p[n] for n in names], None)
+
+
+def test_fwd_varlen_argument_checks(L):
+    d = _desc(B=3, T=200)   # 3 sequences, 200 packed tokens
+    assert fwd_varlen(L, None) == NULL
+    assert fwd_varlen(L, d, cu=None) == NULL
+    assert fwd_varlen(L, d, cu=P(0, misalign=2)) == ALIGN
+    assert fwd_varlen(L, _desc(B=3, T=200, dk=64, dv=32)) == SHAPE
+    assert fwd_varlen(L, d, q=None) == NULL
+    assert fwd_varlen(L, d, o=P(1)) == ALIAS          # o == q
+    assert fwd_varlen(L, d, ST=P(7)) == ALIAS         # ST == S0
+    assert fwd_varlen(L, d, o=P(0)) == ALIAS          # o == cu_seqlens
+    assert fwd_varlen(L, _desc(B=3, T=0), ST=None) == OK
