@@ -67,6 +67,11 @@ __device__ __forceinline__ float pow2_scale(float x) {
     if (!(x > 0.f) || !(x < 3.0e38f)) return 1.f;
     return ldexpf(1.f, -__builtin_amdgcn_frexp_expf(x));
 }
+// The exponent e of pow2_scale(x) = 2^-e (0 where pow2_scale returns 1).
+__device__ __forceinline__ int pow2_exp(float x) {
+    if (!(x > 0.f) || !(x < 3.0e38f)) return 0;
+    return __builtin_amdgcn_frexp_expf(x);
+}
 
 // ---------------------------------------------------------------- bf16 path
 struct Bf16T {
@@ -218,6 +223,23 @@ struct Bf16T {
             wa[4 + e] = cvt(u1[e] * tof(x[4 + e]));
             wb[e] = (_Float16)((u0[e] * su) * tof(x[e]));
             wb[4 + e] = (_Float16)((u1[e] * su) * tof(x[4 + e]));
+        }
+    }
+    // bf16 ua[t] x[t] and fp16 ub[t] x[t] from one read of the row
+    static __device__ __forceinline__ void row_times_pair(const E* row, const float* ua, const float* ub,
+                                                          int ks, int g, Frag& wa, FragH& wb) {
+        const int t0 = KS * ks + 8 * g;
+        const Frag x = *reinterpret_cast<const Frag*>(row + t0);
+        const floatx4 a0 = *reinterpret_cast<const floatx4*>(ua + t0);
+        const floatx4 a1 = *reinterpret_cast<const floatx4*>(ua + t0 + 4);
+        const floatx4 b0 = *reinterpret_cast<const floatx4*>(ub + t0);
+        const floatx4 b1 = *reinterpret_cast<const floatx4*>(ub + t0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wa[e] = cvt(a0[e] * tof(x[e]));
+            wa[4 + e] = cvt(a1[e] * tof(x[4 + e]));
+            wb[e] = (_Float16)(b0[e] * tof(x[e]));
+            wb[4 + e] = (_Float16)(b1[e] * tof(x[4 + e]));
         }
     }
     // the same for two rows sharing one scaled slice of u

@@ -54,12 +54,14 @@ struct Fwd16Smem {
     alignas(16) __bf16 P[2][CH * f16w::LDP];    // tril_0 of the decayed Q K^T, by chunk parity
     alignas(16) float beta[2][CH];
     alignas(16) float c[2][CH];
-    alignas(16) float u[CH];
+    alignas(16) float u[CH];                   // u * s_prev (readout operand, see below)
+    alignas(16) float us[CH];                  // u * usc (update operand)
+    alignas(16) float gs[f16w::D];             // gamma_C * s / s_prev (state decay and rescale)
     alignas(16) float r0q[CH * f16w::LDR];     // r0 partials: [t][4 * wave + lane group]
     alignas(16) float bprod[f16w::NWP][f16w::D];   // product of f over each 8-row block
     alignas(16) float gam[2][f16w::D];             // gamma_C, by chunk parity
     unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
-    unsigned umax;                          // max |u| of the current chunk (bits)
+    float oinv, sinv;                       // 1 / s_prev and 1 / s of the current chunk
 };
 
 // CKPT: also store, per chunk, the records of FwdCkpt: the entering state
@@ -118,14 +120,23 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
     if (tid == 0) {
         for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; sm.unsafe[s] = 0u; }
-        sm.umax = 0u;
+        sm.oinv = 1.f;
+        sm.sinv = 1.f;
     }
     lds_barrier();
 
     // Both teams run the same sequence of barriers (three per chunk, two more
     // in a stage C whose next chunk takes the exact fallback).
     if (consumer) {
+        // The state is kept multiplied by the exact power of two s = usc * ksc
+        // of the last update (the fp16 operand scales below), so that the
+        // update needs one multiply per element: S <- S diag(gamma_C) s / s_prev
+        // + K~'^T W'.  Reads of the state come out scaled by s_prev and are
+        // rescaled once: r0 on the substitution wave, o at the store, S_T at the
+        // end.  Powers of two commute with rounding, so the results are those
+        // of the unscaled state.
         const int i0 = 16 * w;   // value columns i0 .. i0 + 15
+        int e_prev = 0;          // s_prev = 2^-e_prev (substitution wave)
         const uint32_t o_lane = (uint32_t)cl * rs + hoff + i0 + 4 * g;
         floatx4 S[D / 16];       // S^T[16mj + 4g + r][i0 + cl] in S[mj][r]
 #pragma unroll
@@ -142,9 +153,10 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (n >= 0) {
                 if (CKPT) {
                     E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
+                    const float si = sm.sinv;
 #pragma unroll
                     for (int mj = 0; mj < D / 16; ++mj)
-                        st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj]);
+                        st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj] * si);
                 }
                 // Y^T = S Kbar^T, then O^T = S Qbar^T (M = value index, N = token).
                 // The B fragments of the next K-step are loaded before the MFMAs
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     a += pr[2] + pr[6];
                     b += pr[3] + pr[7];
                     a += b;
-                    r0 = (a[0] + a[1]) + (a[2] + a[3]);
+                    r0 = ((a[0] + a[1]) + (a[2] + a[3])) * ldexpf(1.f, e_prev);
                 }
                 float x = sm.c[n & 1][t_] - sm.beta[n & 1][t_] * r0;
                 // M is strictly lower triangular (zeros elsewhere): lane t only
@@ -219,14 +231,25 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int s = 0; s < 16; ++s)
                         if (16 * sb + s < CH - 1) x = fmaf(-Mrow[s], readlane_f(x, 16 * sb + s), x);
                 }
-                sm.u[t_] = x;
                 if (CKPT) {
                     float* du = ck.U + ((size_t)bh * NC + n) * 2 * CH;
                     du[t_] = x;
                     du[CH + t_] = r0;
                 }
+                // scales of this chunk's update: usc = 2^-eu, ksc = 2^-ek, s = 2^-e
                 const float um = wave_max_nonneg(fabsf(x));
-                if (lane == 0) sm.umax = __float_as_uint(um);
+                const int eu = pow2_exp(um * __uint_as_float(sm.vmax[n % 3]));
+                const int e = eu + pow2_exp(__uint_as_float(sm.kmax[n % 3]));
+                sm.u[t_] = x * ldexpf(1.f, -e_prev);
+                sm.us[t_] = x * ldexpf(1.f, -eu);
+                const float rs_ = ldexpf(1.f, e_prev - e);
+                const float2 gm = *reinterpret_cast<const float2*>(&sm.gam[n & 1][2 * t_]);
+                *reinterpret_cast<float2*>(&sm.gs[2 * t_]) = make_float2(gm.x * rs_, gm.y * rs_);
+                if (lane == 0) {
+                    sm.oinv = ldexpf(1.f, e_prev);
+                    sm.sinv = ldexpf(1.f, e);
+                }
+                e_prev = e;
                 __builtin_amdgcn_s_setprio(0);
             }
             if (CKPT && n >= 0 && w >= 1) {
@@ -260,15 +283,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 lds_barrier();
             }
             if (n >= 0) {
-                const float usc = pow2_scale(__uint_as_float(sm.umax) * __uint_as_float(sm.vmax[n % 3]));
-                const float ksc = pow2_scale(__uint_as_float(sm.kmax[n % 3]));
-                const float inv = 1.f / (usc * ksc);
-                // W = u * V of this wave's value columns: bf16 for the readout,
-                // fp16 scaled by usc for the update
+                // W = u * V of this wave's value columns: bf16 scaled by s_prev for
+                // the readout, fp16 scaled by usc for the update
                 Frag wa[KC_];
                 FragH wb[KC_];
 #pragma unroll
-                for (int ks = 0; ks < KC_; ++ks) TR::row_times_both(&sm.VT[(i0 + cl) * LDT], sm.u, usc, ks, g, wa[ks], wb[ks]);
+                for (int ks = 0; ks < KC_; ++ks) TR::row_times_pair(&sm.VT[(i0 + cl) * LDT], sm.u, sm.us, ks, g, wa[ks], wb[ks]);
                 // O^T += W^T P^T (the P fragments of a K-step loaded together)
 #pragma unroll
                 for (int ks = 0; ks < KC_; ++ks) {
@@ -279,20 +299,20 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int tt = 0; tt < NSB; ++tt) Ot[tt] = TR::mma(wa[ks], pf[tt], Ot[tt]);
                 }
                 if (ob) {
+                    const float oi = sm.oinv;
 #pragma unroll
                     for (int tt = 0; tt < NSB; ++tt) {
                         // row offset = scalar part + this lane's part (one register
                         // across the loop instead of one per tt)
                         const uint32_t srow = __builtin_amdgcn_readfirstlane((uint32_t)(n * CH + SB * tt) * rs);
-                        if (n * CH + SB * tt + cl < T) st4(ob + (srow + o_lane), Ot[tt]);
+                        if (n * CH + SB * tt + cl < T) st4(ob + (srow + o_lane), Ot[tt] * oi);
                     }
                 }
-                // S <- (S diag(gamma_C) s + K~'^T W') / s with s = usc * ksc (exact
-                // powers of 2); K-steps outermost, so consecutive MFMAs go to
-                // different accumulators
+                // S <- S diag(gamma_C) s / s_prev + K~'^T W'; K-steps outermost, so
+                // consecutive MFMAs go to different accumulators
 #pragma unroll
                 for (int mj = 0; mj < D / 16; ++mj)
-                    S[mj] = S[mj] * (*reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]) * (usc * ksc));
+                    S[mj] = S[mj] * *reinterpret_cast<const floatx4*>(&sm.gs[16 * mj + 4 * g]);
 #pragma unroll
                 for (int ks = 0; ks < KC_; ++ks) {
                     FragH ak[D / 16];
@@ -301,18 +321,17 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 #pragma unroll
                     for (int mj = 0; mj < D / 16; ++mj) S[mj] = TR::mma_h(ak[mj], wb[ks], S[mj]);
                 }
-#pragma unroll
-                for (int mj = 0; mj < D / 16; ++mj) S[mj] = S[mj] * inv;
             }
             KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
         if (ST) {
+            const float si = sm.sinv;
 #pragma unroll
             for (int mj = 0; mj < D / 16; ++mj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] = S[mj][r];
+                    ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] = S[mj][r] * si;
         }
     } else {
         const int pw = w - NWC;          // producer wave 0..7 (wave-uniform)
@@ -500,8 +519,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
                 // K-tilde is kept scaled by ksc (a power of 2) for the fp16 update;
                 // Kc = K-tilde / gamma_C takes 1 / ksc back through rgC
-                const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
-                const float iksc = 1.f / ksc;
+                const int ek = pow2_exp(__uint_as_float(sm.kmax[nn % 3]));
+                const float ksc = ldexpf(1.f, -ek), iksc = ldexpf(1.f, ek);
                 // ksc * gamma_C / gamma at each row: suffix products within the block
                 float om[RB][2];
 #pragma unroll
