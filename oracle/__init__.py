@@ -14,6 +14,13 @@ Functions
 ``bwd(q, k, v, f, beta, c, S0, dO, dST) -> dict``
     Hand-derived reverse mode of the same loop (gradients w.r.t. q, k, v, f,
     beta, c, S0).
+``gdn2_fwd(q, k, v, alpha, b, w, S0=None) -> (o, S_T)``
+    The Gated Delta Rule-2 recurrence (decoupled erase gate b on the key axis,
+    write gate w on the value axis, key-channel decay alpha) of the aitrends.kr
+    Gated DeltaNet-2 summary (sections 핵심 기여 and 방법론); state [B,H,dk,dv],
+    o_t = S_t^T q_t.  Pinned in tests/test_oracle_gdn2.py (the page's product
+    form, decay-only closed form, exact recall, erase-only annihilation,
+    split/resume, hand-worked fixture).
 
 All arrays are numpy fp64 in the layouts q,k,f:[B,T,H,dk], v:[B,T,H,dv],
 beta,c:[B,T,H], S:[B,H,dv,dk].  Parity status: pinned (see tests/test_oracle.py
@@ -58,6 +65,8 @@ def _load():
         lib.kdo_fwd.restype = i
         lib.kdo_bwd.argtypes = [i, i, i, i, i] + [dp] * 16
         lib.kdo_bwd.restype = i
+        lib.gdo_fwd.argtypes = [i, i, i, i, i] + [dp] * 9
+        lib.gdo_fwd.restype = i
         lib.kdo_num_threads.restype = i
         lib.kdo_set_num_threads.argtypes = [i]
         _lib = lib
@@ -121,3 +130,19 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None):
     if rc != 0:
         raise RuntimeError("oracle kdo_bwd failed: %d" % rc)
     return out
+
+
+def gdn2_fwd(q, k, v, alpha, b, w, S0=None):
+    q, k, v, alpha, b, w, S0 = map(_f64, (q, k, v, alpha, b, w, S0))
+    B, T, H, dk, dv = _dims(q, v)
+    assert k.shape == q.shape and alpha.shape == q.shape and b.shape == q.shape
+    assert v.shape == (B, T, H, dv) and w.shape == (B, T, H, dv)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    rc = _load().gdo_fwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(alpha), _p(b), _p(w),
+                         _p(S0), _p(o), _p(ST))
+    if rc != 0:
+        raise RuntimeError("oracle gdo_fwd failed: %d" % rc)
+    return o, ST

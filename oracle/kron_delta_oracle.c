@@ -281,3 +281,85 @@ int kdo_bwd(int B, int T, int H, int dk, int dv,
     }
     return fail ? KDO_ERR_MEM : KDO_OK;
 }
+
+/* ======================================================================
+ * Gated Delta Rule-2 (decoupled erase and write), forward only.
+ *
+ * Source: aitrends.kr summary of Gated DeltaNet-2 -- sections 핵심 기여
+ * (decoupled erase and write; the update S_t = (I - k_t e_t^T) D_t S_{t-1}
+ * + k_t z_t^T with e_t = b_t * k_t, z_t = w_t * v_t) and 방법론 steps 1, 2
+ * and 4 (channel decay absorbed first, Sbar_t = D_t S_{t-1}, then
+ * S_t = Sbar_t + k_t (z_t - Sbar_t^T e_t)^T; readout o_t = S_t^T q_t).
+ *
+ * State S in R^{dk x dv} (row j over keys, column i over values), per
+ * (b, h), for t = 1..T:
+ *   (G1) Sbar = diag(alpha_t) S_{t-1}       key-channel decay D_t
+ *   (G2) u_t  = w_t * v_t - Sbar^T (b_t * k_t)
+ *                                            what the erase leaves to write
+ *   (G3) S_t  = Sbar + k_t u_t^T
+ *   (G4) o_t  = S_t^T q_t
+ * Layouts: q, k, alpha, b : [B, T, H, dk];  v, w, o : [B, T, H, dv];
+ *          S0, ST : [B, H, dk, dv]  (S[j][i] at j*dv + i).
+ * ====================================================================== */
+static void gdo_step(double *S, int dk, int dv, const double *qt, const double *kt,
+                     const double *vt, const double *at, const double *bt,
+                     const double *wt, double *u, double *ot)
+{
+    int i, j;
+    /* G1 */
+    for (j = 0; j < dk; ++j)
+        for (i = 0; i < dv; ++i)
+            S[(size_t)j * dv + i] *= at[j];
+    /* G2: u = z - Sbar^T e, e = b * k, z = w * v */
+    for (i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < dk; ++j)
+            acc += S[(size_t)j * dv + i] * (bt[j] * kt[j]);
+        u[i] = wt[i] * vt[i] - acc;
+    }
+    /* G3 */
+    for (j = 0; j < dk; ++j)
+        for (i = 0; i < dv; ++i)
+            S[(size_t)j * dv + i] += kt[j] * u[i];
+    /* G4 */
+    for (i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < dk; ++j)
+            acc += S[(size_t)j * dv + i] * qt[j];
+        ot[i] = acc;
+    }
+}
+
+int gdo_fwd(int B, int T, int H, int dk, int dv,
+            const double *q, const double *k, const double *v,
+            const double *alpha, const double *b, const double *w,
+            const double *S0, double *o, double *ST)
+{
+    int bh, fail = 0;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDO_ERR_ARG;
+    if (B * H == 0) return KDO_OK;
+    if (T > 0 && (!q || !k || !v || !alpha || !b || !w || !o)) return KDO_ERR_ARG;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (bh = 0; bh < B * H; ++bh) {
+        int bb = bh / H, h = bh % H, t;
+        size_t sz = (size_t)dk * dv;
+        double *S = (double *)malloc((sz + (size_t)dv) * sizeof(double));
+        if (!S) {
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        double *u = S + sz;
+        if (S0) memcpy(S, S0 + (size_t)bh * sz, sz * sizeof(double));
+        else memset(S, 0, sz * sizeof(double));
+        for (t = 0; t < T; ++t) {
+            size_t n = tok_index(bb, t, h, T, H);
+            gdo_step(S, dk, dv, q + n * dk, k + n * dk, v + n * dv, alpha + n * dk,
+                     b + n * dk, w + n * dv, u, o + n * dv);
+        }
+        if (ST) memcpy(ST + (size_t)bh * sz, S, sz * sizeof(double));
+        free(S);
+    }
+    return fail ? KDO_ERR_MEM : KDO_OK;
+}
