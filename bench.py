@@ -95,6 +95,26 @@ def algorithmic_bytes_decode(w, esize):
     return 2 * w.B * w.H * w.dv * w.dk * 4 + 4 * ntok * w.dk * esize + 2 * ntok * 4 + ntok * w.dv * esize
 
 
+def algorithmic_bytes_gdn2(w, esize):
+    """HBM bytes of one Gated Delta Rule-2 forward launch: q, k, alpha, b (dk)
+    and v, w (dv) once, o once, S_T (fp32) once."""
+    ntok = w.B * w.T * w.H
+    return ntok * (4 * w.dk + 2 * w.dv) * esize + ntok * w.dv * esize + w.B * w.H * w.dk * w.dv * 4
+
+
+def mfma_flops_gdn2(w):
+    """MFMA flops of one Gated Delta Rule-2 launch as issued, per (b, h, chunk)
+    of C = 64 at d = 128: Grams 2 x 10 tiles x 2*16*16*d; Ebar S0 and Qbar S0
+    2 x 2*C*d*d; the blocked solve 10 block products x 3 (hi/lo) x 2*16*16*d;
+    readout 2*C*C*d; update 3 (hi/lo) x 2*C*d*d."""
+    C = 64
+    d = w.dk
+    nch = (w.T + C - 1) // C
+    per = (2 * 10 * 2 * 16 * 16 * d + 2 * 2 * C * d * d + 10 * 3 * 2 * 16 * 16 * d
+           + 2 * C * C * d + 3 * 2 * C * d * d)
+    return w.B * w.H * nch * per
+
+
 def mfma_flops(w):
     """MFMA flops of one launch as issued (full 16x16 tiles, including the
     masked-out upper Gram tiles' partners): per (b, h, chunk) of C = 64 with
@@ -120,6 +140,14 @@ def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
     for _ in range(max_passes):
         for b in range(w.B):
             sl = slice(b, b + 1)
+            if w.gdn2:
+                oracle.gdn2_fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["alpha"][sl],
+                                x_np["b"][sl], x_np["w"][sl], None)
+                nseq += 1
+                done_tok += w.T
+                if time.perf_counter() - t0 > budget_s:
+                    break
+                continue
             oracle.fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["f"][sl],
                        x_np["beta"][sl], x_np["c"][sl],
                        x_np["S0"][sl] if x_np.get("S0") is not None else None)
@@ -136,7 +164,8 @@ def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
     return {"value": done_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "fp64 oracle %s on %d sequences (passes over the %d sequences of the "
                       "workload; T=%d, H=%d, d=%d), same seeded inputs, %.1f s wall"
-                      % ("forward + backward" if w.backward else "forward", nseq, w.B, w.T, w.H,
+                      % ("Gated Delta Rule-2 forward" if w.gdn2 else
+                         "forward + backward" if w.backward else "forward", nseq, w.B, w.T, w.H,
                          w.dk, dt)}
 
 
@@ -181,11 +210,15 @@ def main():
     dev = torch.device("cuda:0")
     x = sy.rounded(sy.draw_workload(w), w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    t = {n: torch.tensor(x[n], dtype=tdt if n in ("q", "k", "v", "f") else torch.float32,
-                         device=dev) for n in ("q", "k", "v", "f", "beta", "c")}
+    per_token = ("q", "k", "v", "f", "alpha", "b", "w")
+    t = {n: torch.tensor(x[n], dtype=tdt if n in per_token else torch.float32, device=dev)
+         for n in (("q", "k", "v", "alpha", "b", "w") if w.gdn2 else ("q", "k", "v", "f", "beta", "c"))}
     esize = 2 if w.dtype == "bf16" else 4
 
-    if w.decode:     # a step is one decode call, the state updated in place
+    if w.gdn2:       # a step is one Gated Delta Rule-2 forward
+        def step():
+            return kd.gdn2_fwd(t["q"], t["k"], t["v"], t["alpha"], t["b"], t["w"], None)
+    elif w.decode:   # a step is one decode call, the state updated in place
         t["S"] = torch.tensor(x["S0"], dtype=torch.float32, device=dev)
 
         def step():
@@ -224,15 +257,18 @@ def main():
 
     tokens = w.B * w.T
     value = tokens / (ms_per_step * 1e-3)
-    abytes = (algorithmic_bytes_decode(w, esize) if w.decode else
+    abytes = (algorithmic_bytes_gdn2(w, esize) if w.gdn2 else
+              algorithmic_bytes_decode(w, esize) if w.decode else
               algorithmic_bytes_fwd_bwd(w, esize) if w.backward else algorithmic_bytes(w, esize))
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
-    flops = mfma_flops(w)
+    flops = mfma_flops_gdn2(w) if w.gdn2 else mfma_flops(w)
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
     traffic = stored_traffic() if args.workload == "train_step" else None
 
     out = {
-        "metric": ("Kron-delta decode tokens/s (H=16,d=128) and % HBM roofline" if w.decode else
+        "metric": ("Gated Delta Rule-2 chunked fwd tokens/s (H=16,d=128) and % HBM roofline"
+                   if w.gdn2 else
+                   "Kron-delta decode tokens/s (H=16,d=128) and % HBM roofline" if w.decode else
                    "Kron-delta chunked fwd+bwd tokens/s (H=16,d=128) and % HBM roofline"
                    if w.backward else METRIC),
         "value": value,
@@ -245,9 +281,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
+        "data": ("synthetic (seeded: L2-normalised N(0,1) q,k,v; alpha=exp(-exp(U(-1,1)) "
+                 "softplus(-N(%g,1))); b,w=sigmoid(N(0,1)) per channel)" % w.mu) if w.gdn2 else
+                "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
                 "beta,c=sigmoid(N(0,1)))" % w.mu,
-        "config": {"workload": ("%s: Kronecker delta rule decode (token by token on the carried "
+        "config": {"workload": ("%s: Gated Delta Rule-2 (decoupled erase and write) chunked "
+                                "forward, B=%d T=%d H=%d dk=dv=%d, chunk 64, %s q/k/v/alpha/b/w, "
+                                "fp32 state, S0=0" % (w.name, w.B, w.T, w.H, w.dk, w.dtype))
+                               if w.gdn2 else
+                               ("%s: Kronecker delta rule decode (token by token on the carried "
                                 "state, updated in place), B=%d T=%d H=%d dk=dv=%d, %s q/k/v/f, "
                                 "fp32 beta/c/state, S ~ N(0, 0.1^2)"
                                 % (w.name, w.B, w.T, w.H, w.dk, w.dtype)) if w.decode else
@@ -258,7 +300,8 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_decode_kernel<bf16,128>" if w.decode else
+                     "kernel": "kd_gdn2_kernel" if w.gdn2 else
+                     "kd_decode_kernel<bf16,128>" if w.decode else
                      "kd_fwd16_kernel<false>" if not w.backward else
                      "kd_fwd16_kernel + kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
                      "kernel_ms": kernel_ms,

@@ -26,7 +26,7 @@ KD_F32, KD_BF16 = 0, 1
 ABI_VERSION = 1
 EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
-            "kron_delta_decode", "kron_delta_fwd_varlen")
+            "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd")
 
 
 class KronDeltaError(RuntimeError):
@@ -66,6 +66,8 @@ def lib():
         L.kron_delta_fwd_varlen.restype = i32
         L.kron_delta_fwd_varlen.argtypes = [dp, vp] + [vp] * 9 + [vp]
         L.kron_delta_decode.argtypes = [dp] + [vp] * 9 + [vp]
+        L.kron_delta_gdn2_fwd.restype = i32
+        L.kron_delta_gdn2_fwd.argtypes = [dp] + [vp] * 9 + [vp]
         if L.kron_delta_abi_version() != ABI_VERSION:
             raise ImportError("libkrondelta.so ABI version mismatch")
         _lib = L
@@ -220,3 +222,37 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None)
     if st != 0:
         raise KronDeltaError(st, "kron_delta_bwd")
     return out
+
+
+def gdn2_fwd(q, k, v, alpha, b, w, S0=None, *, return_state=True):
+    """Gated Delta Rule-2 forward (bf16, d = 128): q, k, alpha, b [B, T, H, dk],
+    v, w [B, T, H, dv]; S0 fp32 [B, H, dk, dv] or None.  Returns (o, S_T)."""
+    import torch
+    L = lib()
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("b", b), ("w", w)):
+        if t.dtype != dt:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, dt))
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("k", k), ("alpha", alpha), ("b", b)):
+        if tuple(t.shape) != (B, T, H, dk):
+            raise ValueError("%s must be [B, T, H, dk]" % name)
+    if tuple(w.shape) != (B, T, H, dv) or tuple(v.shape) != (B, T, H, dv):
+        raise ValueError("v and w must be [B, T, H, dv]")
+    if S0 is not None:
+        if tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be float32 [B, H, dk, dv]")
+        S0 = S0.contiguous()
+    desc = KdDesc(B, T, H, dk, dv, _dtype_code(torch, dt))
+    q, k, v, alpha, b, w = (t.contiguous() for t in (q, k, v, alpha, b, w))
+    o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.kron_delta_gdn2_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                               _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_gdn2_fwd")
+    return o, ST

@@ -17,6 +17,9 @@ hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void*
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
                       float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st);
 size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H);
+hipError_t launch_gdn2(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                       const void* w, const float* S0, void* o, float* ST, int B, int T, int H,
+                       hipStream_t st);
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
                          int B, int T, int H, hipStream_t st);
@@ -212,3 +215,29 @@ kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const v
 }
 
 }  // extern "C"
+
+kd_status kron_delta_gdn2_fwd(const kd_desc* d, const void* q, const void* k, const void* v,
+                              const void* alpha, const void* b, const void* w, const float* S0,
+                              void* o, float* ST, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    if (d->dtype != KD_BF16) return KD_ERR_DTYPE;
+    if (d->dk != 128) return KD_ERR_SHAPE;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !alpha || !b || !w || !o)) return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, b, w, S0, o, ST};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(alpha, xb),
+                         range_of(b, xb), range_of(w, xb), range_of(S0, S0 ? sb : 0)};
+    const Range outs[] = {range_of(o, ntok ? xb : 0), range_of(ST, ST ? sb : 0)};
+    for (const Range& a : outs)
+        for (const Range& c : ins)
+            if (overlap(a, c)) return KD_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
+    if (ntok == 0 && !ST) return KD_OK;
+    hipError_t e = kd::launch_gdn2(q, k, v, alpha, b, w, S0, o, ST, d->B, d->T, d->H, (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}

@@ -21,6 +21,17 @@ q, k, v, f (and dO) are then rounded to the workload's dtype with
 round-to-nearest-even; beta, c and S0 stay fp32.  Both the GPU library and
 the oracle consume the rounded values (the oracle upcasts them exactly).
 
+Gated Delta Rule-2 inputs (``draw_gdn2``; aitrends.kr Gated DeltaNet-2
+summary, sections 방법론 and 기술 상세), same generator and order:
+  1. q, k, v as above.
+  2. x ~ N(mu, 1) of shape [B, T, H, dk] and a_log ~ U(-1, 1) of shape [H];
+     alpha = exp(-exp(a_log[h]) * softplus(-x)), the page's log-decay form
+     (numerically the forget gate of the recipe above).
+  3. b = sigmoid(N(0, 1)) of shape [B, T, H, dk] (erase gate, key axis).
+  4. w = sigmoid(N(0, 1)) of shape [B, T, H, dv] (write gate, value axis).
+  5. S0 ~ N(0, s0_std^2) of shape [B, H, dk, dv] (only when s0_std is given).
+q, k, v, alpha, b, w are rounded to the workload's dtype.
+
 These seeded draws stand in for real activations: the pages measure on
 FineWeb-Edu language-model training, for which no data or weights exist here.
 """
@@ -45,6 +56,7 @@ class Workload:
     seed: int = 1000
     backward: bool = False
     decode: bool = False   # token-by-token on a carried state (S0 drawn, N(0, 0.1^2))
+    gdn2: bool = False     # the Gated Delta Rule-2 variant (decoupled erase and write)
 
     @property
     def tokens(self) -> int:
@@ -65,6 +77,8 @@ WORKLOADS = {
                          beta_scale=2.0, seed=1004),
     # Serving: one new token for each of 32 sequences on their carried states.
     "decode_step": Workload("decode_step", 32, 1, 16, 128, 128, "bf16", seed=1005, decode=True),
+    # Gated Delta Rule-2 at the training-step shape (decoupled erase and write).
+    "gdn2_step": Workload("gdn2_step", 8, 2048, 16, 128, 128, "bf16", seed=1006, gdn2=True),
 }
 
 
@@ -98,7 +112,27 @@ def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
     return out
 
 
+def draw_gdn2(B, T, H, dk, dv, seed, mu=3.0, s0_std=None):
+    """Gated Delta Rule-2 inputs (fp64, before dtype rounding): q, k, v,
+    alpha, b, w and, when s0_std is given, S0 [B, H, dk, dv]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _l2n(rng.standard_normal((B, T, H, dk)))
+    k = _l2n(rng.standard_normal((B, T, H, dk)))
+    v = _l2n(rng.standard_normal((B, T, H, dv)))
+    x = rng.normal(mu, 1.0, (B, T, H, dk))
+    a_log = rng.uniform(-1.0, 1.0, (H,))
+    alpha = np.exp(-np.exp(a_log)[None, None, :, None] * np.logaddexp(0.0, -x))
+    b = _sigmoid(rng.standard_normal((B, T, H, dk)))
+    w = _sigmoid(rng.standard_normal((B, T, H, dv)))
+    out = dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=None)
+    if s0_std is not None:
+        out["S0"] = rng.normal(0.0, s0_std, (B, H, dk, dv))
+    return out
+
+
 def draw_workload(w: Workload, with_dO=None, s0_std=None):
+    if w.gdn2:
+        return draw_gdn2(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, s0_std=s0_std)
     if s0_std is None and w.decode:
         s0_std = 0.1
     return draw(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, beta_scale=w.beta_scale,
@@ -125,7 +159,7 @@ def rounded(inputs: dict, dtype: str) -> dict:
     for key, val in inputs.items():
         if val is None:
             out[key] = None
-        elif key in ("q", "k", "v", "f", "dO"):
+        elif key in ("q", "k", "v", "f", "dO", "alpha", "b", "w"):
             out[key] = round_to(val, dtype)
         else:
             out[key] = round_to(val, "fp32")

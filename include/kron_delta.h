@@ -175,6 +175,30 @@ KD_API kd_status kron_delta_bwd(const kd_desc *desc,
                          float *dbeta, float *dc, float *dS0,
                          void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Forward pass of the Gated Delta Rule-2 (decoupled erase and write), the
+ * variant of the aitrends.kr Gated DeltaNet-2 summary (sections 핵심 기여 and
+ * 방법론 steps 1-4).  Per (b, h) the state S is dk x dv (keys as rows) and,
+ * for every token t,
+ *     Sbar = diag(alpha_t) S;  u_t = w_t * v_t - Sbar^T (b_t * k_t);
+ *     S = Sbar + k_t u_t^T;    o_t = S^T q_t.
+ * Chunked (C = 64) with the WY step U = (I + T)^{-1} (Z - Ebar S0) of that
+ * page's step 3; a key channel whose decay over a chunk drops below 2^-100 is
+ * handled exactly.
+ *  * Supported: desc->dtype == KD_BF16 and dk == dv == 128 (KD_ERR_DTYPE /
+ *    KD_ERR_SHAPE otherwise).
+ *  * q, k, alpha (decay, in [0, 1]), b (erase gate): [B, T, H, dk] bf16;
+ *    v, w (write gate): [B, T, H, dv] bf16; o: [B, T, H, dv] bf16;
+ *    S0 (NULL = zero), ST (NULL = not returned): [B, H, dk, dv] fp32,
+ *    S[j][i] at j*dv + i (note: keys as rows, unlike kron_delta_fwd).
+ *  * Same checks, ownership and stream behaviour as kron_delta_fwd; no
+ *    workspace.
+ */
+KD_API kd_status kron_delta_gdn2_fwd(const kd_desc *desc,
+                         const void *q, const void *k, const void *v,
+                         const void *alpha, const void *b, const void *w,
+                         const float *S0, void *o, float *ST, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,3 +168,23 @@ def test_fwd_varlen_argument_checks(L):
     assert fwd_varlen(L, d, ST=P(7)) == ALIAS         # ST == S0
     assert fwd_varlen(L, d, o=P(0)) == ALIAS          # o == cu_seqlens
     assert fwd_varlen(L, _desc(B=3, T=0), ST=None) == OK
+
+
+def test_gdn2_argument_checks(L):
+    names = ["q", "k", "v", "alpha", "b", "w", "S0", "o", "ST"]
+
+    def call(desc, **over):
+        p = {n: P(i) for i, n in enumerate(names)}
+        p.update(over)
+        d = ctypes.byref(desc) if desc is not None else None
+        return L.kron_delta_gdn2_fwd(d, *[p[n] for n in names], None)
+
+    d = _desc(B=2, T=100, H=3, dk=128, dv=128)
+    assert call(None) == NULL
+    assert call(_desc(dk=64, dv=64)) == SHAPE                  # d = 128 only
+    assert call(_desc(dk=32, dv=32, dtype=kd.KD_F32)) == DTYPE  # bf16 only
+    assert call(d, alpha=None) == NULL
+    assert call(d, w=P(5, misalign=4)) == ALIGN
+    assert call(d, o=P(3)) == ALIAS                            # o == alpha
+    assert call(d, ST=P(6)) == ALIAS                           # ST == S0
+    assert call(_desc(B=2, T=0, H=3, dk=128, dv=128), ST=None) == OK
