@@ -19,16 +19,22 @@
 //
 // One workgroup of eight waves per (b, h); phases separated by barriers:
 //   1. every wave prepares 8 rows of the chunk (two key channels per lane):
-//      decay products, the operands above into LDS; then it issues the loads
-//      of the next chunk's rows;
+//      decay products, the operands above into LDS (the next chunk's rows are
+//      loaded during phases 2 and 3);
 //   2. Gram tiles of T and P; each wave forms Ebar S0 and Qbar S0 for its 16
 //      value columns (the state lives in its MFMA accumulators, keys as rows);
-//   3. the 16 x 16 diagonal blocks of I + T are inverted (wave 0);
-//   4. each wave solves (I + T) U = Z - Ebar S0 for its value columns block by
+//      the wave of each diagonal Gram tile inverts that 16 x 16 block of I + T;
+//   3. each wave solves (I + T) U = Z - Ebar S0 for its value columns block by
 //      block with 16 x 16 x 16 MFMAs on bf16 hi + lo splits (fp32-like
 //      products), then the readout O = Qbar S0 + P U and the update
 //      S <- diag(gamma_C) S + Ktil^T U (Ktil and U also split hi + lo).
 #include "kd_device.h"
+
+// Phase markers: no-ops here; a profiling build may define them to record
+// timestamps at the phase boundaries of the chunk loop.
+#ifndef KD_PHASE_MARK
+#define KD_PHASE_MARK(chunk, id) ((void)0)
+#endif
 
 namespace kd {
 
@@ -144,21 +150,31 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
     Raw8x2 rq, rk, rv, ra, rbb, rw;
     // Rows past the end re-read the last row (in bounds) and are cleared
     // before use; loads are clamped to the last chunk.
-    auto load_rows = [&](int n) {
+    auto row_off = [&](int n, int& last) {
         const int t0 = min(n * CH + rb, T - 1);
-        const int last = min(RB - 1, T - 1 - t0);
-        const uint32_t off = (uint32_t)t0 * rs + hoff + ch0;
+        last = min(RB - 1, T - 1 - t0);
+        return (uint32_t)t0 * rs + hoff + ch0;
+    };
+    auto load_rows_a = [&](int n) {   // q, k, alpha
+        int last;
+        const uint32_t off = row_off(n, last);
         rq.load(qb, off, rs, last);
         rk.load(kb, off, rs, last);
-        rv.load(vb, off, rs, last);
         ra.load(ab, off, rs, last);
+    };
+    auto load_rows_b = [&](int n) {   // v, b, w
+        int last;
+        const uint32_t off = row_off(n, last);
+        rv.load(vb, off, rs, last);
         rbb.load(bgb, off, rs, last);
         rw.load(wgb, off, rs, last);
     };
-    load_rows(0);
+    load_rows_a(0);
+    load_rows_b(0);
     lds_barrier();
 
     for (int n = 0; n < NC; ++n) {
+        KD_PHASE_MARK(n, 0);
         // =========================================== phase 1: operands of chunk n
         if (n * CH + CH > T) {   // ragged last chunk: rows past the end contribute nothing
 #pragma unroll
@@ -256,7 +272,6 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 *reinterpret_cast<uint4*>(&sm.ZT[row + rb]) = make_uint4(zt[c2][0], zt[c2][1], zt[c2][2], zt[c2][3]);
             }
         }
-        if (n + 1 < NC) load_rows(n + 1);   // next chunk's rows, in flight through phases 2-4
         lds_barrier();
 
         // =========================================== exact fallback terms (rare)
@@ -292,9 +307,15 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
             lds_barrier();
         }
 
+        KD_PHASE_MARK(n, 1);
         // =========================================== phase 2: Grams, state products
+        // next chunk's rows, in flight through the rest of this chunk (the raw
+        // rows of this chunk were last read in phase 1)
+        if (n + 1 < NC) load_rows_a(n + 1);
         // Gram tile (I_ >= J_) of T and P: waves 0..7 take tiles 0..7, waves 0, 1
-        // also tiles 8, 9.
+        // also tiles 8, 9.  The wave of a diagonal tile (I_ == J_) then inverts
+        // that 16 x 16 block of I + T: it alone wrote the block, and a wave's LDS
+        // accesses complete in order.
         auto gram_tile = [&](int tile) {
             const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J_ = tile - (I_ * (I_ + 1)) / 2;
@@ -327,6 +348,31 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 else if (s_ == t_) sm.Tm[t_ * LDM + s_] = 0.f;   // clears the P diagonal scratch
                 sm.P[t_ * LDP + TR::pcol(s_)] = (E)((s_ <= t_) ? pp[r] : 0.f);
             }
+            if (I_ == J_) {
+                // (I + T_II)^{-1}: lane c < 16 runs forward substitution down column c
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane < 16) {
+                    const int c = lane;
+                    const float* Tb = &sm.Tm[(16 * I_) * LDM + 16 * I_];
+                    float x[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        // the row of T as four 16-byte reads, the sum over s < r in
+                        // four independent chains
+                        floatx4 tr[4];
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            if (4 * q4 < r) tr[q4] = *reinterpret_cast<const floatx4*>(&Tb[r * LDM + 4 * q4]);
+                        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < r; ++s) a4[s & 3] = fmaf(tr[s >> 2][s & 3], x[s], a4[s & 3]);
+                        const float acc = ((r == c) ? 1.f : 0.f) - ((a4[0] + a4[1]) + (a4[2] + a4[3]));
+                        x[r] = (r < c) ? 0.f : acc;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sm.X[I_][r * LDX + c] = x[r];
+                }
+            }
         };
         gram_tile(w);
         if (w < 2) gram_tile(8 + w);
@@ -357,26 +403,9 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
         }
         lds_barrier();
 
-        // =========================================== phase 3: (I + T_II)^{-1}
-        if (w == 0) {
-            // lane: block I_ = lane / 16, column c = lane % 16; forward
-            // substitution down the column
-            const int I_ = lane >> 4, c = lane & 15;
-            const float* Tb = &sm.Tm[(16 * I_) * LDM + 16 * I_];
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc = fmaf(-Tb[r * LDM + s], x[s], acc);
-                x[r] = (r < c) ? 0.f : acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.X[I_][r * LDX + c] = x[r];
-        }
-        lds_barrier();
-
-        // =========================================== phase 4: solve, readout, update
+        KD_PHASE_MARK(n, 2);
+        // =========================================== phase 3: solve, readout, update
+        if (n + 1 < NC) load_rows_b(n + 1);
         floatx4 U[NSB];
 #pragma unroll
         for (int I_ = 0; I_ < NSB; ++I_) {
@@ -430,6 +459,7 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
             }
         }
         if (tid == 0) sm.unsafe = 0u;
+        KD_PHASE_MARK(n, 3);
         lds_barrier();
     }
     if (ST) {
