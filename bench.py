@@ -229,10 +229,10 @@ def main():
                                                  with_backward=True), 16),
                          dtype=torch.uint8, device=dev)
 
-        def step():
-            kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
+        def step():   # training forward (o plus the backward's records), then the backward
+            kd.fwd_train(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None, workspace=ws)
             return kd.bwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None, t["dO"],
-                          workspace=ws)
+                          workspace=ws, saved=True)
     else:
         def step():
             return kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None)
@@ -303,7 +303,7 @@ def main():
                      "kernel": "kd_gdn2_kernel" if w.gdn2 else
                      "kd_decode_kernel<bf16,128>" if w.decode else
                      "kd_fwd16_kernel<false>" if not w.backward else
-                     "kd_fwd16_kernel + kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
+                     "kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,
                      },

@@ -26,7 +26,8 @@ KD_F32, KD_BF16 = 0, 1
 ABI_VERSION = 1
 EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
-            "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd")
+            "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd",
+            "kron_delta_fwd_train", "kron_delta_bwd_saved")
 
 
 class KronDeltaError(RuntimeError):
@@ -62,6 +63,10 @@ def lib():
         L.kron_delta_fwd.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
         L.kron_delta_bwd.restype = i32
         L.kron_delta_bwd.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+        L.kron_delta_bwd_saved.restype = i32
+        L.kron_delta_bwd_saved.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+        L.kron_delta_fwd_train.restype = i32
+        L.kron_delta_fwd_train.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
         L.kron_delta_decode.restype = i32
         L.kron_delta_fwd_varlen.restype = i32
         L.kron_delta_fwd_varlen.argtypes = [dp, vp] + [vp] * 9 + [vp]
@@ -194,8 +199,33 @@ def workspace_bytes(B, T, H, d, dtype_code, with_backward=True) -> int:
     return int(lib().kron_delta_workspace_bytes(ctypes.byref(desc), 1 if with_backward else 0))
 
 
-def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None):
-    """Gate-aware backward.  Returns a dict with dq, dk, dv, df, dbeta, dc, dS0."""
+def fwd_train(q, k, v, f, beta, c, S0=None, *, return_state=True, workspace=None):
+    """Forward for training: returns (o, S_T, workspace), the workspace holding
+    the per-chunk records that bwd(..., workspace=workspace, saved=True) reads
+    instead of recomputing the forward."""
+    import torch
+    L = lib()
+    desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
+    o = torch.empty((desc.B, desc.T, desc.H, desc.dv), dtype=q.dtype, device=q.device)
+    ST = torch.empty((desc.B, desc.H, desc.dv, desc.dk), dtype=torch.float32,
+                     device=q.device) if return_state else None
+    need = int(L.kron_delta_workspace_bytes(ctypes.byref(desc), 1))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.kron_delta_fwd_train(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+                                _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_fwd_train")
+    return o, ST, workspace
+
+
+def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None, saved=False):
+    """Gate-aware backward.  Returns a dict with dq, dk, dv, df, dbeta, dc, dS0.
+
+    saved=True starts from the records that fwd_train left in `workspace`
+    (same inputs, same workspace) instead of recomputing the forward."""
     import torch
     L = lib()
     desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
@@ -213,14 +243,17 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None)
                if want_dS0 else None)
     need = int(L.kron_delta_workspace_bytes(ctypes.byref(desc), 1))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
+        if saved:
+            raise ValueError("saved=True needs the workspace filled by fwd_train")
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = L.kron_delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
-                          _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
-                          _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
-                          _ptr(out["dS0"]), _ptr(workspace), need, ctypes.c_void_p(stream))
+    fn = L.kron_delta_bwd_saved if saved else L.kron_delta_bwd
+    st = fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+            _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+            _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
+            _ptr(out["dS0"]), _ptr(workspace), need, ctypes.c_void_p(stream))
     if st != 0:
-        raise KronDeltaError(st, "kron_delta_bwd")
+        raise KronDeltaError(st, "kron_delta_bwd_saved" if saved else "kron_delta_bwd")
     return out
 
 

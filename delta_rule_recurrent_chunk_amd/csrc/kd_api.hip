@@ -15,7 +15,11 @@ hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void*
 hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, const void* dO,
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
-                      float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st);
+                      float* dc, float* dS0, void* ws, int B, int T, int H, int recompute,
+                      hipStream_t st);
+hipError_t launch_fwd_train(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                            const float* beta, const float* c, const float* S0, void* o, float* ST,
+                            void* ws, int B, int T, int H, hipStream_t st);
 size_t bwd_workspace_bytes(int bf16, int d, int B, int T, int H);
 hipError_t launch_gdn2(const void* q, const void* k, const void* v, const void* alpha, const void* b,
                        const void* w, const float* S0, void* o, float* ST, int B, int T, int H,
@@ -174,11 +178,12 @@ kd_status kron_delta_decode(const kd_desc* d, const void* q, const void* k, cons
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 
-kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const void* v,
-                         const void* f, const float* beta, const float* c, const float* S0,
-                         const void* dO, const float* dST, void* dq, void* dk, void* dv,
-                         void* df, float* dbeta, float* dc, float* dS0, void* ws,
-                         size_t ws_bytes, void* stream) {
+namespace {
+kd_status bwd_impl(const kd_desc* d, const void* q, const void* k, const void* v,
+                   const void* f, const float* beta, const float* c, const float* S0,
+                   const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                   void* df, float* dbeta, float* dc, float* dS0, void* ws,
+                   size_t ws_bytes, void* stream, int recompute) {
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
     // the chunk-local backward kernel holds its fp32 operands in LDS only up to d = 32
@@ -209,8 +214,58 @@ kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const v
             if (overlap(outs[a], outs[b])) return KD_ERR_ALIAS;
     if (ntok == 0 && !dS0) return KD_OK;
     hipError_t e = kd::launch_bwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, dO, dST,
-                                  dq, dk, dv, df, dbeta, dc, dS0, ws, d->B, d->T, d->H,
+                                  dq, dk, dv, df, dbeta, dc, dS0, ws, d->B, d->T, d->H, recompute,
                                   (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+}  // namespace
+
+kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const void* v,
+                         const void* f, const float* beta, const float* c, const float* S0,
+                         const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                         void* df, float* dbeta, float* dc, float* dS0, void* ws,
+                         size_t ws_bytes, void* stream) {
+    return bwd_impl(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, ws_bytes,
+                    stream, 1);
+}
+
+kd_status kron_delta_bwd_saved(const kd_desc* d, const void* q, const void* k, const void* v,
+                               const void* f, const float* beta, const float* c, const float* S0,
+                               const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                               void* df, float* dbeta, float* dc, float* dS0, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return bwd_impl(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, ws_bytes,
+                    stream, 0);
+}
+
+kd_status kron_delta_fwd_train(const kd_desc* d, const void* q, const void* k, const void* v,
+                               const void* f, const float* beta, const float* c, const float* S0,
+                               void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;   // as kron_delta_bwd
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d);
+    const size_t gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    if (ntok > 0 && (!q || !k || !v || !f || !beta || !c || !o)) return KD_ERR_NULL;
+    const void* ptrs[] = {q, k, v, f, beta, c, S0, o, ST, ws};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return KD_ERR_ALIGN;
+    const size_t need = kron_delta_workspace_bytes(d, 1);
+    if (need > 0 && (!ws || ws_bytes < need)) return KD_ERR_WORKSPACE;
+    const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
+                         range_of(beta, gb), range_of(c, gb), range_of(S0, S0 ? sb : 0)};
+    const Range outs[] = {range_of(o, ntok ? xb : 0), range_of(ST, ST ? sb : 0), range_of(ws, need)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    for (size_t a = 0; a < 3; ++a)
+        for (size_t b = a + 1; b < 3; ++b)
+            if (overlap(outs[a], outs[b])) return KD_ERR_ALIAS;
+    if (ntok == 0 && !ST) return KD_OK;
+    hipError_t e = kd::launch_fwd_train(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST, ws,
+                                        d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

@@ -849,25 +849,44 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
 }
 
 // --------------------------------------------------------------- launchers
-template <class TR, int D>
-static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* f,
-                               const float* beta, const float* c, const float* S0, const void* dO,
-                               const float* dST, void* dq, void* dk, void* dv, void* df,
-                               float* dbeta, float* dc, float* dS0, void* ws, int B, int T, int H,
-                               hipStream_t st)
-{
-    typedef typename TR::E E;
-    const BwdWs L = bwd_ws_layout(sizeof(E), D, B, T, H);
+// the forward's records of each chunk, where the backward workspace keeps them
+static FwdCkpt ckpt_in(void* ws, size_t esize, int D, int B, int T, int H) {
+    const BwdWs L = bwd_ws_layout(esize, D, B, T, H);
     char* wb = static_cast<char*>(ws);
     FwdCkpt ck;
     ck.S = wb + L.s0;
     ck.U = reinterpret_cast<float*>(wb + L.ur);
     ck.M = reinterpret_cast<float*>(wb + L.mm);
     ck.P = wb + L.pp;
+    return ck;
+}
+
+// Forward for training: o, S_T and the per-chunk records the backward reads.
+hipError_t launch_fwd_train(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                            const float* beta, const float* c, const float* S0, void* o, float* ST,
+                            void* ws, int B, int T, int H, hipStream_t st)
+{
+    const FwdCkpt ck = ckpt_in(ws, bf16 ? 2 : 4, d, B, T, H);
+    return launch_fwd(bf16, d, q, k, v, f, beta, c, S0, o, ST, &ck, nullptr, B, T, H, st);
+}
+
+// recompute: run the recording forward first (otherwise the records of a
+// preceding launch_fwd_train on the same inputs and workspace are used)
+template <class TR, int D>
+static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* f,
+                               const float* beta, const float* c, const float* S0, const void* dO,
+                               const float* dST, void* dq, void* dk, void* dv, void* df,
+                               float* dbeta, float* dc, float* dS0, void* ws, int B, int T, int H,
+                               int recompute, hipStream_t st)
+{
+    typedef typename TR::E E;
+    const BwdWs L = bwd_ws_layout(sizeof(E), D, B, T, H);
+    char* wb = static_cast<char*>(ws);
+    const FwdCkpt ck = ckpt_in(ws, sizeof(E), D, B, T, H);
     E* wdS = reinterpret_cast<E*>(wb + L.ds);
     float* wrho = reinterpret_cast<float*>(wb + L.rho);
     const int NC = (T + CH - 1) / CH;
-    if (NC > 0) {
+    if (NC > 0 && recompute) {
         hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr, &ck,
                                   nullptr, B, T, H, st);
         if (e != hipSuccess) return e;
@@ -887,9 +906,10 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
 hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, const void* dO,
                       const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
-                      float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st)
+                      float* dc, float* dS0, void* ws, int B, int T, int H, int recompute,
+                      hipStream_t st)
 {
-#define KD_BWD_ARGS q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, B, T, H, st
+#define KD_BWD_ARGS q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, B, T, H, recompute, st
     if (bf16) {
         switch (d) {
         case 32: return launch_bwd_t<Bf16T, 32>(KD_BWD_ARGS);

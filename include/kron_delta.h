@@ -176,6 +176,37 @@ KD_API kd_status kron_delta_bwd(const kd_desc *desc,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Training pair: a forward that keeps what the backward needs, and a backward
+ * that starts from it instead of recomputing the forward.
+ *
+ * kron_delta_fwd_train: the forward pass (o and, when ST is non-NULL, S_T,
+ * exactly as kron_delta_fwd computes them) that also writes, into ws, the
+ * per-chunk records kron_delta_bwd otherwise recomputes first: the state
+ * entering each chunk, u and r0, and the chunk's M and P.  ws must hold at
+ * least kron_delta_workspace_bytes(desc, 1) bytes (KD_ERR_WORKSPACE) and
+ * overlap no tensor.  Shapes and dtypes as kron_delta_bwd (fp32 only at
+ * d = 32).
+ *
+ * kron_delta_bwd_saved: kron_delta_bwd without its first kernel.  It reads
+ * the records that the last kron_delta_fwd_train left in ws, so the caller
+ * must pass the same inputs (q, k, v, f, beta, c, S0) and the same workspace,
+ * unmodified, and order the two calls on the device (same stream, or an
+ * event).  Results equal kron_delta_bwd's bit for bit.
+ */
+KD_API kd_status kron_delta_fwd_train(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         void *o, float *ST,
+                         void *ws, size_t ws_bytes, void *stream);
+KD_API kd_status kron_delta_bwd_saved(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         const void *dO, const float *dST,
+                         void *dq, void *dk, void *dv, void *df,
+                         float *dbeta, float *dc, float *dS0,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Forward pass of the Gated Delta Rule-2 (decoupled erase and write), the
  * variant of the aitrends.kr Gated DeltaNet-2 summary (sections 핵심 기여 and
  * 방법론 steps 1-4).  Per (b, h) the state S is dk x dv (keys as rows) and,

@@ -188,3 +188,29 @@ def test_gdn2_argument_checks(L):
     assert call(d, o=P(3)) == ALIAS                            # o == alpha
     assert call(d, ST=P(6)) == ALIAS                           # ST == S0
     assert call(_desc(B=2, T=0, H=3, dk=128, dv=128), ST=None) == OK
+
+
+def test_training_pair_argument_checks(L):
+    d = _desc()
+    need = L.kron_delta_workspace_bytes(ctypes.byref(d), 1)
+    names = ["q", "k", "v", "f", "beta", "c", "S0", "o", "ST"]
+
+    def ftrain(desc, ws=P(40), ws_bytes=None, **over):
+        p = {n: P(i) for i, n in enumerate(names)}
+        p.update(over)
+        wsb = need if ws_bytes is None else ws_bytes
+        return L.kron_delta_fwd_train(ctypes.byref(desc), *[p[n] for n in names], ws, wsb, None)
+
+    assert ftrain(d, ws=None) == WORKSPACE
+    assert ftrain(d, ws_bytes=need - 1) == WORKSPACE
+    assert ftrain(d, ws=P(2)) == ALIAS                     # workspace == v
+    assert ftrain(d, o=P(40)) == ALIAS                     # o == workspace
+    assert ftrain(_desc(dk=64, dv=64, dtype=kd.KD_F32)) == DTYPE
+    assert ftrain(d, f=None) == NULL
+    # the saved backward takes the same checks as kron_delta_bwd
+    bn = ["q", "k", "v", "f", "beta", "c", "S0", "dO", "dST", "dq", "dk", "dv", "df",
+          "dbeta", "dc", "dS0"]
+    pb = [P(i) for i in range(len(bn))]
+    assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, None, need, None) == WORKSPACE
+    assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, P(40), need - 1, None) == WORKSPACE
+    assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, P(9), need, None) == ALIAS   # ws == dq

@@ -191,3 +191,23 @@ def test_backward_rejects_fp32_d64():
     t = to_dev(torch, x, "fp32")
     with pytest.raises(kd.KronDeltaError):
         kd.bwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None, t["dO"])
+
+
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 128, 150), ("bf16", 64, 200), ("fp32", 32, 130)])
+def test_training_pair_equals_forward_and_backward_bitwise(dtype, d, T):
+    """kron_delta_fwd_train gives kron_delta_fwd's o and S_T, and
+    kron_delta_bwd_saved from its records gives kron_delta_bwd's gradients,
+    bit for bit (the same kernels, the records kept instead of recomputed)."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    x = sy.rounded(sy.draw(2, T, 2, d, d, seed=800 + d, s0_std=0.1, with_dO=True, dST_std=0.1), dtype)
+    t = to_dev(torch, x, dtype)
+    args = (t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"])
+    o1, S1 = kd.fwd(*args)
+    o2, S2, ws = kd.fwd_train(*args)
+    g2 = kd.bwd(*args, t["dO"], t["dST"], workspace=ws, saved=True)
+    g1 = kd.bwd(*args, t["dO"], t["dST"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for n in GRADS:
+        assert torch.equal(g1[n], g2[n]), n
