@@ -35,6 +35,10 @@
 // of that (b, h), and dS0); dq of the earlier chunks does not and stays exact.
 #include <type_traits>
 
+#include <time.h>
+
+#include <atomic>
+
 #include "kd_device.h"
 
 namespace kd {
@@ -47,8 +51,38 @@ hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void*
 // 256-byte aligned parts (per unit: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4,
 // CH*CH*e bytes).
 struct BwdWs {
-    size_t s0, ur, ds, rho, mm, pp, total;
+    size_t s0, ur, ds, rho, mm, pp, fl, total;   // fl: one hand-off flag per (b, h, chunk)
 };
+
+// Hand-off of the reverse sweep's per-chunk results (dS, rho) to the chunk
+// workers of the fused launch (kd_bwd_fused_kernel).  A flag word carries the
+// launch's epoch (flags of earlier launches never match), the writer's XCD id
+// and bit 1 = PUB_FLUSHED: set only on chunk 0's flag, which goes out after
+// the sweep has written its XCD's L2 back to memory, so a reader on another
+// XCD can wait for that flag and read everything the sweep wrote.
+struct BwdPub {
+    unsigned long long* flags;   // [B*H*NC]
+    unsigned epoch;
+};
+constexpr unsigned long long PUB_FLUSHED = 2ull;
+
+__device__ __forceinline__ unsigned xcc_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));   // HW_REG_XCC_ID[3:0]
+}
+__device__ __forceinline__ unsigned long long pub_word(unsigned epoch, unsigned xcc) {
+    return ((unsigned long long)epoch << 32) | ((unsigned long long)(xcc & 0xffu) << 24) | 1ull;
+}
+// bounded wait of one thread for a flag of this launch that has the bits
+// `need`; false when the bound ran out (then nothing may be read)
+__device__ __forceinline__ bool pub_wait(const unsigned long long* fp, unsigned epoch, unsigned long long need,
+                                         unsigned long long& w) {
+    for (int s = 0; s < (1 << 23); ++s) {
+        w = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(w >> 32) == epoch && (w & need) == need) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
 static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     const size_t nc = (size_t)(T + CH - 1) / CH;
     const size_t units = (size_t)B * H * nc;
@@ -60,7 +94,8 @@ static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     w.rho = w.ds + up(units * d * d * esz);
     w.mm = w.rho + up(units * CH * sizeof(float));
     w.pp = w.mm + up(units * CH * CH * sizeof(float));
-    w.total = w.pp + up(units * CH * CH * esz);
+    w.fl = w.pp + up(units * CH * CH * esz);
+    w.total = w.fl + up(units * sizeof(unsigned long long));
     return w;
 }
 
@@ -124,8 +159,16 @@ struct BwdStateRegs {
     uint4 p[PV];
 };
 
-template <class TR, int D>
-__global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
+// Publishing arguments of the fused launch, in LDS: only the publishing
+// thread reads them, when it publishes, so they hold no register across the
+// sweep's loop.
+__shared__ BwdPub g_pub;
+
+// The sweep of one (b, h); with PUB, each chunk's dS and rho are published
+// (flags of g_pub) once every wave's stores of them have reached L2.
+template <class TR, int D, bool PUB>
+__device__ __forceinline__ void bwd_state_body(
+    BwdStateSmem<TR, D>& sm, int bh,
     const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
@@ -144,17 +187,20 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     constexpr int LD = SM::LD, LDT = SM::LDT, LDM = SM::LDM, LDP = SM::LDP;
     constexpr int EPV = 16 / sizeof(E);   // P elements per 16-byte slice
 
-    __shared__ SM sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
     const PrepIdx pi(tid, D);
     const int r8 = pi.r8, I = pi.I, ch0 = pi.ch0, row0 = pi.row0;
-    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int b = bh / H, h = bh % H;
     const uint32_t rs = (uint32_t)H * D;
     const size_t bbase = (size_t)b * T * H * D;
     const uint32_t hoff = (uint32_t)h * D;
     const int NC = (T + CH - 1) / CH;
+    auto publish = [&](int n, unsigned long long extra) {   // chunk n's dS and rho are in L2 (see the loop's end)
+        __hip_atomic_store(&g_pub.flags[(size_t)bh * NC + n], pub_word(g_pub.epoch, xcc_id()) | extra,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     floatx4 dSt[D / 16];   // dS^T[16mj + 4g + r][16w + cl] = dS[16w + cl][16mj + 4g + r]
 #pragma unroll
@@ -212,6 +258,7 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
     };
 
     for (int n = NC - 1; n >= 0; --n) {
+        if (PUB && tid == 0 && n + 1 < NC) publish(n + 1, 0ull);
         // ---------------- prep (a): decay products within the sub-block; M and P
         if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
 #pragma unroll
@@ -390,7 +437,14 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
                     dSt[mj] = TR::mma(TR::ld_nat(&sm.KT[(16 * mj + cl) * LDT], ks, g), bR[ks], dSt[mj]);
                 }
         }
+        // this wave's stores of chunk n (and everything before them) have
+        // reached L2 before the barrier; the flag goes out after it
+        if (PUB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
+    }
+    if (PUB && tid == 0 && NC > 0) {   // every wave's stores are in L2: write it back, then the last flag
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        publish(0, PUB_FLUSHED);
     }
 
     if (dS0) {
@@ -431,8 +485,12 @@ struct BwdChunkSmem {
     unsigned unsafe_any;
 };
 
+// The gradients of chunk n of (b, h) = bh.  stale (thread 0's is read):
+// nonzero when dS and rho of the unit could not be received; every output of
+// the unit is then NaN, as for an unsafe decay.
 template <class TR, int D>
-__global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
+__device__ __forceinline__ void bwd_chunk_body(
+    BwdChunkSmem<TR, D>& sm, int bh, int n, int tid, unsigned stale,
     const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
     const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
     const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
@@ -451,7 +509,6 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     constexpr int KC_ = CH / TR::KS;
     constexpr int LD = SM::LD, LDP = SM::LDP, LDF = SM::LDF;
 
-    __shared__ SM sm;
     E* Qb = reinterpret_cast<E*>(sm.big);
     E* Kb = Qb + CH * LD;
     E* Kc = Kb + CH * LD;
@@ -468,12 +525,11 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     float* stC = stK + CH * LDF;
     float* stT = stC + CH * LDF;
 
-    const int tid = threadIdx.x;
+    // tid: threadIdx.x (see the fused kernel)
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cl = lane & 15;
     const PrepIdx pi(tid, D);
     const int r8 = pi.r8, I = pi.I, ch0 = pi.ch0, row0 = pi.row0;
     const int NC = (T + CH - 1) / CH;
-    const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
     const int b = bh / H, h = bh % H;
     const uint32_t rs = (uint32_t)H * D;
     const size_t bbase = (size_t)b * T * H * D;
@@ -545,7 +601,7 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     // the upper triangles of P, dGK, dP (hi and lo) are never written
     for (int x = tid; x < 5 * CH * LDP * (int)sizeof(E) / 16; x += NT)
         reinterpret_cast<uint4*>(P)[x] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) sm.unsafe_any = 0u;
+    if (tid == 0) sm.unsafe_any = stale;
     {
         float incl[8];
 #pragma unroll
@@ -848,7 +904,132 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
     }
 }
 
+template <class TR, int D>
+__global__ __launch_bounds__(4 * D) void kd_bwd_state_kernel(
+    const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
+    const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
+    const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const float* __restrict__ ckM, const typename TR::E* __restrict__ ckP,
+    const float* __restrict__ dST, typename TR::E* __restrict__ wsdS, float* __restrict__ wsrho,
+    float* __restrict__ dS0, int T, int H)
+{
+    __shared__ BwdStateSmem<TR, D> sm;
+    bwd_state_body<TR, D, false>(sm, blockIdx.x, q, k, v, f, beta, dO, ckM, ckP, dST, wsdS, wsrho, dS0, T, H);
+}
+
+template <class TR, int D>
+__global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
+    const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
+    const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
+    const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const typename TR::E* __restrict__ ckptS, const float* __restrict__ ckptU,
+    const typename TR::E* __restrict__ wsdS, const float* __restrict__ wsrho,
+    typename TR::E* __restrict__ dq, typename TR::E* __restrict__ dk,
+    typename TR::E* __restrict__ dv, typename TR::E* __restrict__ df,
+    float* __restrict__ dbeta, float* __restrict__ dc, int T, int H)
+{
+    __shared__ BwdChunkSmem<TR, D> sm;
+    const int NC = (T + CH - 1) / CH;
+    bwd_chunk_body<TR, D>(sm, blockIdx.x / NC, blockIdx.x % NC, threadIdx.x, 0u, q, k, v, f, beta, dO, ckptS, ckptU,
+                          wsdS, wsrho, dq, dk, dv, df, dbeta, dc, T, H);
+}
+
+// Both backward kernels in one launch, so the chunk gradients run on the CUs
+// the sweep leaves idle while the sweep goes on.  Blocks 0 .. BHpad - 1 sweep
+// (one per (b, h); blocks past B*H end at once); the others are persistent
+// workers.  Dispatch is in block order on each XCD, so every sweep block is
+// resident before any worker, and a sweep block never waits: the workers'
+// waits always end.  Blocks x and x + 8 share an XCD under round-robin
+// placement, so worker rank r on XCD c = x mod 8 takes the chunks of the
+// heads bh = c (mod 8), newest chunk first (the sweep's order), and reads
+// their dS and rho through the XCD's L2.  Should a worker find the writer on
+// another XCD (the flag's id), it waits for the sweep's closing L2 write-back
+// (chunk 0's flag) and acquires at agent scope before reading.  A wait that
+// runs out of its bound turns the unit's outputs into NaN.
+template <class TR, int D>
+__global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
+    const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
+    const typename TR::E* __restrict__ v, const typename TR::E* __restrict__ f,
+    const float* __restrict__ beta, const typename TR::E* __restrict__ dO,
+    const float* __restrict__ ckM, const typename TR::E* __restrict__ ckP,
+    const typename TR::E* __restrict__ ckptS, const float* __restrict__ ckptU,
+    const float* __restrict__ dST, typename TR::E* __restrict__ wsdS, float* __restrict__ wsrho,
+    float* __restrict__ dS0, typename TR::E* __restrict__ dq, typename TR::E* __restrict__ dk,
+    typename TR::E* __restrict__ dv, typename TR::E* __restrict__ df,
+    float* __restrict__ dbeta, float* __restrict__ dc, int BH, int BHpad, int nwork, BwdPub pub,
+    int T, int H)
+{
+    union Smem {
+        BwdStateSmem<TR, D> s;
+        BwdChunkSmem<TR, D> c;
+    };
+    __shared__ Smem sm;
+    const int x = blockIdx.x;
+    if (x < BHpad) {
+        if (x < BH) {
+            if (threadIdx.x == 0) g_pub = pub;   // read after the sweep's first barriers
+            bwd_state_body<TR, D, true>(sm.s, x, q, k, v, f, beta, dO, ckM, ckP, dST, wsdS, wsrho, dS0, T, H);
+        }
+        return;
+    }
+    const int NC = (T + CH - 1) / CH;
+    const int j = x - BHpad, c = j & 7, r = j >> 3, R = nwork >> 3;
+    const int nh = c < BH ? (BH - c + 7) / 8 : 0;   // heads c, c + 8, ... on this XCD
+    const unsigned me = xcc_id();
+    bool dead = false;   // thread 0: a wait ran out; this and every later unit is NaN
+#pragma unroll 1
+    for (int u = r; u < nh * NC; u += R) {
+        const int n = NC - 1 - u / nh, bh = c + 8 * (u % nh);
+        if (threadIdx.x == 0 && !dead) {
+            unsigned long long w = 0;
+            dead = !pub_wait(&pub.flags[(size_t)bh * NC + n], pub.epoch, 1ull, w);
+            // a writer on another XCD: wait for its L2 write-back, then drop
+            // this XCD's copies
+            if (!dead && ((unsigned)(w >> 24) & 0xffu) != me) {
+                dead = !pub_wait(&pub.flags[(size_t)bh * NC], pub.epoch, PUB_FLUSHED, w);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+        }
+        lds_barrier();
+        // the thread index through an opaque zero: nothing the body derives
+        // from it is invariant across units, so nothing is hoisted out of this
+        // loop to hold registers through the body
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        bwd_chunk_body<TR, D>(sm.c, bh, n, (int)threadIdx.x + z, dead ? 1u : 0u, q, k, v, f, beta, dO, ckptS,
+                              ckptU, wsdS, wsrho, dq, dk, dv, df, dbeta, dc, T, H);
+        lds_barrier();   // the next unit reuses the LDS
+    }
+}
+
 // --------------------------------------------------------------- launchers
+// compute units of the current device (the fused backward sizes its worker
+// pool to the CUs the sweep leaves free)
+static int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load();
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+        cache[dev].store(n);
+    }
+    return n;
+}
+
+// launch epochs of the fused backward: each launch's flags differ from every
+// earlier launch's, so flags left in a reused workspace never match
+static unsigned next_bwd_epoch() {
+    static std::atomic<unsigned> e{0u};
+    unsigned v = e.fetch_add(1u) + 1u;
+    if (v == 1u) {   // first launch of the process: start from the clock
+        const unsigned t = (unsigned)time(nullptr) * 2654435761u;
+        e.fetch_add(t);
+        v += t;
+    }
+    return v;
+}
+
 // the forward's records of each chunk, where the backward workspace keeps them
 static FwdCkpt ckpt_in(void* ws, size_t esize, int D, int B, int T, int H) {
     const BwdWs L = bwd_ws_layout(esize, D, B, T, H);
@@ -890,6 +1071,19 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
         hipError_t e = launch_fwd(sizeof(E) == 2, D, q, k, v, f, beta, c, S0, nullptr, nullptr, &ck,
                                   nullptr, B, T, H, st);
         if (e != hipSuccess) return e;
+    }
+    // The fused launch when at least 64 workers fit beside the sweep blocks.
+    const int BH = B * H, BHpad = (BH + 7) & ~7;
+    const int nwork = ((compute_units() - BHpad) / 8) * 8;
+    if (NC > 0 && nwork >= 64) {
+        BwdPub pub;
+        pub.flags = reinterpret_cast<unsigned long long*>(wb + L.fl);
+        pub.epoch = next_bwd_epoch();
+        hipLaunchKernelGGL((kd_bwd_fused_kernel<TR, D>), dim3((unsigned)(BHpad + nwork)), dim3(4 * D), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
+                           (const float*)ck.M, (const E*)ck.P, (const E*)ck.S, (const float*)ck.U, dST, wdS,
+                           wrho, dS0, (E*)dq, (E*)dk, (E*)dv, (E*)df, dbeta, dc, BH, BHpad, nwork, pub, T, H);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,

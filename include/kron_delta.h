@@ -151,10 +151,11 @@ KD_API kd_status kron_delta_decode(const kd_desc *desc,
  * S0 NULL means S0 = 0; dS0 NULL means the gradient of S0 is not returned.
  * Needs a workspace of kron_delta_workspace_bytes(desc, 1) bytes: it holds,
  * per 64-token chunk and head, the entering state, the WY targets and the
- * chunk matrices M and P of a forward recomputation, and the state gradient
- * of the reverse sweep (about 2*d*d*e + 64*64*(4 + e) + 768 bytes, e the
- * element size); its contents on entry are ignored and on exit are
- * unspecified.
+ * chunk matrices M and P of a forward recomputation, the state gradient
+ * of the reverse sweep and a hand-off flag (about 2*d*d*e + 64*64*(4 + e)
+ * + 776 bytes, e the element size); its contents on entry are ignored and on
+ * exit are unspecified; two calls that overlap on the device must not share
+ * it.
  * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv = 32
  * (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
  * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2
@@ -165,7 +166,14 @@ KD_API kd_status kron_delta_decode(const kd_desc *desc,
  * NaN, and so are those that depend on it through the state gradient (dk,
  * dv, df, dbeta, dc of the earlier chunks of the same (b, h), and dS0); dq of
  * the earlier chunks does not depend on it and stays exact.
- * Enqueued on `stream` as three kernels; no allocation, no synchronisation.
+ * Enqueued on `stream`: the recording forward, then the reverse sweep over
+ * the chunks and the per-chunk gradients, in one launch when B*H leaves at
+ * least 64 compute units free (the per-chunk work then runs beside the sweep,
+ * each chunk as soon as the sweep has passed it) and as two kernels
+ * otherwise; the results are the same bit for bit.  In the single launch a
+ * chunk whose hand-off from the sweep does not arrive within its wait bound
+ * (seconds; it arrives within microseconds) gets NaN gradients rather than
+ * wrong ones.  No allocation, no synchronisation.
  */
 KD_API kd_status kron_delta_bwd(const kd_desc *desc,
                          const void *q, const void *k, const void *v, const void *f,
@@ -187,7 +195,7 @@ KD_API kd_status kron_delta_bwd(const kd_desc *desc,
  * overlap no tensor.  Shapes and dtypes as kron_delta_bwd (fp32 only at
  * d = 32).
  *
- * kron_delta_bwd_saved: kron_delta_bwd without its first kernel.  It reads
+ * kron_delta_bwd_saved: kron_delta_bwd without its recording forward.  It reads
  * the records that the last kron_delta_fwd_train left in ws, so the caller
  * must pass the same inputs (q, k, v, f, beta, c, S0) and the same workspace,
  * unmodified, and order the two calls on the device (same stream, or an

@@ -120,7 +120,11 @@ def test_bwd_argument_checks(L):
 def test_workspace_scales_with_chunks(L):
     a = L.kron_delta_workspace_bytes(ctypes.byref(_desc(T=64)), 1)
     b = L.kron_delta_workspace_bytes(ctypes.byref(_desc(T=65)), 1)
-    assert b == 2 * a
+    # two more (b, h, chunk) units, each at least: S0 and dS (d*d bf16 each),
+    # u, r0, rho (C fp32 each), M (C*C fp32), P (C*C bf16); the 8-byte flags
+    # of a few units fit in the padding of their part
+    per_unit = 2 * 64 * 64 * 2 + 3 * 64 * 4 + 64 * 64 * 4 + 64 * 64 * 2
+    assert 2 * per_unit <= b - a and b <= 2 * a
     assert L.kron_delta_workspace_bytes(ctypes.byref(_desc(dk=48, dv=48)), 1) == 0
 
 

@@ -211,3 +211,25 @@ def test_training_pair_equals_forward_and_backward_bitwise(dtype, d, T):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     for n in GRADS:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_fused_and_two_kernel_backward_agree_bitwise():
+    """With few (b, h) the sweep and the chunk gradients share one launch;
+    with more (b, h) than leave 64 compute units free they run as two
+    kernels.  Both run the same per-unit arithmetic, so the heads of a wide
+    run equal, bit for bit, the same heads run on their own."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = max(8, ((cus - 64) // 8 + 1) * 8)   # (B*H + 7) / 8 * 8 > cus - 64: two kernels
+    x = sy.rounded(sy.draw(1, 130, H, 64, 64, seed=817, s0_std=0.1, with_dO=True, dST_std=0.1), "bf16")
+    t = to_dev(torch, x, "bf16")
+    wide = kd.bwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"], t["dO"], t["dST"])
+    for lo in (0, H - 8):
+        sl = {n: (a[:, lo:lo + 8] if n in ("S0", "dST") else a[:, :, lo:lo + 8]).contiguous()
+              for n, a in t.items() if a is not None}
+        few = kd.bwd(sl["q"], sl["k"], sl["v"], sl["f"], sl["beta"], sl["c"], sl["S0"], sl["dO"], sl["dST"])
+        torch.cuda.synchronize()
+        for n in GRADS:
+            w = wide[n][:, lo:lo + 8] if n == "dS0" else wide[n][:, :, lo:lo + 8]
+            assert torch.equal(w, few[n]), (n, lo)
