@@ -303,7 +303,7 @@ def main():
                      "kernel": "kd_gdn2_kernel" if w.gdn2 else
                      "kd_decode_kernel<bf16,128>" if w.decode else
                      "kd_fwd16_kernel<false>" if not w.backward else
-                     "kd_fwd16_kernel(ckpt) + kd_bwd_state_kernel + kd_bwd_chunk_kernel",
+                     "kd_fwd16_kernel(ckpt) + kd_bwd_fused_kernel",
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,
                      },

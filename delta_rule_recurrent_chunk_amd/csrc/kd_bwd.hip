@@ -51,7 +51,7 @@ hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void*
 // 256-byte aligned parts (per unit: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4,
 // CH*CH*e bytes).
 struct BwdWs {
-    size_t s0, ur, ds, rho, mm, pp, fl, total;   // fl: one hand-off flag per (b, h, chunk)
+    size_t s0, ur, ds, rho, mm, pp, fl, total;   // fl: 8 claim counters, then one flag per (b, h, chunk) at +256
 };
 
 // Hand-off of the reverse sweep's per-chunk results (dS, rho) to the chunk
@@ -60,8 +60,12 @@ struct BwdWs {
 // and bit 1 = PUB_FLUSHED: set only on chunk 0's flag, which goes out after
 // the sweep has written its XCD's L2 back to memory, so a reader on another
 // XCD can wait for that flag and read everything the sweep wrote.
+// The chunks of the heads on one XCD are handed out in the sweep's order by
+// a claim counter per XCD (ctr[c]: epoch in the high word, units claimed in
+// the low word), which the launch's block c sets at its start.
 struct BwdPub {
     unsigned long long* flags;   // [B*H*NC]
+    unsigned long long* ctr;     // [8]
     unsigned epoch;
 };
 constexpr unsigned long long PUB_FLUSHED = 2ull;
@@ -95,7 +99,7 @@ static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     w.mm = w.rho + up(units * CH * sizeof(float));
     w.pp = w.mm + up(units * CH * CH * sizeof(float));
     w.fl = w.pp + up(units * CH * CH * esz);
-    w.total = w.fl + up(units * sizeof(unsigned long long));
+    w.total = w.fl + up(256 + units * sizeof(unsigned long long));
     return w;
 }
 
@@ -936,13 +940,16 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_chunk_kernel(
 
 // Both backward kernels in one launch, so the chunk gradients run on the CUs
 // the sweep leaves idle while the sweep goes on.  Blocks 0 .. BHpad - 1 sweep
-// (one per (b, h); blocks past B*H end at once); the others are persistent
-// workers.  Dispatch is in block order on each XCD, so every sweep block is
-// resident before any worker, and a sweep block never waits: the workers'
-// waits always end.  Blocks x and x + 8 share an XCD under round-robin
-// placement, so worker rank r on XCD c = x mod 8 takes the chunks of the
-// heads bh = c (mod 8), newest chunk first (the sweep's order), and reads
-// their dS and rho through the XCD's L2.  Should a worker find the writer on
+// (one per (b, h); blocks past B*H have no head) and then join the others,
+// persistent workers that take (b, h, chunk) units from their XCD's claim
+// counter.  Dispatch is in block order on each XCD, so every sweep block is
+// resident before any worker, and a sweep never waits: the workers' waits
+// always end.  Blocks x and x + 8 share an XCD under round-robin placement,
+// so the blocks with x = c (mod 8) share the chunks of the heads bh = c
+// (mod 8), handed out in the sweep's order (newest chunk first, then the
+// heads in turn), and read their dS and rho through the XCD's L2.  Block c
+// sets the counter of XCD c before any claim is made (a claimer waits for
+// this launch's epoch in it).  Should a worker find the writer on
 // another XCD (the flag's id), it waits for the sweep's closing L2 write-back
 // (chunk 0's flag) and acquires at agent scope before reading.  A wait that
 // runs out of its bound turns the unit's outputs into NaN.
@@ -964,41 +971,86 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
         BwdChunkSmem<TR, D> c;
     };
     __shared__ Smem sm;
+    __shared__ int g_unit;
     const int x = blockIdx.x;
+    const int NC = (T + CH - 1) / CH;
+    int c;   // this block's XCD under round-robin placement: x mod 8
     if (x < BHpad) {
+        if (x < 8 && threadIdx.x == 0)
+            __hip_atomic_store(&pub.ctr[x], (unsigned long long)pub.epoch << 32, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         if (x < BH) {
             if (threadIdx.x == 0) g_pub = pub;   // read after the sweep's first barriers
             bwd_state_body<TR, D, true>(sm.s, x, q, k, v, f, beta, dO, ckM, ckP, dST, wsdS, wsrho, dS0, T, H);
+            lds_barrier();   // the sweep's LDS is done with: the block joins the workers
         }
-        return;
+        c = x & 7;
+    } else {
+        c = (x - BHpad) & 7;
     }
-    const int NC = (T + CH - 1) / CH;
-    const int j = x - BHpad, c = j & 7, r = j >> 3, R = nwork >> 3;
     const int nh = c < BH ? (BH - c + 7) / 8 : 0;   // heads c, c + 8, ... on this XCD
+    const int total = nh * NC;
     const unsigned me = xcc_id();
-    bool dead = false;   // thread 0: a wait ran out; this and every later unit is NaN
+    // thread 0 only: dyn, units come from the claim counter (pending: the
+    // claim in flight); otherwise, if the counter never showed this launch's
+    // epoch, a worker takes the units r, r + R, ... (next); dead: a wait ran
+    // out, so every unit taken from then on is NaN
+    bool dyn = false, dead = false;
+    int next = -1;
+    unsigned long long pending = 0;
+    if (threadIdx.x == 0 && total > 0) {
+        unsigned long long w = 0;
+        if (pub_wait(&pub.ctr[c], pub.epoch, 0ull, w)) {
+            dyn = true;
+            pending = __hip_atomic_fetch_add(&pub.ctr[c], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            dead = true;
+            next = x < BHpad ? -1 : (x - BHpad) >> 3;
+        }
+    }
 #pragma unroll 1
-    for (int u = r; u < nh * NC; u += R) {
-        const int n = NC - 1 - u / nh, bh = c + 8 * (u % nh);
-        if (threadIdx.x == 0 && !dead) {
-            unsigned long long w = 0;
-            dead = !pub_wait(&pub.flags[(size_t)bh * NC + n], pub.epoch, 1ull, w);
-            // a writer on another XCD: wait for its L2 write-back, then drop
-            // this XCD's copies
-            if (!dead && ((unsigned)(w >> 24) & 0xffu) != me) {
-                dead = !pub_wait(&pub.flags[(size_t)bh * NC], pub.epoch, PUB_FLUSHED, w);
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int u = -1;
+            if (dyn) {
+                const unsigned k = (unsigned)pending;   // units claimed before this one
+                if (k < (unsigned)total) {
+                    u = (int)k;
+                    // the claim of the unit after this one is in flight during the body
+                    pending = __hip_atomic_fetch_add(&pub.ctr[c], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    dyn = false;
+                }
+            } else if (next >= 0 && next < total) {
+                u = next;
+                next += nwork >> 3;
             }
+            if (u >= 0 && !dead) {
+                const int n = NC - 1 - u / nh, bh = c + 8 * (u % nh);
+                unsigned long long w = 0;
+                dead = !pub_wait(&pub.flags[(size_t)bh * NC + n], pub.epoch, 1ull, w);
+                // a writer on another XCD: wait for its L2 write-back, then drop
+                // this XCD's copies
+                if (!dead && ((unsigned)(w >> 24) & 0xffu) != me) {
+                    dead = !pub_wait(&pub.flags[(size_t)bh * NC], pub.epoch, PUB_FLUSHED, w);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                }
+            }
+            g_unit = u < 0 ? -1 : (dead ? -2 - u : u);   // -2 - u: unit u, as NaN
         }
         lds_barrier();
+        const int gu = g_unit;
+        if (gu == -1) break;
+        const int u = gu >= 0 ? gu : -2 - gu;
+        const int n = NC - 1 - u / nh, bh = c + 8 * (u % nh);
         // the thread index through an opaque zero: nothing the body derives
         // from it is invariant across units, so nothing is hoisted out of this
         // loop to hold registers through the body
         int z;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        bwd_chunk_body<TR, D>(sm.c, bh, n, (int)threadIdx.x + z, dead ? 1u : 0u, q, k, v, f, beta, dO, ckptS,
+        bwd_chunk_body<TR, D>(sm.c, bh, n, (int)threadIdx.x + z, gu < 0 ? 1u : 0u, q, k, v, f, beta, dO, ckptS,
                               ckptU, wsdS, wsrho, dq, dk, dv, df, dbeta, dc, T, H);
-        lds_barrier();   // the next unit reuses the LDS
+        lds_barrier();   // the next unit reuses the LDS (and g_unit)
     }
 }
 
@@ -1077,7 +1129,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     const int nwork = ((compute_units() - BHpad) / 8) * 8;
     if (NC > 0 && nwork >= 64) {
         BwdPub pub;
-        pub.flags = reinterpret_cast<unsigned long long*>(wb + L.fl);
+        pub.ctr = reinterpret_cast<unsigned long long*>(wb + L.fl);
+        pub.flags = reinterpret_cast<unsigned long long*>(wb + L.fl + 256);
         pub.epoch = next_bwd_epoch();
         hipLaunchKernelGGL((kd_bwd_fused_kernel<TR, D>), dim3((unsigned)(BHpad + nwork)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
