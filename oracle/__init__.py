@@ -22,6 +22,12 @@ Functions
     form, decay-only closed form, exact recall, erase-only annihilation,
     split/resume, hand-worked fixture).
 
+``oracle.mixer`` (numpy, fp64): the mixer's pre-processing (short causal
+    depthwise convolution, SiLU, L2 normalisation, sigmoid gates, the
+    power-law forget gate) and post-processing (per-head RMSNorm with a
+    sigmoid output gate) around the rule; pinned in
+    tests/test_oracle_mixer.py.
+
 All arrays are numpy fp64 in the layouts q,k,f:[B,T,H,dk], v:[B,T,H,dv],
 beta,c:[B,T,H], S:[B,H,dv,dk].  Parity status: pinned (see tests/test_oracle.py
 for the pins: lifted Widrow-Hoff form, non-expansiveness identity, immediate
