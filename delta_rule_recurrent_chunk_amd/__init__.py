@@ -9,6 +9,7 @@ missing, every entry point raises; there is no CPU fallback.
     grads  = bwd(q, k, v, f, beta, c, S0, dO, dST=None)
     o      = decode(q, k, v, f, beta, c, S)        (S updated in place)
     o, S_T = fwd_varlen(q, k, v, f, beta, c, cu_seqlens, S0=None)   (packed sequences)
+    y, S_T = mixer_fwd(raw, params, g, S0=None)      (projections -> gated, normalised read-out)
 
 Shapes: q, k, f [B, T, H, d]; v [B, T, H, d]; beta, c [B, T, H] fp32;
 S0 / S_T [B, H, d, d] fp32 (S[i][j], i over values, j over keys).
@@ -27,7 +28,9 @@ ABI_VERSION = 1
 EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
             "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd",
-            "kron_delta_fwd_train", "kron_delta_bwd_saved")
+            "kron_delta_fwd_train", "kron_delta_bwd_saved", "kron_delta_mixer_pre",
+            "kron_delta_mixer_post", "kron_delta_mixer_fwd")
+KD_WS_FWD, KD_WS_BWD, KD_WS_MIXER = 0, 1, 2
 
 
 class KronDeltaError(RuntimeError):
@@ -39,6 +42,12 @@ class KronDeltaError(RuntimeError):
 class KdDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class KdMixerParams(ctypes.Structure):
+    _fields_ = [("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+                ("conv_size", ctypes.c_int32), ("a_log", ctypes.c_void_p), ("beta_scale", ctypes.c_float),
+                ("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -73,6 +82,13 @@ def lib():
         L.kron_delta_decode.argtypes = [dp] + [vp] * 9 + [vp]
         L.kron_delta_gdn2_fwd.restype = i32
         L.kron_delta_gdn2_fwd.argtypes = [dp] + [vp] * 9 + [vp]
+        mp = ctypes.POINTER(KdMixerParams)
+        L.kron_delta_mixer_pre.restype = i32
+        L.kron_delta_mixer_pre.argtypes = [dp, mp] + [vp] * 12 + [vp]
+        L.kron_delta_mixer_post.restype = i32
+        L.kron_delta_mixer_post.argtypes = [dp, mp] + [vp] * 3 + [vp]
+        L.kron_delta_mixer_fwd.restype = i32
+        L.kron_delta_mixer_fwd.argtypes = [dp, mp] + [vp] * 10 + [vp, sz, vp]
         if L.kron_delta_abi_version() != ABI_VERSION:
             raise ImportError("libkrondelta.so ABI version mismatch")
         _lib = L
@@ -289,3 +305,108 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, *, return_state=True):
     if st != 0:
         raise KronDeltaError(st, "kron_delta_gdn2_fwd")
     return o, ST
+
+
+def _mixer_params(torch, H, dk, dv, conv_q=None, conv_k=None, conv_v=None, a_log=None, norm_w=None,
+                  beta_scale=1.0, norm_eps=1e-5):
+    """KdMixerParams for the given fp32 device tensors (kept alive by the caller)."""
+    K = 0
+    for name, t, d in (("conv_q", conv_q, dk), ("conv_k", conv_k, dk), ("conv_v", conv_v, dv)):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or t.dim() != 3 or tuple(t.shape[:2]) != (H, d) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float32 [H, d, conv_size] tensor" % name)
+        if K and t.shape[2] != K:
+            raise ValueError("conv_q, conv_k and conv_v must have the same width")
+        K = t.shape[2]
+    if a_log is not None and (a_log.dtype != torch.float32 or tuple(a_log.shape) != (H,)):
+        raise ValueError("a_log must be float32 [H]")
+    if norm_w is not None and (norm_w.dtype != torch.float32 or tuple(norm_w.shape) != (H, dv)
+                               or not norm_w.is_contiguous()):
+        raise ValueError("norm_w must be a contiguous float32 [H, dv] tensor")
+    return KdMixerParams(_ptr(conv_q), _ptr(conv_k), _ptr(conv_v), K, _ptr(a_log), float(beta_scale),
+                         _ptr(norm_w), float(norm_eps))
+
+
+def _raw_desc(torch, q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw):
+    dt = q_raw.dtype
+    for name, t in (("k_raw", k_raw), ("v_raw", v_raw), ("f_raw", f_raw)):
+        if t.dtype != dt or not t.is_cuda:
+            raise TypeError("%s must be a device tensor of q_raw's dtype" % name)
+    B, T, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    if tuple(k_raw.shape) != (B, T, H, dk) or tuple(f_raw.shape) != (B, T, H, dk):
+        raise ValueError("q_raw, k_raw, f_raw must be [B, T, H, dk]")
+    for name, t in (("beta_raw", beta_raw), ("c_raw", c_raw)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, T, H):
+            raise ValueError("%s must be float32 [B, T, H]" % name)
+    return KdDesc(B, T, H, dk, dv, _dtype_code(torch, dt))
+
+
+def mixer_pre(q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, conv_q, conv_k, conv_v, a_log, *,
+              beta_scale=1.0):
+    """The rule's inputs from the projections (conv, SiLU, L2 norm; gates).
+    Returns q, k, v, f (dtype of the projections) and beta, c (float32)."""
+    import torch
+    L = lib()
+    desc = _raw_desc(torch, q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw)
+    p = _mixer_params(torch, desc.H, desc.dk, desc.dv, conv_q, conv_k, conv_v, a_log, beta_scale=beta_scale)
+    ins = [t.contiguous() for t in (q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw)]
+    q, k, v, f = (torch.empty_like(t) for t in ins[:4])
+    beta, c = torch.empty_like(ins[4]), torch.empty_like(ins[5])
+    stream = torch.cuda.current_stream(q_raw.device).cuda_stream
+    st = L.kron_delta_mixer_pre(ctypes.byref(desc), ctypes.byref(p), *[_ptr(t) for t in ins],
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta), _ptr(c), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_mixer_pre")
+    return q, k, v, f, beta, c
+
+
+def mixer_post(o, g, norm_w, *, norm_eps=1e-5):
+    """Gated per-head RMSNorm of the read-out: o / rms(o) * norm_w[h] * sigmoid(g)."""
+    import torch
+    L = lib()
+    if g.dtype != o.dtype or tuple(g.shape) != tuple(o.shape) or o.dim() != 4:
+        raise ValueError("o and g must be [B, T, H, dv] of one dtype")
+    B, T, H, dv = o.shape
+    desc = KdDesc(B, T, H, dv, dv, _dtype_code(torch, o.dtype))
+    p = _mixer_params(torch, H, dv, dv, norm_w=norm_w, norm_eps=norm_eps)
+    o, g = o.contiguous(), g.contiguous()
+    y = torch.empty_like(o)
+    stream = torch.cuda.current_stream(o.device).cuda_stream
+    st = L.kron_delta_mixer_post(ctypes.byref(desc), ctypes.byref(p), _ptr(o), _ptr(g), _ptr(y),
+                                 ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_mixer_post")
+    return y
+
+
+def mixer_fwd(q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, g, conv_q, conv_k, conv_v, a_log, norm_w,
+              S0=None, *, beta_scale=1.0, norm_eps=1e-5, return_state=True, workspace=None):
+    """The mixer forward from the projections: pre-processing, the rule, and the
+    gated RMSNorm of the read-out.  Returns (y, S_T)."""
+    import torch
+    L = lib()
+    desc = _raw_desc(torch, q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw)
+    B, T, H, dk, dv = desc.B, desc.T, desc.H, desc.dk, desc.dv
+    if g.dtype != q_raw.dtype or tuple(g.shape) != (B, T, H, dv):
+        raise ValueError("g must be [B, T, H, dv] of the projections' dtype")
+    if S0 is not None:
+        if tuple(S0.shape) != (B, H, dv, dk) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be float32 [B, H, dv, dk]")
+        S0 = S0.contiguous()
+    p = _mixer_params(torch, H, dk, dv, conv_q, conv_k, conv_v, a_log, norm_w, beta_scale, norm_eps)
+    ins = [t.contiguous() for t in (q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, g)]
+    y = torch.empty((B, T, H, dv), dtype=q_raw.dtype, device=q_raw.device)
+    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q_raw.device) if return_state else None
+    need = int(L.kron_delta_workspace_bytes(ctypes.byref(desc), KD_WS_MIXER))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_raw.device)
+    stream = torch.cuda.current_stream(q_raw.device).cuda_stream
+    st = L.kron_delta_mixer_fwd(ctypes.byref(desc), ctypes.byref(p), *[_ptr(t) for t in ins], _ptr(S0), _ptr(y),
+                                _ptr(ST), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_mixer_fwd")
+    return y, ST
+

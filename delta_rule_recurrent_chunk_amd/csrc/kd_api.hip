@@ -27,6 +27,13 @@ hipError_t launch_gdn2(const void* q, const void* k, const void* v, const void* 
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
                          int B, int T, int H, hipStream_t st);
+bool mixer_grid_ok(int B, int T);
+hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* const out[4],
+                            const float* const conv[3], int K, const float* a_log, const float* beta_raw,
+                            const float* c_raw, float beta_scale, float* beta, float* c, int B, int T, int H,
+                            hipStream_t st);
+hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
+                             int B, int T, int H, hipStream_t st);
 }  // namespace kd
 
 namespace {
@@ -66,6 +73,44 @@ kd_status check_desc(const kd_desc* d, bool fp32_d128 = false) {
 
 size_t esize(const kd_desc* d) { return d->dtype == KD_BF16 ? 2 : 4; }
 
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The mixer forward's workspace: q, k, v, f (desc dtype), beta, c (fp32) and
+// the read-out o, each part 256-byte aligned.
+struct MixWs {
+    size_t x[4], beta, c, o, total;
+};
+MixWs mixer_ws(const kd_desc* d) {
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = up256(ntok * d->dk * esize(d)), gb = up256(ntok * sizeof(float));
+    MixWs w;
+    for (int i = 0; i < 4; ++i) w.x[i] = i * xb;
+    w.beta = 4 * xb;
+    w.c = w.beta + gb;
+    w.o = w.c + gb;
+    w.total = w.o + xb;
+    return w;
+}
+
+// checks of the mixer's parameters: pre (conv, a_log) and/or post (norm_w)
+kd_status check_mixer(const kd_desc* d, const kd_mixer_params* p, bool pre, bool post) {
+    if (!p) return KD_ERR_NULL;
+    if (!kd::mixer_grid_ok(d->B, d->T)) return KD_ERR_SHAPE;
+    if (pre) {
+        if (!p->conv_q || !p->conv_k || !p->conv_v || !p->a_log) return KD_ERR_NULL;
+        if (p->conv_size < 1 || p->conv_size > 4) return KD_ERR_SHAPE;
+        const void* ptrs[] = {p->conv_q, p->conv_k, p->conv_v, p->a_log};
+        for (const void* q : ptrs)
+            if (misaligned(q)) return KD_ERR_ALIGN;
+    }
+    if (post) {
+        if (!p->norm_w) return KD_ERR_NULL;
+        if (misaligned(p->norm_w)) return KD_ERR_ALIGN;
+        if (!(p->norm_eps >= 0.f)) return KD_ERR_SHAPE;
+    }
+    return KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,10 +131,13 @@ const char* kron_delta_status_string(int s) {
     }
 }
 
-size_t kron_delta_workspace_bytes(const kd_desc* d, int with_backward) {
+size_t kron_delta_workspace_bytes(const kd_desc* d, int which) {
     if (check_desc(d) != KD_OK) return 0;
-    if (!with_backward) return 0;
-    return kd::bwd_workspace_bytes(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
+    switch (which) {
+    case KD_WS_BWD: return kd::bwd_workspace_bytes(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
+    case KD_WS_MIXER: return mixer_ws(d).total;
+    default: return 0;
+    }
 }
 
 kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const void* v,
@@ -296,3 +344,117 @@ kd_status kron_delta_gdn2_fwd(const kd_desc* d, const void* q, const void* k, co
     hipError_t e = kd::launch_gdn2(q, k, v, alpha, b, w, S0, o, ST, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
+
+kd_status kron_delta_mixer_pre(const kd_desc* d, const kd_mixer_params* p, const void* q_raw, const void* k_raw,
+                               const void* v_raw, const void* f_raw, const float* beta_raw, const float* c_raw,
+                               void* q, void* k, void* v, void* f, float* beta, float* c, void* stream) {
+    kd_status st = check_desc(d, true);
+    if (st != KD_OK) return st;
+    st = check_mixer(d, p, true, false);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d), gb = ntok * sizeof(float);
+    if (ntok == 0) return KD_OK;
+    const void* ptrs[] = {q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, q, k, v, f, beta, c};
+    for (const void* x : ptrs)
+        if (!x) return KD_ERR_NULL;
+    for (const void* x : ptrs)
+        if (misaligned(x)) return KD_ERR_ALIGN;
+    const size_t hd = (size_t)d->H * d->dk * p->conv_size * sizeof(float);
+    const Range ins[] = {range_of(q_raw, xb), range_of(k_raw, xb), range_of(v_raw, xb), range_of(f_raw, xb),
+                         range_of(beta_raw, gb), range_of(c_raw, gb), range_of(p->conv_q, hd),
+                         range_of(p->conv_k, hd), range_of(p->conv_v, hd),
+                         range_of(p->a_log, (size_t)d->H * sizeof(float))};
+    const Range outs[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb), range_of(beta, gb),
+                          range_of(c, gb)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return KD_ERR_ALIAS;
+    const void* raw[4] = {q_raw, k_raw, v_raw, f_raw};
+    void* out[4] = {q, k, v, f};
+    const float* conv[3] = {p->conv_q, p->conv_k, p->conv_v};
+    hipError_t e = kd::launch_mixer_pre(d->dtype == KD_BF16, d->dk, raw, out, conv, p->conv_size, p->a_log,
+                                        beta_raw, c_raw, p->beta_scale, beta, c, d->B, d->T, d->H,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+kd_status kron_delta_mixer_post(const kd_desc* d, const kd_mixer_params* p, const void* o, const void* g,
+                                void* y, void* stream) {
+    kd_status st = check_desc(d, true);
+    if (st != KD_OK) return st;
+    st = check_mixer(d, p, false, true);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dv * esize(d);
+    if (ntok == 0) return KD_OK;
+    if (!o || !g || !y) return KD_ERR_NULL;
+    if (misaligned(o) || misaligned(g) || misaligned(y)) return KD_ERR_ALIGN;
+    const Range ry = range_of(y, xb);
+    if (overlap(ry, range_of(o, xb)) || overlap(ry, range_of(g, xb)) ||
+        overlap(ry, range_of(p->norm_w, (size_t)d->H * d->dv * sizeof(float))))
+        return KD_ERR_ALIAS;
+    hipError_t e = kd::launch_mixer_post(d->dtype == KD_BF16, d->dv, o, g, p->norm_w, p->norm_eps, y, d->B, d->T,
+                                         d->H, (hipStream_t)stream);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+kd_status kron_delta_mixer_fwd(const kd_desc* d, const kd_mixer_params* p, const void* q_raw, const void* k_raw,
+                               const void* v_raw, const void* f_raw, const float* beta_raw, const float* c_raw,
+                               const void* g, const float* S0, void* y, float* ST, void* ws, size_t ws_bytes,
+                               void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    st = check_mixer(d, p, true, true);
+    if (st != KD_OK) return st;
+    const size_t ntok = (size_t)d->B * d->T * d->H;
+    const size_t xb = ntok * d->dk * esize(d), gb = ntok * sizeof(float);
+    const size_t sb = (size_t)d->B * d->H * d->dv * d->dk * sizeof(float);
+    const MixWs L = mixer_ws(d);
+    if (ntok > 0 && (!q_raw || !k_raw || !v_raw || !f_raw || !beta_raw || !c_raw || !g || !y)) return KD_ERR_NULL;
+    const void* ptrs[] = {q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, g, S0, y, ST, ws};
+    for (const void* x : ptrs)
+        if (misaligned(x)) return KD_ERR_ALIGN;
+    if (ntok > 0 && (!ws || ws_bytes < L.total)) return KD_ERR_WORKSPACE;
+    const size_t hd = (size_t)d->H * d->dk * p->conv_size * sizeof(float);
+    const Range ins[] = {range_of(q_raw, xb), range_of(k_raw, xb), range_of(v_raw, xb), range_of(f_raw, xb),
+                         range_of(beta_raw, gb), range_of(c_raw, gb), range_of(g, xb), range_of(S0, S0 ? sb : 0),
+                         range_of(p->conv_q, hd), range_of(p->conv_k, hd), range_of(p->conv_v, hd),
+                         range_of(p->a_log, (size_t)d->H * sizeof(float)),
+                         range_of(p->norm_w, (size_t)d->H * d->dv * sizeof(float))};
+    const Range outs[] = {range_of(y, ntok ? xb : 0), range_of(ST, ST ? sb : 0),
+                          range_of(ws, ntok ? L.total : 0)};
+    for (const Range& a : outs)
+        for (const Range& b : ins)
+            if (overlap(a, b)) return KD_ERR_ALIAS;
+    if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return KD_ERR_ALIAS;
+    if (ntok == 0) {
+        if (!ST) return KD_OK;
+        hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      nullptr, S0, nullptr, ST, nullptr, nullptr, d->B, d->T, d->H,
+                                      (hipStream_t)stream);
+        return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+    }
+    char* wb = static_cast<char*>(ws);
+    void* x[4];
+    for (int i = 0; i < 4; ++i) x[i] = wb + L.x[i];
+    float* beta = reinterpret_cast<float*>(wb + L.beta);
+    float* c = reinterpret_cast<float*>(wb + L.c);
+    void* o = wb + L.o;
+    const void* raw[4] = {q_raw, k_raw, v_raw, f_raw};
+    const float* conv[3] = {p->conv_q, p->conv_k, p->conv_v};
+    const hipStream_t sm = (hipStream_t)stream;
+    const int bf = d->dtype == KD_BF16;
+    hipError_t e = kd::launch_mixer_pre(bf, d->dk, raw, x, conv, p->conv_size, p->a_log, beta_raw, c_raw,
+                                        p->beta_scale, beta, c, d->B, d->T, d->H, sm);
+    if (e == hipSuccess)
+        e = kd::launch_fwd(bf, d->dk, x[0], x[1], x[2], x[3], beta, c, S0, o, ST, nullptr, nullptr, d->B, d->T,
+                           d->H, sm);
+    if (e == hipSuccess)
+        e = kd::launch_mixer_post(bf, d->dv, o, g, p->norm_w, p->norm_eps, y, d->B, d->T, d->H, sm);
+    return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+

@@ -32,6 +32,19 @@ summary, sections 방법론 and 기술 상세), same generator and order:
   5. S0 ~ N(0, s0_std^2) of shape [B, H, dk, dv] (only when s0_std is given).
 q, k, v, alpha, b, w are rounded to the workload's dtype.
 
+Mixer inputs (``draw_mixer``: the projections and parameters that the
+mixer's pre- and post-processing take; KronLSTM summary page, section "how it
+is used"), same generator, this order:
+  1. q_raw, k_raw, v_raw ~ N(0, 1) of shape [B, T, H, d].
+  2. f_raw ~ N(mu, 1) of shape [B, T, H, dk]; a_log ~ U(-1, 1) of shape [H].
+  3. beta_raw, c_raw ~ N(0, 1) of shape [B, T, H].
+  4. g ~ N(0, 1) of shape [B, T, H, dv] (output-gate logits).
+  5. conv_q, conv_k, conv_v ~ N(0, 1/K) of shape [H, d, K] (K = conv_size).
+  6. norm_w = 1 + 0.1 N(0, 1) of shape [H, dv].
+  7. S0 ~ N(0, s0_std^2) of shape [B, H, dv, dk] (only when s0_std is given).
+The projections and g are rounded to the workload's dtype; the rest stays
+fp32 (conv taps, a_log and norm_w are rounded to fp32).
+
 These seeded draws stand in for real activations: the pages measure on
 FineWeb-Edu language-model training, for which no data or weights exist here.
 """
@@ -57,6 +70,7 @@ class Workload:
     backward: bool = False
     decode: bool = False   # token-by-token on a carried state (S0 drawn, N(0, 0.1^2))
     gdn2: bool = False     # the Gated Delta Rule-2 variant (decoupled erase and write)
+    mixer: bool = False    # from the projections: pre-processing, the rule, gated RMSNorm
 
     @property
     def tokens(self) -> int:
@@ -79,7 +93,11 @@ WORKLOADS = {
     "decode_step": Workload("decode_step", 32, 1, 16, 128, 128, "bf16", seed=1005, decode=True),
     # Gated Delta Rule-2 at the training-step shape (decoupled erase and write).
     "gdn2_step": Workload("gdn2_step", 8, 2048, 16, 128, 128, "bf16", seed=1006, gdn2=True),
+    # The whole mixer forward at the training-step shape, from the projections.
+    "mixer_step": Workload("mixer_step", 8, 2048, 16, 128, 128, "bf16", seed=1007, mixer=True),
 }
+
+MIXER_CONV_SIZE = 4
 
 
 def _sigmoid(x):
@@ -130,7 +148,29 @@ def draw_gdn2(B, T, H, dk, dv, seed, mu=3.0, s0_std=None):
     return out
 
 
+def draw_mixer(B, T, H, dk, dv, seed, mu=3.0, conv_size=MIXER_CONV_SIZE, s0_std=None):
+    """Mixer inputs (fp64 projections before dtype rounding; fp32-exact parameters)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(q_raw=rng.standard_normal((B, T, H, dk)), k_raw=rng.standard_normal((B, T, H, dk)),
+               v_raw=rng.standard_normal((B, T, H, dv)))
+    out["f_raw"] = rng.normal(mu, 1.0, (B, T, H, dk))
+    out["a_log"] = rng.uniform(-1.0, 1.0, (H,))
+    out["beta_raw"] = rng.standard_normal((B, T, H))
+    out["c_raw"] = rng.standard_normal((B, T, H))
+    out["g"] = rng.standard_normal((B, T, H, dv))
+    for n, d in (("conv_q", dk), ("conv_k", dk), ("conv_v", dv)):
+        out[n] = rng.normal(0.0, 1.0 / np.sqrt(conv_size), (H, d, conv_size))
+    out["norm_w"] = 1.0 + 0.1 * rng.standard_normal((H, dv))
+    out["S0"] = rng.normal(0.0, s0_std, (B, H, dv, dk)) if s0_std is not None else None
+    for n in ("a_log", "beta_raw", "c_raw", "conv_q", "conv_k", "conv_v", "norm_w", "S0"):
+        if out[n] is not None:
+            out[n] = out[n].astype(np.float32).astype(np.float64)
+    return out
+
+
 def draw_workload(w: Workload, with_dO=None, s0_std=None):
+    if w.mixer:
+        return draw_mixer(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, s0_std=s0_std)
     if w.gdn2:
         return draw_gdn2(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, s0_std=s0_std)
     if s0_std is None and w.decode:
@@ -159,7 +199,7 @@ def rounded(inputs: dict, dtype: str) -> dict:
     for key, val in inputs.items():
         if val is None:
             out[key] = None
-        elif key in ("q", "k", "v", "f", "dO", "alpha", "b", "w"):
+        elif key in ("q", "k", "v", "f", "dO", "alpha", "b", "w", "q_raw", "k_raw", "v_raw", "f_raw", "g"):
             out[key] = round_to(val, dtype)
         else:
             out[key] = round_to(val, "fp32")

@@ -90,12 +90,16 @@ KD_API int kron_delta_abi_version(void);
 KD_API const char *kron_delta_status_string(int status);
 
 /*
- * Device workspace, in bytes, that kron_delta_fwd (with_backward = 0) or
- * kron_delta_bwd (with_backward = 1) needs for `desc`.  Returns 0 for an
- * invalid descriptor as well as when no workspace is needed; the forward
- * pass needs none.
+ * Device workspace, in bytes, that an entry point needs for `desc`:
+ * which = KD_WS_FWD (0) for kron_delta_fwd (none), KD_WS_BWD (1) for
+ * kron_delta_bwd / kron_delta_fwd_train / kron_delta_bwd_saved, KD_WS_MIXER
+ * (2) for kron_delta_mixer_fwd.  Returns 0 for an invalid descriptor or an
+ * unknown `which`, as well as when no workspace is needed.
  */
-KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int with_backward);
+#define KD_WS_FWD 0
+#define KD_WS_BWD 1
+#define KD_WS_MIXER 2
+KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int which);
 
 /*
  * Forward pass.  Reads q, k, v, f, beta, c and the initial state S0 (NULL
@@ -237,6 +241,73 @@ KD_API kd_status kron_delta_gdn2_fwd(const kd_desc *desc,
                          const void *q, const void *k, const void *v,
                          const void *alpha, const void *b, const void *w,
                          const float *S0, void *o, float *ST, void *stream);
+
+/*
+ * The KronLSTM mixer around the rule: what the onedev.kr KronLSTM summary
+ * (section "어떻게 쓰나") puts before and after it, and the review page
+ * (blog.secrett2633.cloud, KronLSTM review, section 3 and Figure 3) repeats
+ * for q, k, v:
+ *     q, k, v = L2norm(SiLU(causal depthwise conv(projection)))  per (t, h)
+ *     f       = sigmoid(f_raw)^exp(a_log[h])       (key-channel forget gate)
+ *     beta    = beta_scale * sigmoid(beta_raw),   c = sigmoid(c_raw)
+ *     y       = o / sqrt(mean_i o_i^2 + norm_eps) * norm_w[h] * sigmoid(g)
+ * with o the rule's read-out (kron_delta_fwd).  Readings where the pages are
+ * silent: the convolution has no bias and zero history before the first
+ * token, tap conv_size-1 acting on the current token, y_t = sum_tau
+ * w[tau] x_{t-(conv_size-1)+tau}; L2norm(x) = x / sqrt(sum x^2 + 1e-6);
+ * the gate multiplies the normalised read-out.  The output projection is a
+ * plain matrix product left to the caller.
+ */
+typedef struct {
+    const float *conv_q;   /* [H, dk, conv_size] fp32, channel (h, i) at (h*dk + i)*conv_size */
+    const float *conv_k;   /* [H, dk, conv_size] fp32 */
+    const float *conv_v;   /* [H, dv, conv_size] fp32 */
+    int32_t conv_size;     /* 1 .. 4 */
+    const float *a_log;    /* [H] fp32: forget-gate exponent a = exp(a_log) */
+    float beta_scale;      /* 1: beta in (0, 1); 2: the (0, 2) range of state tracking */
+    const float *norm_w;   /* [H, dv] fp32 RMSNorm weight (post-processing only) */
+    float norm_eps;        /* RMSNorm epsilon, >= 0 (post-processing only) */
+} kd_mixer_params;
+
+/*
+ * Pre-processing: q_raw, k_raw, f_raw [B, T, H, dk], v_raw [B, T, H, dv] in
+ * desc->dtype and beta_raw, c_raw [B, T, H] fp32 (the projections) to the
+ * rule's inputs q, k, f, v (desc->dtype) and beta, c (fp32), laid out as for
+ * kron_delta_fwd.  Uses conv_*, conv_size, a_log and beta_scale of `p`.
+ * Supported: dk == dv in {32, 64, 128}, bf16 or fp32, the size limits of
+ * kron_delta_fwd, and T <= 2^21, B <= 16383 (KD_ERR_SHAPE otherwise);
+ * conv_size in 1 .. 4 (KD_ERR_SHAPE).  Every parameter pointer the call
+ * uses must be non-NULL (KD_ERR_NULL) and 16-byte aligned (KD_ERR_ALIGN).
+ * Checks, ownership and stream behaviour as kron_delta_fwd.
+ */
+KD_API kd_status kron_delta_mixer_pre(const kd_desc *desc, const kd_mixer_params *p,
+                         const void *q_raw, const void *k_raw, const void *v_raw,
+                         const void *f_raw, const float *beta_raw, const float *c_raw,
+                         void *q, void *k, void *v, void *f, float *beta, float *c,
+                         void *stream);
+
+/*
+ * Post-processing: the gated per-head RMSNorm y of the read-out o, with the
+ * output-gate logits g; o, g, y are [B, T, H, dv] in desc->dtype.  Uses
+ * norm_w and norm_eps of `p`.  Shapes, checks and stream behaviour as
+ * kron_delta_mixer_pre.
+ */
+KD_API kd_status kron_delta_mixer_post(const kd_desc *desc, const kd_mixer_params *p,
+                         const void *o, const void *g, void *y, void *stream);
+
+/*
+ * The mixer forward from the projections: kron_delta_mixer_pre, then
+ * kron_delta_fwd (S0 NULL = zero; S_T returned when ST is non-NULL), then
+ * kron_delta_mixer_post, enqueued on `stream`.  ws must hold
+ * kron_delta_workspace_bytes(desc, KD_WS_MIXER) bytes (the rule's inputs
+ * and read-out between the steps) and overlap no tensor.  Shapes and
+ * dtypes as kron_delta_fwd (bf16 d in {32, 64, 128}, fp32 d in {32, 64}).
+ */
+KD_API kd_status kron_delta_mixer_fwd(const kd_desc *desc, const kd_mixer_params *p,
+                         const void *q_raw, const void *k_raw, const void *v_raw,
+                         const void *f_raw, const float *beta_raw, const float *c_raw,
+                         const void *g, const float *S0, void *y, float *ST,
+                         void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

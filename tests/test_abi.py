@@ -218,3 +218,70 @@ def test_training_pair_argument_checks(L):
     assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, None, need, None) == WORKSPACE
     assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, P(40), need - 1, None) == WORKSPACE
     assert L.kron_delta_bwd_saved(ctypes.byref(d), *pb, P(9), need, None) == ALIAS   # ws == dq
+
+
+def _mixer_params(conv_size=4, **over):
+    p = dict(conv_q=P(50), conv_k=P(51), conv_v=P(52), conv_size=conv_size, a_log=P(53), beta_scale=1.0,
+             norm_w=P(54), norm_eps=1e-5)
+    p.update(over)
+    return kd.KdMixerParams(**p)
+
+
+def test_mixer_argument_checks(L):
+    d = _desc(B=2, T=100, H=3, dk=128, dv=128)
+    pre_names = ["q_raw", "k_raw", "v_raw", "f_raw", "beta_raw", "c_raw", "q", "k", "v", "f", "beta", "c"]
+
+    def pre(desc, params=None, **over):
+        p = {n: P(i) for i, n in enumerate(pre_names)}
+        p.update(over)
+        prm = ctypes.byref(params if params is not None else _mixer_params())
+        return L.kron_delta_mixer_pre(ctypes.byref(desc), prm, *[p[n] for n in pre_names], None)
+
+    assert L.kron_delta_mixer_pre(ctypes.byref(d), None, *[P(i) for i in range(12)], None) == NULL
+    assert pre(d, _mixer_params(conv_size=5)) == SHAPE
+    assert pre(d, _mixer_params(conv_size=0)) == SHAPE
+    assert pre(d, _mixer_params(conv_k=None)) == NULL
+    assert pre(d, _mixer_params(a_log=P(53, misalign=4))) == ALIGN
+    assert pre(_desc(B=2, T=100, H=3, dk=48, dv=48)) == SHAPE
+    assert pre(_desc(B=2, T=1 << 22, H=1, dk=32, dv=32)) == SHAPE   # past the grid's token limit
+    assert pre(d, q=None) == NULL
+    assert pre(d, c=P(5, misalign=8)) == ALIGN
+    assert pre(d, q=P(0)) == ALIAS                        # q == q_raw
+    assert pre(d, beta=P(50)) == ALIAS                    # beta == conv_q
+    assert pre(d, k=P(6)) == ALIAS                        # k == q (two outputs)
+    assert pre(_desc(B=2, T=0, H=3, dk=128, dv=128)) == OK
+
+    def post(desc, params=None, **over):
+        p = {"o": P(0), "g": P(1), "y": P(2)}
+        p.update(over)
+        prm = ctypes.byref(params if params is not None else _mixer_params())
+        return L.kron_delta_mixer_post(ctypes.byref(desc), prm, p["o"], p["g"], p["y"], None)
+
+    assert post(d, _mixer_params(norm_w=None)) == NULL
+    assert post(d, _mixer_params(norm_eps=-1.0)) == SHAPE
+    assert post(d, y=P(0)) == ALIAS
+    assert post(d, y=P(54)) == ALIAS                      # y == norm_w
+    assert post(d, g=P(1, misalign=2)) == ALIGN
+    assert post(_desc(B=2, T=0, H=3, dk=128, dv=128)) == OK
+
+    need = L.kron_delta_workspace_bytes(ctypes.byref(d), kd.KD_WS_MIXER)
+    ntok = 2 * 100 * 3
+    assert need >= ntok * 128 * 2 * 5 + ntok * 4 * 2      # q, k, v, f, o and beta, c
+    assert L.kron_delta_workspace_bytes(ctypes.byref(d), 7) == 0
+    fwd_names = ["q_raw", "k_raw", "v_raw", "f_raw", "beta_raw", "c_raw", "g", "S0", "y", "ST"]
+
+    def mfwd(desc, params=None, ws=P(40), ws_bytes=None, **over):
+        p = {n: P(i) for i, n in enumerate(fwd_names)}
+        p.update(over)
+        prm = ctypes.byref(params if params is not None else _mixer_params())
+        return L.kron_delta_mixer_fwd(ctypes.byref(desc), prm, *[p[n] for n in fwd_names], ws,
+                                      need if ws_bytes is None else ws_bytes, None)
+
+    assert mfwd(d, ws=None) == WORKSPACE
+    assert mfwd(d, ws_bytes=need - 1) == WORKSPACE
+    assert mfwd(d, y=P(6)) == ALIAS                      # y == g
+    assert mfwd(d, ST=P(40)) == ALIAS                    # ST == workspace
+    assert mfwd(d, ws=P(3)) == ALIAS                     # workspace == f_raw
+    assert mfwd(d, _mixer_params(norm_w=None)) == NULL
+    assert mfwd(_desc(B=2, T=100, H=3, dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE
+    assert mfwd(_desc(B=2, T=0, H=3, dk=128, dv=128), ST=None) == OK
