@@ -102,6 +102,18 @@ def algorithmic_bytes_gdn2(w, esize):
     return ntok * (4 * w.dk + 2 * w.dv) * esize + ntok * w.dv * esize + w.B * w.H * w.dk * w.dv * 4
 
 
+def algorithmic_bytes_mixer(w, esize):
+    """HBM bytes of one mixer forward from the projections: q, k, f
+    projections (dk) and v projection, output-gate logits g (dv) once, the
+    beta and c logits (fp32) once, y once, S_T (fp32) once; the per-head
+    parameters (conv taps, a_log, norm weights) are under 0.1% and not
+    counted.  The rule's inputs and read-out between the steps are the
+    implementation's, not counted."""
+    ntok = w.B * w.T * w.H
+    return (ntok * (3 * w.dk + 2 * w.dv) * esize + 2 * ntok * 4 + ntok * w.dv * esize
+            + w.B * w.H * w.dv * w.dk * 4)
+
+
 def mfma_flops_gdn2(w):
     """MFMA flops of one Gated Delta Rule-2 launch as issued, per (b, h, chunk)
     of C = 64 at d = 128: Grams 2 x 10 tiles x 2*16*16*d; Ebar S0 and Qbar S0
@@ -140,6 +152,19 @@ def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
     for _ in range(max_passes):
         for b in range(w.B):
             sl = slice(b, b + 1)
+            if w.mixer:
+                from oracle import mixer as mx
+                q, k, v, f, beta, c = mx.mixer_pre(x_np["q_raw"][sl], x_np["k_raw"][sl], x_np["v_raw"][sl],
+                                                   x_np["f_raw"][sl], x_np["beta_raw"][sl], x_np["c_raw"][sl],
+                                                   x_np["conv_q"], x_np["conv_k"], x_np["conv_v"],
+                                                   x_np["a_log"])
+                o, _, _ = oracle.fwd(q, k, v, f, beta, c, None)
+                mx.rms_norm_gate(o, x_np["g"][sl], x_np["norm_w"], 1e-5)
+                nseq += 1
+                done_tok += w.T
+                if time.perf_counter() - t0 > budget_s:
+                    break
+                continue
             if w.gdn2:
                 oracle.gdn2_fwd(x_np["q"][sl], x_np["k"][sl], x_np["v"][sl], x_np["alpha"][sl],
                                 x_np["b"][sl], x_np["w"][sl], None)
@@ -164,7 +189,8 @@ def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
     return {"value": done_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "fp64 oracle %s on %d sequences (passes over the %d sequences of the "
                       "workload; T=%d, H=%d, d=%d), same seeded inputs, %.1f s wall"
-                      % ("Gated Delta Rule-2 forward" if w.gdn2 else
+                      % ("mixer forward (pre-processing, rule, gated RMSNorm)" if w.mixer else
+                         "Gated Delta Rule-2 forward" if w.gdn2 else
                          "forward + backward" if w.backward else "forward", nseq, w.B, w.T, w.H,
                          w.dk, dt)}
 
@@ -210,12 +236,24 @@ def main():
     dev = torch.device("cuda:0")
     x = sy.rounded(sy.draw_workload(w), w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    per_token = ("q", "k", "v", "f", "alpha", "b", "w")
-    t = {n: torch.tensor(x[n], dtype=tdt if n in per_token else torch.float32, device=dev)
-         for n in (("q", "k", "v", "alpha", "b", "w") if w.gdn2 else ("q", "k", "v", "f", "beta", "c"))}
+    per_token = ("q", "k", "v", "f", "alpha", "b", "w", "q_raw", "k_raw", "v_raw", "f_raw", "g")
+    names = (("q_raw", "k_raw", "v_raw", "f_raw", "beta_raw", "c_raw", "g", "conv_q", "conv_k", "conv_v",
+              "a_log", "norm_w") if w.mixer else
+             ("q", "k", "v", "alpha", "b", "w") if w.gdn2 else ("q", "k", "v", "f", "beta", "c"))
+    t = {n: torch.tensor(x[n], dtype=tdt if n in per_token else torch.float32, device=dev) for n in names}
     esize = 2 if w.dtype == "bf16" else 4
 
-    if w.gdn2:       # a step is one Gated Delta Rule-2 forward
+    if w.mixer:      # a step is one mixer forward from the projections
+        desc = kd.KdDesc(w.B, w.T, w.H, w.dk, w.dv, 1 if w.dtype == "bf16" else 0)
+        import ctypes
+        mws = torch.empty(max(int(kd.lib().kron_delta_workspace_bytes(ctypes.byref(desc), kd.KD_WS_MIXER)), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def step():
+            return kd.mixer_fwd(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"], t["c_raw"], t["g"],
+                                t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"], t["norm_w"], None,
+                                norm_eps=1e-5, workspace=mws)
+    elif w.gdn2:     # a step is one Gated Delta Rule-2 forward
         def step():
             return kd.gdn2_fwd(t["q"], t["k"], t["v"], t["alpha"], t["b"], t["w"], None)
     elif w.decode:   # a step is one decode call, the state updated in place
@@ -257,7 +295,8 @@ def main():
 
     tokens = w.B * w.T
     value = tokens / (ms_per_step * 1e-3)
-    abytes = (algorithmic_bytes_gdn2(w, esize) if w.gdn2 else
+    abytes = (algorithmic_bytes_mixer(w, esize) if w.mixer else
+              algorithmic_bytes_gdn2(w, esize) if w.gdn2 else
               algorithmic_bytes_decode(w, esize) if w.decode else
               algorithmic_bytes_fwd_bwd(w, esize) if w.backward else algorithmic_bytes(w, esize))
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
@@ -266,7 +305,9 @@ def main():
     traffic = stored_traffic() if args.workload == "train_step" else None
 
     out = {
-        "metric": ("Gated Delta Rule-2 chunked fwd tokens/s (H=16,d=128) and % HBM roofline"
+        "metric": ("KronLSTM mixer fwd (pre + rule + gated RMSNorm) tokens/s (H=16,d=128) and % HBM roofline"
+                   if w.mixer else
+                   "Gated Delta Rule-2 chunked fwd tokens/s (H=16,d=128) and % HBM roofline"
                    if w.gdn2 else
                    "Kron-delta decode tokens/s (H=16,d=128) and % HBM roofline" if w.decode else
                    "Kron-delta chunked fwd+bwd tokens/s (H=16,d=128) and % HBM roofline"
@@ -281,11 +322,20 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": ("synthetic (seeded: L2-normalised N(0,1) q,k,v; alpha=exp(-exp(U(-1,1)) "
+        "data": ("synthetic (seeded: N(0,1) q/k/v projections, beta/c/output-gate logits; f logits "
+                 "N(%g,1), a_log U(-1,1); conv taps N(0,1/%d); norm weights 1+0.1N(0,1))"
+                 % (w.mu, sy.MIXER_CONV_SIZE)) if w.mixer else
+                ("synthetic (seeded: L2-normalised N(0,1) q,k,v; alpha=exp(-exp(U(-1,1)) "
                  "softplus(-N(%g,1))); b,w=sigmoid(N(0,1)) per channel)" % w.mu) if w.gdn2 else
                 "synthetic (seeded: L2-normalised N(0,1) q,k,v; f=sigmoid(N(%g,1))^exp(U(-1,1)); "
                 "beta,c=sigmoid(N(0,1)))" % w.mu,
-        "config": {"workload": ("%s: Gated Delta Rule-2 (decoupled erase and write) chunked "
+        "config": {"workload": ("%s: KronLSTM mixer forward from the projections (causal depthwise "
+                                "conv K=%d, SiLU, L2 norm, gates; the Kronecker delta rule, chunk 64; "
+                                "gated per-head RMSNorm), B=%d T=%d H=%d dk=dv=%d, %s projections, "
+                                "fp32 gate logits and state, S0=0"
+                                % (w.name, sy.MIXER_CONV_SIZE, w.B, w.T, w.H, w.dk, w.dtype))
+                               if w.mixer else
+                               ("%s: Gated Delta Rule-2 (decoupled erase and write) chunked "
                                 "forward, B=%d T=%d H=%d dk=dv=%d, chunk 64, %s q/k/v/alpha/b/w, "
                                 "fp32 state, S0=0" % (w.name, w.B, w.T, w.H, w.dk, w.dtype))
                                if w.gdn2 else
@@ -300,7 +350,9 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_gdn2_kernel" if w.gdn2 else
+                     "kernel": "kd_mixer_pre_kernel + kd_fwd16_kernel<false> + kd_mixer_post_kernel"
+                     if w.mixer else
+                     "kd_gdn2_kernel" if w.gdn2 else
                      "kd_decode_kernel<bf16,128>" if w.decode else
                      "kd_fwd16_kernel<false>" if not w.backward else
                      "kd_fwd16_kernel(ckpt) + kd_bwd_fused_kernel",
@@ -308,7 +360,31 @@ def main():
                      "algorithmic_bytes_per_launch": abytes,
                      },
     }
-    if not w.backward and not w.decode:
+    if w.mixer:   # the three steps timed on their own (events, 10 launches each)
+        q, k, v, f, beta, c = kd.mixer_pre(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"],
+                                           t["c_raw"], t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"])
+        o, _ = kd.fwd(q, k, v, f, beta, c, None)
+        parts = {"pre": lambda: kd.mixer_pre(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"],
+                                             t["c_raw"], t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"]),
+                 "rule": lambda: kd.fwd(q, k, v, f, beta, c, None),
+                 "post": lambda: kd.mixer_post(o, t["g"], t["norm_w"], norm_eps=1e-5)}
+        part_bytes = {"pre": w.B * w.T * w.H * (4 * w.dk * esize * 2 + 4 * 4),
+                      "rule": algorithmic_bytes(w, esize),
+                      "post": w.B * w.T * w.H * w.dv * esize * 3}
+        out["steps"] = {}
+        for name, fn in parts.items():
+            fn()
+            torch.cuda.synchronize()
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(10):
+                fn()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ms = a_.elapsed_time(b_) / 10
+            out["steps"][name] = {"ms": ms, "hbm_frac": part_bytes[name] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not w.backward and not w.decode and not w.mixer:
         out["roofline"]["mfma_tflops"] = flops / (kernel_ms * 1e-3) / 1e12
         out["roofline"]["mfma_frac"] = flops / (kernel_ms * 1e-3) / 1e12 / peak_tf
     if args.cold:

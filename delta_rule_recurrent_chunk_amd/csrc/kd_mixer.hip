@@ -3,21 +3,20 @@
 //   pre:  q, k, v = L2norm(SiLU(short causal depthwise conv(projection)))
 //         f = sigmoid(x)^exp(a_log[h]),  beta = beta_scale * sigmoid(.),  c = sigmoid(.)
 //   post: y = o / sqrt(mean o^2 + eps) * w[h] * sigmoid(g)      (per head)
-// Both are row-wise and bound by HBM: one pass over their inputs and outputs.
-//
-// Layout of a launch: a thread owns eight adjacent channels of one head (a
-// 16-byte bf16 segment) and walks MIX_TT consecutive tokens, so the
-// convolution's window of earlier tokens stays in registers and each raw
-// element is read once (plus MIX_KMAX - 1 tokens of history per walk).  The
-// D/8 lanes of a row are adjacent, so a wave reads whole rows of adjacent
-// heads (one contiguous run per token) and sums a row with lane shuffles.
+// All three kernels are row-wise and bound by HBM: one pass over their inputs
+// and outputs.  A lane owns eight adjacent channels of a row (16 bytes of
+// bf16); the D/8 lanes of a row are adjacent, so a row's sum of squares is a
+// few DPP lane moves, and a wave reads whole 256-byte rows.
 #include <hip/hip_runtime.h>
 
 #include "kd_device.h"
 
 namespace kd {
 
-constexpr int MIX_TT = 32;     // tokens walked by one thread
+constexpr int MIX_TT = 32;     // tokens walked by one thread (post-processing)
+constexpr int MIX_TB = 8;      // tokens whose loads are in flight together
+constexpr int MIX_CT = 64;     // tokens of one convolution block
+constexpr int MIX_GB = 4;      // 16-byte pieces of f per thread
 constexpr int MIX_NT = 256;    // threads per block
 constexpr int MIX_KMAX = 4;    // widest convolution
 constexpr float MIX_EPS_L2 = 1e-6f;
@@ -38,101 +37,157 @@ struct MixPreArgs {
 __device__ __forceinline__ float mix_sigmoid(float x) {
     return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
-// softplus(z) = log(1 + e^z), without overflow for large z
+// softplus(z) = log(1 + e^z) = max(z, 0) + log(1 + e^-|z|), without overflow.
+// The hardware log of 1 + u loses u below fp32's spacing at 1; there the
+// forget gate exp(-a softplus(-x)) is within that spacing of 1 anyway.
 __device__ __forceinline__ float mix_softplus(float z) {
-    return fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z)));
+    return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
 }
 
-// sum over the LPR adjacent lanes of a row (LPR a power of two <= 16)
+template <int CTRL>
+__device__ __forceinline__ float mix_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the LPR adjacent lanes of a row (LPR in {4, 8, 16}, rows aligned
+// to LPR lanes), on DPP lane moves: the partner quad lane, the other quad of
+// the 8-lane half row (half-row mirror), the other half of the 16-lane row
+// (row mirror)
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m, 64);
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "rows of 4, 8 or 16 lanes");
+    x += mix_dpp<0xB1>(x);                   // quad_perm(1, 0, 3, 2): lane ^ 1
+    x += mix_dpp<0x4E>(x);                   // quad_perm(2, 3, 0, 1): lane ^ 2
+    if (LPR >= 8) x += mix_dpp<0x141>(x);    // row_half_mirror
+    if (LPR >= 16) x += mix_dpp<0x140>(x);   // row_mirror
     return x;
 }
 
-template <class E, int D>
-__global__ __launch_bounds__(MIX_NT) void kd_mixer_pre_kernel(MixPreArgs a, int T, int H) {
-    constexpr int LPR = D / 8;   // lanes per row
-    static_assert(MIX_NT % LPR == 0, "a block holds whole rows");
-    const int z = blockIdx.z & 3, b = blockIdx.z >> 2;
-    const int lin = blockIdx.x * MIX_NT + threadIdx.x;
-    const int h = lin / LPR, o8 = lin % LPR;
-    // rows past the last head leave as a whole (all their lanes), so every
-    // shuffle below reads lanes of its own, active row
-    if (h >= H) return;
-    const int t0 = blockIdx.y * MIX_TT;
-    const int t1 = min(t0 + MIX_TT, T);
+// q, k, v: one block per (b, h, tensor) and MIX_CT consecutive tokens.  The
+// block stages the raw rows of its tokens and the K - 1 before them, and the
+// head's taps, in LDS (one coalesced pass), then each row of D/8 lanes makes
+// one output token from K staged rows: convolution, SiLU, the row's sum of
+// squares on DPP lane moves, the scale, one 16-byte store per lane.
+template <class E, int D, int K>
+__global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int T, int H) {
+    constexpr int LPR = D / 8;                  // lanes per row
+    constexpr int TPP = MIX_NT / LPR;           // tokens per pass
+    constexpr int ROWS = MIX_CT + K - 1;
+    constexpr int PPR = D * (int)sizeof(E) / 16; // 16-byte pieces per row
+    static_assert(D * K <= 4 * MIX_NT, "one float4 of taps per thread");
+    __shared__ __align__(16) E st[ROWS * D];
+    __shared__ __align__(16) float sw[D * K];   // taps of (h, channel i) at i*K
+    const int z = blockIdx.z % 3, b = blockIdx.z / 3, h = blockIdx.y;
+    const int t0 = blockIdx.x * MIX_CT;
     const uint32_t rs = (uint32_t)H * D;   // token stride (elements); one batch element fits 2^31 bytes
-    const size_t bbase = (size_t)b * T * rs;
-    const uint32_t off = (uint32_t)h * D + 8 * o8;
-    const E* src = static_cast<const E*>(a.raw[z]) + bbase + off;
-    E* dst = static_cast<E*>(a.out[z]) + bbase + off;
-
-    if (z == 3) {   // forget gate, and the head's scalar gates on the row's first lane
-        const float ex = __expf(a.a_log[h]);
-#pragma unroll 4
-        for (int t = t0; t < t1; ++t) {
-            float x[8];
-            ld8f(src + (uint32_t)t * rs, x);
+    const size_t base = (size_t)b * T * rs + (size_t)h * D;
+    const E* __restrict__ src = static_cast<const E*>(a.raw[z]) + base;
+    E* __restrict__ dst = static_cast<E*>(a.out[z]) + base;
+    const int tid = threadIdx.x;
+    // stage rows t0 - (K-1) .. t0 + MIX_CT - 1 (zero before the first token;
+    // rows past the last token are never read) and the taps: every load is
+    // issued before the first LDS store
+    constexpr int NPC = (ROWS * PPR + MIX_NT - 1) / MIX_NT;
+    uint4 pcs[NPC];
+    floatx4 tw = {0.f, 0.f, 0.f, 0.f};
+    if (tid < D * K / 4) tw = reinterpret_cast<const floatx4*>(a.conv[z] + (size_t)h * D * K)[tid];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __expf(-ex * mix_softplus(-x[e]));
-            st8(dst + (uint32_t)t * rs, x);
-            if (o8 == 0) {
-                const size_t gi = ((size_t)b * T + t) * H + h;
-                a.beta[gi] = a.beta_scale * mix_sigmoid(a.beta_raw[gi]);
-                a.c[gi] = mix_sigmoid(a.c_raw[gi]);
-            }
-        }
-        return;
+    for (int i = 0; i < NPC; ++i) {
+        const int x = tid + i * MIX_NT;
+        const int r = x / PPR, pc = x % PPR;
+        const int t = t0 - (K - 1) + r;
+        pcs[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (x < ROWS * PPR && t >= 0 && t < T)
+            pcs[i] = *reinterpret_cast<const uint4*>(src + (uint32_t)t * rs + pc * (16 / sizeof(E)));
     }
-
-    // taps, aligned right: wt[e][j] multiplies the token t - (MIX_KMAX - 1) + j
-    const int K = a.K;
-    float wt[8][MIX_KMAX];
-    const float* cw = a.conv[z] + ((size_t)h * D + 8 * o8) * K;
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+        const int x = tid + i * MIX_NT;
+        if (x < ROWS * PPR)
+            *reinterpret_cast<uint4*>(&st[(x / PPR) * D + (x % PPR) * (16 / sizeof(E))]) = pcs[i];
+    }
+    if (tid < D * K / 4) reinterpret_cast<floatx4*>(sw)[tid] = tw;
+    __syncthreads();
+    // taps of this lane's eight channels: wt[e][j] multiplies the token t - (K-1) + j
+    const int o8 = tid % LPR, slot = tid / LPR;
+    float wt[8][K];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int j = 0; j < MIX_KMAX; ++j) {
-            const int tau = j - (MIX_KMAX - K);
-            wt[e][j] = tau >= 0 ? cw[e * K + tau] : 0.f;
-        }
-    // the window: raw rows of tokens t-3, t-2, t-1 (zero before the first token)
-    float win[MIX_KMAX - 1][8];
+        for (int j = 0; j < K; ++j) wt[e][j] = sw[(8 * o8 + e) * K + j];
 #pragma unroll
-    for (int j = 0; j < MIX_KMAX - 1; ++j) {
-        const int t = t0 - (MIX_KMAX - 1) + j;
-        if (t >= 0 && j >= MIX_KMAX - K) {
-            ld8f(src + (uint32_t)t * rs, win[j]);
-        } else {
+    for (int ps = 0; ps < MIX_CT / TPP; ++ps) {
+        const int r = ps * TPP + slot;   // output token t0 + r, staged rows r .. r + 3
+        const int t = t0 + r;
+        if (t >= T) break;               // the row's lanes leave together
+        float y[8], ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+        for (int e = 0; e < 8; ++e) y[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            float x[8];
+            ld8f(&st[(r + j) * D + 8 * o8], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = fmaf(wt[e][j], x[e], y[e]);
         }
-    }
-#pragma unroll 4
-    for (int t = t0; t < t1; ++t) {
-        float x[8], y[8];
-        ld8f(src + (uint32_t)t * rs, x);
-        float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float acc = wt[e][MIX_KMAX - 1] * x[e];
-#pragma unroll
-            for (int j = 0; j < MIX_KMAX - 1; ++j) acc = fmaf(wt[e][j], win[j][e], acc);
-            y[e] = acc * mix_sigmoid(acc);   // SiLU
+            y[e] = y[e] * mix_sigmoid(y[e]);   // SiLU
             ss = fmaf(y[e], y[e], ss);
         }
-#pragma unroll
-        for (int j = 0; j + 1 < MIX_KMAX - 1; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) win[j][e] = win[j + 1][e];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) win[MIX_KMAX - 2][e] = x[e];
         const float sc = rsqrtf(row_sum<LPR>(ss) + MIX_EPS_L2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] *= sc;
-        st8(dst + (uint32_t)t * rs, y);
+        st8(dst + (uint32_t)t * rs + 8 * o8, y);
+    }
+}
+
+// f, beta, c: elementwise.  Thread x of the grid takes MIX_GB 16-byte pieces
+// of f (x, x + n, ...; n threads in all), all loaded before any is computed,
+// and, while x < B*T*H / 4, four consecutive beta and c logits.
+template <class E>
+__global__ __launch_bounds__(MIX_NT) void kd_mixer_gate_kernel(MixPreArgs a, int D, int H, size_t ntok) {
+    const size_t n = (size_t)gridDim.x * MIX_NT;
+    const size_t x0 = (size_t)blockIdx.x * MIX_NT + threadIdx.x;
+    const size_t npc = ntok * (size_t)D / 8;   // pieces of f
+    const E* __restrict__ src = static_cast<const E*>(a.raw[3]);
+    E* __restrict__ dst = static_cast<E*>(a.out[3]);
+    float v[MIX_GB][8];
+    float ex[MIX_GB];
+#pragma unroll
+    for (int i = 0; i < MIX_GB; ++i) {
+        const size_t pc = x0 + i * n;
+        if (pc < npc) ld8f(src + pc * 8, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MIX_GB; ++i) {
+        const size_t pc = x0 + i * n;
+        // head of the piece: each token holds H rows of D, so h = (piece / (D/8)) mod H
+        ex[i] = pc < npc ? __expf(a.a_log[(pc / (size_t)(D / 8)) % (size_t)H]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < MIX_GB; ++i) {
+        const size_t pc = x0 + i * n;
+        if (pc >= npc) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = __expf(-ex[i] * mix_softplus(-v[i][e]));
+        st8(dst + pc * 8, v[i]);
+    }
+    if (x0 < ntok / 4) {   // beta and c: four per thread, the last ntok mod 4 below
+        const floatx4 br = reinterpret_cast<const floatx4*>(a.beta_raw)[x0];
+        const floatx4 cr = reinterpret_cast<const floatx4*>(a.c_raw)[x0];
+        floatx4 bo, co;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bo[e] = a.beta_scale * mix_sigmoid(br[e]);
+            co[e] = mix_sigmoid(cr[e]);
+        }
+        reinterpret_cast<floatx4*>(a.beta)[x0] = bo;
+        reinterpret_cast<floatx4*>(a.c)[x0] = co;
+    }
+    if (x0 < ntok % 4) {   // the last ntok % 4 gates
+        const size_t g = ntok / 4 * 4 + x0;
+        a.beta[g] = a.beta_scale * mix_sigmoid(a.beta_raw[g]);
+        a.c[g] = mix_sigmoid(a.c_raw[g]);
     }
 }
 
@@ -142,46 +197,70 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_post_kernel(const E* __restri
                                                                E* __restrict__ y, int T, int H) {
     constexpr int LPR = D / 8;
     const int b = blockIdx.z;
-    const int lin = blockIdx.x * MIX_NT + threadIdx.x;
+    const int lin = blockIdx.y * MIX_NT + threadIdx.x;
     const int h = lin / LPR, o8 = lin % LPR;
-    if (h >= H) return;   // whole rows, as in the pre kernel
-    const int t0 = blockIdx.y * MIX_TT;
+    // rows past the last head leave as a whole (all their lanes), so every
+    // lane move of row_sum reads lanes of its own, active row
+    if (h >= H) return;
+    const int t0 = blockIdx.x * MIX_TT;
     const int t1 = min(t0 + MIX_TT, T);
     const uint32_t rs = (uint32_t)H * D;
     const size_t bbase = (size_t)b * T * rs;
     const uint32_t off = (uint32_t)h * D + 8 * o8;
     float wv[8];
     ld8f(w + (size_t)h * D + 8 * o8, wv);
-#pragma unroll 4
-    for (int t = t0; t < t1; ++t) {
-        float x[8], gv[8];
-        ld8f(o + bbase + (uint32_t)t * rs + off, x);
-        ld8f(g + bbase + (uint32_t)t * rs + off, gv);
-        float ss = 0.f;
+    for (int tb = t0; tb < t1; tb += MIX_TB) {
+        float x[MIX_TB][8], gv[MIX_TB][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-        const float sc = rsqrtf(row_sum<LPR>(ss) * (1.f / D) + eps);
+        for (int i = 0; i < MIX_TB; ++i) {
+            const uint32_t r = (uint32_t)min(tb + i, t1 - 1) * rs + off;
+            ld8f(o + bbase + r, x[i]);
+            ld8f(g + bbase + r, gv[i]);
+        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = x[e] * sc * wv[e] * mix_sigmoid(gv[e]);
-        st8(y + bbase + (uint32_t)t * rs + off, x);
+        for (int i = 0; i < MIX_TB; ++i) {
+            const int t = tb + i;
+            if (t >= t1) break;
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(x[i][e], x[i][e], ss);
+            const float sc = rsqrtf(row_sum<LPR>(ss) * (1.f / D) + eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * sc * wv[e] * mix_sigmoid(gv[i][e]);
+            st8(y + bbase + (uint32_t)t * rs + off, x[i]);
+        }
     }
 }
 
 // ---------------------------------------------------------------- launchers
-static dim3 mix_grid(int B, int T, int H, int D, int zmul) {
-    const int rows_per_block = MIX_NT / (D / 8);
-    return dim3((unsigned)((H + rows_per_block - 1) / rows_per_block), (unsigned)((T + MIX_TT - 1) / MIX_TT),
-                (unsigned)(B * zmul));
+// grid limits of the launches (checked by the caller before any launch)
+bool mixer_grid_ok(int B, int H) {
+    return H <= 65535 && (long long)B * 3 <= 65535;
 }
 
-// grid limits of the two launches (checked by the caller before any launch)
-bool mixer_grid_ok(int B, int T) {
-    return (T + MIX_TT - 1) / MIX_TT <= 65535 && (long long)B * 4 <= 65535;
+template <class E, int D, int K>
+static void launch_conv_t(const MixPreArgs& a, int B, int T, int H, hipStream_t st) {
+    // token tiles vary fastest over the grid
+    hipLaunchKernelGGL((kd_mixer_conv_kernel<E, D, K>), dim3((unsigned)((T + MIX_CT - 1) / MIX_CT), (unsigned)H,
+                                                             (unsigned)(B * 3)),
+                       dim3(MIX_NT), 0, st, a, T, H);
 }
 
 template <class E, int D>
 static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, hipStream_t st) {
-    hipLaunchKernelGGL((kd_mixer_pre_kernel<E, D>), mix_grid(B, T, H, D, 4), dim3(MIX_NT), 0, st, a, T, H);
+    switch (a.K) {
+    case 1: launch_conv_t<E, D, 1>(a, B, T, H, st); break;
+    case 2: launch_conv_t<E, D, 2>(a, B, T, H, st); break;
+    case 3: launch_conv_t<E, D, 3>(a, B, T, H, st); break;
+    default: launch_conv_t<E, D, 4>(a, B, T, H, st); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t ntok = (size_t)B * T * H;
+    const size_t npc = ntok * D / 8;
+    const size_t threads = (npc + MIX_GB - 1) / MIX_GB;
+    hipLaunchKernelGGL((kd_mixer_gate_kernel<E>), dim3((unsigned)((threads + MIX_NT - 1) / MIX_NT)), dim3(MIX_NT),
+                       0, st, a, D, H, ntok);
     return hipGetLastError();
 }
 
@@ -217,7 +296,11 @@ hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* con
 template <class E, int D>
 static hipError_t launch_post_t(const void* o, const void* g, const float* w, float eps, void* y, int B, int T,
                                 int H, hipStream_t st) {
-    hipLaunchKernelGGL((kd_mixer_post_kernel<E, D>), mix_grid(B, T, H, D, 1), dim3(MIX_NT), 0, st,
+    const int rows_per_block = MIX_NT / (D / 8);
+    hipLaunchKernelGGL((kd_mixer_post_kernel<E, D>),
+                       dim3((unsigned)((T + MIX_TT - 1) / MIX_TT), (unsigned)((H + rows_per_block - 1) / rows_per_block),
+                            (unsigned)B),
+                       dim3(MIX_NT), 0, st,
                        (const E*)o, (const E*)g, w, eps, (E*)y, T, H);
     return hipGetLastError();
 }

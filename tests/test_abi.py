@@ -243,7 +243,7 @@ def test_mixer_argument_checks(L):
     assert pre(d, _mixer_params(conv_k=None)) == NULL
     assert pre(d, _mixer_params(a_log=P(53, misalign=4))) == ALIGN
     assert pre(_desc(B=2, T=100, H=3, dk=48, dv=48)) == SHAPE
-    assert pre(_desc(B=2, T=1 << 22, H=1, dk=32, dv=32)) == SHAPE   # past the grid's token limit
+    assert pre(_desc(B=21846, T=1, H=1, dk=32, dv=32)) == SHAPE     # past the grid's batch limit
     assert pre(d, q=None) == NULL
     assert pre(d, c=P(5, misalign=8)) == ALIGN
     assert pre(d, q=P(0)) == ALIAS                        # q == q_raw
