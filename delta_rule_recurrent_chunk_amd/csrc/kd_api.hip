@@ -27,7 +27,7 @@ hipError_t launch_gdn2(const void* q, const void* k, const void* v, const void* 
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
                          int B, int T, int H, hipStream_t st);
-bool mixer_grid_ok(int B, int H);
+bool mixer_grid_ok(int B, int T, int H);
 hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* const out[4],
                             const float* const conv[3], int K, const float* a_log, const float* beta_raw,
                             const float* c_raw, float beta_scale, float* beta, float* c, int B, int T, int H,
@@ -95,7 +95,7 @@ MixWs mixer_ws(const kd_desc* d) {
 // checks of the mixer's parameters: pre (conv, a_log) and/or post (norm_w)
 kd_status check_mixer(const kd_desc* d, const kd_mixer_params* p, bool pre, bool post) {
     if (!p) return KD_ERR_NULL;
-    if (!kd::mixer_grid_ok(d->B, d->H)) return KD_ERR_SHAPE;
+    if (!kd::mixer_grid_ok(d->B, d->T, d->H)) return KD_ERR_SHAPE;
     if (pre) {
         if (!p->conv_q || !p->conv_k || !p->conv_v || !p->a_log) return KD_ERR_NULL;
         if (p->conv_size < 1 || p->conv_size > 4) return KD_ERR_SHAPE;

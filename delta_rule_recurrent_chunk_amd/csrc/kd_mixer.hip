@@ -13,10 +13,9 @@
 
 namespace kd {
 
-constexpr int MIX_TT = 32;     // tokens walked by one thread (post-processing)
+constexpr int MIX_TT = 32;     // tokens walked by one thread (gates, post-processing)
 constexpr int MIX_TB = 8;      // tokens whose loads are in flight together
 constexpr int MIX_CT = 64;     // tokens of one convolution block
-constexpr int MIX_GB = 4;      // 16-byte pieces of f per thread
 constexpr int MIX_NT = 256;    // threads per block
 constexpr int MIX_KMAX = 4;    // widest convolution
 constexpr float MIX_EPS_L2 = 1e-6f;
@@ -141,53 +140,44 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int
     }
 }
 
-// f, beta, c: elementwise.  Thread x of the grid takes MIX_GB 16-byte pieces
-// of f (x, x + n, ...; n threads in all), all loaded before any is computed,
-// and, while x < B*T*H / 4, four consecutive beta and c logits.
-template <class E>
-__global__ __launch_bounds__(MIX_NT) void kd_mixer_gate_kernel(MixPreArgs a, int D, int H, size_t ntok) {
-    const size_t n = (size_t)gridDim.x * MIX_NT;
-    const size_t x0 = (size_t)blockIdx.x * MIX_NT + threadIdx.x;
-    const size_t npc = ntok * (size_t)D / 8;   // pieces of f
-    const E* __restrict__ src = static_cast<const E*>(a.raw[3]);
-    E* __restrict__ dst = static_cast<E*>(a.out[3]);
-    float v[MIX_GB][8];
-    float ex[MIX_GB];
+// f, beta, c: elementwise over the B*T token rows.  A lane owns eight
+// channels of one head and walks MIX_TT token rows, MIX_TB loads in flight at
+// a time; the first lane of a head's row also makes that row's beta and c.
+template <class E, int D>
+__global__ __launch_bounds__(MIX_NT) void kd_mixer_gate_kernel(MixPreArgs a, int BT, int H) {
+    constexpr int LPR = D / 8;
+    const int lin = blockIdx.y * MIX_NT + threadIdx.x;
+    const int h = lin / LPR, o8 = lin % LPR;
+    if (h >= H) return;
+    const int t0 = blockIdx.x * MIX_TT;
+    const int t1 = min(t0 + MIX_TT, BT);
+    const size_t rs = (size_t)H * D;
+    const E* __restrict__ src = static_cast<const E*>(a.raw[3]) + (size_t)h * D + 8 * o8;
+    E* __restrict__ dst = static_cast<E*>(a.out[3]) + (size_t)h * D + 8 * o8;
+    const float ex = __expf(a.a_log[h]);
+    for (int tb = t0; tb < t1; tb += MIX_TB) {
+        float x[MIX_TB][8], br[MIX_TB], cr[MIX_TB];
 #pragma unroll
-    for (int i = 0; i < MIX_GB; ++i) {
-        const size_t pc = x0 + i * n;
-        if (pc < npc) ld8f(src + pc * 8, v[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < MIX_GB; ++i) {
-        const size_t pc = x0 + i * n;
-        // head of the piece: each token holds H rows of D, so h = (piece / (D/8)) mod H
-        ex[i] = pc < npc ? __expf(a.a_log[(pc / (size_t)(D / 8)) % (size_t)H]) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < MIX_GB; ++i) {
-        const size_t pc = x0 + i * n;
-        if (pc >= npc) break;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][e] = __expf(-ex[i] * mix_softplus(-v[i][e]));
-        st8(dst + pc * 8, v[i]);
-    }
-    if (x0 < ntok / 4) {   // beta and c: four per thread, the last ntok mod 4 below
-        const floatx4 br = reinterpret_cast<const floatx4*>(a.beta_raw)[x0];
-        const floatx4 cr = reinterpret_cast<const floatx4*>(a.c_raw)[x0];
-        floatx4 bo, co;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bo[e] = a.beta_scale * mix_sigmoid(br[e]);
-            co[e] = mix_sigmoid(cr[e]);
+        for (int i = 0; i < MIX_TB; ++i) {
+            const size_t t = (size_t)min(tb + i, t1 - 1);
+            ld8f(src + t * rs, x[i]);
+            if (o8 == 0) {
+                br[i] = a.beta_raw[t * H + h];
+                cr[i] = a.c_raw[t * H + h];
+            }
         }
-        reinterpret_cast<floatx4*>(a.beta)[x0] = bo;
-        reinterpret_cast<floatx4*>(a.c)[x0] = co;
-    }
-    if (x0 < ntok % 4) {   // the last ntok % 4 gates
-        const size_t g = ntok / 4 * 4 + x0;
-        a.beta[g] = a.beta_scale * mix_sigmoid(a.beta_raw[g]);
-        a.c[g] = mix_sigmoid(a.c_raw[g]);
+#pragma unroll
+        for (int i = 0; i < MIX_TB; ++i) {
+            const int t = tb + i;
+            if (t >= t1) break;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = __expf(-ex * mix_softplus(-x[i][e]));
+            st8(dst + (size_t)t * rs, x[i]);
+            if (o8 == 0) {
+                a.beta[(size_t)t * H + h] = a.beta_scale * mix_sigmoid(br[i]);
+                a.c[(size_t)t * H + h] = mix_sigmoid(cr[i]);
+            }
+        }
     }
 }
 
@@ -234,8 +224,8 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_post_kernel(const E* __restri
 
 // ---------------------------------------------------------------- launchers
 // grid limits of the launches (checked by the caller before any launch)
-bool mixer_grid_ok(int B, int H) {
-    return H <= 65535 && (long long)B * 3 <= 65535;
+bool mixer_grid_ok(int B, int T, int H) {
+    return H <= 65535 && (long long)B * 3 <= 65535 && (long long)B * T <= 0x7fffffffLL;
 }
 
 template <class E, int D, int K>
@@ -256,11 +246,10 @@ static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, hipStre
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t ntok = (size_t)B * T * H;
-    const size_t npc = ntok * D / 8;
-    const size_t threads = (npc + MIX_GB - 1) / MIX_GB;
-    hipLaunchKernelGGL((kd_mixer_gate_kernel<E>), dim3((unsigned)((threads + MIX_NT - 1) / MIX_NT)), dim3(MIX_NT),
-                       0, st, a, D, H, ntok);
+    const int BT = B * T, rows_per_block = MIX_NT / (D / 8);
+    hipLaunchKernelGGL((kd_mixer_gate_kernel<E, D>),
+                       dim3((unsigned)((BT + MIX_TT - 1) / MIX_TT), (unsigned)((H + rows_per_block - 1) / rows_per_block)),
+                       dim3(MIX_NT), 0, st, a, BT, H);
     return hipGetLastError();
 }
 

@@ -275,7 +275,8 @@ typedef struct {
  * rule's inputs q, k, f, v (desc->dtype) and beta, c (fp32), laid out as for
  * kron_delta_fwd.  Uses conv_*, conv_size, a_log and beta_scale of `p`.
  * Supported: dk == dv in {32, 64, 128}, bf16 or fp32, the size limits of
- * kron_delta_fwd, and H <= 65535, B <= 21845 (KD_ERR_SHAPE otherwise);
+ * kron_delta_fwd, and H <= 65535, B <= 21845, B*T < 2^31 (KD_ERR_SHAPE
+ * otherwise);
  * conv_size in 1 .. 4 (KD_ERR_SHAPE).  Every parameter pointer the call
  * uses must be non-NULL (KD_ERR_NULL) and 16-byte aligned (KD_ERR_ALIGN).
  * Checks, ownership and stream behaviour as kron_delta_fwd.
