@@ -350,11 +350,11 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_mixer_pre_kernel + kd_fwd16_kernel<false> + kd_mixer_post_kernel"
+                     "kernel": "kd_mixer_conv_kernel + kd_fwd16_kernel<false, true> + kd_mixer_post_kernel"
                      if w.mixer else
                      "kd_gdn2_kernel" if w.gdn2 else
                      "kd_decode_kernel<bf16,128>" if w.decode else
-                     "kd_fwd16_kernel<false>" if not w.backward else
+                     "kd_fwd16_kernel<false, false>" if not w.backward else
                      "kd_fwd16_kernel(ckpt) + kd_bwd_fused_kernel",
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": abytes,

@@ -31,7 +31,10 @@ bool mixer_grid_ok(int B, int T, int H);
 hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* const out[4],
                             const float* const conv[3], int K, const float* a_log, const float* beta_raw,
                             const float* c_raw, float beta_scale, float* beta, float* c, int B, int T, int H,
-                            hipStream_t st);
+                            int gates, hipStream_t st);
+hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const void* f_raw,
+                              const float* beta_raw, const float* c_raw, const float* a_log, float beta_scale,
+                              const float* S0, void* o, float* ST, int B, int T, int H, hipStream_t st);
 hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
                              int B, int T, int H, hipStream_t st);
 }  // namespace kd
@@ -377,7 +380,7 @@ kd_status kron_delta_mixer_pre(const kd_desc* d, const kd_mixer_params* p, const
     void* out[4] = {q, k, v, f};
     const float* conv[3] = {p->conv_q, p->conv_k, p->conv_v};
     hipError_t e = kd::launch_mixer_pre(d->dtype == KD_BF16, d->dk, raw, out, conv, p->conv_size, p->a_log,
-                                        beta_raw, c_raw, p->beta_scale, beta, c, d->B, d->T, d->H,
+                                        beta_raw, c_raw, p->beta_scale, beta, c, d->B, d->T, d->H, 1,
                                         (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
@@ -448,11 +451,16 @@ kd_status kron_delta_mixer_fwd(const kd_desc* d, const kd_mixer_params* p, const
     const float* conv[3] = {p->conv_q, p->conv_k, p->conv_v};
     const hipStream_t sm = (hipStream_t)stream;
     const int bf = d->dtype == KD_BF16;
+    // bf16 at d = 128: the forward makes the gates from their logits as it
+    // loads them (the gate kernel's arithmetic, so the same bits)
+    const bool fused_gates = bf && d->dk == 128;
     hipError_t e = kd::launch_mixer_pre(bf, d->dk, raw, x, conv, p->conv_size, p->a_log, beta_raw, c_raw,
-                                        p->beta_scale, beta, c, d->B, d->T, d->H, sm);
+                                        p->beta_scale, beta, c, d->B, d->T, d->H, fused_gates ? 0 : 1, sm);
     if (e == hipSuccess)
-        e = kd::launch_fwd(bf, d->dk, x[0], x[1], x[2], x[3], beta, c, S0, o, ST, nullptr, nullptr, d->B, d->T,
-                           d->H, sm);
+        e = fused_gates ? kd::launch_fwd16_gates(x[0], x[1], x[2], f_raw, beta_raw, c_raw, p->a_log, p->beta_scale,
+                                                 S0, o, ST, d->B, d->T, d->H, sm)
+                        : kd::launch_fwd(bf, d->dk, x[0], x[1], x[2], x[3], beta, c, S0, o, ST, nullptr, nullptr,
+                                         d->B, d->T, d->H, sm);
     if (e == hipSuccess)
         e = kd::launch_mixer_post(bf, d->dv, o, g, p->norm_w, p->norm_eps, y, d->B, d->T, d->H, sm);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;

@@ -594,6 +594,21 @@ template <> struct Col16<float> {
 // Eight consecutive tokens of two adjacent channels ch0, ch0 + 1 (bf16): one
 // 4-byte load per row, so a wave whose lanes cover adjacent channel pairs
 // reads whole rows.
+// The mixer's gates (KronLSTM summary page, section on how the rule is used):
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)), and the forget gate
+// sigmoid(x)^a = 2^(-a log2(1 + 2^(-x log2 e))), on the hardware base-2 exp,
+// log and reciprocal.  Large negative x gives 1 + inf, so the gate is exactly
+// 0; large positive x gives log2(1) = 0, a gate within fp32's spacing of 1.
+// The pre-processing kernel and the forward's fused gates share these, so
+// both give the same bits.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float gate_sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * x));
+}
+__device__ __forceinline__ float forget_gate(float x, float a) {
+    return __builtin_amdgcn_exp2f(-a * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-kLog2e * x)));
+}
+
 struct Raw8x2 {
     uint32_t w[8];   // row e: channel ch0 in the low half, ch0 + 1 in the high half
     // p: wave-uniform base; row e at 32-bit element offset off + min(e, last)*stride.
@@ -611,6 +626,17 @@ struct Raw8x2 {
         w[e] = fb | (fb << 16);
     }
     __device__ __forceinline__ void store(__bf16* dst, int e) const { *reinterpret_cast<uint32_t*>(dst) = w[e]; }
+    // every value x replaced by fn(x), rounded to bf16 (nearest even)
+    template <class F>
+    __device__ __forceinline__ void map(F fn) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x2 r;
+            r[0] = (__bf16)fn(get(e, 0));
+            r[1] = (__bf16)fn(get(e, 1));
+            w[e] = __builtin_bit_cast(uint32_t, r);
+        }
+    }
     // max |x| over the 16 values
     __device__ __forceinline__ float absmax() const {
         typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -802,6 +828,14 @@ __device__ __forceinline__ void st8(float* p, const float* x) {
 
 // Per-chunk records that the checkpointing forward leaves for the backward,
 // each an array over (b, h, chunk) units in that order.
+// Gates computed inside the forward from their logits (the mixer path): f
+// holds forget-gate logits, beta and c the erase and write logits; then
+// f = forget_gate(f, exp(a_log[h])), beta = beta_scale * sigmoid, c = sigmoid.
+struct FwdGates {
+    const float* a_log;   // [H]
+    float beta_scale;
+};
+
 struct FwdCkpt {
     void* S;    // entering state S[i][j], input dtype, d*d per unit
     float* U;   // u, then r0: 2*CH fp32 per unit

@@ -65,13 +65,15 @@ struct Fwd16Smem {
 };
 
 // CKPT: also store, per chunk, the records of FwdCkpt: the entering state
-// (bf16), u and r0, and the chunk's M and P.
-template <bool CKPT>
+// (bf16), u and r0, and the chunk's M and P.  GATES: f, beta and c hold the
+// gates' logits, turned into the gates by the producers as they load them
+// (FwdGates).
+template <bool CKPT, bool GATES>
 __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
-    FwdCkpt ck, const int* __restrict__ cu, int T_, int H)
+    FwdCkpt ck, FwdGates gt, const int* __restrict__ cu, int T_, int H)
 {
     using namespace f16w;
     typedef Bf16T TR;
@@ -344,6 +346,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         Col8 keep_v[2], keep_kt[2];      // v and K-tilde of the prepared chunk, written
                                          //   transposed in the following stage A
         unsigned pmask = 0;              // fallback channels (bit cc: ch0 + cc)
+        const float gex = GATES ? __expf(gt.a_log[h]) : 0.f;   // forget-gate exponent
         // Rows past the sequence end re-read the last row (in bounds) and are
         // cleared before use.  Loads are unconditional (clamped to the last
         // chunk) so the prefetch registers never merge with older values.
@@ -447,6 +450,11 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
             }
             if (prod_on) {   // decay products of chunk nn
+                if (GATES) {   // the gates of chunk nn from their logits
+                    rf.map([&](float x) { return forget_gate(x, gex); });
+                    rb_beta = gt.beta_scale * gate_sigmoid(rb_beta);
+                    rb_c = gate_sigmoid(rb_c);
+                }
                 if (nn * CH + CH > T) {   // ragged last chunk: clear rows past the end
 #pragma unroll
                     for (int e = 0; e < RB; ++e)
@@ -607,13 +615,29 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void*
 {
     typedef __bf16 E;
     if (ck)
-        hipLaunchKernelGGL(kd_fwd16_kernel<true>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
+        hipLaunchKernelGGL((kd_fwd16_kernel<true, false>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           *ck, (const int*)nullptr, T, H);
+                           *ck, FwdGates{}, (const int*)nullptr, T, H);
     else
-        hipLaunchKernelGGL(kd_fwd16_kernel<false>, dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
+        hipLaunchKernelGGL((kd_fwd16_kernel<false, false>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           FwdCkpt{}, cu, T, H);
+                           FwdCkpt{}, FwdGates{}, cu, T, H);
+    return hipGetLastError();
+}
+
+// The forward with the gates made from their logits (f_raw [B,T,H,D] bf16,
+// beta_raw and c_raw [B,T,H] fp32) as the producers load them.
+hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const void* f_raw,
+                              const float* beta_raw, const float* c_raw, const float* a_log, float beta_scale,
+                              const float* S0, void* o, float* ST, int B, int T, int H, hipStream_t st)
+{
+    typedef __bf16 E;
+    FwdGates gt;
+    gt.a_log = a_log;
+    gt.beta_scale = beta_scale;
+    hipLaunchKernelGGL((kd_fwd16_kernel<false, true>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)f_raw, beta_raw, c_raw, S0, (E*)o, ST,
+                       FwdCkpt{}, gt, (const int*)nullptr, T, H);
     return hipGetLastError();
 }
 

@@ -33,16 +33,6 @@ struct MixPreArgs {
     int K;
 };
 
-__device__ __forceinline__ float mix_sigmoid(float x) {
-    return __builtin_amdgcn_rcpf(1.f + __expf(-x));
-}
-// softplus(z) = log(1 + e^z) = max(z, 0) + log(1 + e^-|z|), without overflow.
-// The hardware log of 1 + u loses u below fp32's spacing at 1; there the
-// forget gate exp(-a softplus(-x)) is within that spacing of 1 anyway.
-__device__ __forceinline__ float mix_softplus(float z) {
-    return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
-}
-
 template <int CTRL>
 __device__ __forceinline__ float mix_dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -130,7 +120,7 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            y[e] = y[e] * mix_sigmoid(y[e]);   // SiLU
+            y[e] = y[e] * gate_sigmoid(y[e]);   // SiLU
             ss = fmaf(y[e], y[e], ss);
         }
         const float sc = rsqrtf(row_sum<LPR>(ss) + MIX_EPS_L2);
@@ -171,11 +161,11 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_gate_kernel(MixPreArgs a, int
             const int t = tb + i;
             if (t >= t1) break;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = __expf(-ex * mix_softplus(-x[i][e]));
+            for (int e = 0; e < 8; ++e) x[i][e] = forget_gate(x[i][e], ex);
             st8(dst + (size_t)t * rs, x[i]);
             if (o8 == 0) {
-                a.beta[(size_t)t * H + h] = a.beta_scale * mix_sigmoid(br[i]);
-                a.c[(size_t)t * H + h] = mix_sigmoid(cr[i]);
+                a.beta[(size_t)t * H + h] = a.beta_scale * gate_sigmoid(br[i]);
+                a.c[(size_t)t * H + h] = gate_sigmoid(cr[i]);
             }
         }
     }
@@ -216,7 +206,7 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_post_kernel(const E* __restri
             for (int e = 0; e < 8; ++e) ss = fmaf(x[i][e], x[i][e], ss);
             const float sc = rsqrtf(row_sum<LPR>(ss) * (1.f / D) + eps);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * sc * wv[e] * mix_sigmoid(gv[i][e]);
+            for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * sc * wv[e] * gate_sigmoid(gv[i][e]);
             st8(y + bbase + (uint32_t)t * rs + off, x[i]);
         }
     }
@@ -237,7 +227,7 @@ static void launch_conv_t(const MixPreArgs& a, int B, int T, int H, hipStream_t 
 }
 
 template <class E, int D>
-static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, hipStream_t st) {
+static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, int gates, hipStream_t st) {
     switch (a.K) {
     case 1: launch_conv_t<E, D, 1>(a, B, T, H, st); break;
     case 2: launch_conv_t<E, D, 2>(a, B, T, H, st); break;
@@ -245,7 +235,7 @@ static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, hipStre
     default: launch_conv_t<E, D, 4>(a, B, T, H, st); break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !gates) return e;
     const int BT = B * T, rows_per_block = MIX_NT / (D / 8);
     hipLaunchKernelGGL((kd_mixer_gate_kernel<E, D>),
                        dim3((unsigned)((BT + MIX_TT - 1) / MIX_TT), (unsigned)((H + rows_per_block - 1) / rows_per_block)),
@@ -253,10 +243,11 @@ static hipError_t launch_pre_t(const MixPreArgs& a, int B, int T, int H, hipStre
     return hipGetLastError();
 }
 
+// gates = 0: q, k, v only (the forward then makes the gates from their logits)
 hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* const out[4],
                             const float* const conv[3], int K, const float* a_log, const float* beta_raw,
                             const float* c_raw, float beta_scale, float* beta, float* c, int B, int T, int H,
-                            hipStream_t st) {
+                            int gates, hipStream_t st) {
     if (T == 0) return hipSuccess;
     MixPreArgs a;
     for (int i = 0; i < 4; ++i) { a.raw[i] = raw[i]; a.out[i] = out[i]; }
@@ -270,15 +261,15 @@ hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* con
     a.K = K;
     if (bf16) {
         switch (d) {
-        case 32: return launch_pre_t<__bf16, 32>(a, B, T, H, st);
-        case 64: return launch_pre_t<__bf16, 64>(a, B, T, H, st);
-        default: return launch_pre_t<__bf16, 128>(a, B, T, H, st);
+        case 32: return launch_pre_t<__bf16, 32>(a, B, T, H, gates, st);
+        case 64: return launch_pre_t<__bf16, 64>(a, B, T, H, gates, st);
+        default: return launch_pre_t<__bf16, 128>(a, B, T, H, gates, st);
         }
     }
     switch (d) {
-    case 32: return launch_pre_t<float, 32>(a, B, T, H, st);
-    case 64: return launch_pre_t<float, 64>(a, B, T, H, st);
-    default: return launch_pre_t<float, 128>(a, B, T, H, st);
+    case 32: return launch_pre_t<float, 32>(a, B, T, H, gates, st);
+    case 64: return launch_pre_t<float, 64>(a, B, T, H, gates, st);
+    default: return launch_pre_t<float, 128>(a, B, T, H, gates, st);
     }
 }
 
