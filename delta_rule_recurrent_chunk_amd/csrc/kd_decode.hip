@@ -9,9 +9,12 @@
 // writing it once per call.
 //
 // One workgroup of 256 threads per (b, h).  The state lives in registers for
-// the whole call: thread t owns row i = t / TPR of S and a contiguous run of
-// CPT = d*d / 256 columns (TPR = 256 / d threads per row), read and written as
-// 16-byte vectors so each row's threads cover it with whole cache lines.
+// the whole call.  It is read and written in whole 4 KiB runs: load x of
+// thread t is the 16 bytes at float offset 4 (256 x + t), so one load
+// instruction of a wave covers 1 KiB of contiguous memory.  Thread t then holds
+// four adjacent columns 4 (t mod RL) .. of the rows (256 x + t) / RL, x < NV,
+// with RL = D / 4 lanes per row; a row's sums over its columns are
+// reductions over those RL adjacent lanes.
 #include "kd_device.h"
 
 namespace kd {
@@ -23,22 +26,23 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
     E* __restrict__ o, float* S_out, int T, int H)
 {
     constexpr int NT = 256;
-    constexpr int TPR = NT / D;          // threads per state row
-    constexpr int CPT = D / TPR;         // columns per thread
-    constexpr int NV = CPT / 4;          // float4 per thread
+    constexpr int RL = D / 4;             // lanes per state row
+    constexpr int RPX = NT / RL;          // rows per load step
+    constexpr int NV = D * D / (4 * NT);  // float4 per thread
     __shared__ float sq[D], sk[D], sf[D], sv[D];
-    __shared__ float red[2][NT / 64];    // per-wave partials of r and k.q
-    __shared__ float bc[2];              // beta_t, c_t
+    __shared__ float red[2][NT / 64];     // per-wave partials of r and k.q
+    __shared__ float bc[2];               // beta_t, c_t
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
-    const int i = tid / TPR, j0 = (tid % TPR) * CPT;   // row and first column
+    const int i0 = tid / RL, j0 = 4 * (tid % RL);   // first row, first column
+    const bool lead = tid % RL == 0;                  // counts its rows once
 
-    floatx4 S[NV];
-    const size_t sbase = (size_t)bh * D * D + (size_t)i * D + j0;
+    floatx4 S[NV];   // S[x] = S[i0 + RPX x][j0 .. j0 + 3]
+    const size_t sbase = (size_t)bh * D * D + 4 * (size_t)tid;
 #pragma unroll
     for (int x = 0; x < NV; ++x)
-        S[x] = S_in ? *reinterpret_cast<const floatx4*>(S_in + sbase + 4 * x) : floatx4{0.f, 0.f, 0.f, 0.f};
+        S[x] = S_in ? *reinterpret_cast<const floatx4*>(S_in + sbase + 4 * (size_t)NT * x) : floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int t = 0; t < T; ++t) {
         const size_t row = ((size_t)b * T + t) * H + h;   // token (b, t, h)
@@ -50,27 +54,29 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
         }
         if (tid == 0) { bc[0] = beta[row]; bc[1] = cc[row]; }
         __syncthreads();
-        // Sbar = S diag(f); partial y = Sbar k and z = Sbar q over this thread's columns
-        float y = 0.f, z = 0.f;
+        // Sbar = S diag(f); y = Sbar k and z = Sbar q of each held row, over its RL lanes
+        const floatx4 fj = *reinterpret_cast<const floatx4*>(&sf[j0]);
+        const floatx4 kj = *reinterpret_cast<const floatx4*>(&sk[j0]);
+        const floatx4 qj = *reinterpret_cast<const floatx4*>(&sq[j0]);
+        float y[NV], z[NV];
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
+            S[x] = S[x] * fj;
+            y[x] = S[x][0] * kj[0] + S[x][1] * kj[1] + S[x][2] * kj[2] + S[x][3] * kj[3];
+            z[x] = S[x][0] * qj[0] + S[x][1] * qj[1] + S[x][2] * qj[2] + S[x][3] * qj[3];
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 4 * x + e;
-                const float sb = S[x][e] * sf[j];
-                S[x][e] = sb;
-                y = fmaf(sb, sk[j], y);
-                z = fmaf(sb, sq[j], z);
+        for (int m = 1; m < RL; m <<= 1)
+#pragma unroll
+            for (int x = 0; x < NV; ++x) {
+                y[x] += __shfl_xor(y[x], m, 64);
+                z[x] += __shfl_xor(z[x], m, 64);
             }
-        }
-        // whole-row sums over the TPR threads of the row (adjacent lanes)
+        // r = sum_i v_i y_i (each row once, on its lead lane) and k.q
+        float pr = 0.f;
+        if (lead)
 #pragma unroll
-        for (int m = 1; m < TPR; m <<= 1) {
-            y += __shfl_xor(y, m, 64);
-            z += __shfl_xor(z, m, 64);
-        }
-        // r = sum_i v_i y_i and k.q, each counted once (row leaders, lanes < D)
-        float pr = (tid % TPR == 0) ? sv[i] * y : 0.f;
+            for (int x = 0; x < NV; ++x) pr = fmaf(sv[i0 + RPX * x], y[x], pr);
         float pk = (tid < D) ? sk[tid] * sq[tid] : 0.f;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
@@ -84,16 +90,16 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
         for (int ww = 0; ww < NT / 64; ++ww) { r += red[0][ww]; kq += red[1][ww]; }
         const float a = bc[1] - bc[0] * r;
         // S = Sbar + a v k^T;  o = Sbar q + a v (k.q)
-        const float av = a * sv[i];
 #pragma unroll
-        for (int x = 0; x < NV; ++x)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[x][e] = fmaf(av, sk[j0 + 4 * x + e], S[x][e]);
-        if (tid % TPR == 0) o[row * D + i] = (E)(z + av * kq);
+        for (int x = 0; x < NV; ++x) {
+            const float av = a * sv[i0 + RPX * x];
+            S[x] = S[x] + av * kj;
+            if (lead) o[row * D + i0 + RPX * x] = (E)(z[x] + av * kq);
+        }
         __syncthreads();   // the token vectors and partials are reused
     }
 #pragma unroll
-    for (int x = 0; x < NV; ++x) *reinterpret_cast<floatx4*>(S_out + sbase + 4 * x) = S[x];
+    for (int x = 0; x < NV; ++x) *reinterpret_cast<floatx4*>(S_out + sbase + 4 * (size_t)NT * x) = S[x];
 }
 
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
