@@ -208,10 +208,9 @@ __device__ __forceinline__ void bwd_state_body(
 
     floatx4 dSt[D / 16];   // dS^T[16mj + 4g + r][16w + cl] = dS[16w + cl][16mj + 4g + r]
 #pragma unroll
-    for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dSt[mj][r] = dST ? dST[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g + r] : 0.f;
+    for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte load
+        dSt[mj] = dST ? *reinterpret_cast<const floatx4*>(&dST[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g])
+                      : floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Loads of chunk n into registers; unconditional (n is clamped by the
     // caller, rows past the end re-read the last row and are cleared in the
@@ -453,10 +452,8 @@ __device__ __forceinline__ void bwd_state_body(
 
     if (dS0) {
 #pragma unroll
-        for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dS0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g + r] = dSt[mj][r];
+        for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
+            *reinterpret_cast<floatx4*>(&dS0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g]) = dSt[mj];
     }
 }
 

@@ -173,10 +173,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[nt][mj][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] : 0.f;
+            for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte load
+                S[nt][mj] = S0 ? *reinterpret_cast<const floatx4*>(
+                                     &S0[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g])
+                               : floatx4{0.f, 0.f, 0.f, 0.f};
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;
@@ -337,10 +337,9 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g + r] = S[nt][mj][r];
+                for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
+                    *reinterpret_cast<floatx4*>(&ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g]) =
+                        S[nt][mj];
         }
     } else {
         Raw16x2<TR> rq, rk, rv, rf;         // raw rows of the chunk being prepared

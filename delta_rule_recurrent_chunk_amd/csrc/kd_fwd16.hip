@@ -142,10 +142,9 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         const uint32_t o_lane = (uint32_t)cl * rs + hoff + i0 + 4 * g;
         floatx4 S[D / 16];       // S^T[16mj + 4g + r][i0 + cl] in S[mj][r]
 #pragma unroll
-        for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[mj][r] = S0 ? S0[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] : 0.f;
+        for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte load
+            S[mj] = S0 ? *reinterpret_cast<const floatx4*>(&S0[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g])
+                       : floatx4{0.f, 0.f, 0.f, 0.f};
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;
@@ -330,10 +329,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         if (ST) {
             const float si = sm.sinv;
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g + r] = S[mj][r] * si;
+            for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
+                *reinterpret_cast<floatx4*>(&ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g]) = S[mj] * si;
         }
     } else {
         const int pw = w - NWC;          // producer wave 0..7 (wave-uniform)
