@@ -433,13 +433,23 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 OQ[tt] = TR::mma(TR::ld_state_p(&sm.P[(SB * tt + cl) * LDP], ks, g), uf, OQ[tt]);
         }
         if (o) {
+            // O goes out through LDS (the wave's own 16 columns of the Qbar
+            // tile, last read in phase 2): each lane then stores 16 bytes,
+            // eight adjacent columns of one token, instead of sixteen 2-byte
+            // values; no other wave reads these columns, so no barrier
+            E* ost = sm.Qb;
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = n * CH + SB * tt + 4 * g + r;
-                    if (t < T) o[bbase + (size_t)t * rs + hoff + i0 + cl] = (E)OQ[tt][r];
-                }
+                for (int r = 0; r < 4; ++r) ost[(SB * tt + 4 * g + r) * LD + i0 + cl] = (E)OQ[tt][r];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes before its reads
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int pce = 64 * it + lane, tk = pce >> 1, half = pce & 1;
+                const int t = n * CH + tk;
+                const uint4 val = *reinterpret_cast<const uint4*>(&ost[tk * LD + i0 + 8 * half]);
+                if (t < T) *reinterpret_cast<uint4*>(o + bbase + (size_t)t * rs + hoff + i0 + 8 * half) = val;
+            }
         }
         // S <- diag(gamma_C) S + Ktil^T U
 #pragma unroll
