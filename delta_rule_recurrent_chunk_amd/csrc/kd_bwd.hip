@@ -453,7 +453,7 @@ __device__ __forceinline__ void bwd_state_body(
     if (dS0) {
 #pragma unroll
         for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
-            *reinterpret_cast<floatx4*>(&dS0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g]) = dSt[mj];
+            st4_nt(&dS0[(size_t)bh * D * D + (size_t)(16 * w + cl) * D + 16 * mj + 4 * g], dSt[mj]);
     }
 }
 
@@ -874,9 +874,9 @@ __device__ __forceinline__ void bwd_chunk_body(
                     }
                 }
                 const uint32_t off = (uint32_t)t * rs + hoff + ch0;
-                st8v(dq + bbase + off, dqv[e]);
-                st8v(dk + bbase + off, dkv[e]);
-                st8v(df + bbase + off, dfv[e]);
+                st8v_nt(dq + bbase + off, dqv[e]);
+                st8v_nt(dk + bbase + off, dkv[e]);
+                st8v_nt(df + bbase + off, dfv[e]);
             }
         }
     }
@@ -893,15 +893,15 @@ __device__ __forceinline__ void bwd_chunk_body(
             float x[8];
 #pragma unroll
             for (int c = 0; c < 8; ++c) x[c] = poison ? __builtin_nanf("") : stQ[(row0 + e) * LDF + ch0 + c];
-            st8v(dv + bbase + (uint32_t)t * rs + hoff + ch0, x);
+            st8v_nt(dv + bbase + (uint32_t)t * rs + hoff + ch0, x);
         }
     }
     if (tid < CH && n * CH + tid < T) {
         const size_t gi = ((size_t)b * T + n * CH + tid) * H + h;
         float db = -sm.r0[tid] * sm.drho[tid];
         for (int J = 0; J <= tid / SB; ++J) db += sm.dbp[J][tid];   // fixed order: bitwise reproducible
-        dbeta[gi] = poison ? __builtin_nanf("") : db;
-        dc[gi] = poison ? __builtin_nanf("") : sm.drho[tid];
+        st_nt(&dbeta[gi], poison ? __builtin_nanf("") : db);
+        st_nt(&dc[gi], poison ? __builtin_nanf("") : sm.drho[tid]);
     }
 }
 

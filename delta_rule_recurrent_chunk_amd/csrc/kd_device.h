@@ -430,6 +430,17 @@ __device__ __forceinline__ void st8v(float* p, const float* x) {
     reinterpret_cast<floatx4*>(p)[0] = floatx4{x[0], x[1], x[2], x[3]};
     reinterpret_cast<floatx4*>(p)[1] = floatx4{x[4], x[5], x[6], x[7]};
 }
+// the same as streaming stores (outputs no kernel of the launch reads back)
+__device__ __forceinline__ void st8v_nt(__bf16* p, const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+    __builtin_nontemporal_store(__builtin_bit_cast(floatx4, r), reinterpret_cast<floatx4*>(p));
+}
+__device__ __forceinline__ void st8v_nt(float* p, const float* x) {
+    __builtin_nontemporal_store(floatx4{x[0], x[1], x[2], x[3]}, reinterpret_cast<floatx4*>(p));
+    __builtin_nontemporal_store(floatx4{x[4], x[5], x[6], x[7]}, reinterpret_cast<floatx4*>(p) + 1);
+}
 // Store two consecutive values (a transposed-array entry pair).
 __device__ __forceinline__ void st2h(_Float16* p, float a, float b) {
     _Float16 __attribute__((ext_vector_type(2))) x;
@@ -740,6 +751,22 @@ __device__ __forceinline__ void st4(__bf16* p, floatx4 x) {
     *reinterpret_cast<bf16x4*>(p) = r;
 }
 __device__ __forceinline__ void st4(float* p, floatx4 x) { *reinterpret_cast<floatx4*>(p) = x; }
+// The same as a non-temporal (streaming) store: for outputs no kernel of the
+// launch reads back, so they do not take cache space from the inputs still
+// to be read.
+__device__ __forceinline__ void st4_nt(__bf16* p, floatx4 x) {
+    bf16x4 r;
+    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, r), reinterpret_cast<unsigned long long*>(p));
+}
+__device__ __forceinline__ void st4_nt(float* p, floatx4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<floatx4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, float x) { __builtin_nontemporal_store(x, p); }
+// 16-byte copy, streaming store
+__device__ __forceinline__ void cp16_nt(void* dst, const void* src) {
+    __builtin_nontemporal_store(*reinterpret_cast<const floatx4*>(src), reinterpret_cast<floatx4*>(dst));
+}
 
 // Quad (4-lane group) scans of products, r4 = lane & 3.
 template <int CTRL>

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                         for (int mj = 0; mj < D / 16; ++mj)
-                            st4(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
+                            st4_nt(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
                 }
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
                 floatx4 Yt[2][NSB];
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 sm.u[t_] = x;
                 if (CKPT) {   // u and r0 of the chunk for the backward
                     float* du = ck.U + ((size_t)bh * NC + n) * 2 * CH;
-                    du[t_] = x;
-                    du[CH + t_] = r0;
+                    st_nt(&du[t_], x);
+                    st_nt(&du[CH + t_], r0);
                 }
                 const float um = wave_max_nonneg(fabsf(x));
                 if (lane == 0) sm.umax = __float_as_uint(um);
@@ -261,13 +261,11 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 E* dp = static_cast<E*>(ck.P) + ((size_t)bh * NC + n) * CH * CH;
                 for (int x = tid; x < CH * CH / 4; x += NWC * 64) {
                     const int t = x / (CH / 4), s4 = x % (CH / 4);
-                    *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
-                        *reinterpret_cast<const floatx4*>(&sm.M[t * LDM + 4 * s4]);
+                    cp16_nt(dm + t * CH + 4 * s4, &sm.M[t * LDM + 4 * s4]);
                 }
                 for (int x = tid; x < CH * CH / EPV; x += NWC * 64) {
                     const int t = x / (CH / EPV), sv = x % (CH / EPV);
-                    *reinterpret_cast<uint4*>(dp + t * CH + EPV * sv) =
-                        *reinterpret_cast<const uint4*>(&sm.P[n & 1][t * LDP + EPV * sv]);
+                    cp16_nt(dp + t * CH + EPV * sv, &sm.P[n & 1][t * LDP + EPV * sv]);
                 }
             }
             if (tid == 0 && n >= 0) {
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                         if (t < T) {
 #pragma unroll
                             for (int mt = 0; mt < 2; ++mt)
-                                st4(ob + (uint32_t)t * rs + hoff + i0 + 16 * mt + 4 * g, Ot[mt][tt]);
+                                st4_nt(ob + (uint32_t)t * rs + hoff + i0 + 16 * mt + 4 * g, Ot[mt][tt]);
                         }
                     }
                 }
@@ -338,8 +336,7 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
-                    *reinterpret_cast<floatx4*>(&ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g]) =
-                        S[nt][mj];
+                    st4_nt(&ST[(size_t)bh * D * D + (size_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g], S[nt][mj]);
         }
     } else {
         Raw16x2<TR> rq, rk, rv, rf;         // raw rows of the chunk being prepared

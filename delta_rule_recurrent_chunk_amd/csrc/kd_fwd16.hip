@@ -157,7 +157,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     const float si = sm.sinv;
 #pragma unroll
                     for (int mj = 0; mj < D / 16; ++mj)
-                        st4(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj] * si);
+                        st4_nt(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj] * si);
                 }
                 // Y^T = S Kbar^T, then O^T = S Qbar^T (M = value index, N = token).
                 // The B fragments of the next K-step are loaded before the MFMAs
@@ -234,8 +234,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
                 if (CKPT) {
                     float* du = ck.U + ((size_t)bh * NC + n) * 2 * CH;
-                    du[t_] = x;
-                    du[CH + t_] = r0;
+                    st_nt(&du[t_], x);
+                    st_nt(&du[CH + t_], r0);
                 }
                 // scales of this chunk's update: usc = 2^-eu, ksc = 2^-ek, s = 2^-e
                 const float um = wave_max_nonneg(fabsf(x));
@@ -261,13 +261,11 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 E* dp = static_cast<E*>(ck.P) + ((size_t)bh * NC + n) * CH * CH;
                 for (int x = tid - 64; x < CH * CH / 4; x += (NWC - 1) * 64) {
                     const int t = x >> 4, s4 = x & 15;
-                    *reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4) =
-                        *reinterpret_cast<const floatx4*>(&sm.M[t * LDM + 4 * s4]);
+                    cp16_nt(dm + t * CH + 4 * s4, &sm.M[t * LDM + 4 * s4]);
                 }
                 for (int x = tid - 64; x < CH * CH / 8; x += (NWC - 1) * 64) {
                     const int t = x >> 3, s8 = x & 7;
-                    *reinterpret_cast<uint4*>(dp + t * CH + 8 * s8) =
-                        *reinterpret_cast<const uint4*>(&sm.P[n & 1][t * LDP + 8 * s8]);
+                    cp16_nt(dp + t * CH + 8 * s8, &sm.P[n & 1][t * LDP + 8 * s8]);
                 }
             }
             if (tid == 0 && n >= 0) {
@@ -306,7 +304,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                         // row offset = scalar part + this lane's part (one register
                         // across the loop instead of one per tt)
                         const uint32_t srow = __builtin_amdgcn_readfirstlane((uint32_t)(n * CH + SB * tt) * rs);
-                        if (n * CH + SB * tt + cl < T) st4(ob + (srow + o_lane), Ot[tt] * oi);
+                        if (n * CH + SB * tt + cl < T) st4_nt(ob + (srow + o_lane), Ot[tt] * oi);
                     }
                 }
                 // S <- S diag(gamma_C) s / s_prev + K~'^T W'; K-steps outermost, so
@@ -330,7 +328,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             const float si = sm.sinv;
 #pragma unroll
             for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte store
-                *reinterpret_cast<floatx4*>(&ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g]) = S[mj] * si;
+                st4_nt(&ST[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g], S[mj] * si);
         }
     } else {
         const int pw = w - NWC;          // producer wave 0..7 (wave-uniform)

@@ -448,7 +448,7 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 const int pce = 64 * it + lane, tk = pce >> 1, half = pce & 1;
                 const int t = n * CH + tk;
                 const uint4 val = *reinterpret_cast<const uint4*>(&ost[tk * LD + i0 + 8 * half]);
-                if (t < T) *reinterpret_cast<uint4*>(o + bbase + (size_t)t * rs + hoff + i0 + 8 * half) = val;
+                if (t < T) cp16_nt(o + bbase + (size_t)t * rs + hoff + i0 + 8 * half, &val);
             }
         }
         // S <- diag(gamma_C) S + Ktil^T U
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
 #pragma unroll
         for (int mj = 0; mj < D / 16; ++mj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ST[sbase + (size_t)(16 * mj + 4 * g + r) * D + i0 + cl] = S[mj][r];
+            for (int r = 0; r < 4; ++r) st_nt(&ST[sbase + (size_t)(16 * mj + 4 * g + r) * D + i0 + cl], S[mj][r]);
     }
 }
 
