@@ -126,7 +126,7 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int
         const float sc = rsqrtf(row_sum<LPR>(ss) + MIX_EPS_L2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] *= sc;
-        st8(dst + (uint32_t)t * rs + 8 * o8, y);
+        st8v_nt(dst + (uint32_t)t * rs + 8 * o8, y);
     }
 }
 
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_gate_kernel(MixPreArgs a, int
             if (t >= t1) break;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[i][e] = forget_gate(x[i][e], ex);
-            st8(dst + (size_t)t * rs, x[i]);
+            st8v_nt(dst + (size_t)t * rs, x[i]);
             if (o8 == 0) {
                 a.beta[(size_t)t * H + h] = a.beta_scale * gate_sigmoid(br[i]);
                 a.c[(size_t)t * H + h] = gate_sigmoid(cr[i]);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(MIX_NT) void kd_mixer_post_kernel(const E* __restri
             const float sc = rsqrtf(row_sum<LPR>(ss) * (1.f / D) + eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * sc * wv[e] * gate_sigmoid(gv[i][e]);
-            st8(y + bbase + (uint32_t)t * rs + off, x[i]);
+            st8v_nt(y + bbase + (uint32_t)t * rs + off, x[i]);
         }
     }
 }
