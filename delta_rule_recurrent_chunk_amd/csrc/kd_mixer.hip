@@ -60,6 +60,7 @@ template <class E, int D, int K>
 __global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int T, int H) {
     constexpr int LPR = D / 8;                  // lanes per row
     constexpr int TPP = MIX_NT / LPR;           // tokens per pass
+    static_assert(MIX_CT % TPP == 0, "a block's tokens are whole passes");
     constexpr int ROWS = MIX_CT + K - 1;
     constexpr int PPR = D * (int)sizeof(E) / 16; // 16-byte pieces per row
     static_assert(D * K <= 4 * MIX_NT, "one float4 of taps per thread");
