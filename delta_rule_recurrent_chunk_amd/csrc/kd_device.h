@@ -27,8 +27,11 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;        // chunk length (tokens per chunk)
-// Decay operands are referenced to the chunk start and divide by gamma; a key
-// channel whose decay over a chunk falls below this floor is treated apart.
+// The Gram tiles of a chunk take their decay relative to the 16-token
+// sub-blocks (every operand a product of gates, at most 1).  A diagonal tile
+// divides by its sub-block's decay; a key channel whose decay over one
+// sub-block falls below this floor (an exact reset f = 0 among them) has its
+// diagonal-tile terms computed apart.
 constexpr float kSafeFloor = 7.888609052210118e-31f;  // 2^-100
 constexpr int SB = 16;        // sub-block edge = MFMA tile edge
 constexpr int NSB = CH / SB;  // sub-blocks per chunk
@@ -37,6 +40,15 @@ constexpr int NSB = CH / SB;  // sub-blocks per chunk
 // prefetch loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A zero the compiler cannot see through: adding it to a per-lane index inside
+// a loop keeps the addresses derived from that index from being hoisted out of
+// the loop (where they would hold registers across the whole loop).
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
 }
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
@@ -114,6 +126,17 @@ struct Bf16T {
     static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
         const floatx4 a = acc[2 * ks];
         const floatx4 b = acc[2 * ks + 1];
+        Frag r;
+        r[0] = cvt(a[0]); r[1] = cvt(a[1]); r[2] = cvt(a[2]); r[3] = cvt(a[3]);
+        r[4] = cvt(b[0]); r[5] = cvt(b[1]); r[6] = cvt(b[2]); r[7] = cvt(b[3]);
+        return r;
+    }
+    // state_frag with each key channel j scaled by s[j]: s is a row of D
+    // factors in pcol order, so the fragment's eight channels sit at
+    // s[32ks + 8g .. 32ks + 8g + 7]
+    static __device__ __forceinline__ Frag state_frag_scaled(const floatx4* acc, int ks, const float* s, int g) {
+        const floatx4 a = acc[2 * ks] * *reinterpret_cast<const floatx4*>(s + KS * ks + 8 * g);
+        const floatx4 b = acc[2 * ks + 1] * *reinterpret_cast<const floatx4*>(s + KS * ks + 8 * g + 4);
         Frag r;
         r[0] = cvt(a[0]); r[1] = cvt(a[1]); r[2] = cvt(a[2]); r[3] = cvt(a[3]);
         r[4] = cvt(b[0]); r[5] = cvt(b[1]); r[6] = cvt(b[2]); r[7] = cvt(b[3]);
@@ -285,6 +308,11 @@ struct F32T {
     static __device__ __forceinline__ Frag ld_state_p(const E* row, int ks, int g) { return ld_state(row, ks, g); }
     static __device__ __forceinline__ Frag state_frag(const floatx4* acc, int ks) {
         return acc[ks >> 2][ks & 3];
+    }
+    // key channel j = 16 (ks / 4) + 4g + ks % 4 scaled by s[j] (no column
+    // permutation for fp32)
+    static __device__ __forceinline__ Frag state_frag_scaled(const floatx4* acc, int ks, const float* s, int g) {
+        return acc[ks >> 2][ks & 3] * s[16 * (ks >> 2) + 4 * g + (ks & 3)];
     }
     static __device__ __forceinline__ Frag ld_col(const E* col, int ld, int ks, int g) {
         return col[(KS * ks + g) * ld];
@@ -811,6 +839,21 @@ __device__ __forceinline__ void row16_reduce_step(float* x, int cl) {
         const float keep = up ? x[e + M] : x[e];
         x[e] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
     }
+}
+
+// x[0 .. 3] of every lane summed over the four lane groups (rows of 16
+// lanes): lane (g, cl) returns the sum over g' of x[g] held by lane (g', cl).
+// Two exchange steps, each lane keeping the half of its values that its
+// partner sends back summed (partners 32, then 16 lanes apart).
+__device__ __forceinline__ float group4_transpose_sum(const float (&x)[4], int g) {
+    const bool hi2 = (g & 2) != 0;
+    const float k0 = hi2 ? x[2] : x[0], k1 = hi2 ? x[3] : x[1];
+    const float s0 = hi2 ? x[0] : x[2], s1 = hi2 ? x[1] : x[3];
+    const float y0 = k0 + __shfl_xor(s0, 32, 64);
+    const float y1 = k1 + __shfl_xor(s1, 32, 64);
+    const bool hi1 = (g & 1) != 0;
+    const float kk = hi1 ? y1 : y0, ss = hi1 ? y0 : y1;
+    return kk + __shfl_xor(ss, 16, 64);
 }
 
 // Store two adjacent channels' values (as the path's element type).

@@ -35,12 +35,20 @@
 //    operands of n, decay scans of n+1) -- stage B (consumer: substitution n |
 //    producer: operands of n+1, loads of n+2) -- stage C (consumer: readout
 //    and update n | producer: Gram of n+1), one barrier after each stage.
-//  * Decay folding: Qbar = q*gamma, Kbar = k*gamma and Kc = k/gamma are the
-//    MFMA operands of every Gram tile and of the state reads.  Kc needs
-//    gamma >= 2^-100; a key channel whose decay over the chunk falls below
-//    that has its Kc column zeroed and its Gram terms accumulated exactly by a
-//    scalar fallback, so every input in [0, 1] is handled exactly.
-//    K * gamma_C/gamma comes from suffix products and never divides.
+//  * Decay folding.  The Gram tiles take their decay relative to the four
+//    16-token sub-blocks: a_t = prod of f from the start of t's sub-block
+//    through t, b_s = prod of f after s through the end of s's sub-block, and
+//    the stored operands Qloc = q a, Kloc = k a, Kr = k b are products of gates
+//    (at most 1).  Tile (I, J < I) is Kloc_I diag(D_IJ) Kr_J^T with D_IJ the
+//    decay of the whole sub-blocks between them (1 for neighbours); a diagonal
+//    tile divides Kr by its sub-block's decay.  A channel whose decay over one
+//    sub-block is below 2^-100 (a reset f = 0 among them) is left out of that
+//    diagonal tile and its terms are added exactly on the vector units before
+//    the tile is read, so every input in [0, 1] is handled exactly.  The state
+//    reads go sub-block by sub-block on the state decayed in place to the
+//    sub-block's start, so (S diag(gamma before I)) Kloc^T = S Kbar^T; the
+//    update then needs only the last sub-block's decay.  K * gamma_C/gamma
+//    comes from suffix products and never divides.
 //  * Precision: Grams and state reads take bf16 operands; the rank-64 state
 //    update takes fp16 operands with exact power-of-two scales (max |k|,
 //    max |u| * max |v| per chunk), its accumulation is fp32.
@@ -69,21 +77,28 @@ struct FwdSmem {
     static constexpr int LDP = CH + TR::PAD;   // P
     static constexpr int NWC = D / 32;         // consumer waves
     // row-major [CH][LD] operands, columns in TR::pcol order
-    alignas(16) E Qb[CH * LD];     // q * gamma                     (chunk n+1 from stage B)
-    alignas(16) E Kb[CH * LD];     // k * gamma
-    alignas(16) E Kc[CH * LD];     // k / gamma, 0 for fallback channels
+    alignas(16) E Qb[CH * LD];     // q * a                         (chunk n+1 from stage B)
+    alignas(16) E Kb[CH * LD];     // k * a
+    alignas(16) E Kc[CH * LD];     // k * b
     alignas(16) E V[CH * LD];      // v
     alignas(16) E VT[D * LDT];     // v^T                           (chunk n from stage A)
     alignas(16) Hh KtT[D * LDT];   // (k gamma_C / gamma)^T * kscale
-    alignas(16) float M[CH * LDM]; // beta_t tril_{-1}(G_K * G_V); fallback scratch
+    alignas(16) float M[CH * LDM]; // beta_t tril_{-1}(G_K * G_V)
     alignas(16) E P[2][CH * LDP];  // tril_0 of the decayed Q K^T, by chunk parity
     alignas(16) float beta[2][CH];
     alignas(16) float c[2][CH];
     alignas(16) float u[CH];
     alignas(16) float r0p[NWC][CH];
     alignas(16) float bprod[NSB][D];   // product of f over each 16-token sub-block
-    alignas(16) float gam[2][D];       // gamma_C, by chunk parity
-    unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
+    alignas(16) float gam[2][D];       // decay over the last sub-block, by chunk parity
+    // decay factors of the prepared chunk: rows 0..3, 1 / (decay over sub-block
+    // I) (0 below the floor); 4, 5, 6 the decay between the sub-blocks of tiles
+    // (2,0), (3,1), (3,0) (pcol order); 7..9 the decay over sub-blocks 0..2
+    // (natural order, the state's)
+    alignas(16) float fac[10][D];
+    unsigned kmax[3], vmax[3];              // per chunk mod 3: max |k|, max |v| (bits)
+    unsigned fbm[2][NSB][(D + 31) / 32];    // channels below the floor per sub-block, by chunk parity
+    unsigned fbany[2];
     unsigned umax;                          // max |u| of the current chunk (bits)
 };
 
@@ -156,18 +171,20 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
     }
 
     // ---- one-time init: the upper triangles of M and P are never written
+    constexpr int NFW = (D + 31) / 32;
     for (int x = tid; x < 2 * CH * LDP; x += NT) (&sm.P[0][0])[x] = TR::cvt(0.f);
     for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
+    if (tid < 2 * NSB * NFW) (&sm.fbm[0][0][0])[tid] = 0u;
     if (tid == 0) {
-        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; sm.unsafe[s] = 0u; }
+        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; }
+        sm.fbany[0] = sm.fbany[1] = 0u;
         sm.umax = 0u;
     }
 
     lds_barrier();
 
-    // Both teams run the same loop of barriers: one per stage plus two more in
-    // a stage C whose next chunk takes the exact fallback (the flag is read by
-    // every wave).  Each team's registers live only in its own loop.
+    // Both teams run the same loop of barriers, one per stage.  Each team's
+    // registers live only in its own loop.
     if (consumer) {
         floatx4 S[2][D / 16];   // S^T[16mj + 4g + r][i0 + 16nt + cl] in S[nt][mj]
 #pragma unroll
@@ -192,21 +209,31 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                         for (int mj = 0; mj < D / 16; ++mj)
                             st4_nt(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
                 }
-                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t)
+                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t),
+                // sub-block by sub-block as S_tt Kloc^T and S_tt Qloc^T, the state
+                // decayed in place to the start of sub-block tt
                 floatx4 Yt[2][NSB];
 #pragma unroll
-                for (int ks = 0; ks < KD_; ++ks) {
-                    const Frag a0 = TR::state_frag(S[0], ks);
-                    const Frag a1 = TR::state_frag(S[1], ks);
-                    const floatx4 z = {0.f, 0.f, 0.f, 0.f};   // first K-step: inline-zero accumulator
+                for (int tt = 0; tt < NSB; ++tt) {
 #pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) {
+                    for (int ks = 0; ks < KD_; ++ks) {
+                        const Frag a0 = TR::state_frag(S[0], ks);
+                        const Frag a1 = TR::state_frag(S[1], ks);
+                        const floatx4 z = {0.f, 0.f, 0.f, 0.f};   // first K-step: inline-zero accumulator
                         const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
                         const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
                         Yt[0][tt] = TR::mma(a0, bk, ks ? Yt[0][tt] : z);
                         Yt[1][tt] = TR::mma(a1, bk, ks ? Yt[1][tt] : z);
                         Ot[0][tt] = TR::mma(a0, bq, ks ? Ot[0][tt] : z);
                         Ot[1][tt] = TR::mma(a1, bq, ks ? Ot[1][tt] : z);
+                    }
+                    if (tt + 1 < NSB) {
+#pragma unroll
+                        for (int mj = 0; mj < D / 16; ++mj) {
+                            const floatx4 dc = *reinterpret_cast<const floatx4*>(&sm.fac[7 + tt][16 * mj + 4 * g]);
+                            S[0][mj] = S[0][mj] * dc;
+                            S[1][mj] = S[1][mj] * dc;
+                        }
                     }
                 }
                 // partial r0[t] = sum over this wave's 32 value columns of Y[t,i] v[t,i]
@@ -271,16 +298,18 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             if (tid == 0 && n >= 0) {
                 // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
                 // the previous stage C, the latter's first writer runs in stage A(n+1)
-                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
+                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u;
+            }
+            if (tid < NSB * NFW && n >= 0) {
+                // chunk n's flags were last read in stage A; chunk n + 2 sets them
+                // in stage B(n + 1)
+                (&sm.fbm[n & 1][0][0])[tid] = 0u;
+                if (tid == 0) sm.fbany[n & 1] = 0u;
             }
             KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
-            if (nn < NC && sm.unsafe[nn % 3] != 0u) {   // producers run the exact fallback
-                lds_barrier();
-                lds_barrier();
-            }
             if (n >= 0) {   // readout and state update of chunk n
                 const float usc = pow2_scale(__uint_as_float(sm.umax) * __uint_as_float(sm.vmax[n % 3]));
                 const float ksc = pow2_scale(__uint_as_float(sm.kmax[n % 3]));
@@ -344,7 +373,6 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         float tot[2];                       // product of f over the sub-block, per channel
         Col16<E> keep_v[2];                 // v and K-tilde of the prepared chunk, written
         Col16<Hh> keep_kt[2];               //   transposed in the following stage A
-        unsigned pmask = 0;                 // fallback channels (bit cc: ch0 + cc) of the prepared chunk
         // Rows past the sequence end re-read the last row (in bounds) and are
         // cleared before use (q = k = v = 0, f = 1, beta = c = 0).  Every load
         // is unconditional (clamped to the last chunk), so the prefetch
@@ -371,17 +399,75 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
         load_k(0);
         load_v(0);
         load_f(0);
+        // Exact terms of the diagonal tile I_ of chunk ch for the key channels
+        // whose decay over that sub-block is below the floor (left out of the
+        // tile's matrix product), added to M and P in LDS before they are read:
+        // lane (g, cl) takes the entries t = 4g + r, s = cl (rows of the
+        // sub-block) and sums over those channels k_t k_s E (G_K, s < t) and
+        // q_t k_s E (P, s <= t), E = prod_{s<u<=t} f_u; then M[t][s] += beta_t
+        // dG_K G_V[t][s] (G_V again from V) and P[t][s] += dP.  Rare path: the
+        // rows are re-read from global memory.
+        auto diag_exact = [&](int I_, int ch) {
+            const unsigned* fm = sm.fbm[ch & 1][I_];
+            const int row0 = ch * CH + SB * I_;
+            floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dp = dk;
+#pragma unroll 1
+            for (int wd = 0; wd < NFW; ++wd) {
+                unsigned bits = __builtin_amdgcn_readfirstlane(fm[wd]);
+#pragma unroll 1
+                while (bits) {
+                    const int j = 32 * wd + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const uint32_t cj = hoff + (uint32_t)j;
+                    auto ldv = [&](const E* p, int x) {
+                        const int t = row0 + x;
+                        return t < T ? TR::tof(p[(uint32_t)t * rs + cj]) : 0.f;
+                    };
+                    const float fl = row0 + cl < T ? TR::tof(fb[(uint32_t)(row0 + cl) * rs + cj]) : 1.f;
+                    const float ksv = ldv(kb, cl);
+                    float e4[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+                    for (int u = 1; u < SB; ++u) {
+                        const float fu = readlane_f(fl, u);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e4[r] = (u > cl && u <= 4 * g + r) ? e4[r] * fu : e4[r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * g + r;
+                        const float w_ = ksv * e4[r];
+                        if (t > cl) dk[r] += ldv(kb, t) * w_;
+                        if (t >= cl) dp[r] += ldv(qb, t) * w_;
+                    }
+                }
+            }
+            floatx4 gv = {0.f, 0.f, 0.f, 0.f};
+            const E* aV = &sm.V[(SB * I_ + cl) * LD];
+#pragma unroll
+            for (int ks = 0; ks < KD_; ++ks) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(aV, ks, g), gv);
+            const int s_ = SB * I_ + cl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t_ = SB * I_ + 4 * g + r;
+                if (s_ < t_) sm.M[t_ * LDM + s_] += sm.beta[ch & 1][t_] * dk[r] * gv[r];
+                if (s_ <= t_) {
+                    E& pe = sm.P[ch & 1][t_ * LDP + s_];
+                    pe = TR::cvt(TR::tof(pe) + dp[r]);
+                }
+            }
+        };
         // One lower-triangular 16 x 16 tile (I_ >= J_) of M (DO_M) and / or P
         // (DO_P) for chunk ch, whose operands are in LDS.  The M part writes
-        // only the strictly lower entries of M; the diagonal and the upper
-        // triangle stay zero, except after the exact fallback, whose P terms
-        // sit there: the P part reads them and clears each entry it read.  The
-        // two parts never touch the same entry, so they may run on different
-        // waves in any order.
-        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch, bool fbk) {
+        // only the strictly lower entries of M (the diagonal and the upper
+        // triangle stay zero), the P part the tile's entries of P: the two parts
+        // never touch the same entry, so they may run on different waves in any
+        // order.  The decay between the two sub-blocks goes on the Kr fragment
+        // (fac row fr).
+        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch) {
             constexpr bool DO_M = decltype(do_m)::value, DO_P = decltype(do_p)::value;
             const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J_ = tile - (I_ * (I_ + 1)) / 2;
+            const int fr = I_ == J_ ? I_ : I_ - J_ == 2 ? (J_ == 0 ? 4 : 5) : I_ - J_ == 3 ? 6 : -1;
             floatx4 gk, pp, gv;
             const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
             const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
@@ -391,23 +477,13 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
 #pragma unroll
             for (int ks = 0; ks < KD_; ++ks) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                const Frag fk = TR::ld_nat(bK, ks, g);
+                Frag fk = TR::ld_nat(bK, ks, g);
+                if (fr >= 0) fk = TR::scale_k(fk, 1.f, sm.fac[fr], ks, g);
                 if (DO_M) gk = TR::mma(TR::ld_nat(aK, ks, g), fk, ks ? gk : z);
                 if (DO_P) pp = TR::mma(TR::ld_nat(aQ, ks, g), fk, ks ? pp : z);
                 if (DO_M) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(bV, ks, g), ks ? gv : z);
             }
             const int s_ = SB * J_ + cl;
-            if (fbk) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t_ = SB * I_ + 4 * g + r;
-                    if (DO_M && s_ < t_) gk[r] += sm.M[t_ * LDM + s_];
-                    if (DO_P && s_ <= t_) {
-                        pp[r] += sm.M[s_ * LDM + t_];
-                        sm.M[s_ * LDM + t_] = 0.f;
-                    }
-                }
-            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t_ = SB * I_ + 4 * g + r;
@@ -438,9 +514,14 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                 }
                 if (D == 128) {
                     const int pw = w - NWC;   // producer wave 0..3
-                    const bool fbk = sm.unsafe[n % 3] != 0u;
-                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n, fbk);
-                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n, fbk);
+                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n);
+                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n);
+                }
+                // every tile of chunk n is done (D < 128: in the last stage C)
+                if (D < 128 && sm.fbany[n & 1] != 0u) {
+                    const int pw = w - NWC;
+#pragma unroll 1
+                    for (int I2 = pw; I2 < NSB; I2 += NWP) diag_exact(I2, n);
                 }
             }
             if (prod_on) {   // decay products of chunk nn
@@ -476,36 +557,51 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
             if (prod_on) {   // operands of chunk nn into LDS
-                // gamma before the sub-block (plt), after it (pgt), over the chunk
-                float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, gC[2], rgC[2];
+                // decay over each sub-block (bp), the factor rows this lane
+                // writes, and the decay of the sub-blocks after this one
+                float bp[NSB][2];
 #pragma unroll
                 for (int I2 = 0; I2 < NSB; ++I2) {
                     const float2 x = *reinterpret_cast<const float2*>(&sm.bprod[I2][ch0]);
-                    if (I2 < I) { plt[0] *= x.x; plt[1] *= x.y; }
-                    if (I2 > I) { pgt[0] *= x.x; pgt[1] *= x.y; }
+                    bp[I2][0] = x.x; bp[I2][1] = x.y;
                 }
-                pmask = 0;
+                float after[2] = {1.f, 1.f};
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    gC[c2] = (plt[c2] * tot[c2]) * pgt[c2];
-                    // fallback channels get a zero Kc column (their Gram terms are
-                    // added exactly below)
-                    const bool un = !(gC[c2] >= kSafeFloor);
-                    if (un) pmask |= 1u << c2;
-                    rgC[c2] = un ? 0.f : __builtin_amdgcn_rcpf(gC[c2]);
+                for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                    for (int I2 = 1; I2 < NSB; ++I2)
+                        if (I2 > I) after[c2] *= bp[I2][c2];
+                auto facv = [&](int row, int c2) {
+                    if (row < 4) return bp[row][c2] >= kSafeFloor ? __builtin_amdgcn_rcpf(bp[row][c2]) : 0.f;
+                    if (row == 4) return bp[1][c2];
+                    if (row == 5) return bp[2][c2];
+                    if (row == 6) return bp[1][c2] * bp[2][c2];
+                    return bp[row - 7][c2];
+                };
+                // the lanes of sub-block I write rows I, I + 4 (and 8 + I for I < 2)
+                st2(&sm.fac[I][pc0], facv(I, 0), facv(I, 1));
+                if (I < 3) st2(&sm.fac[4 + I][pc0], facv(4 + I, 0), facv(4 + I, 1));
+                if (I == 3) st2(&sm.fac[7][ch0], facv(7, 0), facv(7, 1));
+                if (I < 2) st2(&sm.fac[8 + I][ch0], facv(8 + I, 0), facv(8 + I, 1));
+                {   // channels of sub-block I below the floor (rare)
+                    const unsigned fl2 = (bp[I][0] >= kSafeFloor ? 0u : 1u) | (bp[I][1] >= kSafeFloor ? 0u : 2u);
+                    if (fl2) {
+                        atomicOr(&sm.fbm[nn & 1][I][ch0 >> 5], fl2 << (ch0 & 31));
+                        atomicOr(&sm.fbany[nn & 1], 1u);
+                    }
                 }
-                if (I == 0) st2(&sm.gam[nn & 1][ch0], gC[0], gC[1]);
-                if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
+                if (I == NSB - 1) st2(&sm.gam[nn & 1][ch0], bp[NSB - 1][0], bp[NSB - 1][1]);
                 const float ksc = pow2_scale(__uint_as_float(sm.kmax[nn % 3]));
-                // gamma_C / gamma at each row: suffix products within the sub-block
-                float om[SB][2];
+                // b (to the sub-block end) as suffix products within the
+                // sub-block; gamma_C / gamma = b * after
+                float bs[SB][2];
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
-                    om[SB - 1][c2] = pgt[c2];
+                    bs[SB - 1][c2] = 1.f;
 #pragma unroll
-                    for (int e = SB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * rf.get(e + 1, c2);
+                    for (int e = SB - 2; e >= 0; --e) bs[e][c2] = bs[e + 1][c2] * rf.get(e + 1, c2);
                 }
-                float ga[2] = {plt[0], plt[1]};   // gamma at the current row (running prefix)
+                float ga[2] = {1.f, 1.f};   // a at the current row (running prefix)
                 float kprev[2] = {0.f, 0.f};
 #pragma unroll
                 for (int e = 0; e < SB; ++e) {
@@ -514,11 +610,10 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
                     for (int c2 = 0; c2 < 2; ++c2) {
                         ga[c2] *= rf.get(e, c2);
                         const float kf = rk.get(e, c2), qf = rq.get(e, c2);
-                        const float kt = kf * om[e][c2];          // K-tilde
+                        const float kt = kf * (bs[e][c2] * after[c2]);   // K-tilde
                         qo[c2] = qf * ga[c2];
                         ko[c2] = kf * ga[c2];
-                        // k / gamma = K-tilde / gamma_C (no reciprocal per element)
-                        co[c2] = kt * rgC[c2];
+                        co[c2] = kf * bs[e][c2];
                         if (e & 1) keep_kt[c2].set_pair(e >> 1, kprev[c2], kt * ksc);
                         else kprev[c2] = kt * ksc;
                     }
@@ -539,43 +634,11 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
-            const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
-            if (fallback) {
-                // Exact Gram terms of key channels of chunk nn whose decay is below
-                // the floor (their Kc columns are zero, so the MFMA tiles leave them
-                // out): G_K[t,s] (s<t) accumulates at M[t][s], P[t,s] (s<t) at
-                // M[s][t], P[t,t] at M[t][t].  Rare path: rows are re-read from
-                // global memory.
-                for (int x = ptid; x < CH * LDM / 4; x += NT - NWC * 64)
-                    reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-                lds_barrier();
-                if (I == 0 && pmask) {
-                    const int t0 = nn * CH;
-#pragma unroll 1
-                    for (int c = 0; c < 2; ++c) {
-                        if (!((pmask >> c) & 1u)) continue;
-                        const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
-#pragma unroll 1
-                        for (int s = 0; s < CH && t0 + s < T; ++s) {
-                            const float ks_ = TR::tof(kb[off + s * rs]);
-                            atomicAdd(&sm.M[s * LDM + s], TR::tof(qb[off + s * rs]) * ks_);
-                            float prod = 1.f;
-#pragma unroll 1
-                            for (int t = s + 1; t < CH && t0 + t < T; ++t) {
-                                prod *= TR::tof(fb[off + t * rs]);
-                                atomicAdd(&sm.M[t * LDM + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
-                                atomicAdd(&sm.M[s * LDM + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
-                            }
-                        }
-                    }
-                }
-                lds_barrier();
-            }
             load_k(npf);
 #pragma unroll
             for (int it = 0; it < NTPW_C; ++it) {   // Gram tiles of chunk nn: M and P
                 const int tile = w - NWC + it * NWP;
-                if (prod_on && tile < 10) gram_tile(kYes(), kYes(), tile, nn, fallback);
+                if (prod_on && tile < 10) gram_tile(kYes(), kYes(), tile, nn);
                 // (it is a compile-time constant in each unrolled copy: no branch)
                 if (it == 0) load_v(npf);
                 if (it == 1) load_f(npf);

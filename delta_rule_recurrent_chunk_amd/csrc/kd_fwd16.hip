@@ -7,7 +7,23 @@
 // steps 3-4): per chunk n,
 //     (I + M) u = c - beta * r0,  r0_t = v_t^T S0 Kbar_t,
 //     O = Qbar S0^T + P (u * V),  S_C = S0 diag(gamma_C) + (u * V)^T Ktilde.
-// What changes is the split of the work: each role has eight waves, so every
+// Decay references.  The state reads take Qbar = q gamma and Kbar = k gamma
+// with gamma referenced to the chunk start; the Gram tiles take their decay
+// relative to the four 16-token sub-blocks, so that every stored operand is a
+// product of gates (at most 1, never a quotient):
+//     a_t = prod of f from the start of t's sub-block through t,
+//     b_s = prod of f after s through the end of s's sub-block,
+//     Qloc = q a, Kloc = k a, Kr = k b   (LDS arrays Qb, Kb, Kc),
+//     G_K[t,s] = sum_j Kloc_tj Kr_sj D_IJ,j   (t in sub-block I, s in J < I),
+// where D_IJ is the decay of the whole sub-blocks between J and I (1 for
+// neighbours).  A diagonal tile (I = J) divides by its sub-block's decay
+// (Kr / prod over the sub-block); a channel whose sub-block decay is below
+// 2^-100 is left out of that tile's matrix product and its terms are added
+// exactly on the vector units.  The state reads go sub-block by sub-block,
+// decaying the state in place by each sub-block's decay after its reads, so
+// that sub-block I reads (S diag(gamma before I)) Kloc^T = S Kbar^T; after
+// the last one the update needs only the last sub-block's decay.
+// The split of the work: each role has eight waves, so every
 // SIMD holds two consumer and two producer waves (128 registers each) and
 // one wave's LDS, matrix-core or dependency wait is covered by the others.
 //   consumers (waves 0..7): 16 value columns of the fp32 state each, held
@@ -40,27 +56,41 @@ constexpr int LD = D + 16;        // row-major [CH][D] operands (columns in pcol
 constexpr int LDT = CH + 8;       // transposed [D][CH] operands
 constexpr int LDM = CH + 4;       // fp32 M
 constexpr int LDP = CH + 8;       // P
-constexpr int LDR = 4 * NWC + 4;  // r0 partials per token (row stride 36: conflict-free stores)
 }  // namespace f16w
 
+// Rows of the factor table Fwd16Smem::fac (key channels in pcol order).
+// Rows DIAG .. D30 are the Gram tiles' (pcol order); rows SUB + I are the
+// decay over sub-block I in natural channel order (the state's decay).
+namespace facrow {
+constexpr int DIAG = 0;    // DIAG + I: 1 / (decay over sub-block I), 0 for a channel below the floor
+constexpr int D20 = 4;     // decay over sub-block 1 (tile I=2, J=0)
+constexpr int D31 = 5;     // decay over sub-block 2 (tile I=3, J=1)
+constexpr int D30 = 6;     // decay over sub-blocks 1 and 2 (tile I=3, J=0)
+constexpr int SUB = 7;     // SUB + I (I = 0..2): decay over sub-block I, natural order
+constexpr int N = 10;
+}  // namespace facrow
+
 struct Fwd16Smem {
-    alignas(16) __bf16 Qb[CH * f16w::LD];       // q * gamma
-    alignas(16) __bf16 Kb[CH * f16w::LD];       // k * gamma
-    alignas(16) __bf16 Kc[CH * f16w::LD];       // k / gamma (0 for fallback channels)
+    alignas(16) __bf16 Qb[CH * f16w::LD];       // q * a (decay from the sub-block start)
+    alignas(16) __bf16 Kb[CH * f16w::LD];       // k * a
+    alignas(16) __bf16 Kc[CH * f16w::LD];       // k * b (decay to the sub-block end)
     alignas(16) __bf16 V[CH * f16w::LD];        // v
     alignas(16) __bf16 VT[f16w::D * f16w::LDT];     // v^T
     alignas(16) _Float16 KtT[f16w::D * f16w::LDT];  // (k gamma_C / gamma)^T * kscale
-    alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V); fallback scratch
+    alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V)
     alignas(16) __bf16 P[2][CH * f16w::LDP];    // tril_0 of the decayed Q K^T, by chunk parity
     alignas(16) float beta[2][CH];
     alignas(16) float c[2][CH];
     alignas(16) float u[CH];                   // u * s_prev (readout operand, see below)
     alignas(16) float us[CH];                  // u * usc (update operand)
     alignas(16) float gs[f16w::D];             // gamma_C * s / s_prev (state decay and rescale)
-    alignas(16) float r0q[CH * f16w::LDR];     // r0 partials: [t][4 * wave + lane group]
+    alignas(16) float r0p[CH * f16w::NWC];     // r0 partials: [t][consumer wave, rotated by t / 4]
     alignas(16) float bprod[f16w::NWP][f16w::D];   // product of f over each 8-row block
-    alignas(16) float gam[2][f16w::D];             // gamma_C, by chunk parity
-    unsigned kmax[3], vmax[3], unsafe[3];   // per chunk mod 3: max |k|, max |v| (bits), fallback flag
+    alignas(16) float gam[2][f16w::D];             // decay over the last sub-block, by chunk parity
+    alignas(16) float fac[facrow::N][f16w::D];     // decay factors of the prepared chunk (facrow)
+    unsigned kmax[3], vmax[3];              // per chunk mod 3: max |k|, max |v| (bits)
+    unsigned fbm[2][NSB][f16w::D / 32];     // channels below the floor per sub-block, by chunk parity
+    unsigned fbany[2];                      // any such channel in the chunk, by chunk parity
     float oinv, sinv;                       // 1 / s_prev and 1 / s of the current chunk
 };
 
@@ -120,15 +150,16 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     // one-time init: the upper triangles of M and P are never written
     for (int x = tid; x < 2 * CH * LDP; x += NT) (&sm.P[0][0])[x] = TR::cvt(0.f);
     for (int x = tid; x < CH * LDM; x += NT) sm.M[x] = 0.f;
+    if (tid < 2 * NSB * (D / 32)) (&sm.fbm[0][0][0])[tid] = 0u;
+    if (tid < 2) sm.fbany[tid] = 0u;
     if (tid == 0) {
-        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; sm.unsafe[s] = 0u; }
+        for (int s = 0; s < 3; ++s) { sm.kmax[s] = 0u; sm.vmax[s] = 0u; }
         sm.oinv = 1.f;
         sm.sinv = 1.f;
     }
     lds_barrier();
 
-    // Both teams run the same sequence of barriers (three per chunk, two more
-    // in a stage C whose next chunk takes the exact fallback).
+    // Both teams run the same sequence of barriers, three per chunk.
     if (consumer) {
         // The state is kept multiplied by the exact power of two s = usc * ksc
         // of the last update (the fp16 operand scales below), so that the
@@ -159,46 +190,44 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int mj = 0; mj < D / 16; ++mj)
                         st4_nt(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj] * si);
                 }
-                // Y^T = S Kbar^T, then O^T = S Qbar^T (M = value index, N = token).
-                // The B fragments of the next K-step are loaded before the MFMAs
-                // of this one.
-                auto state_pass = [&](const E* op, floatx4* acc) {
-                    Frag bc[NSB];
+                // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index, N = token)
+                // per token sub-block tt, as S_tt Kloc^T and S_tt Qloc^T with S_tt
+                // the state decayed to the start of sub-block tt (in place);
+                // partial r0[t] over value columns i0 + 4g .. i0 + 4g + 3 (adjacent
+                // under pcol) for the tokens t = 16tt + cl
+                float x[NSB];
 #pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) bc[tt] = TR::ld_state_p(&op[(SB * tt + cl) * LD], 0, g);
+                for (int tt = 0; tt < NSB; ++tt) {
+                    floatx4 Yt;
 #pragma unroll
                     for (int ks = 0; ks < KD_; ++ks) {
-                        Frag bn[NSB];
-                        if (ks + 1 < KD_) {
-#pragma unroll
-                            for (int tt = 0; tt < NSB; ++tt) bn[tt] = TR::ld_state_p(&op[(SB * tt + cl) * LD], ks + 1, g);
-                        }
-                        const Frag a = TR::state_frag(S, ks);
                         const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int tt = 0; tt < NSB; ++tt) acc[tt] = TR::mma(a, bc[tt], ks ? acc[tt] : z);
-                        if (ks + 1 < KD_) {
-#pragma unroll
-                            for (int tt = 0; tt < NSB; ++tt) bc[tt] = bn[tt];
+                        const Frag a = TR::state_frag(S, ks);
+                        if (tt + 1 < NSB) {   // the two state tiles of this K-step, decayed past sub-block tt
+                            const float* dc = &sm.fac[facrow::SUB + tt][32 * ks + 4 * g];
+                            S[2 * ks] = S[2 * ks] * *reinterpret_cast<const floatx4*>(dc);
+                            S[2 * ks + 1] = S[2 * ks + 1] * *reinterpret_cast<const floatx4*>(dc + 16);
                         }
+                        const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
+                        const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
+                        Yt = TR::mma(a, bk, ks ? Yt : z);
+                        Ot[tt] = TR::mma(a, bq, ks ? Ot[tt] : z);
                     }
-                };
-                {
-                    floatx4 Yt[NSB];
-                    state_pass(sm.Kb, Yt);
-                    // partial r0[t] over value columns i0 + 4g .. i0 + 4g + 3 (adjacent
-                    // under pcol); the substitution wave adds the 32 partials of t
+                    const bf16x4 vr = *reinterpret_cast<const bf16x4*>(
+                        &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 4 * g)]);
+                    x[tt] = 0.f;
 #pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) {
-                        const bf16x4 vr = *reinterpret_cast<const bf16x4*>(
-                            &sm.V[(SB * tt + cl) * LD + TR::pcol(i0 + 4 * g)]);
-                        float x = 0.f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) x += Yt[tt][r] * TR::tof(vr[r]);
-                        sm.r0q[(SB * tt + cl) * LDR + 4 * w + g] = x;
-                    }
+                    for (int r = 0; r < 4; ++r) x[tt] += Yt[r] * TR::tof(vr[r]);
                 }
-                state_pass(sm.Qb, Ot);
+                // the producers' exact pass over chunk n's diagonal tiles (rare)
+                if (sm.fbany[n & 1] != 0u) lds_barrier();
+                {
+                    // summed over the lane groups: lane (g, cl) then holds this
+                    // wave's partial of token 16g + cl
+                    const float xs = group4_transpose_sum(x, g);
+                    const int t = SB * g + cl;
+                    sm.r0p[t * NWC + ((w + (t >> 2)) & (NWC - 1))] = xs;
+                }
             }
             KD_PHASE_MARK(n, 3);
             lds_barrier();
@@ -209,11 +238,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 __builtin_amdgcn_s_setprio(3);   // the chain every other wave waits for
                 float r0;
                 {
-                    const floatx4* pr = reinterpret_cast<const floatx4*>(&sm.r0q[t_ * LDR]);
-                    floatx4 a = pr[0] + pr[4], b = pr[1] + pr[5];
-                    a += pr[2] + pr[6];
-                    b += pr[3] + pr[7];
-                    a += b;
+                    const floatx4* pr = reinterpret_cast<const floatx4*>(&sm.r0p[t_ * NWC]);
+                    const floatx4 a = pr[0] + pr[1];
                     r0 = ((a[0] + a[1]) + (a[2] + a[3])) * ldexpf(1.f, e_prev);
                 }
                 float x = sm.c[n & 1][t_] - sm.beta[n & 1][t_] * r0;
@@ -271,16 +297,18 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (tid == 0 && n >= 0) {
                 // slot (n+2)%3 = chunks n-1 and n+2: the former's last reader ran in
                 // the previous stage C, the latter's first writer runs in stage A(n+1)
-                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u; sm.unsafe[(n + 2) % 3] = 0u;
+                sm.kmax[(n + 2) % 3] = 0u; sm.vmax[(n + 2) % 3] = 0u;
+            }
+            if (tid < NSB * (D / 32) && n >= 0) {
+                // chunk n's flags were last read in stage A; chunk n + 2 sets them
+                // in stage B(n + 1)
+                (&sm.fbm[n & 1][0][0])[tid] = 0u;
+                if (tid == 0) sm.fbany[n & 1] = 0u;
             }
             KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
-            if (nn < NC && sm.unsafe[nn % 3] != 0u) {   // producers run the exact fallback
-                lds_barrier();
-                lds_barrier();
-            }
             if (n >= 0) {
                 // W = u * V of this wave's value columns: bf16 scaled by s_prev for
                 // the readout, fp16 scaled by usc for the update
@@ -340,7 +368,6 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         float tot[2];                    // product of f over the 8 rows, per channel
         Col8 keep_v[2], keep_kt[2];      // v and K-tilde of the prepared chunk, written
                                          //   transposed in the following stage A
-        unsigned pmask = 0;              // fallback channels (bit cc: ch0 + cc)
         const float gex = GATES ? __expf(gt.a_log[h]) : 0.f;   // forget-gate exponent
         // Rows past the sequence end re-read the last row (in bounds) and are
         // cleared before use.  Loads are unconditional (clamped to the last
@@ -366,54 +393,111 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         load_k(0);
         load_v(0);
         load_f(0);
+        // Exact terms of the diagonal tile I_ of chunk ch for the key channels
+        // whose decay over that sub-block is below the floor (left out of the
+        // tile's matrix product), added to M and P in LDS: lane (g, cl) takes
+        // the entries t = 4g + r, s = cl (rows of the sub-block) and sums over
+        // those channels k_t k_s E (G_K, s < t) and q_t k_s E (P, s <= t),
+        // E = prod_{s<u<=t} f_u; then M[t][s] += beta_t dG_K G_V[t][s] (G_V again
+        // from V) and P[t][s] += dP.  Rare path: the rows are re-read from
+        // global memory, and the forget gate is made again from its logit
+        // (GATES) with the producers' function and rounding.
+        auto diag_exact = [&](int I_, int ch) {
+            const unsigned* fm = sm.fbm[ch & 1][I_];
+            unsigned any = 0u;
+#pragma unroll
+            for (int wd = 0; wd < D / 32; ++wd) any |= fm[wd];
+            if (__builtin_amdgcn_readfirstlane(any) == 0u) return;
+            const int row0 = ch * CH + SB * I_;
+            floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dp = dk;
+#pragma unroll 1
+            for (int wd = 0; wd < D / 32; ++wd) {
+                unsigned bits = __builtin_amdgcn_readfirstlane(fm[wd]);
+#pragma unroll 1
+                while (bits) {
+                    const int j = 32 * wd + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const uint32_t cj = hoff + (uint32_t)j;
+                    auto ldv = [&](const E* p, int x) {
+                        const int t = row0 + x;
+                        return t < T ? TR::tof(p[(uint32_t)t * rs + cj]) : 0.f;
+                    };
+                    float fl = 1.f;   // f of row cl (1 past the end)
+                    if (row0 + cl < T) {
+                        fl = TR::tof(fb[(uint32_t)(row0 + cl) * rs + cj]);
+                        if (GATES) fl = TR::tof(TR::cvt(forget_gate(fl, gex)));
+                    }
+                    const float ksv = ldv(kb, cl);
+                    float e4[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+                    for (int u = 1; u < SB; ++u) {
+                        const float fu = readlane_f(fl, u);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e4[r] = (u > cl && u <= 4 * g + r) ? e4[r] * fu : e4[r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * g + r;
+                        const float w_ = ksv * e4[r];
+                        if (t > cl) dk[r] += ldv(kb, t) * w_;
+                        if (t >= cl) dp[r] += ldv(qb, t) * w_;
+                    }
+                }
+            }
+            floatx4 gv = {0.f, 0.f, 0.f, 0.f};
+            const E* aV = &sm.V[(SB * I_ + cl) * LD];
+#pragma unroll
+            for (int ks = 0; ks < KD_; ++ks) gv = TR::mma(TR::ld_nat(aV, ks, g), TR::ld_nat(aV, ks, g), gv);
+            const int s_ = SB * I_ + cl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t_ = SB * I_ + 4 * g + r;
+                if (s_ < t_) sm.M[t_ * LDM + s_] += sm.beta[ch & 1][t_] * dk[r] * gv[r];
+                if (s_ <= t_) {
+                    E& pe = sm.P[ch & 1][t_ * LDP + s_];
+                    pe = TR::cvt(TR::tof(pe) + dp[r]);
+                }
+            }
+        };
         // One lower-triangular 16 x 16 tile (I_ >= J_) of M (DO_M) and / or P
         // (DO_P) for chunk ch.  The M part writes only the strictly lower
-        // entries of M; after the exact fallback, whose P terms sit on and
-        // above the diagonal of M, the P part reads and clears them.  The two
-        // parts never touch the same entry.
-        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch, bool fbk) {
+        // entries of M, the P part the tile's entries of P; the two parts never
+        // touch the same entry.  The decay between the two sub-blocks goes on
+        // the Kr fragment (fac row fr).
+        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch) {
             constexpr bool DO_M = decltype(do_m)::value, DO_P = decltype(do_p)::value;
             const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J_ = tile - (I_ * (I_ + 1)) / 2;
+            const int fr = I_ == J_ ? facrow::DIAG + I_
+                         : I_ - J_ == 2 ? (J_ == 0 ? facrow::D20 : facrow::D31)
+                         : I_ - J_ == 3 ? facrow::D30 : -1;
             floatx4 gk, pp, gv;
             const E* aK = &sm.Kb[(SB * I_ + cl) * LD];
             const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
             const E* aV = &sm.V[(SB * I_ + cl) * LD];
             const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
             const E* bV = &sm.V[(SB * J_ + cl) * LD];
-            // operands of one K-step; those of the next are loaded before the
-            // MFMAs of the current one
+            // operands of one K-step (not prefetched a step ahead: the registers
+            // are needed elsewhere, and the other waves of the SIMD cover the
+            // LDS latency)
             struct GF { Frag k, a, q, v, w; };
             auto ldg = [&](int ks) {
                 GF r;
                 r.k = TR::ld_nat(bK, ks, g);
+                if (fr >= 0) r.k = TR::scale_k(r.k, 1.f, sm.fac[fr], ks, g);
                 if (DO_M) { r.a = TR::ld_nat(aK, ks, g); r.v = TR::ld_nat(aV, ks, g); r.w = TR::ld_nat(bV, ks, g); }
                 if (DO_P) r.q = TR::ld_nat(aQ, ks, g);
                 return r;
             };
-            GF cur = ldg(0);
 #pragma unroll
             for (int ks = 0; ks < KD_; ++ks) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                GF nxt;
-                if (ks + 1 < KD_) nxt = ldg(ks + 1);
+                const GF cur = ldg(ks);
                 if (DO_M) gk = TR::mma(cur.a, cur.k, ks ? gk : z);
                 if (DO_P) pp = TR::mma(cur.q, cur.k, ks ? pp : z);
                 if (DO_M) gv = TR::mma(cur.v, cur.w, ks ? gv : z);
-                if (ks + 1 < KD_) cur = nxt;
             }
-            const int s_ = SB * J_ + cl;
-            if (fbk) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t_ = SB * I_ + 4 * g + r;
-                    if (DO_M && s_ < t_) gk[r] += sm.M[t_ * LDM + s_];
-                    if (DO_P && s_ <= t_) {
-                        pp[r] += sm.M[s_ * LDM + t_];
-                        sm.M[s_ * LDM + t_] = 0.f;
-                    }
-                }
-            }
+            const int s_ = SB * J_ + cl + opaque_zero();   // addresses formed here, not hoisted
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t_ = SB * I_ + 4 * g + r;
@@ -427,6 +511,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
             const bool prod_on = nn < NC;
+            const int oz = opaque_zero();     // per-lane LDS addresses stay inside the loop
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
             if (n >= 0) {   // transposed operands of chunk n and its last two Gram tiles
@@ -439,9 +524,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 // (M) and the readout (P) of chunk n: their M and P parts run
                 // here on producer waves 0..3, one SIMD each
                 if (pw < 4) {
-                    const bool fbk = sm.unsafe[n % 3] != 0u;
-                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n, fbk);
-                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n, fbk);
+                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n);
+                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n);
+                }
+                if (sm.fbany[n & 1] != 0u) {   // every tile of chunk n is done: exact pass
+                    lds_barrier();
+                    if ((pw & 1) == 0) diag_exact(pw >> 1, n);
                 }
             }
             if (prod_on) {   // decay products of chunk nn
@@ -481,60 +569,93 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
             if (prod_on) {   // operands of chunk nn into LDS
-                // gamma before this block (plt), after it (pgt), and over the chunk
-                // (gC, multiplied in one fixed order so every wave agrees on it).
+                // Decay products from the 8-row blocks of the producer waves
+                // (bprod[p]; sub-block I2 = blocks 2 I2 and 2 I2 + 1), per wave:
+                // astart / bstart = decay of its sub-block's rows before / after
+                // its own, after = decay of the sub-blocks after its own, and the
+                // factor-table rows it writes (row pw; waves 0, 1 also row pw + 8).
                 // pw is wave-uniform: one straight-line case per value.
-                float plt[2] = {1.f, 1.f}, pgt[2] = {1.f, 1.f}, gC[2] = {1.f, 1.f}, rgC[2];
-                {
-                    float2 xb[NWP];
-#pragma unroll
-                    for (int p = 0; p < NWP; ++p) xb[p] = *reinterpret_cast<const float2*>(&sm.bprod[p][ch0]);
-                    auto prods = [&](auto pw_c) {
-                        constexpr int PW = decltype(pw_c)::value;
-#pragma unroll
-                        for (int p = 0; p < NWP; ++p) {
-                            gC[0] *= xb[p].x; gC[1] *= xb[p].y;
-                            if (p < PW) { plt[0] *= xb[p].x; plt[1] *= xb[p].y; }
-                            if (p > PW) { pgt[0] *= xb[p].x; pgt[1] *= xb[p].y; }
+                float astart[2], bstart[2], after[2], fv0[2], fv1[2], lastsub[2];
+                const float* bpb = &sm.bprod[0][ch0 + oz];   // one base, constant offsets
+                unsigned fl2 = 0u;
+                auto consts = [&](auto pw_c) {
+                    constexpr int PW = decltype(pw_c)::value, I = PW >> 1, H2 = PW & 1;
+                    auto xbp = [&](int p) { return *reinterpret_cast<const float2*>(bpb + p * D); };
+                    auto sub = [&](int I2) { const float2 a = xbp(2 * I2), b = xbp(2 * I2 + 1); return make_float2(a.x * b.x, a.y * b.y); };
+                    auto mul = [](float2 a, float2 b) { return make_float2(a.x * b.x, a.y * b.y); };
+                    auto facv = [&](auto row_c) {
+                        constexpr int R = decltype(row_c)::value;
+                        if constexpr (R < facrow::D20) {
+                            const float2 x = sub(R - facrow::DIAG);
+                            return make_float2(x.x >= kSafeFloor ? __builtin_amdgcn_rcpf(x.x) : 0.f,
+                                               x.y >= kSafeFloor ? __builtin_amdgcn_rcpf(x.y) : 0.f);
+                        } else if constexpr (R == facrow::D20) {
+                            return sub(1);
+                        } else if constexpr (R == facrow::D31) {
+                            return sub(2);
+                        } else if constexpr (R == facrow::D30) {
+                            return mul(sub(1), sub(2));
+                        } else {
+                            return sub(R - facrow::SUB);
                         }
                     };
-                    switch (pw) {
-                    case 0: prods(std::integral_constant<int, 0>()); break;
-                    case 1: prods(std::integral_constant<int, 1>()); break;
-                    case 2: prods(std::integral_constant<int, 2>()); break;
-                    case 3: prods(std::integral_constant<int, 3>()); break;
-                    case 4: prods(std::integral_constant<int, 4>()); break;
-                    case 5: prods(std::integral_constant<int, 5>()); break;
-                    case 6: prods(std::integral_constant<int, 6>()); break;
-                    default: prods(std::integral_constant<int, 7>()); break;
+                    const float2 h0 = xbp(2 * I), h1 = xbp(2 * I + 1);
+                    astart[0] = H2 ? h0.x : 1.f; astart[1] = H2 ? h0.y : 1.f;
+                    bstart[0] = H2 ? 1.f : h1.x; bstart[1] = H2 ? 1.f : h1.y;
+                    float2 af = make_float2(1.f, 1.f);
+                    if constexpr (I < 3) af = sub(3);
+                    if constexpr (I < 2) af = mul(sub(2), af);
+                    if constexpr (I < 1) af = mul(sub(1), af);
+                    after[0] = af.x; after[1] = af.y;
+                    const float2 f0 = facv(std::integral_constant<int, PW>());
+                    fv0[0] = f0.x; fv0[1] = f0.y;
+                    if constexpr (PW + NWP < facrow::N) {
+                        const float2 f1 = facv(std::integral_constant<int, PW + NWP>());
+                        fv1[0] = f1.x; fv1[1] = f1.y;
                     }
+                    if constexpr (H2 == 0) {   // channels of sub-block I below the floor
+                        const float2 x = mul(h0, h1);
+                        fl2 = (x.x >= kSafeFloor ? 0u : 1u) | (x.y >= kSafeFloor ? 0u : 2u);
+                    }
+                    if constexpr (PW == 0) {   // the state's decay over the last sub-block
+                        const float2 x = sub(NSB - 1);
+                        lastsub[0] = x.x; lastsub[1] = x.y;
+                    }
+                };
+                switch (pw) {
+                case 0: consts(std::integral_constant<int, 0>()); break;
+                case 1: consts(std::integral_constant<int, 1>()); break;
+                case 2: consts(std::integral_constant<int, 2>()); break;
+                case 3: consts(std::integral_constant<int, 3>()); break;
+                case 4: consts(std::integral_constant<int, 4>()); break;
+                case 5: consts(std::integral_constant<int, 5>()); break;
+                case 6: consts(std::integral_constant<int, 6>()); break;
+                default: consts(std::integral_constant<int, 7>()); break;
                 }
-                pmask = 0;
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    // fallback channels get a zero Kc column (their Gram terms are
-                    // added exactly in stage C)
-                    const bool un = !(gC[c2] >= kSafeFloor);
-                    if (un) pmask |= 1u << c2;
-                    rgC[c2] = un ? 0.f : __builtin_amdgcn_rcpf(gC[c2]);
+                // Gram rows in pcol order, the state's rows in natural order
+                st2(&sm.fac[pw][pw < facrow::SUB ? pc0 : ch0], fv0[0], fv0[1]);
+                if (pw + NWP < facrow::N) st2(&sm.fac[pw + NWP][ch0], fv1[0], fv1[1]);
+                if (fl2) {
+                    atomicOr(&sm.fbm[nn & 1][pw >> 1][ch0 >> 5], fl2 << (ch0 & 31));
+                    atomicOr(&sm.fbany[nn & 1], 1u);
                 }
-                if (pw == 0) st2(&sm.gam[nn & 1][ch0], gC[0], gC[1]);
-                if (pmask) atomicOr(&sm.unsafe[nn % 3], 1u);
-                // K-tilde is kept scaled by ksc (a power of 2) for the fp16 update;
-                // Kc = K-tilde / gamma_C takes 1 / ksc back through rgC
+                if (pw == 0) st2(&sm.gam[nn & 1][ch0], lastsub[0], lastsub[1]);
+                // K-tilde is kept scaled by ksc (a power of 2) for the fp16 update
                 const int ek = pow2_exp(__uint_as_float(sm.kmax[nn % 3]));
-                const float ksc = ldexpf(1.f, -ek), iksc = ldexpf(1.f, ek);
-                // ksc * gamma_C / gamma at each row: suffix products within the block
-                float om[RB][2];
+                const float ksc = ldexpf(1.f, -ek);
+                // suffix products within the wave's rows: b (to the sub-block end);
+                // ksc * gamma_C / gamma (to the chunk end) is b times tk
+                float bs[RB][2], tk[2];
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
-                    rgC[c2] *= iksc;
-                    om[RB - 1][c2] = pgt[c2] * ksc;
+                    tk[c2] = after[c2] * ksc;
+                    bs[RB - 1][c2] = bstart[c2];
 #pragma unroll
-                    for (int e = RB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * rf.get(e + 1, c2);
+                    for (int e = RB - 2; e >= 0; --e) bs[e][c2] = bs[e + 1][c2] * rf.get(e + 1, c2);
                 }
-                float ga[2] = {plt[0], plt[1]};   // gamma at the current row
+                float ga[2] = {astart[0], astart[1]};   // a at the current row
                 float kprev[2] = {0.f, 0.f};
+                const int pcz = pc0 + oz;
 #pragma unroll
                 for (int e = 0; e < RB; ++e) {
                     float qo[2], ko[2], co[2];
@@ -542,17 +663,17 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int c2 = 0; c2 < 2; ++c2) {
                         ga[c2] *= rf.get(e, c2);
                         const float kf = rk.get(e, c2), qf = rq.get(e, c2);
-                        const float kt = kf * om[e][c2];   // K-tilde * ksc
+                        const float kt = kf * (bs[e][c2] * tk[c2]);   // K-tilde * ksc
                         qo[c2] = qf * ga[c2];
                         ko[c2] = kf * ga[c2];
-                        co[c2] = kt * rgC[c2];             // k / gamma = K-tilde / gamma_C
+                        co[c2] = kf * bs[e][c2];
                         if (e & 1) keep_kt[c2].set_pair_h(e >> 1, kprev[c2], kt);
                         else kprev[c2] = kt;
                     }
-                    st2(&sm.Qb[(rb + e) * LD + pc0], qo[0], qo[1]);
-                    st2(&sm.Kb[(rb + e) * LD + pc0], ko[0], ko[1]);
-                    st2(&sm.Kc[(rb + e) * LD + pc0], co[0], co[1]);
-                    rv.store(&sm.V[(rb + e) * LD + pc0], e);
+                    st2(&sm.Qb[(rb + e) * LD + pcz], qo[0], qo[1]);
+                    st2(&sm.Kb[(rb + e) * LD + pcz], ko[0], ko[1]);
+                    st2(&sm.Kc[(rb + e) * LD + pcz], co[0], co[1]);
+                    rv.store(&sm.V[(rb + e) * LD + pcz], e);
                 }
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
@@ -563,39 +684,8 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
-            const bool fallback = prod_on && sm.unsafe[nn % 3] != 0u;
-            if (fallback) {
-                // Exact Gram terms of the key channels of chunk nn whose decay is
-                // below the floor: G_K[t,s] (s<t) accumulates at M[t][s], P[t,s]
-                // (s<t) at M[s][t], P[t,t] at M[t][t].  Rare path: rows are
-                // re-read from global memory.
-                for (int x = tid - NWC * 64; x < CH * LDM / 4; x += NWP * 64)
-                    reinterpret_cast<floatx4*>(sm.M)[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-                lds_barrier();
-                if (pw == 0 && pmask) {
-                    const int t0 = nn * CH;
-#pragma unroll 1
-                    for (int c = 0; c < 2; ++c) {
-                        if (!((pmask >> c) & 1u)) continue;
-                        const uint32_t off = (uint32_t)t0 * rs + hoff + ch0 + c;
-#pragma unroll 1
-                        for (int s = 0; s < CH && t0 + s < T; ++s) {
-                            const float ks_ = TR::tof(kb[off + s * rs]);
-                            atomicAdd(&sm.M[s * LDM + s], TR::tof(qb[off + s * rs]) * ks_);
-                            float prod = 1.f;
-#pragma unroll 1
-                            for (int t = s + 1; t < CH && t0 + t < T; ++t) {
-                                prod *= TR::tof(fb[off + t * rs]);
-                                atomicAdd(&sm.M[t * LDM + s], TR::tof(kb[off + t * rs]) * ks_ * prod);
-                                atomicAdd(&sm.M[s * LDM + t], TR::tof(qb[off + t * rs]) * ks_ * prod);
-                            }
-                        }
-                    }
-                }
-                lds_barrier();
-            }
             load_k(npf);
-            if (prod_on) gram_tile(kYes(), kYes(), pw, nn, fallback);   // tiles 0..7
+            if (prod_on) gram_tile(kYes(), kYes(), pw, nn);   // tiles 0..7
             load_v(npf);
             load_f(npf);
             KD_PHASE_MARK(n, 5);

@@ -17,6 +17,13 @@ Recipe (fixed draw order from one ``numpy.random.Generator(PCG64(seed))``):
   6. c = sigmoid(N(0, 1)) of shape [B, T, H].
   7. dO ~ N(0, 1) of shape [B, T, H, dv] (only when requested).
   8. S0 ~ N(0, s0_std^2) of shape [B, H, dv, dk] (only when s0_std is given).
+  9. dS_T ~ N(0, dST_std^2) (only when dST_std is given).
+  10. resets: that many (b, t, h) rows per (b, h), drawn uniformly, get f = 0
+      on every key channel (an exact reset of the state; only when requested).
+With a_log_value given, step 3 still draws (so every later draw is the same)
+but every head takes exp(a_log_value) as its exponent: a_log_value = 1 with
+mu = 0 gives the fast-decay gates sigmoid(N(0, 1))^e, whose decay over a
+64-token chunk falls below 2^-100 on most key channels.
 q, k, v, f (and dO) are then rounded to the workload's dtype with
 round-to-nearest-even; beta, c and S0 stay fp32.  Both the GPU library and
 the oracle consume the rounded values (the oracle upcasts them exactly).
@@ -71,6 +78,7 @@ class Workload:
     decode: bool = False   # token-by-token on a carried state (S0 drawn, N(0, 0.1^2))
     gdn2: bool = False     # the Gated Delta Rule-2 variant (decoupled erase and write)
     mixer: bool = False    # from the projections: pre-processing, the rule, gated RMSNorm
+    a_log_value: float | None = None   # every head's gate exponent is exp(a_log_value)
 
     @property
     def tokens(self) -> int:
@@ -95,6 +103,9 @@ WORKLOADS = {
     "gdn2_step": Workload("gdn2_step", 8, 2048, 16, 128, 128, "bf16", seed=1006, gdn2=True),
     # The whole mixer forward at the training-step shape, from the projections.
     "mixer_step": Workload("mixer_step", 8, 2048, 16, 128, 128, "bf16", seed=1007, mixer=True),
+    # The training-step forward under fast-decay gates sigmoid(N(0,1))^e.
+    "fast_decay": Workload("fast_decay", 8, 2048, 16, 128, 128, "bf16", mu=0.0, seed=1008,
+                           a_log_value=1.0),
 }
 
 MIXER_CONV_SIZE = 4
@@ -109,7 +120,7 @@ def _l2n(x):
 
 
 def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
-         s0_std=None, dST_std=None):
+         s0_std=None, dST_std=None, a_log_value=None, resets=0):
     """Draw fp64 inputs (before dtype rounding).  Returns a dict."""
     rng = np.random.Generator(np.random.PCG64(seed))
     q = _l2n(rng.standard_normal((B, T, H, dk)))
@@ -117,6 +128,8 @@ def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
     v = _l2n(rng.standard_normal((B, T, H, dv)))
     x = rng.normal(mu, 1.0, (B, T, H, dk))
     a_log = rng.uniform(-1.0, 1.0, (H,))
+    if a_log_value is not None:
+        a_log = np.full((H,), float(a_log_value))
     f = _sigmoid(x) ** np.exp(a_log)[None, None, :, None]
     beta = beta_scale * _sigmoid(rng.standard_normal((B, T, H)))
     c = _sigmoid(rng.standard_normal((B, T, H)))
@@ -127,6 +140,10 @@ def draw(B, T, H, dk, dv, seed, mu=3.0, beta_scale=1.0, with_dO=False,
         out["S0"] = rng.normal(0.0, s0_std, (B, H, dv, dk))
     if dST_std is not None:
         out["dST"] = rng.normal(0.0, dST_std, (B, H, dv, dk))
+    if resets and T > 0:
+        for b in range(B):
+            for h in range(H):
+                out["f"][b, rng.integers(0, T, resets), h, :] = 0.0
     return out
 
 
@@ -176,7 +193,8 @@ def draw_workload(w: Workload, with_dO=None, s0_std=None):
     if s0_std is None and w.decode:
         s0_std = 0.1
     return draw(w.B, w.T, w.H, w.dk, w.dv, w.seed, mu=w.mu, beta_scale=w.beta_scale,
-                with_dO=w.backward if with_dO is None else with_dO, s0_std=s0_std)
+                with_dO=w.backward if with_dO is None else with_dO, s0_std=s0_std,
+                a_log_value=w.a_log_value)
 
 
 def round_to(x, dtype: str):

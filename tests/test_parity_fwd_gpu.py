@@ -65,7 +65,7 @@ def check(x, dtype, tol=None):
 
 
 # ------------------------------------------------------------ named workloads
-@pytest.mark.parametrize("name", ["tiny_fp32", "single_seq", "train_step", "long_ctx"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "single_seq", "train_step", "long_ctx", "fast_decay"])
 def test_workload_full_size(name):
     w = sy.WORKLOADS[name]
     x = sy.draw_workload(w, with_dO=False)
@@ -95,10 +95,11 @@ def test_empty_sequence_returns_initial_state():
 
 
 # ------------------------------------------------------------ structured inputs
-def test_clustered_repeated_keys_beta_near_two():
+@pytest.mark.parametrize("T", [256, 2048])
+def test_clustered_repeated_keys_beta_near_two(T):
     """Repeated / clustered keys and values make (I + M) far from identity."""
     rng = np.random.default_rng(77)
-    B, T, H, d = 1, 256, 4, 128
+    B, H, d = 1, 4, 128
     x = sy.draw(B, T, H, d, d, seed=77, mu=5.0, beta_scale=2.0)
     base_k = rng.standard_normal((H, 4, d))
     base_v = rng.standard_normal((H, 4, d))
@@ -112,10 +113,34 @@ def test_clustered_repeated_keys_beta_near_two():
     check(x, "bf16")
 
 
+FAST = [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp32", 32), ("fp32", 64)]
+
+
+@pytest.mark.parametrize("dtype,d", FAST)
+@pytest.mark.parametrize("mu", [0.0, 1.0])
+def test_fast_decay_gates(dtype, d, mu):
+    """Gates sigmoid(N(mu, 1))^e: over a 64-token chunk most key channels
+    (mu = 0) or about half of them (mu = 1) decay below 2^-100, while over a
+    16-token sub-block none does.  Several chunks and a ragged tail."""
+    x = sy.draw(2, 1024 + 37, 3, d, d, seed=120 + d + int(4 * mu), mu=mu, a_log_value=1.0,
+                beta_scale=2.0, s0_std=0.1)
+    check(x, dtype)
+
+
+@pytest.mark.parametrize("dtype,d", FAST)
+def test_resets_under_fast_decay(dtype, d):
+    """Exact resets (f = 0 on every key channel at random tokens) on top of
+    fast-decay gates: the sub-blocks that hold a reset take the exact path of
+    their diagonal Gram tile."""
+    x = sy.draw(2, 700, 3, d, d, seed=140 + d, mu=0.0, a_log_value=1.0, s0_std=0.1, resets=6)
+    check(x, dtype)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_extreme_decay_takes_exact_fallback(dtype):
     """Sub-blocks whose decay product drops below 2^-100 (tiny f, and exact
-    zeros = full reset) go through the exact scalar fallback."""
+    zeros = partial and full resets) take the exact path of their diagonal
+    Gram tile; sub-blocks without decay next to them do not."""
     rng = np.random.default_rng(78)
     B, T, H, d = 1, 192, 2, 64 if dtype == "bf16" else 32
     x = sy.draw(B, T, H, d, d, seed=78, s0_std=0.2)
