@@ -28,11 +28,10 @@
 //      while the previous chunk is processed;
 //   3. kd_bwd_chunk_kernel: one workgroup per (b, h, chunk), all chunks in
 //      parallel: every local gradient.
-// A chunk with a key channel whose decay over the chunk falls below 2^-100
-// (the forward's exact-fallback case, which includes f = 0) is not handled
-// here: all its gradients are NaN, and so is every gradient that depends on
-// it through the state gradient (dk, dv, df, dbeta, dc of the earlier chunks
-// of that (b, h), and dS0); dq of the earlier chunks does not and stays exact.
+// Every gate value in [0, 1] is handled exactly: the sweep forms K-tilde from
+// suffix products, and the chunk gradients take the forward's 16-token
+// sub-block decay references (with an exact pass for sub-blocks whose decay
+// falls below 2^-100 and for gates below 2^-16, f = 0 among them).
 #include <type_traits>
 
 #include <time.h>
@@ -146,7 +145,6 @@ struct BwdStateSmem {
     alignas(16) float dup[NW][CH];                    // partial du per wave
     alignas(16) float bprod[NSB][D];
     alignas(16) float gam[D];
-    unsigned unsafe_any;
 };
 
 // One chunk's inputs as held in registers between its prefetch and its prep:
@@ -246,7 +244,6 @@ __device__ __forceinline__ void bwd_state_body(
         for (int i = 0; i < RG::PV; ++i) cur.p[i] = reinterpret_cast<const uint4*>(pg)[tid + NT * i];
     };
     if (NC > 0) {
-        if (tid == 0) sm.unsafe_any = 0u;
         load_part1(NC - 1);
         load_part2(NC - 1);
         load_part3(NC - 1);
@@ -296,9 +293,12 @@ __device__ __forceinline__ void bwd_state_body(
 
         // ---------------- prep (b): operands
         {
-            float plt[8], gC[8];
+            // gamma before this sub-block (plt), the decay of the sub-blocks
+            // after it (aft) and over the chunk (gC); K-tilde = k gamma_C / gamma
+            // as suffix products (no quotient: every f in [0, 1] is exact)
+            float plt[8], gC[8], aft[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; }
+            for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC[c] = 1.f; aft[c] = 1.f; }
 #pragma unroll
             for (int I2 = 0; I2 < NSB; ++I2)
 #pragma unroll
@@ -308,14 +308,10 @@ __device__ __forceinline__ void bwd_state_body(
                     for (int e = 0; e < 4; ++e) {
                         gC[4 * c4 + e] *= x[e];
                         if (I2 < I) plt[4 * c4 + e] *= x[e];
+                        if (I2 > I) aft[4 * c4 + e] *= x[e];
                     }
                 }
-            unsigned unsafe = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (!(gC[c] >= kSafeFloor)) unsafe |= 1u << c;
             if (I == 0 && r8 == 0) st8v(&sm.gam[ch0], gC);
-            if (unsafe) atomicOr(&sm.unsafe_any, 1u);
             float qo[2][8], ko[2][8];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -324,10 +320,10 @@ __device__ __forceinline__ void bwd_state_body(
                 for (int c = 0; c < 8; ++c) {
                     const float ga = plt[c] * (e == 0 ? excl[c] * cur.f.get(0, c) : incl[c]);
                     const float kf = cur.k.get(e, c);
-                    const bool un = (unsafe >> c) & 1u;
+                    const float sfx = group8_excl_suffix_prod(cur.f.get(0, c) * cur.f.get(1, c), r8);
                     qo[e][c] = cur.q.get(e, c) * ga;
                     ko[e][c] = kf * ga;
-                    kt[c] = un ? 0.f : kf * __builtin_amdgcn_rcpf(ga) * gC[c];   // K-tilde
+                    kt[c] = kf * ((e == 0 ? cur.f.get(1, c) * sfx : sfx) * aft[c]);   // K-tilde
                 }
                 st8v(&sm.Kt[(row0 + e) * LD + ch0], kt);
                 cur.v.store(&sm.V[(row0 + e) * LD + ch0], e);
@@ -412,7 +408,6 @@ __device__ __forceinline__ void bwd_state_body(
                 const float y = fmaf(-Mcol[s], readlane_f(x, s), x);
                 x = (t_ < s) ? y : x;
             }
-            if (sm.unsafe_any) x = __builtin_nanf("");
             wsrho[((size_t)bh * NC + n) * CH + t_] = x;
             sm.dr0[t_] = -sm.beta[t_] * x;
         }
@@ -421,7 +416,6 @@ __device__ __forceinline__ void bwd_state_body(
         lds_barrier();
 
         // ---------------- dS <- dS diag(gamma_C) + dO^T Qbar + V^T diag(dr0) Kbar
-        if (tid == 0) sm.unsafe_any = 0u;   // read for the last time above
         {
             Frag bO[KC_], bR[KC_];
 #pragma unroll
@@ -460,35 +454,72 @@ __device__ __forceinline__ void bwd_state_body(
 // ======================================================================
 // Chunk-local gradients, every chunk in parallel
 // ======================================================================
+// Gates below this go through the exact pass: d log f_s is a suffix sum
+// whose non-spanning Gram pairs cancel only to the rounding of the fp32
+// accumulation, and df = d log f / f divides that residual by f (f = 0 gives
+// 0 / 0).  The bound is where the amplified residual stays well under each
+// dtype's error bar: 2^-16 for bf16 inputs, 2^-4 for fp32 inputs (measured
+// under sigmoid(N(0,1))^e gates: at 2^-7 the fp32 df error was 1.5e-5).
+template <class TR> struct TinyGate { static constexpr float value = 1.52587890625e-05f; };   // 2^-16
+template <> struct TinyGate<F32T> { static constexpr float value = 0.0625f; };              // 2^-4
+
 template <class TR, int D>
 struct BwdChunkSmem {
     typedef typename TR::E E;
     static constexpr int LD = D + TR::PAD;     // [CH][D] operands
     static constexpr int LDP = CH + TR::PAD;   // [CH][CH] matrices
     static constexpr int LDF = D + 4;          // fp32 staging of the results
+    static constexpr int NFW = (D + 31) / 32;  // words of a per-channel bit set
     static constexpr size_t ROWB = (size_t)CH * LD * sizeof(E);
     static constexpr size_t SQB = (size_t)CH * LDP * sizeof(E);
     static constexpr size_t OPB = 5 * ROWB + 6 * SQB;
     static constexpr size_t STB = 4 * (size_t)CH * LDF * sizeof(float);
-    // operands (Qb, Kb, Kc, V, dO, then P, dGK hi/lo, dP hi/lo, Gsym); later the staging
+    // operands (Qloc, Kloc, Kr, V, dO, then P, dGK hi/lo, dP hi/lo, Gsym); later the staging
     alignas(16) unsigned char big[OPB > STB ? OPB : STB];
-    alignas(16) float gam[D];          // gamma_C
     alignas(16) float beta[CH];
     alignas(16) float u[CH];
     alignas(16) float r0[CH];
     alignas(16) float drho[CH];
     alignas(16) float dr0[CH];
     alignas(16) float dbp[NSB][CH];    // dbeta partial of row t from column block J (J <= t / 16)
-    alignas(16) float bprod[NSB][D];
+    alignas(16) float bprod[NSB][D];   // decay over each sub-block
+    // per key channel: tile factors (0 .. 3: 1 / decay over sub-block I, 0 below
+    // the floor; 4, 5, 6: the decay between the sub-blocks of tiles (2,0),
+    // (3,1), (3,0)), gamma before each sub-block, decay after each sub-block
+    alignas(16) float fac[7][D];
+    alignas(16) float gmm[NSB][D];
+    alignas(16) float aft[NSB][D];
     alignas(16) float gC2[D];          // sum_i dS[i][j] S0[i][j]
     alignas(16) float gsub[NSB][D];    // sub-block sums of g
     alignas(16) float hsub[NSB][D];    // sub-block sums of dKt * Kt
-    unsigned unsafe_any;
+    unsigned fbm[NSB][NFW];            // diagonal tiles: channels below the floor
+    unsigned xset[NSB][NFW];           // (sub-block, channel) pairs of the exact pass
+    unsigned stale;
 };
 
 // The gradients of chunk n of (b, h) = bh.  stale (thread 0's is read):
 // nonzero when dS and rho of the unit could not be received; every output of
-// the unit is then NaN, as for an unsafe decay.
+// the unit is then NaN.
+//
+// Decay references as in the forward: a_t = prod of f from the start of t's
+// 16-token sub-block through t, b_t = prod of f after t to the sub-block's
+// end; Qloc = q a, Kloc = k a, Kr = k b (at most 1).  Tile (I, J) of the Grams
+// is Kloc_I diag(fac_IJ) Kr_J^T.  Their gradients go per sub-block pair, the
+// pair's factor applied to the accumulator (a per-lane scalar of the output
+// column), so that each Gram pair (t, s) enters the row sum of t and the
+// column sum of s of the decay gradient with the same rounded operands:
+//   row role   XQ_t = sum_J fac (dP_IJ Kr_J),  XK_t = sum_J fac (dGK_IJ Kr_J),
+//   column role Y_s = sum_I fac (dGK_IJ^T Kloc_I + dP_IJ^T Qloc_I),
+// and the state parts, in the same local variables:
+//   dq_t = a_t (Gamma_I (dO S0)_t + XQ_t),
+//   dk_t = a_t (Gamma_I dr0_t (V S0)_t + XK_t) + b_t Y_t + b_t after_I (W dS)_t,
+//   g_t  = Qloc_t (.) + Kloc_t (.) - Kr_t Y_t - Kt_t (W dS)_t,
+//   d log f_s = sum_{t >= s} g_t + g_C,  df = d log f / f,
+// with Gamma_I = gamma before sub-block I and after_I the decay of the
+// sub-blocks after I.  For a (sub-block, channel) pair whose diagonal tile
+// left the channel out (decay below the floor) or that holds a gate below
+// TinyGate<TR>::value, the exact pass writes dq, dk and df of those 16 tokens from the
+// recurrence on the state's column j (from the records S0 and dS).
 template <class TR, int D>
 __device__ __forceinline__ void bwd_chunk_body(
     BwdChunkSmem<TR, D>& sm, int bh, int n, int tid, unsigned stale,
@@ -503,16 +534,17 @@ __device__ __forceinline__ void bwd_chunk_body(
 {
     typedef typename TR::E E;
     typedef typename TR::Frag Frag;
+    typedef typename TR::F16 F16;
     typedef BwdChunkSmem<TR, D> SM;
     constexpr int NT = 4 * D;
     constexpr int NW = D / 16;
     constexpr int KD_ = D / TR::KS;
     constexpr int KC_ = CH / TR::KS;
-    constexpr int LD = SM::LD, LDP = SM::LDP, LDF = SM::LDF;
+    constexpr int LD = SM::LD, LDP = SM::LDP, LDF = SM::LDF, NFW = SM::NFW;
 
-    E* Qb = reinterpret_cast<E*>(sm.big);
-    E* Kb = Qb + CH * LD;
-    E* Kc = Kb + CH * LD;
+    E* Qb = reinterpret_cast<E*>(sm.big);   // Qloc
+    E* Kb = Qb + CH * LD;                   // Kloc
+    E* Kc = Kb + CH * LD;                   // Kr
     E* Vs = Kc + CH * LD;
     E* Do = Vs + CH * LD;
     E* P = Do + CH * LD;
@@ -556,29 +588,20 @@ __device__ __forceinline__ void bwd_chunk_body(
                 if (n * CH + row0 + e >= T) { rq_.clear(e, 0.f); rk_.clear(e, 0.f); rf_.clear(e, 1.f); }
         }
     };
-    // gamma at this thread's two rows and gamma_C, from f and the sub-block
-    // products in sm.bprod (the same arithmetic every time it is called)
-    auto gammas = [&](const Row2x8<TR>& rf_, float (&ga_)[2][8], float (&gC_)[8]) {
-        float plt[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) { plt[c] = 1.f; gC_[c] = 1.f; }
-#pragma unroll
-        for (int I2 = 0; I2 < NSB; ++I2)
-#pragma unroll
-            for (int c4 = 0; c4 < 2; ++c4) {
-                const floatx4 x = *reinterpret_cast<const floatx4*>(&sm.bprod[I2][ch0 + 4 * c4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gC_[4 * c4 + e] *= x[e];
-                    if (I2 < I) plt[4 * c4 + e] *= x[e];
-                }
-            }
+    // a and b at this thread's two rows (the same arithmetic every time it is
+    // called): prefix and suffix products inside the 8-lane group of the
+    // sub-block's row pairs
+    auto locals = [&](const Row2x8<TR>& rf_, float (&a_)[2][8], float (&b_)[2][8]) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float incl = group8_prefix_prod(rf_.get(0, c) * rf_.get(1, c), r8);
+            const float f0 = rf_.get(0, c), f1 = rf_.get(1, c);
+            const float incl = group8_prefix_prod(f0 * f1, r8);
             const float excl = group8_shift1(incl, r8);
-            ga_[0][c] = plt[c] * (excl * rf_.get(0, c));
-            ga_[1][c] = plt[c] * incl;
+            const float sfx = group8_excl_suffix_prod(f0 * f1, r8);
+            a_[0][c] = excl * f0;
+            a_[1][c] = incl;
+            b_[1][c] = sfx;
+            b_[0][c] = f1 * sfx;
         }
     };
     Row2x8<TR> pq, pk, rv, pf, ro;   // prep copies of q, k, f
@@ -602,7 +625,8 @@ __device__ __forceinline__ void bwd_chunk_body(
     // the upper triangles of P, dGK, dP (hi and lo) are never written
     for (int x = tid; x < 5 * CH * LDP * (int)sizeof(E) / 16; x += NT)
         reinterpret_cast<uint4*>(P)[x] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid == 0) sm.unsafe_any = stale;
+    if (tid < NSB * NFW) { (&sm.fbm[0][0])[tid] = 0u; (&sm.xset[0][0])[tid] = 0u; }
+    if (tid == 0) sm.stale = stale;
     {
         float incl[8];
 #pragma unroll
@@ -611,27 +635,57 @@ __device__ __forceinline__ void bwd_chunk_body(
     }
     lds_barrier();
 
-    // ---------------- prep (b): operands
+    // ---------------- prep (b): operands, factors, the exact pass's pairs
     {
-        float ga[2][8], gC[8];
-        gammas(pf, ga, gC);
-        unsigned unsafe = 0;
+        float bp[NSB][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            if (!(gC[c] >= kSafeFloor)) unsafe |= 1u << c;
-        if (unsafe) atomicOr(&sm.unsafe_any, 1u);
-        if (I == 0 && r8 == 0) st8v(&sm.gam[ch0], gC);
+        for (int I2 = 0; I2 < NSB; ++I2) ld8f(&sm.bprod[I2][ch0], bp[I2]);
+        float a_[2][8], b_[2][8];
+        locals(pf, a_, b_);
+        unsigned fl = 0u, tiny = 0u;   // bit c: channel ch0 + c
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (!(bp[I][c] >= kSafeFloor)) fl |= 1u << c;
+            if (!(pf.get(0, c) >= TinyGate<TR>::value) || !(pf.get(1, c) >= TinyGate<TR>::value)) tiny |= 1u << c;
+        }
+        if (r8 == 0 && fl) atomicOr(&sm.fbm[I][ch0 >> 5], fl << (ch0 & 31));
+        if (fl | tiny) atomicOr(&sm.xset[I][ch0 >> 5], (fl | tiny) << (ch0 & 31));
+        if (r8 == 0) {   // this sub-block's diagonal factor; sub-block 0 also the rest
+            float x[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = bp[I][c] >= kSafeFloor ? __builtin_amdgcn_rcpf(bp[I][c]) : 0.f;
+            st8v(&sm.fac[I][ch0], x);
+            if (I == 0) {
+                float y[8], z[8], gm[NSB][8], af[NSB][8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    x[c] = bp[1][c]; y[c] = bp[2][c]; z[c] = bp[1][c] * bp[2][c];
+                    gm[0][c] = 1.f;
+#pragma unroll
+                    for (int I2 = 1; I2 < NSB; ++I2) gm[I2][c] = gm[I2 - 1][c] * bp[I2 - 1][c];
+                    af[NSB - 1][c] = 1.f;
+#pragma unroll
+                    for (int I2 = NSB - 2; I2 >= 0; --I2) af[I2][c] = af[I2 + 1][c] * bp[I2 + 1][c];
+                }
+                st8v(&sm.fac[4][ch0], x);
+                st8v(&sm.fac[5][ch0], y);
+                st8v(&sm.fac[6][ch0], z);
+#pragma unroll
+                for (int I2 = 0; I2 < NSB; ++I2) {
+                    st8v(&sm.gmm[I2][ch0], gm[I2]);
+                    st8v(&sm.aft[I2][ch0], af[I2]);
+                }
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float qo[8], ko[8], co[8];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float kf = pk.get(e, c);
-                const bool un = (unsafe >> c) & 1u;
-                const float kr = kf * __builtin_amdgcn_rcpf(ga[e][c]);
-                qo[c] = pq.get(e, c) * ga[e][c];
-                ko[c] = kf * ga[e][c];
-                co[c] = un ? 0.f : kr;
+                qo[c] = pq.get(e, c) * a_[e][c];
+                ko[c] = kf * a_[e][c];
+                co[c] = kf * b_[e][c];
             }
             st8v(&Qb[(row0 + e) * LD + ch0], qo);
             st8v(&Kb[(row0 + e) * LD + ch0], ko);
@@ -647,17 +701,54 @@ __device__ __forceinline__ void bwd_chunk_body(
     for (int tile = w; tile < 10; tile += NW) {
         const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
         const int J_ = tile - (I_ * (I_ + 1)) / 2;
+        const int fr = I_ == J_ ? I_ : I_ - J_ == 2 ? (J_ == 0 ? 4 : 5) : I_ - J_ == 3 ? 6 : -1;
         const int s_ = SB * J_ + cl;
         floatx4 gk = {0.f, 0.f, 0.f, 0.f}, gv = gk, pp = gk, dp = gk;
         const float us = sm.u[s_];
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
-            const Frag fk = TR::ld_nat(&Kc[(SB * J_ + cl) * LD], ks, g);
+            Frag fk = TR::ld_nat(&Kc[(SB * J_ + cl) * LD], ks, g);
+            if (fr >= 0) fk = TR::scale_k(fk, 1.f, sm.fac[fr], ks, g);
             const Frag fv = TR::ld_nat(&Vs[(SB * J_ + cl) * LD], ks, g);
             gk = TR::mma(TR::ld_nat(&Kb[(SB * I_ + cl) * LD], ks, g), fk, gk);
             pp = TR::mma(TR::ld_nat(&Qb[(SB * I_ + cl) * LD], ks, g), fk, pp);
             gv = TR::mma(TR::ld_nat(&Vs[(SB * I_ + cl) * LD], ks, g), fv, gv);
             dp = TR::mma(TR::ld_nat(&Do[(SB * I_ + cl) * LD], ks, g), fv, dp);
+        }
+        if (I_ == J_) {
+            // channels below the floor, left out of this diagonal tile: their
+            // G_K and P terms exactly (rows re-read from global memory)
+            const int rb0 = n * CH + SB * I_;
+#pragma unroll 1
+            for (int wd = 0; wd < NFW; ++wd) {
+                unsigned bits = __builtin_amdgcn_readfirstlane(sm.fbm[I_][wd]);
+#pragma unroll 1
+                while (bits) {
+                    const int j = 32 * wd + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const uint32_t cj = hoff + (uint32_t)j;
+                    auto ldv = [&](const E* p, int x) {
+                        const int t = rb0 + x;
+                        return t < T ? TR::tof(p[bbase + (uint32_t)t * rs + cj]) : 0.f;
+                    };
+                    const float fl = rb0 + cl < T ? TR::tof(f[bbase + (uint32_t)(rb0 + cl) * rs + cj]) : 1.f;
+                    const float ksv = ldv(k, cl);
+                    float e4[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll 1
+                    for (int uu = 1; uu < SB; ++uu) {
+                        const float fu = readlane_f(fl, uu);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e4[r] = (uu > cl && uu <= 4 * g + r) ? e4[r] * fu : e4[r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * g + r;
+                        const float w_ = ksv * e4[r];
+                        if (t > cl) gk[r] += ldv(k, t) * w_;
+                        if (t >= cl) pp[r] += ldv(q, t) * w_;
+                    }
+                }
+            }
         }
         dp = dp * us;   // dP[t][s] = u_s (dO V^T)[t][s]: column s = this lane's
 #pragma unroll
@@ -705,10 +796,10 @@ __device__ __forceinline__ void bwd_chunk_body(
 
     // ---------------- C x D results, this wave's 16 columns, all 64 rows
     // Scalings by u[t] or dr0[t] of the output row t are applied to the
-    // accumulators, not to the operands: aK and aT start as V S0 and V dS, and
-    // dV is accumulated in two parts, aVu = Kt dS^T + P^T dO (times u) and
-    // aVr = dr0 (Kbar S0^T) + (dGV + dGV^T) V.  The key-channel scaling of
-    // Kt = Kc gamma_C goes on the dS fragment, once per K-step.
+    // accumulators: aK and aT start as V S0 and V dS, and dV is accumulated in
+    // two parts, aVu = Kt dS^T + P^T dO (times u) and aVr = dr0 (Kbar S0^T) +
+    // (dGV + dGV^T) V.  Kt = Kr after_tt and Kbar = Kloc Gamma_tt take their
+    // key-channel factors on the dS and S0 fragments, per token sub-block.
     floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB], aVu[NSB], aVr[NSB];
 #pragma unroll
     for (int tt = 0; tt < NSB; ++tt) {
@@ -732,8 +823,8 @@ __device__ __forceinline__ void bwd_chunk_body(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) gc2 += ts[hh][r] * td[hh][r];
             }
-            const Frag b_dsg = TR::scale_k(TR::ld_nat(dSn + jc * D, ks, g), 1.f, sm.gam, ks, g);   // B[j][i] = dS[i][j] gamma_C[j]
-            const Frag b_s0 = TR::ld_nat(S0n + jc * D, ks, g);     // B[j][i] = S0[i][j]
+            const Frag r_ds = TR::ld_nat(dSn + jc * D, ks, g);   // B[j][i] = dS[i][j]
+            const Frag r_s0 = TR::ld_nat(S0n + jc * D, ks, g);   // B[j][i] = S0[i][j]
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) {
                 const int tr = SB * tt + cl;
@@ -741,8 +832,10 @@ __device__ __forceinline__ void bwd_chunk_body(
                 aQ[tt] = TR::mma(TR::ld_colmatch(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);   // dO S0
                 aK[tt] = TR::mma(a_v, b_s0t, aK[tt]);                                      // V S0
                 aT[tt] = TR::mma(a_v, b_dst, aT[tt]);                                      // V dS
-                aVu[tt] = TR::mma(TR::ld_nat(&Kc[tr * LD], ks, g), b_dsg, aVu[tt]);       // Kt dS^T
-                aVr[tt] = TR::mma(TR::ld_nat(&Kb[tr * LD], ks, g), b_s0, aVr[tt]);        // Kbar S0^T
+                const Frag b_dsa = tt + 1 < NSB ? TR::scale_k(r_ds, 1.f, sm.aft[tt], ks, g) : r_ds;
+                const Frag b_s0g = tt ? TR::scale_k(r_s0, 1.f, sm.gmm[tt], ks, g) : r_s0;
+                aVu[tt] = TR::mma(TR::ld_nat(&Kc[tr * LD], ks, g), b_dsa, aVu[tt]);      // Kt dS^T
+                aVr[tt] = TR::mma(TR::ld_nat(&Kb[tr * LD], ks, g), b_s0g, aVr[tt]);      // Kbar S0^T
             }
         }
         if (std::is_same<TR, Bf16T>::value) {
@@ -755,33 +848,63 @@ __device__ __forceinline__ void bwd_chunk_body(
     for (int tt = 0; tt < NSB; ++tt) {
         const floatx4 r0v = *reinterpret_cast<const floatx4*>(&sm.dr0[SB * tt + 4 * g]);
         const floatx4 uv = *reinterpret_cast<const floatx4*>(&sm.u[SB * tt + 4 * g]);
-        aK[tt] = aK[tt] * r0v;    // dr0 (V S0)
-        aT[tt] = aT[tt] * uv;     // W dS
-        aVr[tt] = aVr[tt] * r0v;  // dr0 (Kbar S0^T)
+        const float gmj = sm.gmm[tt][jc];
+        aQ[tt] = aQ[tt] * gmj;             // Gamma (dO S0): the local variable of q
+        aK[tt] = aK[tt] * (r0v * gmj);     // Gamma dr0 (V S0)
+        aT[tt] = aT[tt] * uv;              // W dS
+        aVr[tt] = aVr[tt] * r0v;           // dr0 (Kbar S0^T)
+    }
+    // Gram gradients, per sub-block pair (K = the 16 tokens of one sub-block);
+    // dP and dGK enter as hi + lo (their bf16 rounding would dominate the
+    // error of dq and df).  Row role: rows t of sub-block I, contraction over
+    // s in J; column role: rows s of sub-block J, contraction over t in I.
+    auto pfac = [&](int I_, int J_) {   // the pair's factor for this lane's column
+        return I_ == J_ ? sm.fac[I_][jc] : I_ - J_ == 1 ? 1.f : I_ - J_ == 2 ? sm.fac[J_ == 0 ? 4 : 5][jc]
+                                                                          : sm.fac[6][jc];
+    };
+#pragma unroll
+    for (int J_ = 0; J_ < NSB; ++J_) {
+        const F16 bk = TR::ld16_col(&Kc[(SB * J_) * LD + jc], LD, g);   // Kr[s][j], s in J
+#pragma unroll
+        for (int I_ = J_; I_ < NSB; ++I_) {
+            const int tr = SB * I_ + cl;
+            floatx4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq;
+            xq = TR::mma16(TR::ld16_row(&dP[tr * LDP + SB * J_], g), bk, xq);
+            xk = TR::mma16(TR::ld16_row(&dGK[tr * LDP + SB * J_], g), bk, xk);
+            if (TR::SPLIT) {
+                xq = TR::mma16(TR::ld16_row(&dPl[tr * LDP + SB * J_], g), bk, xq);
+                xk = TR::mma16(TR::ld16_row(&dGKl[tr * LDP + SB * J_], g), bk, xk);
+            }
+            const float fa = pfac(I_, J_);
+            aQ[I_] += xq * fa;
+            aK[I_] += xk * fa;
+        }
+    }
+#pragma unroll
+    for (int I_ = 0; I_ < NSB; ++I_) {
+        const F16 bkb = TR::ld16_col(&Kb[(SB * I_) * LD + jc], LD, g);   // Kloc[t][j], t in I
+        const F16 bqb = TR::ld16_col(&Qb[(SB * I_) * LD + jc], LD, g);   // Qloc[t][j]
+#pragma unroll
+        for (int J_ = 0; J_ <= I_; ++J_) {
+            const int sc = SB * J_ + cl;   // row s of the result
+            floatx4 y = {0.f, 0.f, 0.f, 0.f};
+            y = TR::mma16(TR::ld16_col(&dGK[(SB * I_) * LDP + sc], LDP, g), bkb, y);
+            y = TR::mma16(TR::ld16_col(&dP[(SB * I_) * LDP + sc], LDP, g), bqb, y);
+            if (TR::SPLIT) {
+                y = TR::mma16(TR::ld16_col(&dGKl[(SB * I_) * LDP + sc], LDP, g), bkb, y);
+                y = TR::mma16(TR::ld16_col(&dPl[(SB * I_) * LDP + sc], LDP, g), bqb, y);
+            }
+            aC[J_] += y * pfac(I_, J_);
+        }
     }
     // contractions over the chunk: transposed operands read in place
 #pragma unroll
     for (int ks = 0; ks < KC_; ++ks) {
-        const Frag b_kc = TR::ld_col(&Kc[jc], LD, ks, g);   // B[s][j] = Kc[s][j]
-        const Frag b_kb = TR::ld_col(&Kb[jc], LD, ks, g);   // B[t][j] = Kbar[t][j]
-        const Frag b_qb = TR::ld_col(&Qb[jc], LD, ks, g);   // B[t][j] = Qbar[t][j]
         const Frag b_v = TR::ld_col(&Vs[jc], LD, ks, g);    // B[s][i] = V[s][i]
         const Frag b_do = TR::ld_col(&Do[jc], LD, ks, g);   // B[t][i] = dO[t][i]
 #pragma unroll
         for (int tt = 0; tt < NSB; ++tt) {
             const int tr = SB * tt + cl;
-            // dP and dGK enter as hi + lo (their bf16 rounding would dominate the
-            // error of dq and df)
-            aQ[tt] = TR::mma(TR::ld_nat(&dP[tr * LDP], ks, g), b_kc, aQ[tt]);            // dP Kc
-            aK[tt] = TR::mma(TR::ld_nat(&dGK[tr * LDP], ks, g), b_kc, aK[tt]);           // dGK Kc
-            aC[tt] = TR::mma(TR::ld_col(&dGK[tr], LDP, ks, g), b_kb, aC[tt]);            // dGK^T Kbar
-            aC[tt] = TR::mma(TR::ld_col(&dP[tr], LDP, ks, g), b_qb, aC[tt]);             // dP^T Qbar
-            if (TR::SPLIT) {
-                aQ[tt] = TR::mma(TR::ld_nat(&dPl[tr * LDP], ks, g), b_kc, aQ[tt]);
-                aK[tt] = TR::mma(TR::ld_nat(&dGKl[tr * LDP], ks, g), b_kc, aK[tt]);
-                aC[tt] = TR::mma(TR::ld_col(&dGKl[tr], LDP, ks, g), b_kb, aC[tt]);
-                aC[tt] = TR::mma(TR::ld_col(&dPl[tr], LDP, ks, g), b_qb, aC[tt]);
-            }
             aVr[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aVr[tt]);           // (dGV + dGV^T) V
             aVu[tt] = TR::mma(TR::ld_col(&P[tr], LDP, ks, g), b_do, aVu[tt]);            // P^T dO
         }
@@ -808,39 +931,67 @@ __device__ __forceinline__ void bwd_chunk_body(
 
     // ---------------- elementwise: dq, dk, and the decay gradient (prep layout)
     clear_qkf(rq, rk, rf);
-    float ga[2][8], gC[8];
-    gammas(rf, ga, gC);   // bitwise the values the prep used
-    const bool poison = sm.unsafe_any != 0u;
-    float dqv[2][8], dkv[2][8], suf0[8], suf1[8], totg[8], toth[8];
+    float a_[2][8], b_[2][8];
+    locals(rf, a_, b_);   // bitwise the values the prep used
+    const bool poison = sm.stale != 0u;
+    const unsigned xs = (sm.xset[I][ch0 >> 5] >> (ch0 & 31)) & 0xffu;   // channels the exact pass writes
+    // dq and dk go out at once (not needed by the suffix sums); df after them
+    auto put8 = [&](E* base_, int e, const float* x) {
+        const int t = n * CH + row0 + e;
+        if (t >= T) return;
+        const uint32_t off = (uint32_t)t * rs + hoff + ch0;
+        float y[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        float gg[2], hh[2];
+        for (int c = 0; c < 8; ++c) y[c] = poison ? __builtin_nanf("") : x[c];
+        if (xs == 0u || poison) {
+            st8v_nt(base_ + bbase + off, y);
+        } else {   // the exact pass writes the channels of xs
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (!((xs >> c) & 1u)) base_[bbase + off + c] = TR::cvt(y[c]);
+        }
+    };
+    float suf0[8], suf1[8], totg[8], toth[8];
+    {
+        float dqv[2][8], dkv[2][8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float aftc = 1.f;
+#pragma unroll
+            for (int I2 = 0; I2 < NSB; ++I2)
+                if (I2 > I) aftc *= sm.bprod[I2][ch0 + c];
+            float gg[2], hh[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int idx = (row0 + e) * LDF + ch0 + c;
+                const float dQ = stQ[idx], dK = stK[idx], dC = stC[idx], dT = stT[idx];
+                const float av = a_[e][c], bv = b_[e][c];
+                const float qf = rq.get(e, c), kf = rk.get(e, c);
+                // Qloc, Kloc, Kr exactly as the MFMA products saw them (same fp32
+                // arithmetic as the prep, same rounding): each Gram pair (t, s)
+                // then enters g_t and g_s with equal and opposite values, and the
+                // suffix sums below cancel it.  Kt enters no product whose result
+                // feeds g, so it is taken exact.
+                const float Ql = TR::tof(TR::cvt(qf * av)), Kl = TR::tof(TR::cvt(kf * av));
+                const float Kr = TR::tof(TR::cvt(kf * bv)), kta = bv * aftc, Ktv = kf * kta;
+                dqv[e][c] = dQ * av;
+                dkv[e][c] = dK * av + dC * bv + dT * kta;
+                gg[e] = dQ * Ql + dK * Kl - dC * Kr - dT * Ktv;
+                hh[e] = dT * Ktv;
+            }
+            const float pair = gg[0] + gg[1];
+            const float inc = group8_suffix_sum(pair, r8);
+            const float nxt = group8_next1(inc, r8);
+            toth[c] = group8_suffix_sum(hh[0] + hh[1], r8);
+            totg[c] = inc;
+            suf1[c] = nxt + gg[1];
+            suf0[c] = suf1[c] + gg[0];
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int idx = (row0 + e) * LDF + ch0 + c;
-            const float dQ = stQ[idx], dKb = stK[idx], dKc = stC[idx], dKt = stT[idx];
-            const float gm = ga[e][c], rg = __builtin_amdgcn_rcpf(gm);
-            const float qf = rq.get(e, c), kf = rk.get(e, c);
-            // Qbar, Kbar, Kc exactly as the MFMA products saw them (same fp32
-            // arithmetic as the prep, same rounding): each Gram pair (t, s)
-            // then enters g_t and g_s with equal and opposite values, and the
-            // suffix sums below cancel it exactly.  Kt enters no product whose
-            // result feeds g, so it is taken exact.
-            const float kr = kf * rg;
-            const float Qbar = TR::tof(TR::cvt(qf * gm)), Kbar = TR::tof(TR::cvt(kf * gm));
-            const float Kcv = TR::tof(TR::cvt(kr)), Ktv = kr * gC[c];
-            dqv[e][c] = dQ * gm;
-            dkv[e][c] = dKb * gm + dKc * rg + dKt * (gC[c] * rg);
-            gg[e] = dQ * Qbar + dKb * Kbar - dKc * Kcv - dKt * Ktv;
-            hh[e] = dKt * Ktv;
+            put8(dq, e, dqv[e]);
+            put8(dk, e, dkv[e]);
         }
-        const float pair = gg[0] + gg[1];
-        const float inc = group8_suffix_sum(pair, r8);
-        const float nxt = group8_next1(inc, r8);
-        toth[c] = group8_suffix_sum(hh[0] + hh[1], r8);
-        totg[c] = inc;
-        suf1[c] = nxt + gg[1];
-        suf0[c] = suf1[c] + gg[0];
     }
     if (r8 == 0) {
         st8v(&sm.gsub[I][ch0], totg);
@@ -851,34 +1002,19 @@ __device__ __forceinline__ void bwd_chunk_body(
         float dfv[2][8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            float later = 0.f, htot = 0.f;
+            float later = 0.f, htot = 0.f, gCc = 1.f;
 #pragma unroll
             for (int I2 = 0; I2 < NSB; ++I2) {
                 if (I2 > I) later += sm.gsub[I2][ch0 + c];
                 htot += sm.hsub[I2][ch0 + c];
+                gCc *= sm.bprod[I2][ch0 + c];
             }
-            const float base = later + gC[c] * sm.gC2[ch0 + c] + htot;
+            const float base = later + gCc * sm.gC2[ch0 + c] + htot;
             dfv[0][c] = (suf0[c] + base) / rf.get(0, c);
             dfv[1][c] = (suf1[c] + base) / rf.get(1, c);
         }
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int t = n * CH + row0 + e;
-            if (t < T) {
-                if (poison) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        dqv[e][c] = __builtin_nanf("");
-                        dkv[e][c] = dqv[e][c];
-                        dfv[e][c] = dqv[e][c];
-                    }
-                }
-                const uint32_t off = (uint32_t)t * rs + hoff + ch0;
-                st8v_nt(dq + bbase + off, dqv[e]);
-                st8v_nt(dk + bbase + off, dkv[e]);
-                st8v_nt(df + bbase + off, dfv[e]);
-            }
-        }
+        for (int e = 0; e < 2; ++e) put8(df, e, dfv[e]);
     }
     lds_barrier();   // staging reads done before dV reuses it
 #pragma unroll
@@ -902,6 +1038,102 @@ __device__ __forceinline__ void bwd_chunk_body(
         for (int J = 0; J <= tid / SB; ++J) db += sm.dbp[J][tid];   // fixed order: bitwise reproducible
         st_nt(&dbeta[gi], poison ? __builtin_nanf("") : db);
         st_nt(&dc[gi], poison ? __builtin_nanf("") : sm.drho[tid]);
+    }
+
+    // ---------------- the exact pass (rare): for each (sub-block I, channel j)
+    // of xset, one wave runs the recurrence on column j of the state and of its
+    // gradient over the chunk and writes dq, dk, df of the sub-block's tokens:
+    //   S_t = S_{t-1} f_t + u_t v_t k_t                 (column j; S_{-1} = S0)
+    //   G_t = dO_t q_t + f_{t+1} (G_{t+1} + dr0_{t+1} v_{t+1} k_{t+1})   (G_last = dS + dO q)
+    //   dq_t = S_t . dO_t,  dk_t = u_t (G_t . v_t) + dr0_t f_t (S_{t-1} . v_t),
+    //   df_t = S_{t-1} . (G_t + dr0_t v_t k_t)
+    // (the reverse mode of the per-token rule; dr0 = -beta drho, drho the
+    // total gradient of the chunk's targets u).
+    if (!poison) {
+        constexpr int NI = (D + 63) / 64;   // value rows i = lane + 64 m of this lane
+        int pair = 0;
+#pragma unroll 1
+        for (int I2 = 0; I2 < NSB; ++I2)
+#pragma unroll 1
+            for (int wd = 0; wd < NFW; ++wd) {
+                unsigned bits = __builtin_amdgcn_readfirstlane(sm.xset[I2][wd]);
+#pragma unroll 1
+                while (bits) {
+                    const int j = 32 * wd + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    if ((pair++ % NW) != w) continue;
+                    const uint32_t cj = hoff + (uint32_t)j;
+                    auto ldj = [&](const E* p, int r, float dflt) {   // row r of the chunk, channel j (wave-uniform)
+                        const int t = n * CH + r;
+                        return t < T ? TR::tof(p[bbase + (uint32_t)t * rs + cj]) : dflt;
+                    };
+                    auto ldi = [&](const E* p, int r, int m) {   // row r, value index lane + 64 m
+                        const int t = n * CH + r, i = lane + 64 * m;
+                        return (t < T && i < D) ? TR::tof(p[bbase + (uint32_t)t * rs + hoff + i]) : 0.f;
+                    };
+                    float S[NI], G[NI], Spre[NI], Sb[SB][NI];
+#pragma unroll
+                    for (int m = 0; m < NI; ++m) {
+                        const int i = lane + 64 * m;
+                        S[m] = i < D ? TR::tof(S0n[i * D + j]) : 0.f;
+                        G[m] = i < D ? TR::tof(dSn[i * D + j]) : 0.f;
+                    }
+                    const int rb0 = SB * I2;
+#pragma unroll 1
+                    for (int r = 0; r < rb0; ++r) {
+                        const float fr_ = ldj(f, r, 1.f), kr = ldj(k, r, 0.f) * sm.u[r];
+#pragma unroll
+                        for (int m = 0; m < NI; ++m) S[m] = S[m] * fr_ + kr * ldi(v, r, m);
+                    }
+#pragma unroll
+                    for (int m = 0; m < NI; ++m) Spre[m] = S[m];
+#pragma unroll
+                    for (int rr = 0; rr < SB; ++rr) {
+                        const int r = rb0 + rr;
+                        const float fr_ = ldj(f, r, 1.f), kr = ldj(k, r, 0.f) * sm.u[r];
+#pragma unroll
+                        for (int m = 0; m < NI; ++m) {
+                            S[m] = S[m] * fr_ + kr * ldi(v, r, m);
+                            Sb[rr][m] = S[m];
+                        }
+                    }
+#pragma unroll 1
+                    for (int r = CH - 1; r >= rb0 + SB; --r) {
+                        const float qr = ldj(q, r, 0.f), kr = ldj(k, r, 0.f) * sm.dr0[r], fr_ = ldj(f, r, 1.f);
+#pragma unroll
+                        for (int m = 0; m < NI; ++m) G[m] = (G[m] + qr * ldi(dO, r, m) + kr * ldi(v, r, m)) * fr_;
+                    }
+#pragma unroll
+                    for (int rr = SB - 1; rr >= 0; --rr) {
+                        const int r = rb0 + rr;
+                        const float qr = ldj(q, r, 0.f), kraw = ldj(k, r, 0.f), fr_ = ldj(f, r, 1.f);
+                        const float ur = sm.u[r], d0 = sm.dr0[r];
+                        float pq_ = 0.f, pgv = 0.f, psv = 0.f, pdf = 0.f;
+#pragma unroll
+                        for (int m = 0; m < NI; ++m) {
+                            const float dOi = ldi(dO, r, m), vi = ldi(v, r, m);
+                            const float Sp = rr ? Sb[rr - 1][m] : Spre[m];
+                            G[m] += qr * dOi;                       // gradient of S_t
+                            pq_ += Sb[rr][m] * dOi;
+                            pgv += G[m] * vi;
+                            psv += Sp * vi;
+                            const float Gb = G[m] + d0 * kraw * vi;   // gradient of S_{t-1} f_t
+                            pdf += Sp * Gb;
+                            G[m] = Gb * fr_;
+                        }
+                        const float dqx = wave_sum(pq_);
+                        const float dkx = ur * wave_sum(pgv) + d0 * fr_ * wave_sum(psv);
+                        const float dfx = wave_sum(pdf);
+                        const int t = n * CH + r;
+                        if (lane == 0 && t < T) {
+                            const size_t o = bbase + (uint32_t)t * rs + cj;
+                            dq[o] = TR::cvt(dqx);
+                            dk[o] = TR::cvt(dkx);
+                            df[o] = TR::cvt(dfx);
+                        }
+                    }
+                }
+            }
     }
 }
 

@@ -25,6 +25,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;        // chunk length (tokens per chunk)
 // The Gram tiles of a chunk take their decay relative to the 16-token
@@ -72,6 +73,23 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
     return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 #undef KD_DPP_UMAX
+
+// Sum over the 64 lanes of a wave, returned wave-uniform: DPP steps reduce
+// each row of 16 lanes, then the four row sums are read out as scalars and
+// added in a fixed order.
+#define KD_DPP_FADD(x, ctrl) ((x) + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), (ctrl), 0xf, 0xf, false)))
+__device__ __forceinline__ float wave_sum(float x) {
+    x = KD_DPP_FADD(x, 0xB1);    // quad_perm [1,0,3,2]
+    x = KD_DPP_FADD(x, 0x4E);    // quad_perm [2,3,0,1]
+    x = KD_DPP_FADD(x, 0x141);   // row_half_mirror
+    x = KD_DPP_FADD(x, 0x140);   // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+#undef KD_DPP_FADD
 
 // 2^-e for the exponent e of x (x = m 2^e, 0.5 <= m < 1): scales x into
 // [0.5, 1).  Returns 1 for x == 0 (or non-finite x).
@@ -190,6 +208,22 @@ struct Bf16T {
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[4 + e] = cvt(tof(x[4 + e]) * (s * b[e]));
         return r;
+    }
+    // Contractions of length 16 (one sub-block): one 16x16x16 MFMA, lane group
+    // g holding K = 4g .. 4g + 3.  From a row (K contiguous) or a column (K
+    // strided by ld).
+    typedef s16x4 F16;
+    static __device__ __forceinline__ F16 ld16_row(const E* row, int g) {
+        return *reinterpret_cast<const F16*>(row + 4 * g);
+    }
+    static __device__ __forceinline__ F16 ld16_col(const E* col, int ld, int g) {
+        F16 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(short, col[(4 * g + e) * ld]);
+        return r;
+    }
+    static __device__ __forceinline__ floatx4 mma16(F16 a, F16 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
     // operands that need more than bf16 precision are stored as hi + lo
     static constexpr bool SPLIT = true;
@@ -328,6 +362,19 @@ struct F32T {
     static __device__ __forceinline__ Frag scale_k(Frag x, float s, const float* sv, int ks, int g) {
         return x * (s * sv[KS * ks + g]);
     }
+    // Contractions of length 16: four 16x16x4 MFMAs, step e taking K = 4e + g.
+    typedef floatx4 F16;
+    static __device__ __forceinline__ F16 ld16_row(const E* row, int g) {
+        return F16{row[g], row[4 + g], row[8 + g], row[12 + g]};
+    }
+    static __device__ __forceinline__ F16 ld16_col(const E* col, int ld, int g) {
+        return F16{col[g * ld], col[(4 + g) * ld], col[(8 + g) * ld], col[(12 + g) * ld]};
+    }
+    static __device__ __forceinline__ floatx4 mma16(F16 a, F16 b, floatx4 c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = mma(a[e], b[e], c);
+        return c;
+    }
     static constexpr bool SPLIT = false;
     static __device__ __forceinline__ E lo_part(float, E) { return 0.f; }
     static __device__ __forceinline__ Frag row_times(const E* row, const float* u, int ks, int g) {
@@ -440,6 +487,22 @@ __device__ __forceinline__ float group8_suffix_sum(float x, int r8) {
     y = dpp_row_shl0<4>(x);
     x = (r8 <= 3) ? x + y : x;
     return x;
+}
+// product over the lanes after this one in its aligned 8-lane group (1 for
+// the last lane): the exclusive suffix product
+template <int S>
+__device__ __forceinline__ float dpp_row_shl1(float x) {   // lane i <- lane i+S of its 16-lane row (1 if none)
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x100 + S, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float group8_excl_suffix_prod(float x, int r8) {
+    float y = dpp_row_shl1<1>(x);
+    x = (r8 <= 6) ? x * y : x;        // lanes r8 .. r8+1
+    y = dpp_row_shl1<2>(x);
+    x = (r8 <= 5) ? x * y : x;        // r8 .. r8+3
+    y = dpp_row_shl1<4>(x);
+    x = (r8 <= 3) ? x * y : x;        // r8 .. 7: inclusive suffix
+    y = dpp_row_shl1<1>(x);
+    return r8 <= 6 ? y : 1.f;
 }
 // value of x in the next lane of the group (0 for the last lane)
 __device__ __forceinline__ float group8_next1(float x, int r8) {
