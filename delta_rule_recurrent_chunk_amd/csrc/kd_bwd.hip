@@ -1283,6 +1283,19 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
     }
 }
 
+// Zeroes the claim counters and the hand-off flags of a fused launch: every
+// launch starts from cleared words, so a flag left by an earlier launch (or
+// by an earlier replay of a captured graph, whose kernel arguments, epoch
+// included, are frozen) can never match.  A kernel rather than a memset node,
+// so that the clearing is captured and replayed like the launch it precedes.
+__global__ void kd_bwd_clear_kernel(unsigned long long* __restrict__ ctr, unsigned long long* __restrict__ flags,
+                                    int nflags)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 8) ctr[i] = 0ull;
+    if (i < nflags) flags[i] = 0ull;
+}
+
 // --------------------------------------------------------------- launchers
 // compute units of the current device (the fused backward sizes its worker
 // pool to the CUs the sweep leaves free)
@@ -1361,6 +1374,9 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
         pub.ctr = reinterpret_cast<unsigned long long*>(wb + L.fl);
         pub.flags = reinterpret_cast<unsigned long long*>(wb + L.fl + 256);
         pub.epoch = next_bwd_epoch();
+        const int nfl = BH * NC;
+        hipLaunchKernelGGL(kd_bwd_clear_kernel, dim3((unsigned)((nfl + 255) / 256)), dim3(256), 0, st, pub.ctr,
+                           pub.flags, nfl);
         hipLaunchKernelGGL((kd_bwd_fused_kernel<TR, D>), dim3((unsigned)(BHpad + nwork)), dim3(4 * D), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
                            (const float*)ck.M, (const E*)ck.P, (const E*)ck.S, (const float*)ck.U, dST, wdS,

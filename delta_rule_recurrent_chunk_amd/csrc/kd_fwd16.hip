@@ -234,7 +234,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
             if (n >= 0 && w == 0) {   // forward substitution (I + M) u = c - beta r0
-                const int t_ = lane;
+                const int t_ = lane + opaque_zero();   // its addresses are formed here, not hoisted
                 __builtin_amdgcn_s_setprio(3);   // the chain every other wave waits for
                 float r0;
                 {
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (tid < NSB * (D / 32) && n >= 0) {
                 // chunk n's flags were last read in stage A; chunk n + 2 sets them
                 // in stage B(n + 1)
-                (&sm.fbm[n & 1][0][0])[tid] = 0u;
+                (&sm.fbm[n & 1][0][0])[tid + opaque_zero()] = 0u;
                 if (tid == 0) sm.fbany[n & 1] = 0u;
             }
             KD_PHASE_MARK(n, 4);

@@ -165,11 +165,11 @@ KD_API kd_status kron_delta_decode(const kd_desc *desc,
  * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2
  * summary, section "핵심 기여" (gate-aware backward pass), applied to the rule
  * of the onedev.kr KronLSTM summary, section "어떻게 동작하나".
- * Limitation: a chunk in which some key channel decays below 2^-100 over
- * the chunk (for instance f = 0) is not differentiated: all its gradients are
- * NaN, and so are those that depend on it through the state gradient (dk,
- * dv, df, dbeta, dc of the earlier chunks of the same (b, h), and dS0); dq of
- * the earlier chunks does not depend on it and stays exact.
+ * Every gate value in [0, 1] is differentiated exactly (f = 0 included): the
+ * decay enters through products of gates referenced to 16-token sub-blocks,
+ * and a (sub-block, key channel) pair whose decay falls below 2^-100, or that
+ * holds a gate below 2^-16 (bf16) or 2^-4 (fp32), has its dq, dk and df taken
+ * from the per-token recurrence on that channel's column of the state.
  * Enqueued on `stream`: the recording forward, then the reverse sweep over
  * the chunks and the per-chunk gradients, in one launch when B*H leaves at
  * least 64 compute units free (the per-chunk work then runs beside the sweep,

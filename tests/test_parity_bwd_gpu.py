@@ -230,6 +230,41 @@ def test_training_pair_equals_forward_and_backward_bitwise(dtype, d, T):
         assert torch.equal(g1[n], g2[n]), n
 
 
+def test_fused_backward_replays_under_graph_capture():
+    """The fused backward captured in a graph and replayed with new inputs: a
+    clearing kernel ahead of each launch keeps the hand-off flags of the
+    previous replay (same frozen epoch) from matching.  Every replay equals an
+    eager call on the same inputs, bit for bit, with eager work between the
+    replays."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    xs = [sy.rounded(sy.draw(1, 200, 8, 64, 64, seed=830 + i, s0_std=0.1, with_dO=True, dST_std=0.1), "bf16")
+          for i in range(2)]
+    t = to_dev(torch, xs[0], "bf16")
+    args = lambda: (t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"], t["dO"], t["dST"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            kd.bwd(*args())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = kd.bwd(*args())
+    for rep, i in enumerate((0, 1, 0, 1, 1)):
+        src = to_dev(torch, xs[i], "bf16")
+        for n in t:
+            if t[n] is not None:
+                t[n].copy_(src[n])
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = kd.bwd(*args())
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(out[n], ref[n]), (rep, n)
+
+
 def test_fused_and_two_kernel_backward_agree_bitwise():
     """With few (b, h) the sweep and the chunk gradients share one launch;
     with more (b, h) than leave 64 compute units free they run as two
