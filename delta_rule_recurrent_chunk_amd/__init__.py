@@ -29,8 +29,10 @@ EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
             "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd",
             "kron_delta_fwd_train", "kron_delta_bwd_saved", "kron_delta_mixer_pre",
-            "kron_delta_mixer_post", "kron_delta_mixer_fwd")
+            "kron_delta_mixer_post", "kron_delta_mixer_fwd", "kron_delta_bwd_noalloc")
 KD_WS_FWD, KD_WS_BWD, KD_WS_MIXER = 0, 1, 2
+KD_ERR_SCRATCH = -8     # kron_delta_bwd_noalloc: the problem needs more than its fixed scratch
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KronDeltaError(RuntimeError):
@@ -74,6 +76,8 @@ def lib():
         L.kron_delta_bwd.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
         L.kron_delta_bwd_saved.restype = i32
         L.kron_delta_bwd_saved.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
+        L.kron_delta_bwd_noalloc.restype = i32
+        L.kron_delta_bwd_noalloc.argtypes = [dp] + [vp] * 16 + [vp]
         L.kron_delta_fwd_train.restype = i32
         L.kron_delta_fwd_train.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
         L.kron_delta_decode.restype = i32
@@ -270,6 +274,37 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None,
             _ptr(out["dS0"]), _ptr(workspace), need, ctypes.c_void_p(stream))
     if st != 0:
         raise KronDeltaError(st, "kron_delta_bwd_saved" if saved else "kron_delta_bwd")
+    return out
+
+
+def bwd_noalloc(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, out=None):
+    """kron_delta_bwd_noalloc: the gate-aware backward with the library's
+    fixed scratch as its workspace (no workspace argument; raises
+    KronDeltaError with KD_ERR_SCRATCH when the problem needs more).  `out`
+    may hold preallocated gradient tensors (dict as returned by bwd)."""
+    import torch
+    L = lib()
+    desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
+    if dO.dtype != q.dtype or tuple(dO.shape) != (desc.B, desc.T, desc.H, desc.dv):
+        raise ValueError("dO must match o's shape and dtype")
+    dO = dO.contiguous()
+    if dST is not None:
+        if tuple(dST.shape) != (desc.B, desc.H, desc.dv, desc.dk) or dST.dtype != torch.float32:
+            raise ValueError("dST must be float32 [B, H, dv, dk]")
+        dST = dST.contiguous()
+    dev = q.device
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                   df=torch.empty_like(f), dbeta=torch.empty_like(beta), dc=torch.empty_like(c),
+                   dS0=torch.empty((desc.B, desc.H, desc.dv, desc.dk), dtype=torch.float32, device=dev)
+                   if want_dS0 else None)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = L.kron_delta_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
+                                  _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                                  _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
+                                  _ptr(out["dS0"]), ctypes.c_void_p(stream))
+    if st != 0:
+        raise KronDeltaError(st, "kron_delta_bwd_noalloc")
     return out
 
 

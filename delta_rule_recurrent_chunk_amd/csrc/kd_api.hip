@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "kron_delta.h"
 
 namespace kd {
@@ -114,6 +116,33 @@ kd_status check_mixer(const kd_desc* d, const kd_mixer_params* p, bool pre, bool
     return KD_OK;
 }
 
+// The allocation-free backward's workspace: one fixed array in device memory,
+// which every GPU the library runs on holds until the process ends.  Host
+// code never uses the array's name as an address (on the host it is a
+// stand-in): the device address comes from hipGetSymbolAddress, once per
+// device.
+constexpr size_t kScratchBytes = KRON_DELTA_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Device address of `scratch` on the current device, looked up the first time
+// the device is seen (null when the lookup fails).
+void* scratch_address() {
+    static std::atomic<void*> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+        cache[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
 }  // namespace
 
 extern "C" {
@@ -130,6 +159,9 @@ const char* kron_delta_status_string(int s) {
     case KD_ERR_WORKSPACE: return "workspace missing or too small";
     case KD_ERR_LAUNCH: return "kernel launch failed";
     case KD_ERR_ALIAS: return "an output overlaps an input";
+    case KD_ERR_SCRATCH:
+        return "the problem needs more workspace than kron_delta_bwd_noalloc's fixed scratch "
+               "(KRON_DELTA_NOALLOC_SCRATCH_BYTES = 64 MiB)";
     default: return "unknown status";
     }
 }
@@ -249,6 +281,7 @@ kd_status bwd_impl(const kd_desc* d, const void* q, const void* k, const void* v
     const void* ptrs[] = {q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws};
     for (const void* p : ptrs)
         if (misaligned(p)) return KD_ERR_ALIGN;
+    if (ntok == 0 && !dS0) return KD_OK;   // nothing to compute, nothing launched
     const size_t need = kron_delta_workspace_bytes(d, 1);
     if (need > 0 && (!ws || ws_bytes < need)) return KD_ERR_WORKSPACE;
     const Range ins[] = {range_of(q, xb), range_of(k, xb), range_of(v, xb), range_of(f, xb),
@@ -263,7 +296,6 @@ kd_status bwd_impl(const kd_desc* d, const void* q, const void* k, const void* v
     for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a)
         for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
             if (overlap(outs[a], outs[b])) return KD_ERR_ALIAS;
-    if (ntok == 0 && !dS0) return KD_OK;
     hipError_t e = kd::launch_bwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, dO, dST,
                                   dq, dk, dv, df, dbeta, dc, dS0, ws, d->B, d->T, d->H, recompute,
                                   (hipStream_t)stream);
@@ -278,6 +310,23 @@ kd_status kron_delta_bwd(const kd_desc* d, const void* q, const void* k, const v
                          size_t ws_bytes, void* stream) {
     return bwd_impl(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, ws_bytes,
                     stream, 1);
+}
+
+kd_status kron_delta_bwd_noalloc(const kd_desc* d, const void* q, const void* k, const void* v,
+                                 const void* f, const float* beta, const float* c, const float* S0,
+                                 const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                                 void* df, float* dbeta, float* dc, float* dS0, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    const size_t need = kron_delta_workspace_bytes(d, 1);
+    if (need > kScratchBytes) return KD_ERR_SCRATCH;
+    void* ws = nullptr;   // looked up only for a call that launches
+    const bool launches = (size_t)d->B * d->T * d->H > 0 || dS0 != nullptr;
+    if (need > 0 && launches) {
+        ws = scratch_address();
+        if (ws == nullptr) return KD_ERR_LAUNCH;
+    }
+    return bwd_impl(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, need, stream, 1);
 }
 
 kd_status kron_delta_bwd_saved(const kd_desc* d, const void* q, const void* k, const void* v,

@@ -71,7 +71,8 @@ typedef enum {
     KD_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned           */
     KD_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required    */
     KD_ERR_LAUNCH = -6,     /* the HIP runtime rejected a kernel launch   */
-    KD_ERR_ALIAS = -7       /* an output overlaps an input                */
+    KD_ERR_ALIAS = -7,      /* an output overlaps an input                */
+    KD_ERR_SCRATCH = -8     /* kron_delta_bwd_noalloc: needs more than its fixed scratch */
 } kd_status;
 
 typedef struct {
@@ -186,6 +187,30 @@ KD_API kd_status kron_delta_bwd(const kd_desc *desc,
                          void *dq, void *dk, void *dv, void *df,
                          float *dbeta, float *dc, float *dS0,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid allocation): kron_delta_bwd with its workspace in a fixed array
+ * of KRON_DELTA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds in each
+ * GPU's memory until the process ends (its device address is looked up once
+ * per device).  Same arguments as kron_delta_bwd without ws and ws_bytes; the
+ * same kernels, so the results equal kron_delta_bwd's bit for bit.  A problem
+ * whose kron_delta_workspace_bytes(desc, 1) exceeds the scratch returns
+ * KD_ERR_SCRATCH without launching (at d = 128, bf16 about 2.9 MB per head
+ * of T = 2048: up to 22 heads of that length).  Calls no allocating routine.
+ * Every call on a GPU uses that GPU's one array, whose contents the call
+ * rewrites before reading (the hand-off words are cleared by a kernel ahead
+ * of each launch): two calls that overlap on the same GPU (different streams
+ * without an ordering event) race and must not be made.
+ */
+#define KRON_DELTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+KD_API kd_status kron_delta_bwd_noalloc(const kd_desc *desc,
+                         const void *q, const void *k, const void *v, const void *f,
+                         const float *beta, const float *c, const float *S0,
+                         const void *dO, const float *dST,
+                         void *dq, void *dk, void *dv, void *df,
+                         float *dbeta, float *dc, float *dS0, void *stream);
 
 /*
  * Training pair: a forward that keeps what the backward needs, and a backward

@@ -16,7 +16,7 @@ import delta_rule_recurrent_chunk_amd as kd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kron_delta.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def declared_functions():
@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_abi_version_and_strings(L):
     assert L.kron_delta_abi_version() == 1
-    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS, 12345):
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH, ALIAS, SCRATCH, 12345):
         assert isinstance(kd.status_string(s), str) and kd.status_string(s)
 
 
@@ -115,6 +115,29 @@ def test_bwd_argument_checks(L):
     assert bwd(L, d, ws=P(13)) == ALIAS              # workspace == dbeta (an output)
     assert bwd(L, d, df=P(12, misalign=2)) == ALIGN
     assert bwd(L, _desc(T=0), dS0=None) == OK
+
+
+def bwd_noalloc(L, desc, **over):
+    names = ["q", "k", "v", "f", "beta", "c", "S0", "dO", "dST", "dq", "dk", "dv", "df",
+             "dbeta", "dc", "dS0"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    p.update(over)
+    return L.kron_delta_bwd_noalloc(ctypes.byref(desc), *[p[n] for n in names], None)
+
+
+def test_bwd_noalloc_rejects_before_any_device_call(L):
+    """Checks that return before the scratch is looked up or anything is
+    launched: a problem larger than the fixed scratch, bad descriptors, and an
+    empty call."""
+    assert "64 MiB" in kd.status_string(SCRATCH)
+    big = _desc(B=2, T=2048, H=16, dk=128, dv=128)   # 32 heads of 2048 tokens
+    assert L.kron_delta_workspace_bytes(ctypes.byref(big), 1) > kd.NOALLOC_SCRATCH_BYTES
+    assert bwd_noalloc(L, big) == SCRATCH
+    fits = _desc(B=1, T=2048, H=16, dk=128, dv=128)
+    assert L.kron_delta_workspace_bytes(ctypes.byref(fits), 1) <= kd.NOALLOC_SCRATCH_BYTES
+    assert bwd_noalloc(L, _desc(dtype=3)) == DTYPE
+    assert bwd_noalloc(L, _desc(dk=48, dv=48)) == SHAPE
+    assert bwd_noalloc(L, _desc(T=0), dS0=None) == OK
 
 
 def test_workspace_scales_with_chunks(L):
