@@ -139,11 +139,39 @@ def mfma_flops(w):
     return w.B * w.H * nch * per
 
 
-def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64):
+def cpu_model():
+    """The host CPU's model name and logical CPU count, from /proc/cpuinfo."""
+    name, n = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.partition(":")[2].strip()
+                    n += 1
+    except OSError:
+        pass
+    return {"model": name, "logical_cpus": n, "affinity": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(x_np, w, budget_s=10.0, max_passes=64, one_core_s=5.0):
     """The fp64 oracle, unmodified, on the host cores: whole sequences of the
     same seeded workload, repeated in passes until about budget_s of wall time
-    has been spent (the last pass may stop early)."""
-    import numpy as np
+    has been spent (the last pass may stop early); then the same on one thread
+    for about one_core_s."""
+    import oracle
+    res = _cpu_leg(x_np, w, budget_s, max_passes)
+    threads = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        one = _cpu_leg(x_np, w, one_core_s, max_passes)
+    finally:
+        oracle.set_num_threads(threads)
+    res["one_core"] = {"value": one["value"], "unit": "tokens/s", "cores": one["cores"], "sample": one["sample"]}
+    res["cpu"] = cpu_model()
+    return res
+
+
+def _cpu_leg(x_np, w, budget_s, max_passes):
     import oracle
     threads = oracle.num_threads()
     done_tok = 0
@@ -202,8 +230,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="train_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time launches after evicting the caches with a 1 GiB write")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the launches timed after evicting the caches with a 1 GiB write")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain elementwise copy kernel (1 GiB read, 1 GiB written; "
                          "the reference for the HBM byte counters) three times and exit")
@@ -280,17 +308,17 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)   # the stream the binding launches on
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):   # back to back; one event between consecutive steps
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps     # avg launch duration (events)
+    per_launch = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps     # avg launch duration (events)
     ms_per_step = wall * 1e3 / args.steps
 
     tokens = w.B * w.T
@@ -357,6 +385,9 @@ def main():
                      "kd_fwd16_kernel<false, false>" if not w.backward else
                      "kd_fwd16_kernel(ckpt) + kd_bwd_fused_kernel",
                      "kernel_ms": kernel_ms,
+                     "launch_ms": {"mean": kernel_ms, "median": float(np.median(per_launch)),
+                                   "p10": float(np.percentile(per_launch, 10)),
+                                   "p90": float(np.percentile(per_launch, 90))},
                      "algorithmic_bytes_per_launch": abytes,
                      },
     }
@@ -387,10 +418,10 @@ def main():
     if not w.backward and not w.decode and not w.mixer:
         out["roofline"]["mfma_tflops"] = flops / (kernel_ms * 1e-3) / 1e12
         out["roofline"]["mfma_frac"] = flops / (kernel_ms * 1e-3) / 1e12 / peak_tf
-    if args.cold:
+    if not args.no_cold:
         big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         times = []
-        for i in range(min(args.steps, 20)):
+        for i in range(min(args.steps, 10)):
             big.fill_(i & 255)
             a = torch.cuda.Event(enable_timing=True)
             b_ = torch.cuda.Event(enable_timing=True)
@@ -401,7 +432,9 @@ def main():
             times.append(a.elapsed_time(b_))
         cold_ms = float(np.median(times))
         out["cold_cache"] = {"kernel_ms": cold_ms, "tokens_per_s": tokens / (cold_ms * 1e-3),
-                             "hbm_frac": abytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                             "hbm_frac": abytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "how": "median of %d launches, each after a 1 GiB fill that evicts "
+                                    "the L2 and the last-level cache" % len(times)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(out), flush=True)

@@ -91,6 +91,7 @@ struct Fwd16Smem {
     unsigned kmax[3], vmax[3];              // per chunk mod 3: max |k|, max |v| (bits)
     unsigned fbm[2][NSB][f16w::D / 32];     // channels below the floor per sub-block, by chunk parity
     unsigned fbany[2];                      // any such channel in the chunk, by chunk parity
+    unsigned slow[2];                       // chunk-start references (see below), by chunk parity
     float oinv, sinv;                       // 1 / s_prev and 1 / s of the current chunk
 };
 
@@ -196,18 +197,14 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 // partial r0[t] over value columns i0 + 4g .. i0 + 4g + 3 (adjacent
                 // under pcol) for the tokens t = 16tt + cl
                 float x[NSB];
-#pragma unroll
-                for (int tt = 0; tt < NSB; ++tt) {
+                // token sub-block tt with the state operand of K-step ks from a_of
+                auto read_sub = [&](auto tt_c, auto a_of) {
+                    constexpr int tt = decltype(tt_c)::value;
                     floatx4 Yt;
 #pragma unroll
                     for (int ks = 0; ks < KD_; ++ks) {
                         const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                        const Frag a = TR::state_frag(S, ks);
-                        if (tt + 1 < NSB) {   // the two state tiles of this K-step, decayed past sub-block tt
-                            const float* dc = &sm.fac[facrow::SUB + tt][32 * ks + 4 * g];
-                            S[2 * ks] = S[2 * ks] * *reinterpret_cast<const floatx4*>(dc);
-                            S[2 * ks + 1] = S[2 * ks + 1] * *reinterpret_cast<const floatx4*>(dc + 16);
-                        }
+                        const Frag a = a_of(ks);
                         const Frag bk = TR::ld_state_p(&sm.Kb[(SB * tt + cl) * LD], ks, g);
                         const Frag bq = TR::ld_state_p(&sm.Qb[(SB * tt + cl) * LD], ks, g);
                         Yt = TR::mma(a, bk, ks ? Yt : z);
@@ -218,6 +215,36 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     x[tt] = 0.f;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[tt] += Yt[r] * TR::tof(vr[r]);
+                };
+                typedef std::integral_constant<int, 0> T0;
+                typedef std::integral_constant<int, 1> T1;
+                typedef std::integral_constant<int, 2> T2;
+                typedef std::integral_constant<int, 3> T3;
+                if (sm.slow[n & 1]) {
+                    // operands referenced to the chunk start: the state as it
+                    // entered the chunk, converted once
+                    Frag a[KD_];
+#pragma unroll
+                    for (int ks = 0; ks < KD_; ++ks) a[ks] = TR::state_frag(S, ks);
+                    auto a_of = [&](int ks) { return a[ks]; };
+                    read_sub(T0(), a_of); read_sub(T1(), a_of); read_sub(T2(), a_of); read_sub(T3(), a_of);
+                } else {
+                    // operands referenced to each sub-block's start: the state
+                    // decayed in place past every sub-block as it is read
+                    auto a_dec = [&](auto tt_c) {
+                        constexpr int tt = decltype(tt_c)::value;
+                        return [&](int ks) {
+                            const Frag a = TR::state_frag(S, ks);
+                            if (tt + 1 < NSB) {   // the two state tiles of this K-step, decayed past sub-block tt
+                                const float* dc = &sm.fac[facrow::SUB + tt][32 * ks + 4 * g];
+                                S[2 * ks] = S[2 * ks] * *reinterpret_cast<const floatx4*>(dc);
+                                S[2 * ks + 1] = S[2 * ks + 1] * *reinterpret_cast<const floatx4*>(dc + 16);
+                            }
+                            return a;
+                        };
+                    };
+                    read_sub(T0(), a_dec(T0())); read_sub(T1(), a_dec(T1()));
+                    read_sub(T2(), a_dec(T2())); read_sub(T3(), a_dec(T3()));
                 }
                 // the producers' exact pass over chunk n's diagonal tiles (rare)
                 if (sm.fbany[n & 1] != 0u) lds_barrier();
@@ -366,6 +393,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         Raw8x2 rq, rk, rv, rf;           // raw rows of the chunk being prepared
         float rb_beta = 0.f, rb_c = 0.f; // beta_t, c_t for t = lane (used by wave 0)
         float tot[2];                    // product of f over the 8 rows, per channel
+        bool slow_p = true;              // the prepared chunk's references (see stage B)
         Col8 keep_v[2], keep_kt[2];      // v and K-tilde of the prepared chunk, written
                                          //   transposed in the following stage A
         const float gex = GATES ? __expf(gt.a_log[h]) : 0.f;   // forget-gate exponent
@@ -484,7 +512,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             auto ldg = [&](int ks) {
                 GF r;
                 r.k = TR::ld_nat(bK, ks, g);
-                if (fr >= 0) r.k = TR::scale_k(r.k, 1.f, sm.fac[fr], ks, g);
+                if (fr >= 0 && !slow_p) r.k = TR::scale_k(r.k, 1.f, sm.fac[fr], ks, g);
                 if (DO_M) { r.a = TR::ld_nat(aK, ks, g); r.v = TR::ld_nat(aV, ks, g); r.w = TR::ld_nat(bV, ks, g); }
                 if (DO_P) r.q = TR::ld_nat(aQ, ks, g);
                 return r;
@@ -575,7 +603,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 // its own, after = decay of the sub-blocks after its own, and the
                 // factor-table rows it writes (row pw; waves 0, 1 also row pw + 8).
                 // pw is wave-uniform: one straight-line case per value.
-                float astart[2], bstart[2], after[2], fv0[2], fv1[2], lastsub[2];
+                float astart[2], bstart[2], after[2], fv0[2], fv1[2], lastsub[2], gcv[2], gst[2];
                 const float* bpb = &sm.bprod[0][ch0 + oz];   // one base, constant offsets
                 unsigned fl2 = 0u;
                 auto consts = [&](auto pw_c) {
@@ -621,6 +649,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                         const float2 x = sub(NSB - 1);
                         lastsub[0] = x.x; lastsub[1] = x.y;
                     }
+                    // decay before sub-block I and over the whole chunk (one
+                    // association, the same in every wave)
+                    const float2 p1 = sub(0), p2 = mul(p1, sub(1)), p3 = mul(p2, sub(2)), pc = mul(p3, sub(3));
+                    const float2 ps = I == 0 ? make_float2(1.f, 1.f) : I == 1 ? p1 : I == 2 ? p2 : p3;
+                    gst[0] = ps.x; gst[1] = ps.y;
+                    gcv[0] = pc.x; gcv[1] = pc.y;
                 };
                 switch (pw) {
                 case 0: consts(std::integral_constant<int, 0>()); break;
@@ -632,6 +666,14 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 case 6: consts(std::integral_constant<int, 6>()); break;
                 default: consts(std::integral_constant<int, 7>()); break;
                 }
+                // A chunk with every channel's decay at or above the floor takes
+                // operands referenced to the chunk start: Qb = q gamma, Kb = k gamma,
+                // Kc = k / gamma (gamma: decay from the chunk start), so its Gram
+                // tiles need no factors and the consumers read the state as it
+                // entered the chunk.  Otherwise the sub-block references above.
+                // Every wave holds every channel: the vote is the same in all.
+                slow_p = __builtin_amdgcn_ballot_w64(!(gcv[0] >= kSafeFloor && gcv[1] >= kSafeFloor)) == 0ull;
+                if (pw == 0 && lane == 0) sm.slow[nn & 1] = slow_p ? 1u : 0u;
                 // Gram rows in pcol order, the state's rows in natural order
                 st2(&sm.fac[pw][pw < facrow::SUB ? pc0 : ch0], fv0[0], fv0[1]);
                 if (pw + NWP < facrow::N) st2(&sm.fac[pw + NWP][ch0], fv1[0], fv1[1]);
@@ -639,7 +681,9 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     atomicOr(&sm.fbm[nn & 1][pw >> 1][ch0 >> 5], fl2 << (ch0 & 31));
                     atomicOr(&sm.fbany[nn & 1], 1u);
                 }
-                if (pw == 0) st2(&sm.gam[nn & 1][ch0], lastsub[0], lastsub[1]);
+                // the state's decay in stage C: over the chunk, or over its last
+                // sub-block when the earlier ones were applied as it was read
+                if (pw == 0) st2(&sm.gam[nn & 1][ch0], slow_p ? gcv[0] : lastsub[0], slow_p ? gcv[1] : lastsub[1]);
                 // K-tilde is kept scaled by ksc (a power of 2) for the fp16 update
                 const int ek = pow2_exp(__uint_as_float(sm.kmax[nn % 3]));
                 const float ksc = ldexpf(1.f, -ek);
@@ -653,7 +697,14 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 #pragma unroll
                     for (int e = RB - 2; e >= 0; --e) bs[e][c2] = bs[e + 1][c2] * rf.get(e + 1, c2);
                 }
-                float ga[2] = {astart[0], astart[1]};   // a at the current row
+                // chunk-start references: a times the decay before the sub-block,
+                // and Kc = k b (decay after the sub-block) / gamma_C
+                float ga[2], cm[2];   // a (or gamma) at the current row; Kc = k bs cm
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    ga[c2] = slow_p ? astart[c2] * gst[c2] : astart[c2];
+                    cm[c2] = slow_p ? after[c2] * __builtin_amdgcn_rcpf(gcv[c2]) : 1.f;
+                }
                 float kprev[2] = {0.f, 0.f};
                 const int pcz = pc0 + oz;
 #pragma unroll
@@ -666,7 +717,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                         const float kt = kf * (bs[e][c2] * tk[c2]);   // K-tilde * ksc
                         qo[c2] = qf * ga[c2];
                         ko[c2] = kf * ga[c2];
-                        co[c2] = kf * bs[e][c2];
+                        co[c2] = kf * (bs[e][c2] * cm[c2]);
                         if (e & 1) keep_kt[c2].set_pair_h(e >> 1, kprev[c2], kt);
                         else kprev[c2] = kt;
                     }
