@@ -54,6 +54,7 @@ constexpr int NWP = 8;            // producer waves
 constexpr int RB = CH / NWP;      // rows per producer wave
 constexpr int LD = D + 16;        // row-major [CH][D] operands (columns in pcol order)
 constexpr int LDT = CH + 8;       // transposed [D][CH] operands
+constexpr int LDO = D + 8;        // o staging rows
 constexpr int LDM = CH + 4;       // fp32 M
 constexpr int LDP = CH + 8;       // P
 }  // namespace f16w
@@ -75,7 +76,7 @@ struct Fwd16Smem {
     alignas(16) __bf16 Kb[CH * f16w::LD];       // k * a
     alignas(16) __bf16 Kc[CH * f16w::LD];       // k * b (decay to the sub-block end)
     alignas(16) __bf16 V[CH * f16w::LD];        // v
-    alignas(16) __bf16 VT[f16w::D * f16w::LDT];     // v^T
+    alignas(16) __bf16 Os[CH * f16w::LDO];      // o of the chunk, natural columns (staging)
     alignas(16) _Float16 KtT[f16w::D * f16w::LDT];  // (k gamma_C / gamma)^T * kscale
     alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V)
     alignas(16) __bf16 P[2][CH * f16w::LDP];    // tril_0 of the decayed Q K^T, by chunk parity
@@ -171,18 +172,43 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         // of the unscaled state.
         const int i0 = 16 * w;   // value columns i0 .. i0 + 15
         int e_prev = 0;          // s_prev = 2^-e_prev (substitution wave)
-        const uint32_t o_lane = (uint32_t)cl * rs + hoff + i0 + 4 * g;
+        // chunk nc's o from the staging rows to global memory: 16 lanes per
+        // row, 16 bytes each, so every store instruction writes whole rows
+        auto copy_o = [&](int nc, int tid0, int nthr) {
+            if (!ob) return;
+            for (int x = tid - tid0; x < CH * D / 8; x += nthr) {
+                const int t = x >> 4, c8 = 8 * (x & 15);
+                const int tok = nc * CH + t;
+                if (tok < T) cp16_nt(ob + ((uint32_t)tok * rs + hoff + c8), &sm.Os[t * LDO + c8]);
+            }
+        };
         floatx4 S[D / 16];       // S^T[16mj + 4g + r][i0 + cl] in S[mj][r]
 #pragma unroll
         for (int mj = 0; mj < D / 16; ++mj)   // four adjacent columns: one 16-byte load
             S[mj] = S0 ? *reinterpret_cast<const floatx4*>(&S0[(size_t)bh * D * D + (size_t)(i0 + cl) * D + 16 * mj + 4 * g])
                        : floatx4{0.f, 0.f, 0.f, 0.f};
 
+        floatx4 Ot[NSB];   // O^T[i0 + 4g + r][16tt + cl]: from stage A to the next stage A
+        // o of the previous chunk (this wave's columns) into the staging rows,
+        // scaled by 1 / s_prev of that chunk; written out as whole rows in the
+        // following stage B
+        auto stage_o = [&]() {
+            const float oi = sm.oinv;
+            __bf16* od = &sm.Os[(uint32_t)cl * LDO + i0 + 4 * g + opaque_zero()];
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt) {
+                const floatx4 y = Ot[tt] * oi;
+                bf16x4 r;
+                r[0] = (__bf16)y[0]; r[1] = (__bf16)y[1]; r[2] = (__bf16)y[2]; r[3] = (__bf16)y[3];
+                *reinterpret_cast<bf16x4*>(od + SB * tt * LDO) = r;
+            }
+        };
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
-            floatx4 Ot[NSB];   // O^T[i0 + 4g + r][16tt + cl], lives to stage C
+            if (n >= 1) stage_o();
+            Frag vw[KC_];      // v of value column i0 + cl, tokens 32ks + 8g .. + 7 (to stage C)
             if (n >= 0) {
                 if (CKPT) {
                     E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
@@ -246,6 +272,14 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     read_sub(T0(), a_dec(T0())); read_sub(T1(), a_dec(T1()));
                     read_sub(T2(), a_dec(T2())); read_sub(T3(), a_dec(T3()));
                 }
+                {   // V holds chunk n until stage B; read after the state so as not to
+                    // hold up its operand loads
+                    const E* vcol = &sm.V[(uint32_t)(8 * g) * LD + TR::pcol(i0 + cl) + opaque_zero()];
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) vw[ks][e] = vcol[(TR::KS * ks + e) * LD];
+                }
                 // the producers' exact pass over chunk n's diagonal tiles (rare)
                 if (sm.fbany[n & 1] != 0u) lds_barrier();
                 {
@@ -306,6 +340,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 e_prev = e;
                 __builtin_amdgcn_s_setprio(0);
             }
+            if (n >= 1 && w >= 1) copy_o(n - 1, 64, (NWC - 1) * 64);   // chunk n - 1's o rows
             if (CKPT && n >= 0 && w >= 1) {
                 // M and P of chunk n are complete (their last tiles ran in stage
                 // A) and nobody writes them in this stage: the idle consumer waves
@@ -339,10 +374,26 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (n >= 0) {
                 // W = u * V of this wave's value columns: bf16 scaled by s_prev for
                 // the readout, fp16 scaled by usc for the update
+                // (value column i0 + cl, tokens 32ks + 8g .. + 7, read in stage A)
                 Frag wa[KC_];
                 FragH wb[KC_];
+                {
 #pragma unroll
-                for (int ks = 0; ks < KC_; ++ks) TR::row_times_pair(&sm.VT[(i0 + cl) * LDT], sm.u, sm.us, ks, g, wa[ks], wb[ks]);
+                    for (int ks = 0; ks < KC_; ++ks) {
+                        const int t0 = TR::KS * ks + 8 * g;
+                        const floatx4 a0 = *reinterpret_cast<const floatx4*>(&sm.u[t0]);
+                        const floatx4 a1 = *reinterpret_cast<const floatx4*>(&sm.u[t0 + 4]);
+                        const floatx4 b0 = *reinterpret_cast<const floatx4*>(&sm.us[t0]);
+                        const floatx4 b1 = *reinterpret_cast<const floatx4*>(&sm.us[t0 + 4]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xv = TR::tof(vw[ks][e]);
+                            const float ua = e < 4 ? a0[e] : a1[e - 4], ub = e < 4 ? b0[e] : b1[e - 4];
+                            wa[ks][e] = TR::cvt(ua * xv);
+                            wb[ks][e] = (_Float16)(ub * xv);
+                        }
+                    }
+                }
                 // O^T += W^T P^T (the P fragments of a K-step loaded together)
 #pragma unroll
                 for (int ks = 0; ks < KC_; ++ks) {
@@ -351,16 +402,6 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     for (int tt = 0; tt < NSB; ++tt) pf[tt] = TR::ld_nat(&sm.P[n & 1][(SB * tt + cl) * LDP], ks, g);
 #pragma unroll
                     for (int tt = 0; tt < NSB; ++tt) Ot[tt] = TR::mma(wa[ks], pf[tt], Ot[tt]);
-                }
-                if (ob) {
-                    const float oi = sm.oinv;
-#pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) {
-                        // row offset = scalar part + this lane's part (one register
-                        // across the loop instead of one per tt)
-                        const uint32_t srow = __builtin_amdgcn_readfirstlane((uint32_t)(n * CH + SB * tt) * rs);
-                        if (n * CH + SB * tt + cl < T) st4_nt(ob + (srow + o_lane), Ot[tt] * oi);
-                    }
                 }
                 // S <- S diag(gamma_C) s / s_prev + K~'^T W'; K-steps outermost, so
                 // consecutive MFMAs go to different accumulators
@@ -379,6 +420,9 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
+        stage_o();        // the last chunk's o rows
+        lds_barrier();    // (the producers' matching barrier follows their loop)
+        copy_o(NC - 1, 0, NWC * 64);
         if (ST) {
             const float si = sm.sinv;
 #pragma unroll
@@ -394,7 +438,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         float rb_beta = 0.f, rb_c = 0.f; // beta_t, c_t for t = lane (used by wave 0)
         float tot[2];                    // product of f over the 8 rows, per channel
         bool slow_p = true;              // the prepared chunk's references (see stage B)
-        Col8 keep_v[2], keep_kt[2];      // v and K-tilde of the prepared chunk, written
+        Col8 keep_kt[2];                 // K-tilde of the prepared chunk, written
                                          //   transposed in the following stage A
         const float gex = GATES ? __expf(gt.a_log[h]) : 0.f;   // forget-gate exponent
         // Rows past the sequence end re-read the last row (in bounds) and are
@@ -542,10 +586,9 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             const int oz = opaque_zero();     // per-lane LDS addresses stay inside the loop
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
-            if (n >= 0) {   // transposed operands of chunk n and its last two Gram tiles
+            if (n >= 0) {   // transposed K-tilde of chunk n and its last two Gram tiles
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
-                    keep_v[c2].store(&sm.VT[(ch0 + c2) * LDT + rb]);
                     keep_kt[c2].store(&sm.KtT[(ch0 + c2) * LDT + rb]);
                 }
                 // tiles 8 and 9 (rows 48..63) are first read by the substitution
@@ -726,8 +769,6 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     st2(&sm.Kc[(rb + e) * LD + pcz], co[0], co[1]);
                     rv.store(&sm.V[(rb + e) * LD + pcz], e);
                 }
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) keep_v[c2].set_raw(rv, c2);
             }
             const int npf = min(nn + 1, NC - 1);   // prefetch of chunk nn + 1
             load_q(npf);
@@ -742,6 +783,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             KD_PHASE_MARK(n, 5);
             lds_barrier();
         }
+        lds_barrier();   // the consumers stage the last chunk's o
     }
 }
 
