@@ -36,6 +36,7 @@ hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* con
                             int gates, hipStream_t st);
 hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const void* f_raw,
                               const float* beta_raw, const float* c_raw, const float* a_log, float beta_scale,
+                              const void* og, const float* norm_w, float norm_eps,
                               const float* S0, void* o, float* ST, int B, int T, int H, hipStream_t st);
 hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
                              int B, int T, int H, hipStream_t st);
@@ -501,16 +502,18 @@ kd_status kron_delta_mixer_fwd(const kd_desc* d, const kd_mixer_params* p, const
     const hipStream_t sm = (hipStream_t)stream;
     const int bf = d->dtype == KD_BF16;
     // bf16 at d = 128: the forward makes the gates from their logits as it
-    // loads them (the gate kernel's arithmetic, so the same bits)
+    // loads them (the gate kernel's arithmetic, so the same bits) and writes
+    // y through the gated norm as it stores each chunk's rows (the
+    // post-processing kernel's arithmetic)
     const bool fused_gates = bf && d->dk == 128;
     hipError_t e = kd::launch_mixer_pre(bf, d->dk, raw, x, conv, p->conv_size, p->a_log, beta_raw, c_raw,
                                         p->beta_scale, beta, c, d->B, d->T, d->H, fused_gates ? 0 : 1, sm);
     if (e == hipSuccess)
         e = fused_gates ? kd::launch_fwd16_gates(x[0], x[1], x[2], f_raw, beta_raw, c_raw, p->a_log, p->beta_scale,
-                                                 S0, o, ST, d->B, d->T, d->H, sm)
+                                                 g, p->norm_w, p->norm_eps, S0, y, ST, d->B, d->T, d->H, sm)
                         : kd::launch_fwd(bf, d->dk, x[0], x[1], x[2], x[3], beta, c, S0, o, ST, nullptr, nullptr,
                                          d->B, d->T, d->H, sm);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !fused_gates)
         e = kd::launch_mixer_post(bf, d->dv, o, g, p->norm_w, p->norm_eps, y, d->B, d->T, d->H, sm);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }

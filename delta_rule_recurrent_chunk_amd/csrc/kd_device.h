@@ -704,6 +704,24 @@ template <> struct Col16<float> {
 // The pre-processing kernel and the forward's fused gates share these, so
 // both give the same bits.
 constexpr float kLog2e = 1.4426950408889634f;
+template <int CTRL>
+__device__ __forceinline__ float mix_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the LPR adjacent lanes of a row (LPR in {4, 8, 16}, rows aligned
+// to LPR lanes), on DPP lane moves: the partner quad lane, the other quad of
+// the 8-lane half row (half-row mirror), the other half of the 16-lane row
+// (row mirror)
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "rows of 4, 8 or 16 lanes");
+    x += mix_dpp<0xB1>(x);                   // quad_perm(1, 0, 3, 2): lane ^ 1
+    x += mix_dpp<0x4E>(x);                   // quad_perm(2, 3, 0, 1): lane ^ 2
+    if (LPR >= 8) x += mix_dpp<0x141>(x);    // row_half_mirror
+    if (LPR >= 16) x += mix_dpp<0x140>(x);   // row_mirror
+    return x;
+}
+
 __device__ __forceinline__ float gate_sigmoid(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
@@ -967,6 +985,11 @@ __device__ __forceinline__ void st8(float* p, const float* x) {
 struct FwdGates {
     const float* a_log;   // [H]
     float beta_scale;
+    // with og set: o leaves as y = o / sqrt(mean_i o_i^2 + norm_eps) * norm_w[h]
+    // * sigmoid(og), per (b, t, h) (og [B, T, H, D] bf16 gate logits, norm_w [H, D])
+    const __bf16* og;
+    const float* norm_w;
+    float norm_eps;
 };
 
 struct FwdCkpt {

@@ -173,9 +173,45 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         const int i0 = 16 * w;   // value columns i0 .. i0 + 15
         int e_prev = 0;          // s_prev = 2^-e_prev (substitution wave)
         // chunk nc's o from the staging rows to global memory: 16 lanes per
-        // row, 16 bytes each, so every store instruction writes whole rows
+        // row (one DPP row), 16 bytes each, so every store instruction writes
+        // whole rows.  With the gated norm (GATES and og set) the row leaves
+        // as y: its sum of squares over the 16 lanes, then the norm weight
+        // and the output gate, in the arithmetic order of the stand-alone
+        // post-processing kernel.  At most 3 rows per lane (nthr >= 448); the
+        // gate logits of all of them are loaded first.
         auto copy_o = [&](int nc, int tid0, int nthr) {
             if (!ob) return;
+            if (GATES && gt.og) {
+                const int c8 = 8 * (lane & 15);   // the same columns on every row of this lane
+                constexpr int MAXR = 3;
+                bf16x8 gv[MAXR];   // raw logits, widened when used
+#pragma unroll
+                for (int it = 0; it < MAXR; ++it) {
+                    const int x = tid - tid0 + it * nthr;
+                    const int tok = min(nc * CH + (x >> 4), T - 1);
+                    if (x < CH * D / 8)
+                        gv[it] = *reinterpret_cast<const bf16x8*>(gt.og + bbase + ((uint32_t)tok * rs + hoff + c8));
+                }
+                float wv[8];
+                ld8f(gt.norm_w + (uint32_t)h * D + c8, wv);
+#pragma unroll
+                for (int it = 0; it < MAXR; ++it) {
+                    const int x = tid - tid0 + it * nthr;
+                    if (x < CH * D / 8) {   // the same for all 16 lanes of the row
+                        const int t = x >> 4;
+                        float xv[8];
+                        ld8f(&sm.Os[t * LDO + c8], xv);
+                        float ss = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ss = fmaf(xv[e], xv[e], ss);
+                        const float sc = rsqrtf(row_sum<16>(ss) * (1.f / D) + gt.norm_eps);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) xv[e] = xv[e] * sc * wv[e] * gate_sigmoid((float)gv[it][e]);
+                        if (nc * CH + t < T) st8v_nt(ob + ((uint32_t)(nc * CH + t) * rs + hoff + c8), xv);
+                    }
+                }
+                return;
+            }
             for (int x = tid - tid0; x < CH * D / 8; x += nthr) {
                 const int t = x >> 4, c8 = 8 * (x & 15);
                 const int tok = nc * CH + t;
@@ -804,15 +840,20 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void*
 }
 
 // The forward with the gates made from their logits (f_raw [B,T,H,D] bf16,
-// beta_raw and c_raw [B,T,H] fp32) as the producers load them.
+// beta_raw and c_raw [B,T,H] fp32) as the producers load them; with og set,
+// o leaves through the gated per-head norm (FwdGates).
 hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const void* f_raw,
                               const float* beta_raw, const float* c_raw, const float* a_log, float beta_scale,
+                              const void* og, const float* norm_w, float norm_eps,
                               const float* S0, void* o, float* ST, int B, int T, int H, hipStream_t st)
 {
     typedef __bf16 E;
     FwdGates gt;
     gt.a_log = a_log;
     gt.beta_scale = beta_scale;
+    gt.og = static_cast<const E*>(og);
+    gt.norm_w = norm_w;
+    gt.norm_eps = norm_eps;
     hipLaunchKernelGGL((kd_fwd16_kernel<false, true>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f_raw, beta_raw, c_raw, S0, (E*)o, ST,
                        FwdCkpt{}, gt, (const int*)nullptr, T, H);

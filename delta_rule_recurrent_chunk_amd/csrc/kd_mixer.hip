@@ -33,24 +33,6 @@ struct MixPreArgs {
     int K;
 };
 
-template <int CTRL>
-__device__ __forceinline__ float mix_dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-// sum over the LPR adjacent lanes of a row (LPR in {4, 8, 16}, rows aligned
-// to LPR lanes), on DPP lane moves: the partner quad lane, the other quad of
-// the 8-lane half row (half-row mirror), the other half of the 16-lane row
-// (row mirror)
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "rows of 4, 8 or 16 lanes");
-    x += mix_dpp<0xB1>(x);                   // quad_perm(1, 0, 3, 2): lane ^ 1
-    x += mix_dpp<0x4E>(x);                   // quad_perm(2, 3, 0, 1): lane ^ 2
-    if (LPR >= 8) x += mix_dpp<0x141>(x);    // row_half_mirror
-    if (LPR >= 16) x += mix_dpp<0x140>(x);   // row_mirror
-    return x;
-}
-
 // q, k, v: one block per (b, h, tensor) and MIX_CT consecutive tokens.  The
 // block stages the raw rows of its tokens and the K - 1 before them, and the
 // head's taps, in LDS (one coalesced pass), then each row of D/8 lanes makes
