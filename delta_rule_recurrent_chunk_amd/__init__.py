@@ -141,8 +141,11 @@ def _prep(torch, q, k, v, f, beta, c, S0):
         beta.contiguous(), c.contiguous(), S0
 
 
-def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True):
-    """Chunkwise forward.  Returns (o, S_T); S_T is None if return_state=False."""
+def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True, workspace=None):
+    """Chunkwise forward.  Returns (o, S_T); S_T is None if return_state=False.
+    workspace: None (allocated when the shape takes the few-heads path), or a
+    uint8 device tensor passed through (an empty one forces the one-launch
+    path)."""
     import torch
     L = lib()
     desc, q, k, v, f, beta, c, S0 = _prep(torch, q, k, v, f, beta, c, S0)
@@ -150,8 +153,15 @@ def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True):
     ST = torch.empty((desc.B, desc.H, desc.dv, desc.dk), dtype=torch.float32,
                      device=q.device) if return_state else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    # few heads: the library runs the chunk-parallel preparation when given
+    # its workspace (one hand-off image per head and chunk)
+    need = int(L.kron_delta_workspace_bytes(ctypes.byref(desc), 0)) if workspace is None else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
     st = L.kron_delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
-                          _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), None, 0, ctypes.c_void_p(stream))
+                          _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), wsp, wsb, ctypes.c_void_p(stream))
     if st != 0:
         raise KronDeltaError(st, "kron_delta_fwd")
     return o, ST

@@ -40,6 +40,10 @@ hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const
                               const float* S0, void* o, float* ST, int B, int T, int H, hipStream_t st);
 hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
                              int B, int T, int H, hipStream_t st);
+size_t fwd16_split_ws_bytes(int B, int T, int H);
+hipError_t launch_fwd16_split(const void* q, const void* k, const void* v, const void* f, const float* beta,
+                              const float* c, const float* S0, void* o, float* ST, void* ws, int B, int T,
+                              int H, hipStream_t st);
 }  // namespace kd
 
 namespace {
@@ -167,9 +171,19 @@ const char* kron_delta_status_string(int s) {
     }
 }
 
+// Workspace of kron_delta_fwd: the few-heads path (bf16, d = 128, at most
+// KRON_DELTA_FWD_SPLIT_MAX_HEADS heads B*H, T > 0) takes one hand-off image
+// per (b, h, chunk); 0 otherwise.
+static size_t fwd_ws_bytes(const kd_desc* d) {
+    if (d->dtype != KD_BF16 || d->dk != 128 || d->dv != 128 || d->T <= 0) return 0;
+    if ((long long)d->B * d->H > KRON_DELTA_FWD_SPLIT_MAX_HEADS) return 0;
+    return kd::fwd16_split_ws_bytes(d->B, d->T, d->H);
+}
+
 size_t kron_delta_workspace_bytes(const kd_desc* d, int which) {
     if (check_desc(d) != KD_OK) return 0;
     switch (which) {
+    case KD_WS_FWD: return fwd_ws_bytes(d);
     case KD_WS_BWD: return kd::bwd_workspace_bytes(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
     case KD_WS_MIXER: return mixer_ws(d).total;
     default: return 0;
@@ -179,8 +193,6 @@ size_t kron_delta_workspace_bytes(const kd_desc* d, int which) {
 kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const void* v,
                          const void* f, const float* beta, const float* c, const float* S0,
                          void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
     const size_t ntok = (size_t)d->B * d->T * d->H;
@@ -199,6 +211,17 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
             if (overlap(a, b)) return KD_ERR_ALIAS;
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
+    const size_t need = fwd_ws_bytes(d);
+    if (need > 0 && ws && ws_bytes >= need) {   // few heads: preparation, then the state pass
+        if (misaligned(ws)) return KD_ERR_ALIGN;
+        const Range wr = range_of(ws, need);
+        for (const Range& b : ins)
+            if (overlap(wr, b)) return KD_ERR_ALIAS;
+        if (overlap(wr, outs[0]) || overlap(wr, outs[1])) return KD_ERR_ALIAS;
+        hipError_t e = kd::launch_fwd16_split(q, k, v, f, beta, c, S0, o, ST, ws, d->B, d->T, d->H,
+                                              (hipStream_t)stream);
+        return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+    }
     hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
                                   nullptr, nullptr, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;

@@ -92,10 +92,11 @@ KD_API const char *kron_delta_status_string(int status);
 
 /*
  * Device workspace, in bytes, that an entry point needs for `desc`:
- * which = KD_WS_FWD (0) for kron_delta_fwd (none), KD_WS_BWD (1) for
- * kron_delta_bwd / kron_delta_fwd_train / kron_delta_bwd_saved, KD_WS_MIXER
- * (2) for kron_delta_mixer_fwd.  Returns 0 for an invalid descriptor or an
- * unknown `which`, as well as when no workspace is needed.
+ * which = KD_WS_FWD (0) for kron_delta_fwd (nonzero only for the few-heads
+ * path, see there), KD_WS_BWD (1) for kron_delta_bwd / kron_delta_fwd_train /
+ * kron_delta_bwd_saved, KD_WS_MIXER (2) for kron_delta_mixer_fwd.  Returns 0
+ * for an invalid descriptor or an unknown `which`, as well as when no
+ * workspace is needed.
  */
 #define KD_WS_FWD 0
 #define KD_WS_BWD 1
@@ -105,8 +106,18 @@ KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int which);
 /*
  * Forward pass.  Reads q, k, v, f, beta, c and the initial state S0 (NULL
  * means S0 = 0); writes o and, when ST is non-NULL, the final state S_T.
- * ws / ws_bytes are accepted for symmetry and may be NULL / 0.
+ * ws / ws_bytes may be NULL / 0.  Few heads (bf16, dk = dv = 128, B*H at
+ * most KRON_DELTA_FWD_SPLIT_MAX_HEADS): given a workspace of at least
+ * kron_delta_workspace_bytes(desc, KD_WS_FWD) bytes (16-byte aligned, not
+ * overlapping any argument; about 99 KiB per head and 64-token chunk), the
+ * forward runs as two launches on the stream: every chunk's state-free part
+ * (decay products, operands, the Gram matrices M and P and the inverse
+ * A = (I + M)^{-1}, aitrends.kr Gated DeltaNet-2 summary, "방법론" step 3)
+ * in parallel, then one pass per head over the chunks, u = A (c - beta r0).
+ * Without it, or for other shapes, one launch (the substitution form).  Both
+ * hold the same tolerance against the definition.
  */
+#define KRON_DELTA_FWD_SPLIT_MAX_HEADS 64
 KD_API kd_status kron_delta_fwd(const kd_desc *desc,
                          const void *q, const void *k, const void *v, const void *f,
                          const float *beta, const float *c, const float *S0,

@@ -308,3 +308,17 @@ def test_mixer_argument_checks(L):
     assert mfwd(d, _mixer_params(norm_w=None)) == NULL
     assert mfwd(_desc(B=2, T=100, H=3, dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE
     assert mfwd(_desc(B=2, T=0, H=3, dk=128, dv=128), ST=None) == OK
+
+
+def test_few_heads_workspace_query():
+    """The workspace that selects the few-heads path: one image per (b, h,
+    64-token chunk) up to the head limit, none past it or for other shapes."""
+    import ctypes
+    import delta_rule_recurrent_chunk_amd as kd
+    L = kd.lib()
+
+    def ws(B, T, H, d=128, dt=1):
+        return int(L.kron_delta_workspace_bytes(ctypes.byref(kd.KdDesc(B, T, H, d, d, dt)), 0))
+    unit = ws(1, 64, 1)
+    assert unit > 0 and ws(1, 65, 1) == 2 * unit and ws(4, 130, 16) == 64 * 3 * unit
+    assert ws(5, 130, 13) == 0 and ws(1, 64, 1, d=64) == 0 and ws(1, 64, 1, dt=0) == 0

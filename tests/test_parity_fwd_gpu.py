@@ -159,6 +159,62 @@ def test_no_decay_no_erase_is_linear_attention():
     check(x, "bf16")
 
 
+# ------------------------------------------------------------ few-heads path
+def run_fwd_path(x, dtype, split):
+    """kd.fwd with the library's few-heads path (split=True: the workspace the
+    binding allocates) or forced onto the one-launch kernel (an empty
+    workspace)."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    t = to_dev(torch, x, dtype)
+    ws = None if split else torch.empty(0, dtype=torch.uint8, device="cuda")
+    print("case: B,T,H,d =", tuple(x["q"].shape), dtype, "split" if split else "one-launch", flush=True)
+    o, ST = kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), ST.double().cpu().numpy()
+
+
+def _clustered(B, T, H, d, seed):
+    rng = np.random.default_rng(seed)
+    x = sy.draw(B, T, H, d, d, seed=seed, mu=5.0, beta_scale=2.0)
+    base_k = rng.standard_normal((H, 4, d))
+    base_v = rng.standard_normal((H, 4, d))
+    for b in range(B):
+        for h in range(H):
+            idx = rng.integers(0, 4, T)
+            k = base_k[h, idx] + 0.05 * rng.standard_normal((T, d))
+            v = base_v[h, idx] + 0.05 * rng.standard_normal((T, d))
+            x["k"][b, :, h] = k / np.linalg.norm(k, axis=1, keepdims=True)
+            x["v"][b, :, h] = v / np.linalg.norm(v, axis=1, keepdims=True)
+    x["beta"][:] = 1.95 + 0.04 * rng.random(x["beta"].shape)
+    return x
+
+
+FEW = {
+    "ragged_state": lambda: sy.draw(2, 200, 3, 128, 128, seed=301, beta_scale=2.0, s0_std=0.1),
+    "fast_decay_resets": lambda: sy.draw(1, 700, 3, 128, 128, seed=302, mu=0.0, a_log_value=1.0,
+                                         s0_std=0.1, resets=6),
+    "clustered_beta2": lambda: _clustered(1, 512, 4, 128, 303),
+    "single_token": lambda: sy.draw(1, 1, 2, 128, 128, seed=304, s0_std=0.2),
+    "max_heads": lambda: sy.draw(4, 130, 16, 128, 128, seed=305, s0_std=0.05),
+}
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("name", list(FEW))
+def test_few_heads_paths_match_oracle(name, split):
+    """Both forms of the bf16 d = 128 forward against the oracle: the
+    chunk-parallel preparation + streaming state pass (u = A b with
+    A = (I + M)^-1 by 16-blocks) and the one-launch substitution form."""
+    xr = sy.rounded(FEW[name](), "bf16")
+    o, ST = run_fwd_path(xr, "bf16", split)
+    o_ref, ST_ref, _ = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["f"], xr["beta"], xr["c"], xr["S0"])
+    e_o, e_s = rel(o, o_ref), rel(ST, ST_ref)
+    print("  err o=%.3e  S_T=%.3e" % (e_o, e_s), flush=True)
+    assert np.isfinite(o).all() and np.isfinite(ST).all()
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (e_o, e_s)
+
+
 # ------------------------------------------------------------ run properties
 def test_deterministic_bitwise():
     torch = _torch()
