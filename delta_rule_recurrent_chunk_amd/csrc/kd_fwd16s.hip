@@ -65,7 +65,10 @@ static_assert(G1_BYTES % 256 == 0 && G2_BYTES % 256 == 0, "images of whole 256-b
 // preparation: eight waves of eight rows
 constexpr int PNT = 512, PNW = 8, PRB = CH / PNW;
 // state pass: four consumer waves (32 value columns each), four loader waves
-constexpr int SNT = 512, NWC = 4, NWL = 4, CPW = D / NWC, NHV = CPW / 16;
+#ifndef KD_FWD16S_NWC
+#define KD_FWD16S_NWC 4
+#endif
+constexpr int NWC = KD_FWD16S_NWC, NWL = 4, SNT = 64 * (NWC + NWL), CPW = D / NWC, NHV = CPW / 16;
 constexpr int G1_SLOTS = (G1_BYTES / 16 + NWL * 64 - 1) / (NWL * 64);
 constexpr int G2_SLOTS = (G2_BYTES / 16 + NWL * 64 - 1) / (NWL * 64);
 // factor rows of the Gram tiles (sub-block references), pcol order
@@ -636,7 +639,10 @@ __global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
                 const int t_ = lane;
                 float r0;
                 {
-                    const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.r0p[t_ * NWC]);
+                    const floatx4* pr = reinterpret_cast<const floatx4*>(&sm.r0p[t_ * NWC]);
+                    floatx4 a = pr[0];
+#pragma unroll
+                    for (int i = 1; i < NWC / 4; ++i) a = a + pr[i];
                     r0 = ((a[0] + a[1]) + (a[2] + a[3])) * ldexpf(1.f, e_prev);
                 }
                 // b = c - beta r0 through LDS (this wave's own stores, read back

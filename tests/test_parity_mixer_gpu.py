@@ -138,7 +138,9 @@ def test_mixer_fwd_equals_its_three_steps_bitwise():
     y, ST = run_mixer_fwd(torch, kd, t)
     q, k, v, f, beta, c = kd.mixer_pre(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"], t["c_raw"],
                                        t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"])
-    o, ST2 = kd.fwd(q, k, v, f, beta, c, t["S0"])
+    # the mixer runs the rule's one-launch kernel (an empty workspace keeps
+    # kron_delta_fwd off the few-heads path)
+    o, ST2 = kd.fwd(q, k, v, f, beta, c, t["S0"], workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
     y2 = kd.mixer_post(o, t["g"], t["norm_w"], norm_eps=1e-5)
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(ST, ST2)

@@ -77,7 +77,10 @@ def test_equal_lengths_match_batched_forward_bitwise(d):
     x = sy.rounded(sy.draw(B, T, H, d, d, seed=510, s0_std=0.1), "bf16")
     t = {n: torch.tensor(x[n], dtype=torch.bfloat16 if n in ("q", "k", "v", "f") else torch.float32,
                          device="cuda") for n in ("q", "k", "v", "f", "beta", "c", "S0")}
-    o1, S1 = kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"])
+    # the packed forward runs the one-launch kernel: compare with that form
+    # of the batched forward (an empty workspace keeps it off the few-heads path)
+    o1, S1 = kd.fwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"],
+                    workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
     cu = torch.tensor([0, T, 2 * T, 3 * T], dtype=torch.int32, device="cuda")
     flat = {n: t[n].reshape((B * T,) + tuple(t[n].shape[2:])) for n in ("q", "k", "v", "f", "beta", "c")}
     o2, S2 = kd.fwd_varlen(flat["q"], flat["k"], flat["v"], flat["f"], flat["beta"], flat["c"], cu, t["S0"])
