@@ -29,9 +29,11 @@ EXPORTED = ("kron_delta_abi_version", "kron_delta_status_string",
             "kron_delta_workspace_bytes", "kron_delta_fwd", "kron_delta_bwd",
             "kron_delta_decode", "kron_delta_fwd_varlen", "kron_delta_gdn2_fwd",
             "kron_delta_fwd_train", "kron_delta_bwd_saved", "kron_delta_mixer_pre",
-            "kron_delta_mixer_post", "kron_delta_mixer_fwd", "kron_delta_bwd_noalloc")
+            "kron_delta_mixer_post", "kron_delta_mixer_fwd", "kron_delta_bwd_noalloc",
+            "kron_delta_bwd_status", "kron_delta_bwd_set_wait_limit")
 KD_WS_FWD, KD_WS_BWD, KD_WS_MIXER = 0, 1, 2
 KD_ERR_SCRATCH = -8     # kron_delta_bwd_noalloc: the problem needs more than its fixed scratch
+KD_ERR_TIMEOUT = -9     # kron_delta_bwd_status: a bounded wait of the backward ran out
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -78,6 +80,10 @@ def lib():
         L.kron_delta_bwd_saved.argtypes = [dp] + [vp] * 16 + [vp, sz, vp]
         L.kron_delta_bwd_noalloc.restype = i32
         L.kron_delta_bwd_noalloc.argtypes = [dp] + [vp] * 16 + [vp]
+        L.kron_delta_bwd_status.restype = i32
+        L.kron_delta_bwd_status.argtypes = [dp, vp, sz, vp]
+        L.kron_delta_bwd_set_wait_limit.restype = None
+        L.kron_delta_bwd_set_wait_limit.argtypes = [ctypes.c_uint32]
         L.kron_delta_fwd_train.restype = i32
         L.kron_delta_fwd_train.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
         L.kron_delta_decode.restype = i32
@@ -285,6 +291,25 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None,
     if st != 0:
         raise KronDeltaError(st, "kron_delta_bwd_saved" if saved else "kron_delta_bwd")
     return out
+
+
+def bwd_status(q, workspace=None):
+    """kron_delta_bwd_status for the backward that ran on `workspace` (None:
+    kron_delta_bwd_noalloc's scratch) with inputs shaped like q [B, T, H, d]:
+    0 or KD_ERR_TIMEOUT.  Waits for the current stream."""
+    import torch
+    L = lib()
+    B, T, Hq, dq_ = q.shape
+    desc = KdDesc(B, T, Hq, dq_, dq_, _dtype_code(torch, q.dtype))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return int(L.kron_delta_bwd_status(ctypes.byref(desc), wsp, wsb, ctypes.c_void_p(stream)))
+
+
+def bwd_set_wait_limit(polls: int) -> None:
+    """kron_delta_bwd_set_wait_limit (0: the default bound)."""
+    lib().kron_delta_bwd_set_wait_limit(int(polls))
 
 
 def bwd_noalloc(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, out=None):

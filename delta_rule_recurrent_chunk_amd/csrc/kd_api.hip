@@ -41,6 +41,8 @@ hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const
 hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
                              int B, int T, int H, hipStream_t st);
 size_t fwd16_split_ws_bytes(int B, int T, int H);
+void set_bwd_wait_polls(unsigned polls);
+size_t bwd_status_offset(int bf16, int d, int B, int T, int H);
 hipError_t launch_fwd16_split(const void* q, const void* k, const void* v, const void* f, const float* beta,
                               const float* c, const float* S0, void* o, float* ST, void* ws, int B, int T,
                               int H, hipStream_t st);
@@ -164,6 +166,8 @@ const char* kron_delta_status_string(int s) {
     case KD_ERR_WORKSPACE: return "workspace missing or too small";
     case KD_ERR_LAUNCH: return "kernel launch failed";
     case KD_ERR_ALIAS: return "an output overlaps an input";
+    case KD_ERR_TIMEOUT:
+        return "a chunk worker of the backward gave up waiting for the reverse sweep (its gradients are NaN)";
     case KD_ERR_SCRATCH:
         return "the problem needs more workspace than kron_delta_bwd_noalloc's fixed scratch "
                "(KRON_DELTA_NOALLOC_SCRATCH_BYTES = 64 MiB)";
@@ -352,6 +356,29 @@ kd_status kron_delta_bwd_noalloc(const kd_desc* d, const void* q, const void* k,
     }
     return bwd_impl(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, need, stream, 1);
 }
+
+kd_status kron_delta_bwd_status(const kd_desc* d, const void* ws, size_t ws_bytes, void* stream) {
+    kd_status st = check_desc(d);
+    if (st != KD_OK) return st;
+    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;
+    const size_t need = kron_delta_workspace_bytes(d, 1);
+    if (ws == nullptr) {   // the fixed scratch of kron_delta_bwd_noalloc on the current device
+        if (need > kScratchBytes) return KD_ERR_SCRATCH;
+        ws = scratch_address();
+        if (ws == nullptr) return KD_ERR_LAUNCH;
+    } else {
+        if (misaligned(ws)) return KD_ERR_ALIGN;
+        if (ws_bytes < need) return KD_ERR_WORKSPACE;
+    }
+    const size_t off = kd::bwd_status_offset(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
+    unsigned long long word = 0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KD_ERR_LAUNCH;
+    if (hipMemcpy(&word, static_cast<const char*>(ws) + off, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return KD_ERR_LAUNCH;
+    return word ? KD_ERR_TIMEOUT : KD_OK;
+}
+
+void kron_delta_bwd_set_wait_limit(uint32_t polls) { kd::set_bwd_wait_polls(polls); }
 
 kd_status kron_delta_bwd_saved(const kd_desc* d, const void* q, const void* k, const void* v,
                                const void* f, const float* beta, const float* c, const float* S0,

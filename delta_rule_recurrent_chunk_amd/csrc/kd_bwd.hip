@@ -64,9 +64,13 @@ struct BwdWs {
 // the low word), which the launch's block c sets at its start.
 struct BwdPub {
     unsigned long long* flags;   // [B*H*NC]
-    unsigned long long* ctr;     // [8]
+    unsigned long long* ctr;     // [8] claim counters, then [8]: the launch's status word
     unsigned epoch;
+    unsigned spin;               // polls of a bounded wait before it gives up
 };
+// ctr[BWD_STATUS]: nonzero when some worker's bounded wait ran out (its units
+// were then written as NaN); cleared before every backward launch
+constexpr int BWD_STATUS = 8;
 constexpr unsigned long long PUB_FLUSHED = 2ull;
 
 __device__ __forceinline__ unsigned xcc_id() {
@@ -78,8 +82,8 @@ __device__ __forceinline__ unsigned long long pub_word(unsigned epoch, unsigned 
 // bounded wait of one thread for a flag of this launch that has the bits
 // `need`; false when the bound ran out (then nothing may be read)
 __device__ __forceinline__ bool pub_wait(const unsigned long long* fp, unsigned epoch, unsigned long long need,
-                                         unsigned long long& w) {
-    for (int s = 0; s < (1 << 23); ++s) {
+                                         unsigned long long& w, unsigned spin) {
+    for (unsigned s = 0; s < spin; ++s) {
         w = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((unsigned)(w >> 32) == epoch && (w & need) == need) return true;
         __builtin_amdgcn_s_sleep(2);
@@ -1229,12 +1233,13 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
     unsigned long long pending = 0;
     if (threadIdx.x == 0 && total > 0) {
         unsigned long long w = 0;
-        if (pub_wait(&pub.ctr[c], pub.epoch, 0ull, w)) {
+        if (pub_wait(&pub.ctr[c], pub.epoch, 0ull, w, pub.spin)) {
             dyn = true;
             pending = __hip_atomic_fetch_add(&pub.ctr[c], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             dead = true;
             next = x < BHpad ? -1 : (x - BHpad) >> 3;
+            __hip_atomic_fetch_or(&pub.ctr[BWD_STATUS], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 #pragma unroll 1
@@ -1257,13 +1262,15 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
             if (u >= 0 && !dead) {
                 const int n = NC - 1 - u / nh, bh = c + 8 * (u % nh);
                 unsigned long long w = 0;
-                dead = !pub_wait(&pub.flags[(size_t)bh * NC + n], pub.epoch, 1ull, w);
+                dead = !pub_wait(&pub.flags[(size_t)bh * NC + n], pub.epoch, 1ull, w, pub.spin);
                 // a writer on another XCD: wait for its L2 write-back, then drop
                 // this XCD's copies
                 if (!dead && ((unsigned)(w >> 24) & 0xffu) != me) {
-                    dead = !pub_wait(&pub.flags[(size_t)bh * NC], pub.epoch, PUB_FLUSHED, w);
+                    dead = !pub_wait(&pub.flags[(size_t)bh * NC], pub.epoch, PUB_FLUSHED, w, pub.spin);
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 }
+                if (dead)   // reported through the status word (kron_delta_bwd_status)
+                    __hip_atomic_fetch_or(&pub.ctr[BWD_STATUS], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             g_unit = u < 0 ? -1 : (dead ? -2 - u : u);   // -2 - u: unit u, as NaN
         }
@@ -1283,7 +1290,8 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
     }
 }
 
-// Zeroes the claim counters and the hand-off flags of a fused launch: every
+// Zeroes the claim counters, the status word and the hand-off flags of a
+// backward launch (nflags = 0: the status word and counters only): every
 // launch starts from cleared words, so a flag left by an earlier launch (or
 // by an earlier replay of a captured graph, whose kernel arguments, epoch
 // included, are frozen) can never match.  A kernel rather than a memset node,
@@ -1292,7 +1300,7 @@ __global__ void kd_bwd_clear_kernel(unsigned long long* __restrict__ ctr, unsign
                                     int nflags)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < 8) ctr[i] = 0ull;
+    if (i <= BWD_STATUS) ctr[i] = 0ull;
     if (i < nflags) flags[i] = 0ull;
 }
 
@@ -1309,6 +1317,19 @@ static int compute_units() {
         cache[dev].store(n);
     }
     return n;
+}
+
+// polls of the fused backward's bounded waits: 2^23 (each poll sleeps briefly;
+// the waits take microseconds), or a smaller test value
+static std::atomic<unsigned> g_bwd_wait_polls{0u};
+void set_bwd_wait_polls(unsigned polls) { g_bwd_wait_polls.store(polls); }
+static unsigned bwd_wait_polls() {
+    const unsigned p = g_bwd_wait_polls.load();
+    return p ? p : (1u << 23);
+}
+// byte offset of the status word in a backward workspace
+size_t bwd_status_offset(int bf16, int d, int B, int T, int H) {
+    return bwd_ws_layout(bf16 ? 2 : 4, d, B, T, H).fl + 8 * BWD_STATUS;
 }
 
 // launch epochs of the fused backward: each launch's flags differ from every
@@ -1374,6 +1395,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
         pub.ctr = reinterpret_cast<unsigned long long*>(wb + L.fl);
         pub.flags = reinterpret_cast<unsigned long long*>(wb + L.fl + 256);
         pub.epoch = next_bwd_epoch();
+        pub.spin = bwd_wait_polls();
         const int nfl = BH * NC;
         hipLaunchKernelGGL(kd_bwd_clear_kernel, dim3((unsigned)((nfl + 255) / 256)), dim3(256), 0, st, pub.ctr,
                            pub.flags, nfl);
@@ -1383,6 +1405,9 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                            wrho, dS0, (E*)dq, (E*)dk, (E*)dv, (E*)df, dbeta, dc, BH, BHpad, nwork, pub, T, H);
         return hipGetLastError();
     }
+    // no waits on this path: its status word reads 0
+    hipLaunchKernelGGL(kd_bwd_clear_kernel, dim3(1), dim3(64), 0, st,
+                       reinterpret_cast<unsigned long long*>(wb + L.fl), (unsigned long long*)nullptr, 0);
     hipLaunchKernelGGL((kd_bwd_state_kernel<TR, D>), dim3((unsigned)(B * H)), dim3(4 * D), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, (const E*)dO,
                        (const float*)ck.M, (const E*)ck.P, dST, wdS, wrho, dS0, T, H);

@@ -72,7 +72,8 @@ typedef enum {
     KD_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required    */
     KD_ERR_LAUNCH = -6,     /* the HIP runtime rejected a kernel launch   */
     KD_ERR_ALIAS = -7,      /* an output overlaps an input                */
-    KD_ERR_SCRATCH = -8     /* kron_delta_bwd_noalloc: needs more than its fixed scratch */
+    KD_ERR_SCRATCH = -8,    /* kron_delta_bwd_noalloc: needs more than its fixed scratch */
+    KD_ERR_TIMEOUT = -9     /* kron_delta_bwd_status: a bounded wait of the backward ran out */
 } kd_status;
 
 typedef struct {
@@ -253,6 +254,28 @@ KD_API kd_status kron_delta_bwd_saved(const kd_desc *desc,
                          void *dq, void *dk, void *dv, void *df,
                          float *dbeta, float *dc, float *dS0,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Status of the last backward launch on workspace `ws` (kron_delta_bwd,
+ * kron_delta_bwd_saved; ws NULL: kron_delta_bwd_noalloc's fixed scratch on
+ * the current device).  When many heads run, the backward's chunk workers
+ * wait, with a bound, for the reverse sweep's per-chunk results; a wait that
+ * runs out (it should never: the sweeps never wait and are scheduled first)
+ * writes that unit's gradients as NaN and sets a status word in the
+ * workspace, cleared by every backward launch.  This call waits for `stream`
+ * to finish (hipStreamSynchronize), reads the word and returns KD_OK or
+ * KD_ERR_TIMEOUT (argument errors as for kron_delta_bwd).  Calls that did
+ * not launch (T = 0 without dS0) leave the previous launch's status.
+ */
+KD_API kd_status kron_delta_bwd_status(const kd_desc *desc, const void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Number of polls a bounded wait of the backward makes before it gives up
+ * (0 restores the default, 2^23 polls with a short sleep each: seconds).  For
+ * tests of the timeout path, which set a small value so that the workers give
+ * up at once; process-wide, read at each backward launch.
+ */
+KD_API void kron_delta_bwd_set_wait_limit(uint32_t polls);
 
 /*
  * Forward pass of the Gated Delta Rule-2 (decoupled erase and write), the

@@ -288,3 +288,32 @@ def test_fused_and_two_kernel_backward_agree_bitwise():
         for n in GRADS:
             w = wide[n][:, lo:lo + 8] if n == "dS0" else wide[n][:, :, lo:lo + 8]
             assert torch.equal(w, few[n]), (n, lo)
+
+
+def test_wait_timeout_is_reported():
+    """A chunk worker of the fused backward that gives up waiting for the
+    reverse sweep writes its unit's gradients as NaN and sets the status word:
+    kron_delta_bwd_status returns KD_ERR_TIMEOUT.  The condition is forced
+    from the host with a one-poll wait limit (every wait still ends); the next
+    backward with the default limit reads KD_OK and gives the oracle's values."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    x = sy.rounded(sy.draw(2, 1024, 4, 64, 64, seed=850, s0_std=0.1, with_dO=True), "bf16")
+    t = to_dev(torch, x, "bf16")
+    args = (t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], t["S0"], t["dO"])
+    need = kd.workspace_bytes(2, 1024, 4, 64, 1, with_backward=True)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    try:
+        kd.bwd_set_wait_limit(1)
+        g = kd.bwd(*args, workspace=ws)
+        st = kd.bwd_status(t["q"], ws)
+    finally:
+        kd.bwd_set_wait_limit(0)
+    assert st == kd.KD_ERR_TIMEOUT
+    assert not torch.isfinite(g["dk"].float()).all()
+    g = kd.bwd(*args, workspace=ws)
+    assert kd.bwd_status(t["q"], ws) == 0
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["f"], x["beta"], x["c"], x["S0"], x["dO"])
+    for n in ("dq", "dk", "df"):
+        assert rel(g[n].double().cpu().numpy(), ref[n]) <= 2e-2, n
+
