@@ -146,6 +146,53 @@ def test_mixer_fwd_equals_its_three_steps_bitwise():
     assert torch.equal(y, y2) and torch.equal(ST, ST2)
 
 
+def draw_fast_forget(B, T, H, d, dtype, seed):
+    """Mixer inputs whose forget gates run fast on some channels: logits
+    N(-8, 1) on channels 0-15 (sub-block decays below 2^-100: the diagonal
+    tiles' exact pass), N(-2, 1) on 16-47 (chunk decays below 2^-100: the
+    sub-block references), the usual draw elsewhere."""
+    x = sy.draw_mixer(B, T, H, d, d, seed, conv_size=4, s0_std=0.05)
+    x["f_raw"] = np.array(x["f_raw"])
+    x["f_raw"][..., :16] -= 8.0
+    x["f_raw"][..., 16:48] -= 2.0
+    return sy.rounded(x, dtype)
+
+
+def test_mixer_fwd_fast_forget_matches_oracle():
+    """The gates made inside the forward on chunks that take the sub-block
+    references and the exact pass (which makes its decay again from the
+    logit, with the producers' function)."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    x = draw_fast_forget(2, 300, 3, 128, "bf16", seed=995)
+    t = to_dev(torch, x, "bf16")
+    y, ST = run_mixer_fwd(torch, kd, t)
+    torch.cuda.synchronize()
+    ry, rST = oracle_mixer_fwd(x, "bf16")
+    ey, es = rel(host(y), ry), rel(host(ST), rST)
+    print("  y=%.2e ST=%.2e" % (ey, es), flush=True)
+    assert np.isfinite(host(y)).all()
+    assert ey <= FWD_TOL["bf16"] and es <= FWD_TOL["bf16"], (ey, es)
+
+
+def test_mixer_fwd_fast_forget_equals_its_three_steps_bitwise():
+    """With fast-forget gates, the fused mixer forward (gates made from their
+    logits inside the forward, including its exact pass) equals the gate
+    kernel + the one-launch forward + the post-processing kernel, bit for
+    bit."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    x = draw_fast_forget(2, 300, 3, 128, "bf16", seed=996)
+    t = to_dev(torch, x, "bf16")
+    y, ST = run_mixer_fwd(torch, kd, t)
+    q, k, v, f, beta, c = kd.mixer_pre(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"], t["c_raw"],
+                                       t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"])
+    o, ST2 = kd.fwd(q, k, v, f, beta, c, t["S0"], workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    y2 = kd.mixer_post(o, t["g"], t["norm_w"], norm_eps=1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(ST, ST2)
+
+
 def test_mixer_step_workload_sampled():
     """The full mixer_step shape (B=8, T=2048, H=16, d=128, bf16) as bench.py
     runs it; the oracle checks two sampled sequences end to end."""
