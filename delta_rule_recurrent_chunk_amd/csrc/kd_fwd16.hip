@@ -7,33 +7,42 @@
 // steps 3-4): per chunk n,
 //     (I + M) u = c - beta * r0,  r0_t = v_t^T S0 Kbar_t,
 //     O = Qbar S0^T + P (u * V),  S_C = S0 diag(gamma_C) + (u * V)^T Ktilde.
-// Decay references.  The state reads take Qbar = q gamma and Kbar = k gamma
-// with gamma referenced to the chunk start; the Gram tiles take their decay
-// relative to the four 16-token sub-blocks, so that every stored operand is a
-// product of gates (at most 1, never a quotient):
+// Decay references: two, chosen per chunk by a vote of the producers (every
+// producer wave holds every key channel, so all reach the same vote).
+//   Chunk start, when every channel's decay over the chunk is at least 2^-100:
+//     Qb = q gamma, Kb = k gamma, Kc = k / gamma (= k b after / gamma_C),
+//     gamma from the chunk start; the Gram tiles need no factors and the
+//     consumers read the state as it entered the chunk.
+//   16-token sub-blocks otherwise, so that every stored operand is a product
+//   of gates (at most 1, never a quotient):
 //     a_t = prod of f from the start of t's sub-block through t,
 //     b_s = prod of f after s through the end of s's sub-block,
 //     Qloc = q a, Kloc = k a, Kr = k b   (LDS arrays Qb, Kb, Kc),
 //     G_K[t,s] = sum_j Kloc_tj Kr_sj D_IJ,j   (t in sub-block I, s in J < I),
-// where D_IJ is the decay of the whole sub-blocks between J and I (1 for
-// neighbours).  A diagonal tile (I = J) divides by its sub-block's decay
-// (Kr / prod over the sub-block); a channel whose sub-block decay is below
-// 2^-100 is left out of that tile's matrix product and its terms are added
-// exactly on the vector units.  The state reads go sub-block by sub-block,
-// decaying the state in place by each sub-block's decay after its reads, so
-// that sub-block I reads (S diag(gamma before I)) Kloc^T = S Kbar^T; after
-// the last one the update needs only the last sub-block's decay.
+//   where D_IJ is the decay of the whole sub-blocks between J and I (1 for
+//   neighbours).  A diagonal tile (I = J) divides by its sub-block's decay
+//   (Kr / prod over the sub-block); a channel whose sub-block decay is below
+//   2^-100 is left out of that tile's matrix product and its terms are added
+//   exactly on the vector units.  The state reads go sub-block by sub-block,
+//   decaying the state in place by each sub-block's decay after its reads, so
+//   that sub-block I reads (S diag(gamma before I)) Kloc^T = S Kbar^T; after
+//   the last one the update needs only the last sub-block's decay.
 // The split of the work: each role has eight waves, so every
 // SIMD holds two consumer and two producer waves (128 registers each) and
 // one wave's LDS, matrix-core or dependency wait is covered by the others.
 //   consumers (waves 0..7): 16 value columns of the fp32 state each, held
 //     transposed as MFMA accumulators (S^T[j][i], key index j as rows);
-//     state reads, the forward substitution (wave 0), readout and update.
+//     state reads, the forward substitution (wave 0), readout and update;
+//     o leaves through an LDS staging tile as whole rows (written out by
+//     waves 1..7 during the next substitution).
 //   producers (waves 8..15): 8 rows of the chunk being prepared each, two
 //     adjacent key channels per lane; decay products, operands, Gram tiles.
-// Stage A: state reads of n | transposed operands of n, decay products of n+1.
-// Stage B: substitution of n | operands of n+1, first prefetch of n+2.
-// Stage C: readout and update of n | Gram tiles of n+1, rest of the prefetch.
+// Stage A: state reads of n, o of n-1 staged | K-tilde^T of n, tiles 8-9 of
+//          n, decay products of n+1.
+// Stage B: substitution of n, o rows of n-1 out | operands of n+1, first
+//          prefetch of n+2.
+// Stage C: readout and update of n | Gram tiles 0-7 of n+1, rest of the
+//          prefetch.
 #include <type_traits>
 
 #include "kd_device.h"
