@@ -160,14 +160,26 @@ struct Bf16T {
         r[4] = cvt(b[0]); r[5] = cvt(b[1]); r[6] = cvt(b[2]); r[7] = cvt(b[3]);
         return r;
     }
+    // Column reads of a row-major LDS tile through the transpose read
+    // (ds_read_b64_tr_b16).  In each 16-lane block, lanes 4e .. 4e + 3 each
+    // name four consecutive elements of row e (together columns c0 .. c0 + 15)
+    // and lane j of the block receives column c0 + j of the four rows.  col
+    // points at column c0 + cl of the first row (cl = lane % 16, c0 a multiple
+    // of 4 and ld a multiple of 4, so every address is 8-byte aligned); every
+    // lane of the wave takes part, so callers stay in wave-uniform code.
+    static __device__ __forceinline__ s16x4 ld_tr4(const E* col, int ld) {
+        const int cl = (int)__lane_id() & 15;
+        const E* p = col - cl + (cl >> 2) * ld + 4 * (cl & 3);
+        typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
+        return __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) v4s*)(p)));
+    }
     // natural-order fragment from a column: K = 32ks + 8g + e at col[K * ld]
-    // (a transposed operand read in place, one element per load)
+    // (a transposed operand read in place: two transpose reads of 4 rows)
     static __device__ __forceinline__ Frag ld_col(const E* col, int ld, int ks, int g) {
         const E* p = col + (KS * ks + 8 * g) * ld;
-        Frag r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = p[e * ld];
-        return r;
+        const s16x4 lo = ld_tr4(p, ld), hi = ld_tr4(p + 4 * ld, ld);
+        return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // Column fragments of a row-major matrix without strided loads: B operand
     // with K = rows 32ks .. 32ks + 31 (in the "state" order) and N = columns
@@ -217,10 +229,7 @@ struct Bf16T {
         return *reinterpret_cast<const F16*>(row + 4 * g);
     }
     static __device__ __forceinline__ F16 ld16_col(const E* col, int ld, int g) {
-        F16 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(short, col[(4 * g + e) * ld]);
-        return r;
+        return ld_tr4(col + 4 * g * ld, ld);
     }
     static __device__ __forceinline__ floatx4 mma16(F16 a, F16 b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
