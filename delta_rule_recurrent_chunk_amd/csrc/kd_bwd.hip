@@ -40,6 +40,12 @@
 
 #include "kd_device.h"
 
+// Stage markers of the chunk gradients: no-ops here; a profiling build may
+// define them to record timestamps at the stage boundaries.
+#ifndef KD_BWD_MARK
+#define KD_BWD_MARK(id) ((void)0)
+#endif
+
 namespace kd {
 
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
@@ -572,6 +578,7 @@ __device__ __forceinline__ void bwd_chunk_body(
     const size_t bbase = (size_t)b * T * H * D;
     const uint32_t hoff = (uint32_t)h * D;
     const size_t unit = (size_t)bh * NC + n;
+    KD_BWD_MARK(0);
 
     // ---------------- prep (a)
     // q, k, f and the decay factors are needed again by the elementwise stage
@@ -638,6 +645,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
     }
     lds_barrier();
+    KD_BWD_MARK(1);
 
     // ---------------- prep (b): operands, factors, the exact pass's pairs
     {
@@ -700,6 +708,7 @@ __device__ __forceinline__ void bwd_chunk_body(
     }
     if (tid < CH) sm.dr0[tid] = -sm.beta[tid] * sm.drho[tid];
     lds_barrier();
+    KD_BWD_MARK(2);
 
     // ---------------- C x C tiles: P, dP, dGK, dGV (+ its transpose), dbeta
     for (int tile = w; tile < 10; tile += NW) {
@@ -797,22 +806,82 @@ __device__ __forceinline__ void bwd_chunk_body(
         if (g == 0) sm.gC2[jc] = acc;
     }
     lds_barrier();
+    KD_BWD_MARK(3);
 
     // ---------------- C x D results, this wave's 16 columns, all 64 rows
     // Scalings by u[t] or dr0[t] of the output row t are applied to the
-    // accumulators: aK and aT start as V S0 and V dS, and dV is accumulated in
-    // two parts, aVu = Kt dS^T + P^T dO (times u) and aVr = dr0 (Kbar S0^T) +
-    // (dGV + dGV^T) V.  Kt = Kr after_tt and Kbar = Kloc Gamma_tt take their
-    // key-channel factors on the dS and S0 fragments, per token sub-block.
-    floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB], aVu[NSB], aVr[NSB];
+    // accumulators.  dV comes first and leaves at once, so that its two
+    // accumulators are not held through the rest: aVu = Kt dS^T + P^T dO
+    // (times u) and aVr = dr0 (Kbar S0^T) + (dGV + dGV^T) V.  Then aK and aT
+    // start as V S0 and V dS, aQ as dO S0.  Kt = Kr after_tt and Kbar = Kloc
+    // Gamma_tt take their key-channel factors on the dS and S0 fragments, per
+    // token sub-block.  Contractions over a d-long index take their B
+    // operands from the state checkpoints in global memory (L2): rows
+    // directly, columns through col_frag (whose tiles also give
+    // colsum(dS * S0) for bf16).
+    {
+        floatx4 aVu[NSB], aVr[NSB];
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt) {
+            aVu[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            aVr[tt] = aVu[tt];
+        }
+#pragma unroll
+        for (int ks = 0; ks < KD_; ++ks) {
+            const Frag r_ds = TR::ld_nat(dSn + jc * D, ks, g);   // B[j][i] = dS[i][j]
+            const Frag r_s0 = TR::ld_nat(S0n + jc * D, ks, g);   // B[j][i] = S0[i][j]
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt) {
+                const int tr = SB * tt + cl;
+                const Frag b_dsa = tt + 1 < NSB ? TR::scale_k(r_ds, 1.f, sm.aft[tt], ks, g) : r_ds;
+                const Frag b_s0g = tt ? TR::scale_k(r_s0, 1.f, sm.gmm[tt], ks, g) : r_s0;
+                aVu[tt] = TR::mma(TR::ld_nat(&Kc[tr * LD], ks, g), b_dsa, aVu[tt]);      // Kt dS^T
+                aVr[tt] = TR::mma(TR::ld_nat(&Kb[tr * LD], ks, g), b_s0g, aVr[tt]);      // Kbar S0^T
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt)
+            aVr[tt] = aVr[tt] * *reinterpret_cast<const floatx4*>(&sm.dr0[SB * tt + 4 * g]);   // dr0 (Kbar S0^T)
+        // contractions over the chunk: transposed operands read in place
+#pragma unroll
+        for (int ks = 0; ks < KC_; ++ks) {
+            const Frag b_v = TR::ld_col(&Vs[jc], LD, ks, g);    // B[s][i] = V[s][i]
+            const Frag b_do = TR::ld_col(&Do[jc], LD, ks, g);   // B[t][i] = dO[t][i]
+#pragma unroll
+            for (int tt = 0; tt < NSB; ++tt) {
+                const int tr = SB * tt + cl;
+                aVr[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aVr[tt]);           // (dGV + dGV^T) V
+                aVu[tt] = TR::mma(TR::ld_col(&P[tr], LDP, ks, g), b_do, aVu[tt]);            // P^T dO
+            }
+        }
+        // dV = u (Kt dS^T + P^T dO) + aVr, rows 16 tt + 4 g + r of column jc:
+        // lanes cl and cl ^ 1 trade one value per row pair, so that each
+        // stores two adjacent columns of one row as one 4-byte word
+        const bool odd = cl & 1, vpoison = sm.stale != 0u;
+        const uint32_t vcol = hoff + (uint32_t)(jc & ~1);
+#pragma unroll
+        for (int tt = 0; tt < NSB; ++tt) {
+            const floatx4 aV = aVu[tt] * *reinterpret_cast<const floatx4*>(&sm.u[SB * tt + 4 * g]) + aVr[tt];
+#pragma unroll
+            for (int rp = 0; rp < 4; rp += 2) {
+                const float give = odd ? aV[rp] : aV[rp + 1];
+                const float got = __int_as_float(__builtin_amdgcn_update_dpp(
+                    0, __float_as_int(give), 0xB1, 0xf, 0xf, false));   // quad_perm [1, 0, 3, 2]
+                const float lo = odd ? got : aV[rp], hi = odd ? aV[rp + 1] : got;
+                const int t = n * CH + SB * tt + 4 * g + rp + (odd ? 1 : 0);
+                if (t < T) {
+                    const float x0 = vpoison ? __builtin_nanf("") : lo, x1 = vpoison ? __builtin_nanf("") : hi;
+                    st2_nt(dv + bbase + (uint32_t)t * rs + vcol, x0, x1);
+                }
+            }
+        }
+    }
+    floatx4 aQ[NSB], aK[NSB], aC[NSB], aT[NSB];
 #pragma unroll
     for (int tt = 0; tt < NSB; ++tt) {
         aQ[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt]; aVu[tt] = aQ[tt]; aVr[tt] = aQ[tt];
+        aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt];
     }
-    // contractions over a d-long index, B operands from the state checkpoints
-    // in global memory (L2): rows directly, columns through col_frag (whose
-    // tiles also give colsum(dS * S0) for bf16)
     {
         const Frag csel = TR::col_sel(16 * w, g, cl);
         float gc2 = 0.f;
@@ -827,8 +896,6 @@ __device__ __forceinline__ void bwd_chunk_body(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) gc2 += ts[hh][r] * td[hh][r];
             }
-            const Frag r_ds = TR::ld_nat(dSn + jc * D, ks, g);   // B[j][i] = dS[i][j]
-            const Frag r_s0 = TR::ld_nat(S0n + jc * D, ks, g);   // B[j][i] = S0[i][j]
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) {
                 const int tr = SB * tt + cl;
@@ -836,10 +903,6 @@ __device__ __forceinline__ void bwd_chunk_body(
                 aQ[tt] = TR::mma(TR::ld_colmatch(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);   // dO S0
                 aK[tt] = TR::mma(a_v, b_s0t, aK[tt]);                                      // V S0
                 aT[tt] = TR::mma(a_v, b_dst, aT[tt]);                                      // V dS
-                const Frag b_dsa = tt + 1 < NSB ? TR::scale_k(r_ds, 1.f, sm.aft[tt], ks, g) : r_ds;
-                const Frag b_s0g = tt ? TR::scale_k(r_s0, 1.f, sm.gmm[tt], ks, g) : r_s0;
-                aVu[tt] = TR::mma(TR::ld_nat(&Kc[tr * LD], ks, g), b_dsa, aVu[tt]);      // Kt dS^T
-                aVr[tt] = TR::mma(TR::ld_nat(&Kb[tr * LD], ks, g), b_s0g, aVr[tt]);      // Kbar S0^T
             }
         }
         if (std::is_same<TR, Bf16T>::value) {
@@ -856,8 +919,8 @@ __device__ __forceinline__ void bwd_chunk_body(
         aQ[tt] = aQ[tt] * gmj;             // Gamma (dO S0): the local variable of q
         aK[tt] = aK[tt] * (r0v * gmj);     // Gamma dr0 (V S0)
         aT[tt] = aT[tt] * uv;              // W dS
-        aVr[tt] = aVr[tt] * r0v;           // dr0 (Kbar S0^T)
     }
+    KD_BWD_MARK(4);
     // Gram gradients, per sub-block pair (K = the 16 tokens of one sub-block);
     // dP and dGK enter as hi + lo (their bf16 rounding would dominate the
     // error of dq and df).  Row role: rows t of sub-block I, contraction over
@@ -901,22 +964,8 @@ __device__ __forceinline__ void bwd_chunk_body(
             aC[J_] += y * pfac(I_, J_);
         }
     }
-    // contractions over the chunk: transposed operands read in place
-#pragma unroll
-    for (int ks = 0; ks < KC_; ++ks) {
-        const Frag b_v = TR::ld_col(&Vs[jc], LD, ks, g);    // B[s][i] = V[s][i]
-        const Frag b_do = TR::ld_col(&Do[jc], LD, ks, g);   // B[t][i] = dO[t][i]
-#pragma unroll
-        for (int tt = 0; tt < NSB; ++tt) {
-            const int tr = SB * tt + cl;
-            aVr[tt] = TR::mma(TR::ld_nat(&Gs[tr * LDP], ks, g), b_v, aVr[tt]);           // (dGV + dGV^T) V
-            aVu[tt] = TR::mma(TR::ld_col(&P[tr], LDP, ks, g), b_do, aVu[tt]);            // P^T dO
-        }
-    }
-    floatx4 aV[NSB];   // dV = u (Kt dS^T + P^T dO) + aVr
-#pragma unroll
-    for (int tt = 0; tt < NSB; ++tt)
-        aV[tt] = aVu[tt] * *reinterpret_cast<const floatx4*>(&sm.u[SB * tt + 4 * g]) + aVr[tt];
+    KD_BWD_MARK(5);
+    KD_BWD_MARK(6);
     // q, k, f again for the elementwise stage (in flight during the staging)
     Row2x8<TR> rq, rk, rf;
     load_qkf(rq, rk, rf);
@@ -932,6 +981,7 @@ __device__ __forceinline__ void bwd_chunk_body(
             stT[row * LDF + jc] = aT[tt][r];
         }
     lds_barrier();
+    KD_BWD_MARK(7);
 
     // ---------------- elementwise: dq, dk, and the decay gradient (prep layout)
     clear_qkf(rq, rk, rf);
@@ -960,10 +1010,14 @@ __device__ __forceinline__ void bwd_chunk_body(
         float dqv[2][8], dkv[2][8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
+            // (reads unconditional, selects for the sub-blocks after I: the
+            // same products as multiplying by the later ones only)
             float aftc = 1.f;
 #pragma unroll
-            for (int I2 = 0; I2 < NSB; ++I2)
-                if (I2 > I) aftc *= sm.bprod[I2][ch0 + c];
+            for (int I2 = 0; I2 < NSB; ++I2) {
+                const float bpv = sm.bprod[I2][ch0 + c];
+                aftc *= I2 > I ? bpv : 1.f;
+            }
             float gg[2], hh[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -1002,6 +1056,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         st8v(&sm.hsub[I][ch0], toth);
     }
     lds_barrier();
+    KD_BWD_MARK(8);
     {
         float dfv[2][8];
 #pragma unroll
@@ -1009,7 +1064,8 @@ __device__ __forceinline__ void bwd_chunk_body(
             float later = 0.f, htot = 0.f, gCc = 1.f;
 #pragma unroll
             for (int I2 = 0; I2 < NSB; ++I2) {
-                if (I2 > I) later += sm.gsub[I2][ch0 + c];
+                const float gsv = sm.gsub[I2][ch0 + c];
+                later += I2 > I ? gsv : 0.f;   // +0 before the first later term: the same sum
                 htot += sm.hsub[I2][ch0 + c];
                 gCc *= sm.bprod[I2][ch0 + c];
             }
@@ -1020,22 +1076,7 @@ __device__ __forceinline__ void bwd_chunk_body(
 #pragma unroll
         for (int e = 0; e < 2; ++e) put8(df, e, dfv[e]);
     }
-    lds_barrier();   // staging reads done before dV reuses it
-#pragma unroll
-    for (int tt = 0; tt < NSB; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stQ[(SB * tt + 4 * g + r) * LDF + jc] = aV[tt][r];
-    lds_barrier();
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int t = n * CH + row0 + e;
-        if (t < T) {
-            float x[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = poison ? __builtin_nanf("") : stQ[(row0 + e) * LDF + ch0 + c];
-            st8v_nt(dv + bbase + (uint32_t)t * rs + hoff + ch0, x);
-        }
-    }
+    KD_BWD_MARK(9);
     if (tid < CH && n * CH + tid < T) {
         const size_t gi = ((size_t)b * T + n * CH + tid) * H + h;
         float db = -sm.r0[tid] * sm.drho[tid];
@@ -1043,6 +1084,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         st_nt(&dbeta[gi], poison ? __builtin_nanf("") : db);
         st_nt(&dc[gi], poison ? __builtin_nanf("") : sm.drho[tid]);
     }
+    KD_BWD_MARK(10);
 
     // ---------------- the exact pass (rare): for each (sub-block I, channel j)
     // of xset, one wave runs the recurrence on column j of the state and of its
@@ -1053,7 +1095,10 @@ __device__ __forceinline__ void bwd_chunk_body(
     //   df_t = S_{t-1} . (G_t + dr0_t v_t k_t)
     // (the reverse mode of the per-token rule; dr0 = -beta drho, drho the
     // total gradient of the chunk's targets u).
-    if (!poison) {
+    unsigned anyx = 0u;   // any pair at all (most chunks have none)
+#pragma unroll
+    for (int x = 0; x < NSB * NFW; ++x) anyx |= (&sm.xset[0][0])[x];
+    if (!poison && __builtin_amdgcn_readfirstlane(anyx) != 0u) {
         constexpr int NI = (D + 63) / 64;   // value rows i = lane + 64 m of this lane
         int pair = 0;
 #pragma unroll 1
@@ -1139,6 +1184,7 @@ __device__ __forceinline__ void bwd_chunk_body(
                 }
             }
     }
+    KD_BWD_MARK(11);
 }
 
 template <class TR, int D>

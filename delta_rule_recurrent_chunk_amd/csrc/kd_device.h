@@ -541,6 +541,15 @@ __device__ __forceinline__ void st8v_nt(float* p, const float* x) {
     __builtin_nontemporal_store(floatx4{x[0], x[1], x[2], x[3]}, reinterpret_cast<floatx4*>(p));
     __builtin_nontemporal_store(floatx4{x[4], x[5], x[6], x[7]}, reinterpret_cast<floatx4*>(p) + 1);
 }
+// Two adjacent values of one row as a streaming store.
+__device__ __forceinline__ void st2_nt(__bf16* p, float a, float b) {
+    const __bf16 __attribute__((ext_vector_type(2))) r = {(__bf16)a, (__bf16)b};
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned, r), reinterpret_cast<unsigned*>(p));
+}
+__device__ __forceinline__ void st2_nt(float* p, float a, float b) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(f2v{a, b}, reinterpret_cast<f2v*>(p));
+}
 // Store two consecutive values (a transposed-array entry pair).
 __device__ __forceinline__ void st2h(_Float16* p, float a, float b) {
     _Float16 __attribute__((ext_vector_type(2))) x;
