@@ -45,6 +45,9 @@
 #ifndef KD_BWD_MARK
 #define KD_BWD_MARK(id) ((void)0)
 #endif
+#ifndef KD_SWEEP_MARK
+#define KD_SWEEP_MARK(chunk, id) ((void)0)
+#endif
 
 namespace kd {
 
@@ -142,8 +145,13 @@ struct BwdStateSmem {
     static constexpr int LDM = CH + 4;         // fp32 M
     static constexpr int LDP = CH + TR::PAD;
     static constexpr int NW = D / 16;
-    alignas(16) E Kt[CH * LD];                        // K-tilde rows
-    alignas(16) E V[CH * LD];
+    union {
+        struct {
+            alignas(16) E Kt[CH * LD];                // K-tilde rows
+            alignas(16) E V[CH * LD];
+        } kv;
+        alignas(16) E dSs[D * LD];                    // after the state read: dS[i][j] of the chunk
+    };
     alignas(16) E VT[D * LDT];                        // v^T
     alignas(16) E OT[D * LDT];                        // dO^T
     alignas(16) E QT[D * LDT];                        // (q gamma)^T
@@ -259,16 +267,29 @@ __device__ __forceinline__ void bwd_state_body(
         load_part3(NC - 1);
     }
 
-    // gradient of the state leaving chunk n, dS[i][j], for the chunk-local kernel
-    auto store_dS = [&](int n) {
+    // gradient of the state leaving chunk n, dS[i][j], for the chunk-local
+    // kernel.  It leaves through LDS (the K-tilde and V rows, free after the
+    // state read): a lane's accumulators cover 16 rows x 8 bytes per store,
+    // while the copy-out stores whole 16-byte runs, 1 KB of a row-major
+    // matrix per instruction.
+    static_assert(D <= 2 * CH, "dS staging fits the K-tilde and V rows");
+    auto stage_dS = [&]() {
+#pragma unroll
+        for (int mj = 0; mj < D / 16; ++mj) st4(&sm.dSs[(16 * w + cl) * LD + 16 * mj + 4 * g], dSt[mj]);
+    };
+    auto copy_dS = [&](int n) {
+        constexpr int EPV = 16 / sizeof(E);
         E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-        for (int mj = 0; mj < D / 16; ++mj)
-            st4(dst + ((uint32_t)(16 * w + cl) * D + 16 * mj + 4 * g), dSt[mj]);
+        for (int x = tid; x < D * D / EPV; x += NT) {
+            const int i = x / (D / EPV), j0 = EPV * (x % (D / EPV));
+            *reinterpret_cast<uint4*>(dst + (uint32_t)(i * D + j0)) = *reinterpret_cast<const uint4*>(&sm.dSs[i * LD + j0]);
+        }
     };
 
     for (int n = NC - 1; n >= 0; --n) {
         if (PUB && tid == 0 && n + 1 < NC) publish(n + 1, 0ull);
+        KD_SWEEP_MARK(n, 0);
         // ---------------- prep (a): decay products within the sub-block; M and P
         if (n * CH + CH > T) {   // ragged last chunk: rows past the end are inert
 #pragma unroll
@@ -300,6 +321,7 @@ __device__ __forceinline__ void bwd_state_body(
             for (int e = 0; e < EPV; ++e) sm.PT[(s0 + e) * LDP + t] = pe[e];
         }
         lds_barrier();
+        KD_SWEEP_MARK(n, 1);
 
         // ---------------- prep (b): operands
         {
@@ -335,8 +357,8 @@ __device__ __forceinline__ void bwd_state_body(
                     ko[e][c] = kf * ga;
                     kt[c] = kf * ((e == 0 ? cur.f.get(1, c) * sfx : sfx) * aft[c]);   // K-tilde
                 }
-                st8v(&sm.Kt[(row0 + e) * LD + ch0], kt);
-                cur.v.store(&sm.V[(row0 + e) * LD + ch0], e);
+                st8v(&sm.kv.Kt[(row0 + e) * LD + ch0], kt);
+                cur.v.store(&sm.kv.V[(row0 + e) * LD + ch0], e);
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -349,19 +371,20 @@ __device__ __forceinline__ void bwd_state_body(
         const int npf = max(n - 1, 0);   // the next chunk's loads run under this one
         load_part1(npf);
         lds_barrier();
+        KD_SWEEP_MARK(n, 2);
 
         // ---------------- state read: dW = Kt dS^T + P^T dO (rows t, this wave's 16 columns i)
         floatx4 dW[NSB];
         {
             Frag ac[NSB];
 #pragma unroll
-            for (int tt = 0; tt < NSB; ++tt) ac[tt] = TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], 0, g);
+            for (int tt = 0; tt < NSB; ++tt) ac[tt] = TR::ld_state(&sm.kv.Kt[(SB * tt + cl) * LD], 0, g);
 #pragma unroll
             for (int ks = 0; ks < KD_; ++ks) {
                 Frag an[NSB];
                 if (ks + 1 < KD_) {
 #pragma unroll
-                    for (int tt = 0; tt < NSB; ++tt) an[tt] = TR::ld_state(&sm.Kt[(SB * tt + cl) * LD], ks + 1, g);
+                    for (int tt = 0; tt < NSB; ++tt) an[tt] = TR::ld_state(&sm.kv.Kt[(SB * tt + cl) * LD], ks + 1, g);
                 }
                 const Frag bS = TR::state_frag(dSt, ks);
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
@@ -391,7 +414,7 @@ __device__ __forceinline__ void bwd_state_body(
             for (int tt = 0; tt < NSB; ++tt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    x[4 * tt + r] = dW[tt][r] * TR::tof(sm.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
+                    x[4 * tt + r] = dW[tt][r] * TR::tof(sm.kv.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
             row16_reduce_step<8>(x, cl);
             row16_reduce_step<4>(x, cl);
             row16_reduce_step<2>(x, cl);
@@ -399,9 +422,10 @@ __device__ __forceinline__ void bwd_state_body(
             sm.dup[w][SB * (cl >> 2) + 4 * g + (cl & 3)] = x[0];
         }
         lds_barrier();
+        KD_SWEEP_MARK(n, 3);
 
         // ---------------- back substitution (I + M)^T drho = du; every wave
-        // then stores dS and issues the rest of the next chunk's loads (the
+        // then stages dS and issues the rest of the next chunk's loads (the
         // others while wave 0 solves)
         if (w == 0) {
             const int t_ = lane;
@@ -411,21 +435,34 @@ __device__ __forceinline__ void bwd_state_body(
             float Mcol[CH];
 #pragma unroll
             for (int s = 0; s < CH; ++s) Mcol[s] = sm.M[s * LDM + t_];
-            // lane t takes the finished drho_s of every later row s; the mask
-            // keeps a non-finite drho_s of an earlier row out of lane t
+            // lane t takes the finished drho_s of every later row s.  M[s][t]
+            // is an exact zero for t >= s (the forward writes only s < t), so
+            // lanes t >= s add -0 * drho_s, which leaves them unchanged while
+            // drho_s is finite; only the sign of a zero result can differ from
+            // skipping them.  Should some drho come out non-finite, the chain
+            // runs again with lanes t >= s masked, so that a non-finite drho_s
+            // of an earlier row stays out of lane t.
+            const float x0 = x;
 #pragma unroll
-            for (int s = CH - 1; s >= 1; --s) {
-                const float y = fmaf(-Mcol[s], readlane_f(x, s), x);
-                x = (t_ < s) ? y : x;
+            for (int s = CH - 1; s >= 1; --s) x = fmaf(-Mcol[s], readlane_f(x, s), x);
+            if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(x)) != 0ull) {
+                x = x0;
+#pragma unroll 1
+                for (int s = CH - 1; s >= 1; --s) {
+                    const float y = fmaf(-sm.M[s * LDM + t_], readlane_f(x, s), x);
+                    x = (t_ < s) ? y : x;
+                }
             }
             wsrho[((size_t)bh * NC + n) * CH + t_] = x;
             sm.dr0[t_] = -sm.beta[t_] * x;
         }
-        store_dS(n);
+        stage_dS();
         load_part3(npf);
         lds_barrier();
+        KD_SWEEP_MARK(n, 4);
 
         // ---------------- dS <- dS diag(gamma_C) + dO^T Qbar + V^T diag(dr0) Kbar
+        copy_dS(n);
         {
             Frag bO[KC_], bR[KC_];
 #pragma unroll
@@ -448,6 +485,7 @@ __device__ __forceinline__ void bwd_state_body(
         // reached L2 before the barrier; the flag goes out after it
         if (PUB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
+        KD_SWEEP_MARK(n, 5);
     }
     if (PUB && tid == 0 && NC > 0) {   // every wave's stores are in L2: write it back, then the last flag
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
