@@ -268,22 +268,32 @@ __device__ __forceinline__ void bwd_state_body(
     }
 
     // gradient of the state leaving chunk n, dS[i][j], for the chunk-local
-    // kernel.  It leaves through LDS (the K-tilde and V rows, free after the
-    // state read): a lane's accumulators cover 16 rows x 8 bytes per store,
-    // while the copy-out stores whole 16-byte runs, 1 KB of a row-major
-    // matrix per instruction.
+    // kernel.  bf16: in record order, straight from the accumulators (one
+    // 16-byte run per store, 1 KB per instruction).  fp32 (row-major): through
+    // LDS (the K-tilde and V rows, free after the state read), since a lane's
+    // accumulators cover 16 rows x 16 bytes per store while the copy-out
+    // stores whole 16-byte runs of a row.
+    constexpr bool RUNS = std::is_same<TR, Bf16T>::value;
     static_assert(D <= 2 * CH, "dS staging fits the K-tilde and V rows");
-    auto stage_dS = [&]() {
+    auto stage_dS = [&](int n) {
+        if constexpr (RUNS) {
+            E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-        for (int mj = 0; mj < D / 16; ++mj) st4(&sm.dSs[(16 * w + cl) * LD + 16 * mj + 4 * g], dSt[mj]);
+            for (int kb = 0; kb < D / 32; ++kb) st_run(dst + rec_run<D>(16 * w + cl, kb, g), dSt[2 * kb], dSt[2 * kb + 1]);
+        } else {
+#pragma unroll
+            for (int mj = 0; mj < D / 16; ++mj) st4(&sm.dSs[(16 * w + cl) * LD + 16 * mj + 4 * g], dSt[mj]);
+        }
     };
     auto copy_dS = [&](int n) {
-        constexpr int EPV = 16 / sizeof(E);
-        E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
+        if constexpr (!RUNS) {
+            constexpr int EPV = 16 / sizeof(E);
+            E* dst = wsdS + ((size_t)bh * NC + n) * D * D;
 #pragma unroll
-        for (int x = tid; x < D * D / EPV; x += NT) {
-            const int i = x / (D / EPV), j0 = EPV * (x % (D / EPV));
-            *reinterpret_cast<uint4*>(dst + (uint32_t)(i * D + j0)) = *reinterpret_cast<const uint4*>(&sm.dSs[i * LD + j0]);
+            for (int x = tid; x < D * D / EPV; x += NT) {
+                const int i = x / (D / EPV), j0 = EPV * (x % (D / EPV));
+                *reinterpret_cast<uint4*>(dst + (uint32_t)(i * D + j0)) = *reinterpret_cast<const uint4*>(&sm.dSs[i * LD + j0]);
+            }
         }
     };
 
@@ -456,7 +466,7 @@ __device__ __forceinline__ void bwd_state_body(
             wsrho[((size_t)bh * NC + n) * CH + t_] = x;
             sm.dr0[t_] = -sm.beta[t_] * x;
         }
-        stage_dS();
+        stage_dS(n);
         load_part3(npf);
         lds_barrier();
         KD_SWEEP_MARK(n, 4);
@@ -833,11 +843,29 @@ __device__ __forceinline__ void bwd_chunk_body(
     const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
     const E* S0n = ckptS + unit * D * D;   // S0[i][j]
     const E* dSn = wsdS + unit * D * D;    // dS[i][j]
+    // The state records: bf16 in record order (16-byte runs of the writers'
+    // accumulator lanes), fp32 row-major.
+    constexpr bool RUNS = std::is_same<TR, Bf16T>::value;
+    auto rec_at = [&](int i, int j) -> uint32_t {   // element (i, j)
+        if constexpr (RUNS) return rec_idx<D>(i, j);
+        else return (uint32_t)(i * D + j);
+    };
+    // natural-order fragment of row i, K = 32ks + 8g + e: two half runs
+    auto rec_row = [&](const E* m, int i, int ks) -> Frag {
+        if constexpr (RUNS) {
+            const uint32_t o = 4u * (uint32_t)(g >> 1);
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1)) + o);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1) + 1) + o);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return TR::ld_nat(m + i * D, ks, g);
+        }
+    };
     if (!std::is_same<TR, Bf16T>::value) {   // colsum(dS * S0) for column jc (bf16: below)
         float acc = 0.f;
         for (int x = 0; x < D / 4; ++x) {
             const int i = g * (D / 4) + x;
-            acc += TR::tof(S0n[i * D + jc]) * TR::tof(dSn[i * D + jc]);
+            acc += TR::tof(S0n[rec_at(i, jc)]) * TR::tof(dSn[rec_at(i, jc)]);
         }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
@@ -866,8 +894,8 @@ __device__ __forceinline__ void bwd_chunk_body(
         }
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
-            const Frag r_ds = TR::ld_nat(dSn + jc * D, ks, g);   // B[j][i] = dS[i][j]
-            const Frag r_s0 = TR::ld_nat(S0n + jc * D, ks, g);   // B[j][i] = S0[i][j]
+            const Frag r_ds = rec_row(dSn, jc, ks);   // B[j][i] = dS[i][j]
+            const Frag r_s0 = rec_row(S0n, jc, ks);   // B[j][i] = S0[i][j]
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) {
                 const int tr = SB * tt + cl;
@@ -921,13 +949,34 @@ __device__ __forceinline__ void bwd_chunk_body(
         aK[tt] = aQ[tt]; aC[tt] = aQ[tt]; aT[tt] = aQ[tt];
     }
     {
-        const Frag csel = TR::col_sel(16 * w, g, cl);
+        // Column fragments: rows i = 32ks + 16hh + cl against a 0/1 selection
+        // of column 16w + cl (one term per output, so exact in any K order);
+        // bf16 takes the K order of a record run (one 16-byte load per row)
+        Frag csel;
+        if constexpr (RUNS) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                csel[e] = TR::cvt((e < 4 ? 4 * g + e : 12 + 4 * g + e) == ((16 * w) & 31) + cl ? 1.f : 0.f);
+        } else {
+            csel = TR::col_sel(16 * w, g, cl);
+        }
+        auto col_of = [&](const E* m, int ks, floatx4* tiles) -> Frag {
+            if constexpr (RUNS) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    tiles[hh] = TR::mma(*reinterpret_cast<const Frag*>(m + rec_run<D>(TR::KS * ks + 16 * hh + cl, w >> 1, g)),
+                                        csel, floatx4{0.f, 0.f, 0.f, 0.f});
+                return TR::state_frag(tiles, 0);
+            } else {
+                return TR::col_frag(m, D, ks, 16 * w, csel, g, cl, tiles);
+            }
+        };
         float gc2 = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
             floatx4 ts[2], td[2];
-            const Frag b_s0t = TR::col_frag(S0n, D, ks, 16 * w, csel, g, cl, ts);   // B[i][j] = S0[i][j]
-            const Frag b_dst = TR::col_frag(dSn, D, ks, 16 * w, csel, g, cl, td);   // B[i][j] = dS[i][j]
+            const Frag b_s0t = col_of(S0n, ks, ts);   // B[i][j] = S0[i][j]
+            const Frag b_dst = col_of(dSn, ks, td);   // B[i][j] = dS[i][j]
             if (std::is_same<TR, Bf16T>::value) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
@@ -1162,8 +1211,8 @@ __device__ __forceinline__ void bwd_chunk_body(
 #pragma unroll
                     for (int m = 0; m < NI; ++m) {
                         const int i = lane + 64 * m;
-                        S[m] = i < D ? TR::tof(S0n[i * D + j]) : 0.f;
-                        G[m] = i < D ? TR::tof(dSn[i * D + j]) : 0.f;
+                        S[m] = i < D ? TR::tof(S0n[rec_at(i, j)]) : 0.f;
+                        G[m] = i < D ? TR::tof(dSn[rec_at(i, j)]) : 0.f;
                     }
                     const int rb0 = SB * I2;
 #pragma unroll 1

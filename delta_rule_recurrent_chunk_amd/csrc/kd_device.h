@@ -519,6 +519,36 @@ __device__ __forceinline__ float group8_next1(float x, int r8) {
     return r8 <= 6 ? y : 0.f;
 }
 
+// Element order of the per-chunk state records of bf16 runs (the entering
+// state S0 and the state gradient dS of every chunk, D x D, D a multiple of
+// 32): blocks of 16 rows i by 32 columns j, each block 64 runs of eight
+// elements; run g * 16 + i % 16 holds row i's columns 4g .. 4g + 3 and
+// 16 + 4g .. 16 + 4g + 3 of the block.  That is the order in which an MFMA
+// accumulator lane holds a row of the state (tiles 2kb and 2kb + 1, rows
+// 4g .. 4g + 3 of each), so a writer's lane stores its values as 16-byte runs
+// and one store instruction covers 1 KB.  rec_run: element offset of a run.
+template <int D>
+__device__ __forceinline__ uint32_t rec_run(int i, int kb, int g) {
+    return ((uint32_t)((i >> 4) * (D / 32) + kb) * 64u + (uint32_t)(g * 16 + (i & 15))) * 8u;
+}
+template <int D>
+__device__ __forceinline__ uint32_t rec_idx(int i, int j) {
+    return rec_run<D>(i, j >> 5, (j >> 2) & 3) + (uint32_t)((((j >> 4) & 1) << 2) | (j & 3));
+}
+// One run from two accumulator tiles (times s): elements 0 .. 3 from a, 4 .. 7 from b.
+__device__ __forceinline__ void st_run_nt(__bf16* p, floatx4 a, floatx4 b, float s) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { r[e] = (__bf16)(a[e] * s); r[4 + e] = (__bf16)(b[e] * s); }
+    __builtin_nontemporal_store(__builtin_bit_cast(floatx4, r), reinterpret_cast<floatx4*>(p));
+}
+__device__ __forceinline__ void st_run(__bf16* p, floatx4 a, floatx4 b) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { r[e] = (__bf16)a[e]; r[4 + e] = (__bf16)b[e]; }
+    *reinterpret_cast<bf16x8*>(p) = r;
+}
+
 // Store eight values as one 16-byte row segment.
 __device__ __forceinline__ void st8v(__bf16* p, const float* x) {
     bf16x8 r;

@@ -201,13 +201,21 @@ __global__ __launch_bounds__(4 * D) void kd_fwd_kernel(
             KD_PHASE_MARK(n, 0);
             floatx4 Ot[2][NSB];   // O^T[i0 + 16mt + 4g + r][16tt + cl], lives to stage C
             if (n >= 0) {
-                if (CKPT) {   // chunk-start state for the backward, S[i][j]
+                if (CKPT) {   // chunk-start state for the backward: S[i][j] (bf16: in record order)
                     E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
+                    if constexpr (std::is_same<TR, Bf16T>::value) {
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
+                        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                        for (int mj = 0; mj < D / 16; ++mj)
-                            st4_nt(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
+                            for (int kb = 0; kb < D / 32; ++kb)
+                                st_run_nt(dst + rec_run<D>(i0 + 16 * nt + cl, kb, g), S[nt][2 * kb], S[nt][2 * kb + 1], 1.f);
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                            for (int mj = 0; mj < D / 16; ++mj)
+                                st4_nt(dst + ((uint32_t)(i0 + 16 * nt + cl) * D + 16 * mj + 4 * g), S[nt][mj]);
+                    }
                 }
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index i, N = token t),
                 // sub-block by sub-block as S_tt Kloc^T and S_tt Qloc^T, the state

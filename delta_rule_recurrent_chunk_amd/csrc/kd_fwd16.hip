@@ -257,10 +257,10 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (n >= 0) {
                 if (CKPT) {
                     E* dst = static_cast<E*>(ck.S) + ((size_t)bh * NC + n) * D * D;
-                    const float si = sm.sinv;
+                    const float si = sm.sinv;   // in record order (16-byte runs)
 #pragma unroll
-                    for (int mj = 0; mj < D / 16; ++mj)
-                        st4_nt(dst + ((uint32_t)(i0 + cl) * D + 16 * mj + 4 * g), S[mj] * si);
+                    for (int kb = 0; kb < D / 32; ++kb)
+                        st_run_nt(dst + rec_run<D>(i0 + cl, kb, g), S[2 * kb], S[2 * kb + 1], si);
                 }
                 // Y^T = S Kbar^T and O^T = S Qbar^T (M = value index, N = token)
                 // per token sub-block tt, as S_tt Kloc^T and S_tt Qloc^T with S_tt
