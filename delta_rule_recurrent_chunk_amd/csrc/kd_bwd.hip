@@ -758,6 +758,35 @@ __device__ __forceinline__ void bwd_chunk_body(
     lds_barrier();
     KD_BWD_MARK(2);
 
+    const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
+    const E* S0n = ckptS + unit * D * D;   // S0[i][j]
+    const E* dSn = wsdS + unit * D * D;    // dS[i][j]
+    // The state records: bf16 in record order (16-byte runs of the writers'
+    // accumulator lanes), fp32 row-major.
+    constexpr bool RUNS = std::is_same<TR, Bf16T>::value;
+    auto rec_at = [&](int i, int j) -> uint32_t {   // element (i, j)
+        if constexpr (RUNS) return rec_idx<D>(i, j);
+        else return (uint32_t)(i * D + j);
+    };
+    // natural-order fragment of row i, K = 32ks + 8g + e: two half runs
+    auto rec_row = [&](const E* m, int i, int ks) -> Frag {
+        if constexpr (RUNS) {
+            const uint32_t o = 4u * (uint32_t)(g >> 1);
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1)) + o);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1) + 1) + o);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return TR::ld_nat(m + i * D, ks, g);
+        }
+    };
+    // the dV stage's rows of the records (L2), in flight during the C x C tiles
+    Frag rds[KD_], rs0[KD_];
+#pragma unroll
+    for (int ks = 0; ks < KD_; ++ks) {
+        rds[ks] = rec_row(dSn, jc, ks);   // B[j][i] = dS[i][j]
+        rs0[ks] = rec_row(S0n, jc, ks);   // B[j][i] = S0[i][j]
+    }
+
     // ---------------- C x C tiles: P, dP, dGK, dGV (+ its transpose), dbeta
     for (int tile = w; tile < 10; tile += NW) {
         const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
@@ -840,27 +869,6 @@ __device__ __forceinline__ void bwd_chunk_body(
             if (cl == 0) sm.dbp[J_][t_] = db;
         }
     }
-    const int jc = 16 * w + cl;   // this lane's output column (key j, or value i for dV)
-    const E* S0n = ckptS + unit * D * D;   // S0[i][j]
-    const E* dSn = wsdS + unit * D * D;    // dS[i][j]
-    // The state records: bf16 in record order (16-byte runs of the writers'
-    // accumulator lanes), fp32 row-major.
-    constexpr bool RUNS = std::is_same<TR, Bf16T>::value;
-    auto rec_at = [&](int i, int j) -> uint32_t {   // element (i, j)
-        if constexpr (RUNS) return rec_idx<D>(i, j);
-        else return (uint32_t)(i * D + j);
-    };
-    // natural-order fragment of row i, K = 32ks + 8g + e: two half runs
-    auto rec_row = [&](const E* m, int i, int ks) -> Frag {
-        if constexpr (RUNS) {
-            const uint32_t o = 4u * (uint32_t)(g >> 1);
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1)) + o);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(m + rec_run<D>(i, ks, 2 * (g & 1) + 1) + o);
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-            return TR::ld_nat(m + i * D, ks, g);
-        }
-    };
     if (!std::is_same<TR, Bf16T>::value) {   // colsum(dS * S0) for column jc (bf16: below)
         float acc = 0.f;
         for (int x = 0; x < D / 4; ++x) {
@@ -894,8 +902,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         }
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
-            const Frag r_ds = rec_row(dSn, jc, ks);   // B[j][i] = dS[i][j]
-            const Frag r_s0 = rec_row(S0n, jc, ks);   // B[j][i] = S0[i][j]
+            const Frag r_ds = rds[ks], r_s0 = rs0[ks];
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) {
                 const int tr = SB * tt + cl;
