@@ -893,6 +893,19 @@ __device__ __forceinline__ void bwd_chunk_body(
     // operands from the state checkpoints in global memory (L2): rows
     // directly, columns through col_frag (whose tiles also give
     // colsum(dS * S0) for bf16).
+    // the rows of the column fragments below (bf16 record runs), in flight
+    // during the dV stage
+    Frag cs0[KD_][2], cds[KD_][2];
+    if constexpr (RUNS) {
+#pragma unroll
+        for (int ks = 0; ks < KD_; ++ks)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint32_t o = rec_run<D>(TR::KS * ks + 16 * hh + cl, w >> 1, g);
+                cs0[ks][hh] = *reinterpret_cast<const Frag*>(S0n + o);
+                cds[ks][hh] = *reinterpret_cast<const Frag*>(dSn + o);
+            }
+    }
     {
         floatx4 aVu[NSB], aVr[NSB];
 #pragma unroll
@@ -967,12 +980,10 @@ __device__ __forceinline__ void bwd_chunk_body(
         } else {
             csel = TR::col_sel(16 * w, g, cl);
         }
-        auto col_of = [&](const E* m, int ks, floatx4* tiles) -> Frag {
+        auto col_of = [&](const E* m, int ks, floatx4* tiles, const Frag* pre) -> Frag {
             if constexpr (RUNS) {
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    tiles[hh] = TR::mma(*reinterpret_cast<const Frag*>(m + rec_run<D>(TR::KS * ks + 16 * hh + cl, w >> 1, g)),
-                                        csel, floatx4{0.f, 0.f, 0.f, 0.f});
+                for (int hh = 0; hh < 2; ++hh) tiles[hh] = TR::mma(pre[hh], csel, floatx4{0.f, 0.f, 0.f, 0.f});
                 return TR::state_frag(tiles, 0);
             } else {
                 return TR::col_frag(m, D, ks, 16 * w, csel, g, cl, tiles);
@@ -982,8 +993,8 @@ __device__ __forceinline__ void bwd_chunk_body(
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
             floatx4 ts[2], td[2];
-            const Frag b_s0t = col_of(S0n, ks, ts);   // B[i][j] = S0[i][j]
-            const Frag b_dst = col_of(dSn, ks, td);   // B[i][j] = dS[i][j]
+            const Frag b_s0t = col_of(S0n, ks, ts, cs0[ks]);   // B[i][j] = S0[i][j]
+            const Frag b_dst = col_of(dSn, ks, td, cds[ks]);   // B[i][j] = dS[i][j]
             if (std::is_same<TR, Bf16T>::value) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
