@@ -841,12 +841,14 @@ __device__ __forceinline__ void bwd_chunk_body(
             }
         }
         dp = dp * us;   // dP[t][s] = u_s (dO V^T)[t][s]: column s = this lane's
+        const floatx4 drho4 = *reinterpret_cast<const floatx4*>(&sm.drho[SB * I_ + 4 * g]);
+        const floatx4 beta4 = *reinterpret_cast<const floatx4*>(&sm.beta[SB * I_ + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t_ = SB * I_ + 4 * g + r;
             const bool low = s_ < t_, inc = s_ <= t_;
-            const float dM = low ? -sm.drho[t_] * us : 0.f;
-            const float bt = sm.beta[t_];
+            const float dM = low ? -drho4[r] * us : 0.f;
+            const float bt = beta4[r];
             const float dgv = bt * dM * gk[r];
             P[t_ * LDP + s_] = TR::cvt(inc ? pp[r] : 0.f);
             const float dpv = inc ? dp[r] : 0.f, dgkv = bt * dM * gv[r];
@@ -861,11 +863,7 @@ __device__ __forceinline__ void bwd_chunk_body(
             } else if (s_ == t_) {
                 Gs[t_ * LDP + t_] = TR::cvt(0.f);
             }
-            float db = dM * gk[r] * gv[r];
-            db += __shfl_xor(db, 1, 64);
-            db += __shfl_xor(db, 2, 64);
-            db += __shfl_xor(db, 4, 64);
-            db += __shfl_xor(db, 8, 64);
+            const float db = row16_sum(dM * gk[r] * gv[r]);
             if (cl == 0) sm.dbp[J_][t_] = db;
         }
     }

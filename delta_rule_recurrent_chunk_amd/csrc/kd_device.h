@@ -951,6 +951,18 @@ __device__ __forceinline__ void quad_excl_prod(float x, int r4, float& pre, floa
     suf = (r4 <= 2) ? y3 : 1.f;
 }
 
+// The sum over the 16 lanes of a DPP row, in every lane of the row, as the
+// butterfly over lane ^ 1, ^ 2, ^ 4, ^ 8.  The last two partners come from the
+// half-row and row mirrors: at that point they hold the same partial sums as
+// lane ^ 4 and lane ^ 8, so every addition has the butterfly's operands.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_quad<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_quad<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));   // half-row mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));   // row mirror
+    return x;
+}
+
 // One step of a transpose-reduce over the 16 lanes of a DPP row: x[0 .. 2M)
 // of every lane are summed in pairs with a partner lane whose bit M of the
 // row index differs, and each lane keeps the half selected by that bit (the
