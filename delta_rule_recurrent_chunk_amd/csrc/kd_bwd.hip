@@ -697,15 +697,16 @@ __device__ __forceinline__ void bwd_chunk_body(
 
     // ---------------- prep (b): operands, factors, the exact pass's pairs
     {
-        float bp[NSB][8];
+        float bp[NSB][8], bpI[8];   // bpI: this thread's own sub-block (an LDS read, not a register select)
 #pragma unroll
         for (int I2 = 0; I2 < NSB; ++I2) ld8f(&sm.bprod[I2][ch0], bp[I2]);
+        ld8f(&sm.bprod[I][ch0], bpI);
         float a_[2][8], b_[2][8];
         locals(pf, a_, b_);
         unsigned fl = 0u, tiny = 0u;   // bit c: channel ch0 + c
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            if (!(bp[I][c] >= kSafeFloor)) fl |= 1u << c;
+            if (!(bpI[c] >= kSafeFloor)) fl |= 1u << c;
             if (!(pf.get(0, c) >= TinyGate<TR>::value) || !(pf.get(1, c) >= TinyGate<TR>::value)) tiny |= 1u << c;
         }
         if (r8 == 0 && fl) atomicOr(&sm.fbm[I][ch0 >> 5], fl << (ch0 & 31));
@@ -713,7 +714,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         if (r8 == 0) {   // this sub-block's diagonal factor; sub-block 0 also the rest
             float x[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = bp[I][c] >= kSafeFloor ? __builtin_amdgcn_rcpf(bp[I][c]) : 0.f;
+            for (int c = 0; c < 8; ++c) x[c] = bpI[c] >= kSafeFloor ? __builtin_amdgcn_rcpf(bpI[c]) : 0.f;
             st8v(&sm.fac[I][ch0], x);
             if (I == 0) {
                 float y[8], z[8], gm[NSB][8], af[NSB][8];
