@@ -206,6 +206,11 @@ __device__ __forceinline__ void bwd_state_body(
     constexpr int KC_ = CH / TR::KS;
     constexpr int LD = SM::LD, LDT = SM::LDT, LDM = SM::LDM, LDP = SM::LDP;
     constexpr int EPV = 16 / sizeof(E);   // P elements per 16-byte slice
+    // bf16 at d >= 64: dO, Qbar and Kbar are kept row-major (in the space of
+    // the transposed arrays OT, QT, KT; VT is not used) and their columns are
+    // read with the transpose read; otherwise the transposed copies.
+    constexpr bool ROWOPS = std::is_same<TR, Bf16T>::value && D >= 64;
+    static_assert(!ROWOPS || CH * LD <= D * LDT, "row-major operands fit the transposed arrays");
 
 
     const int tid = threadIdx.x;
@@ -370,12 +375,21 @@ __device__ __forceinline__ void bwd_state_body(
                 st8v(&sm.kv.Kt[(row0 + e) * LD + ch0], kt);
                 cur.v.store(&sm.kv.V[(row0 + e) * LD + ch0], e);
             }
+            if constexpr (ROWOPS) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                st2(&sm.VT[(ch0 + c) * LDT + row0], cur.v.get(0, c), cur.v.get(1, c));
-                st2(&sm.OT[(ch0 + c) * LDT + row0], cur.o.get(0, c), cur.o.get(1, c));
-                st2(&sm.QT[(ch0 + c) * LDT + row0], qo[0][c], qo[1][c]);
-                st2(&sm.KT[(ch0 + c) * LDT + row0], ko[0][c], ko[1][c]);
+                for (int e = 0; e < 2; ++e) {
+                    cur.o.store(&sm.OT[(row0 + e) * LD + ch0], e);
+                    st8v(&sm.QT[(row0 + e) * LD + ch0], qo[e]);
+                    st8v(&sm.KT[(row0 + e) * LD + ch0], ko[e]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    st2(&sm.VT[(ch0 + c) * LDT + row0], cur.v.get(0, c), cur.v.get(1, c));
+                    st2(&sm.OT[(ch0 + c) * LDT + row0], cur.o.get(0, c), cur.o.get(1, c));
+                    st2(&sm.QT[(ch0 + c) * LDT + row0], qo[0][c], qo[1][c]);
+                    st2(&sm.KT[(ch0 + c) * LDT + row0], ko[0][c], ko[1][c]);
+                }
             }
         }
         const int npf = max(n - 1, 0);   // the next chunk's loads run under this one
@@ -408,7 +422,9 @@ __device__ __forceinline__ void bwd_state_body(
         }
 #pragma unroll
         for (int ks = 0; ks < KC_; ++ks) {
-            const Frag bO = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
+            Frag bO;
+            if constexpr (ROWOPS) bO = TR::ld_col(&sm.OT[16 * w + cl], LD, ks, g);
+            else bO = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
             Frag ap[NSB];
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) ap[tt] = TR::ld_nat(&sm.PT[(SB * tt + cl) * LDP], ks, g);
@@ -421,10 +437,21 @@ __device__ __forceinline__ void bwd_state_body(
             // mirror, quad swaps), after which lane cl holds element cl
             float x[16];
 #pragma unroll
-            for (int tt = 0; tt < NSB; ++tt)
+            for (int tt = 0; tt < NSB; ++tt) {
+                if constexpr (std::is_same<TR, Bf16T>::value) {
+                    // V rows 16tt + 4g .. + 3 of column 16w + cl: one transpose read.
+                    // The elements are taken from a bf16x4 view of the result: a
+                    // bit cast of each 16-bit element to __bf16 compiled to a copy
+                    // of element 0 into all four here.
+                    const bf16x4 vc = __builtin_bit_cast(bf16x4, TR::ld16_col(&sm.kv.V[(SB * tt) * LD + 16 * w + cl], LD, g));
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[4 * tt + r] = dW[tt][r] * TR::tof(sm.kv.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
+                    for (int r = 0; r < 4; ++r) x[4 * tt + r] = dW[tt][r] * TR::tof(vc[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x[4 * tt + r] = dW[tt][r] * TR::tof(sm.kv.V[(SB * tt + 4 * g + r) * LD + 16 * w + cl]);
+                }
+            }
             row16_reduce_step<8>(x, cl);
             row16_reduce_step<4>(x, cl);
             row16_reduce_step<2>(x, cl);
@@ -477,8 +504,13 @@ __device__ __forceinline__ void bwd_state_body(
             Frag bO[KC_], bR[KC_];
 #pragma unroll
             for (int ks = 0; ks < KC_; ++ks) {
-                bO[ks] = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
-                bR[ks] = TR::row_times(&sm.VT[(16 * w + cl) * LDT], sm.dr0, ks, g);
+                if constexpr (ROWOPS) {   // columns of the row-major dO and V; dr0[t] on V's column
+                    bO[ks] = TR::ld_col(&sm.OT[16 * w + cl], LD, ks, g);
+                    bR[ks] = TR::scale_k(TR::ld_col(&sm.kv.V[16 * w + cl], LD, ks, g), 1.f, sm.dr0, ks, g);
+                } else {
+                    bO[ks] = TR::ld_nat(&sm.OT[(16 * w + cl) * LDT], ks, g);
+                    bR[ks] = TR::row_times(&sm.VT[(16 * w + cl) * LDT], sm.dr0, ks, g);
+                }
             }
 #pragma unroll
             for (int mj = 0; mj < D / 16; ++mj)
@@ -487,8 +519,16 @@ __device__ __forceinline__ void bwd_state_body(
             for (int ks = 0; ks < KC_; ++ks)
 #pragma unroll
                 for (int mj = 0; mj < D / 16; ++mj) {
-                    dSt[mj] = TR::mma(TR::ld_nat(&sm.QT[(16 * mj + cl) * LDT], ks, g), bO[ks], dSt[mj]);
-                    dSt[mj] = TR::mma(TR::ld_nat(&sm.KT[(16 * mj + cl) * LDT], ks, g), bR[ks], dSt[mj]);
+                    Frag aq, ak;
+                    if constexpr (ROWOPS) {
+                        aq = TR::ld_col(&sm.QT[16 * mj + cl], LD, ks, g);
+                        ak = TR::ld_col(&sm.KT[16 * mj + cl], LD, ks, g);
+                    } else {
+                        aq = TR::ld_nat(&sm.QT[(16 * mj + cl) * LDT], ks, g);
+                        ak = TR::ld_nat(&sm.KT[(16 * mj + cl) * LDT], ks, g);
+                    }
+                    dSt[mj] = TR::mma(aq, bO[ks], dSt[mj]);
+                    dSt[mj] = TR::mma(ak, bR[ks], dSt[mj]);
                 }
         }
         // this wave's stores of chunk n (and everything before them) have
