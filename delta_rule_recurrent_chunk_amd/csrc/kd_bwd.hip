@@ -618,7 +618,13 @@ struct BwdChunkSmem {
 // left the channel out (decay below the floor) or that holds a gate below
 // TinyGate<TR>::value, the exact pass writes dq, dk and df of those 16 tokens from the
 // recurrence on the state's column j (from the records S0 and dS).
-template <class TR, int D>
+// No warm-up of a next unit (one unit per block).
+struct NoNextUnit {
+    __device__ void publish() const {}
+    __device__ bool target(int&, int&) const { return false; }
+};
+
+template <class TR, int D, class NX = NoNextUnit>
 __device__ __forceinline__ void bwd_chunk_body(
     BwdChunkSmem<TR, D>& sm, int bh, int n, int tid, unsigned stale,
     const typename TR::E* __restrict__ q, const typename TR::E* __restrict__ k,
@@ -628,7 +634,7 @@ __device__ __forceinline__ void bwd_chunk_body(
     const typename TR::E* __restrict__ wsdS, const float* __restrict__ wsrho,
     typename TR::E* __restrict__ dq, typename TR::E* __restrict__ dk,
     typename TR::E* __restrict__ dv, typename TR::E* __restrict__ df,
-    float* __restrict__ dbeta, float* __restrict__ dc, int T, int H)
+    float* __restrict__ dbeta, float* __restrict__ dc, int T, int H, const NX& nx = NX())
 {
     typedef typename TR::E E;
     typedef typename TR::Frag Frag;
@@ -732,6 +738,7 @@ __device__ __forceinline__ void bwd_chunk_body(
         for (int c = 0; c < 8; ++c) incl[c] = group8_prefix_prod(pf.get(0, c) * pf.get(1, c), r8);
         if (r8 == 7) st8v(&sm.bprod[I][ch0], incl);
     }
+    nx.publish();   // the next unit (a persistent worker's claim), once this unit's rows have arrived
     lds_barrier();
     KD_BWD_MARK(1);
 
@@ -1195,6 +1202,28 @@ __device__ __forceinline__ void bwd_chunk_body(
             put8(dk, e, dkv[e]);
         }
     }
+    // The next unit's rows of q, k, v, f, dO into L2 while this one finishes:
+    // one 4-byte load per 128-byte line (5 inputs x 64 rows x 2D / 128 lines),
+    // its value kept until the end of the unit so the load stays.
+    constexpr int LPR = D * (int)sizeof(E) > 128 ? D * (int)sizeof(E) / 128 : 1;   // lines per row
+    constexpr int NLN = 5 * CH * LPR;
+    static_assert((CH * LPR) % 64 == 0, "the lines of one input fill whole waves");
+    unsigned warm[(NLN + NT - 1) / NT];
+    int wbh = 0, wn = 0;
+    const bool do_warm = nx.target(wbh, wn);
+#pragma unroll
+    for (int x = 0; x < (NLN + NT - 1) / NT; ++x) {
+        warm[x] = 0u;
+        const int L = tid + NT * x;
+        if (do_warm && L < NLN) {
+            const int a = __builtin_amdgcn_readfirstlane(L / (CH * LPR));   // uniform over the wave
+            const int t = min(wn * CH + (L / LPR) % CH, T - 1), part = L % LPR;
+            const E* src = a == 0 ? q : a == 1 ? k : a == 2 ? v : a == 3 ? f : dO;
+            const size_t off = (size_t)(wbh / H) * T * H * D + (uint32_t)t * rs + (uint32_t)(wbh % H) * D +
+                               part * (128 / sizeof(E));
+            warm[x] = *reinterpret_cast<const unsigned*>(src + off);
+        }
+    }
     if (r8 == 0) {
         st8v(&sm.gsub[I][ch0], totg);
         st8v(&sm.hsub[I][ch0], toth);
@@ -1329,6 +1358,8 @@ __device__ __forceinline__ void bwd_chunk_body(
             }
     }
     KD_BWD_MARK(11);
+#pragma unroll
+    for (int x = 0; x < (NLN + NT - 1) / NT; ++x) asm volatile("" ::"v"(warm[x]));
 }
 
 template <class TR, int D>
@@ -1395,6 +1426,7 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
     };
     __shared__ Smem sm;
     __shared__ int g_unit;
+    __shared__ int g_next;   // the unit claimed after the current one (-1: none)
     const int x = blockIdx.x;
     const int NC = (T + CH - 1) / CH;
     int c;   // this block's XCD under round-robin placement: x mod 8
@@ -1474,8 +1506,31 @@ __global__ __launch_bounds__(4 * D) void kd_bwd_fused_kernel(
         // loop to hold registers through the body
         int z;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        bwd_chunk_body<TR, D>(sm.c, bh, n, (int)threadIdx.x + z, gu < 0 ? 1u : 0u, q, k, v, f, beta, dO, ckptS,
-                              ckptU, wsdS, wsrho, dq, dk, dv, df, dbeta, dc, T, H);
+        // the next unit for the body's L2 warm-up: thread 0 publishes the
+        // claim in flight (or the next static unit) during the body's first
+        // stage, every thread reads it after that stage's barrier
+        struct NextUnit {
+            bool dyn; unsigned long long pending; int next;   // thread 0's (others: unused)
+            int total, nh, c, NC;
+            __device__ void publish() const {
+                if (threadIdx.x == 0) {
+                    int u2 = -1;
+                    if (dyn) { if ((unsigned)pending < (unsigned)total) u2 = (int)(unsigned)pending; }
+                    else if (next >= 0 && next < total) u2 = next;
+                    g_next = u2;
+                }
+            }
+            __device__ bool target(int& bh2, int& n2) const {
+                const int u2 = g_next;
+                if (u2 < 0) return false;
+                n2 = NC - 1 - u2 / nh;
+                bh2 = c + 8 * (u2 % nh);
+                return true;
+            }
+        };
+        const NextUnit nx{dyn, pending, next, total, nh, c, NC};
+        bwd_chunk_body<TR, D, NextUnit>(sm.c, bh, n, (int)threadIdx.x + z, gu < 0 ? 1u : 0u, q, k, v, f, beta, dO,
+                                        ckptS, ckptU, wsdS, wsrho, dq, dk, dv, df, dbeta, dc, T, H, nx);
         lds_barrier();   // the next unit reuses the LDS (and g_unit)
     }
 }
