@@ -192,11 +192,15 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             if (!ob) return;
             if (GATES && gt.og) {
                 const int c8 = 8 * (lane & 15);   // the same columns on every row of this lane
+                // the row indices are formed here on every call (an opaque zero on
+                // the thread index): hoisted out of the chunk loop they were
+                // spilled, and each reload waited for every load and store in flight
+                const int tx = tid - tid0 + opaque_zero();
                 constexpr int MAXR = 3;
                 bf16x8 gv[MAXR];   // raw logits, widened when used
 #pragma unroll
                 for (int it = 0; it < MAXR; ++it) {
-                    const int x = tid - tid0 + it * nthr;
+                    const int x = tx + it * nthr;
                     const int tok = min(nc * CH + (x >> 4), T - 1);
                     if (x < CH * D / 8)
                         gv[it] = *reinterpret_cast<const bf16x8*>(gt.og + bbase + ((uint32_t)tok * rs + hoff + c8));
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 ld8f(gt.norm_w + (uint32_t)h * D + c8, wv);
 #pragma unroll
                 for (int it = 0; it < MAXR; ++it) {
-                    const int x = tid - tid0 + it * nthr;
+                    const int x = tx + it * nthr;
                     if (x < CH * D / 8) {   // the same for all 16 lanes of the row
                         const int t = x >> 4;
                         float xv[8];
