@@ -71,6 +71,9 @@ constexpr int LDP = CH + 8;       // P
 // Rows of the factor table Fwd16Smem::fac (key channels in pcol order).
 // Rows DIAG .. D30 are the Gram tiles' (pcol order); rows SUB + I are the
 // decay over sub-block I in natural channel order (the state's decay).
+// parts of a Gram tile (gram_tile)
+constexpr int GT_MP = 0, GT_P = 1, GT_GK = 2, GT_GV = 3;
+
 namespace facrow {
 constexpr int DIAG = 0;    // DIAG + I: 1 / (decay over sub-block I), 0 for a channel below the floor
 constexpr int D20 = 4;     // decay over sub-block 1 (tile I=2, J=0)
@@ -87,7 +90,9 @@ struct Fwd16Smem {
     alignas(16) __bf16 V[CH * f16w::LD];        // v
     alignas(16) __bf16 Os[CH * f16w::LDO];      // o of the chunk, natural columns (staging)
     alignas(16) _Float16 KtT[f16w::D * f16w::LDT];  // (k gamma_C / gamma)^T * kscale
-    alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V)
+    alignas(16) float M[CH * f16w::LDM];        // beta_t tril_{-1}(G_K * G_V); rows 48..63 of tiles
+                                                 //   (3,2), (3,3): beta_t G_K only (times G3 when read)
+    alignas(16) float G3[2][SB * SB];           // G_V of tiles (3,2), (3,3), [tile][t][s]
     alignas(16) __bf16 P[2][CH * f16w::LDP];    // tril_0 of the decayed Q K^T, by chunk parity
     alignas(16) float beta[2][CH];
     alignas(16) float c[2][CH];
@@ -360,7 +365,11 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     float Mrow[16];
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) {
-                        const floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t_ * LDM + 16 * sb + 4 * s4]);
+                        floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t_ * LDM + 16 * sb + 4 * s4]);
+                        if (sb >= 2) {   // tiles (3,2), (3,3): G_V on M's beta G_K (1 on rows < 48)
+                            const floatx4 g4 = *reinterpret_cast<const floatx4*>(&sm.G3[sb - 2][(t_ & 15) * SB + 4 * s4]);
+                            m4 = t_ >= 48 ? m4 * g4 : m4;
+                        }
                         Mrow[4 * s4] = m4[0]; Mrow[4 * s4 + 1] = m4[1];
                         Mrow[4 * s4 + 2] = m4[2]; Mrow[4 * s4 + 3] = m4[3];
                     }
@@ -396,11 +405,15 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 // copy them out
                 float* dm = ck.M + ((size_t)bh * NC + n) * CH * CH;
                 E* dp = static_cast<E*>(ck.P) + ((size_t)bh * NC + n) * CH * CH;
-                for (int x = tid - 64; x < CH * CH / 4; x += (NWC - 1) * 64) {
+                const int tc = tid - 64 + opaque_zero();   // formed here, not hoisted out of the loop
+                for (int x = tc; x < CH * CH / 4; x += (NWC - 1) * 64) {
                     const int t = x >> 4, s4 = x & 15;
-                    cp16_nt(dm + t * CH + 4 * s4, &sm.M[t * LDM + 4 * s4]);
+                    floatx4 m4 = *reinterpret_cast<const floatx4*>(&sm.M[t * LDM + 4 * s4]);
+                    if (t >= 48 && s4 >= 8)   // tiles (3,2), (3,3): times G_V, as the substitution read them
+                        m4 = m4 * *reinterpret_cast<const floatx4*>(&sm.G3[(s4 >> 2) - 2][(t - 48) * SB + 4 * (s4 & 3)]);
+                    __builtin_nontemporal_store(m4, reinterpret_cast<floatx4*>(dm + t * CH + 4 * s4));
                 }
-                for (int x = tid - 64; x < CH * CH / 8; x += (NWC - 1) * 64) {
+                for (int x = tc; x < CH * CH / 8; x += (NWC - 1) * 64) {
                     const int t = x >> 3, s8 = x & 7;
                     cp16_nt(dp + t * CH + 8 * s8, &sm.P[n & 1][t * LDP + 8 * s8]);
                 }
@@ -573,7 +586,10 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t_ = SB * I_ + 4 * g + r;
-                if (s_ < t_) sm.M[t_ * LDM + s_] += sm.beta[ch & 1][t_] * dk[r] * gv[r];
+                if (s_ < t_) {   // tile (3,3) holds beta G_K (its G_V goes on when read)
+                    if (I_ == NSB - 1) sm.M[t_ * LDM + s_] += sm.beta[ch & 1][t_] * dk[r];
+                    else sm.M[t_ * LDM + s_] += sm.beta[ch & 1][t_] * dk[r] * gv[r];
+                }
                 if (s_ <= t_) {
                     E& pe = sm.P[ch & 1][t_ * LDP + s_];
                     pe = TR::cvt(TR::tof(pe) + dp[r]);
@@ -585,8 +601,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         // entries of M, the P part the tile's entries of P; the two parts never
         // touch the same entry.  The decay between the two sub-blocks goes on
         // the Kr fragment (fac row fr).
-        auto gram_tile = [&](auto do_m, auto do_p, int tile, int ch) {
-            constexpr bool DO_M = decltype(do_m)::value, DO_P = decltype(do_p)::value;
+        // MODE: GT_MP both parts; GT_P the P part; GT_GK M's rows as beta G_K
+        // (tiles 8, 9; G_V goes on when M is read); GT_GV G_V into G3 (tiles 8, 9).
+        auto gram_tile = [&](auto mode_c, int tile, int ch) {
+            constexpr int MODE = decltype(mode_c)::value;
+            constexpr bool DO_GK = MODE == GT_MP || MODE == GT_GK, DO_GV = MODE == GT_MP || MODE == GT_GV;
+            constexpr bool DO_M = DO_GK || DO_GV, DO_P = MODE == GT_MP || MODE == GT_P;
             const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J_ = tile - (I_ * (I_ + 1)) / 2;
             const int fr = I_ == J_ ? facrow::DIAG + I_
@@ -604,9 +624,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             struct GF { Frag k, a, q, v, w; };
             auto ldg = [&](int ks) {
                 GF r;
-                r.k = TR::ld_nat(bK, ks, g);
-                if (fr >= 0 && !slow_p) r.k = TR::scale_k(r.k, 1.f, sm.fac[fr], ks, g);
-                if (DO_M) { r.a = TR::ld_nat(aK, ks, g); r.v = TR::ld_nat(aV, ks, g); r.w = TR::ld_nat(bV, ks, g); }
+                if (DO_GK || DO_P) {
+                    r.k = TR::ld_nat(bK, ks, g);
+                    if (fr >= 0 && !slow_p) r.k = TR::scale_k(r.k, 1.f, sm.fac[fr], ks, g);
+                }
+                if (DO_GK) r.a = TR::ld_nat(aK, ks, g);
+                if (DO_GV) { r.v = TR::ld_nat(aV, ks, g); r.w = TR::ld_nat(bV, ks, g); }
                 if (DO_P) r.q = TR::ld_nat(aQ, ks, g);
                 return r;
             };
@@ -614,20 +637,24 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             for (int ks = 0; ks < KD_; ++ks) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
                 const GF cur = ldg(ks);
-                if (DO_M) gk = TR::mma(cur.a, cur.k, ks ? gk : z);
+                if (DO_GK) gk = TR::mma(cur.a, cur.k, ks ? gk : z);
                 if (DO_P) pp = TR::mma(cur.q, cur.k, ks ? pp : z);
-                if (DO_M) gv = TR::mma(cur.v, cur.w, ks ? gv : z);
+                if (DO_GV) gv = TR::mma(cur.v, cur.w, ks ? gv : z);
             }
             const int s_ = SB * J_ + cl + opaque_zero();   // addresses formed here, not hoisted
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t_ = SB * I_ + 4 * g + r;
-                if (DO_M && s_ < t_) sm.M[t_ * LDM + s_] = sm.beta[ch & 1][t_] * gk[r] * gv[r];
+                if (MODE == GT_MP && s_ < t_) sm.M[t_ * LDM + s_] = sm.beta[ch & 1][t_] * gk[r] * gv[r];
+                if (MODE == GT_GK && s_ < t_) sm.M[t_ * LDM + s_] = sm.beta[ch & 1][t_] * gk[r];
+                if (MODE == GT_GV) sm.G3[tile - 8][(4 * g + r) * SB + cl] = gv[r];
                 if (DO_P) sm.P[ch & 1][t_ * LDP + s_] = TR::cvt((s_ <= t_) ? pp[r] : 0.f);
             }
         };
-        typedef std::integral_constant<bool, true> kYes;
-        typedef std::integral_constant<bool, false> kNo;
+        typedef std::integral_constant<int, GT_MP> kMP;
+        typedef std::integral_constant<int, GT_P> kP;
+        typedef std::integral_constant<int, GT_GK> kGK;
+        typedef std::integral_constant<int, GT_GV> kGV;
 
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
@@ -641,12 +668,14 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                     keep_kt[c2].store(&sm.KtT[(ch0 + c2) * LDT + rb]);
                 }
                 // tiles 8 and 9 (rows 48..63) are first read by the substitution
-                // (M) and the readout (P) of chunk n: their M and P parts run
-                // here on producer waves 0..3, one SIMD each
-                if (pw < 4) {
-                    if (pw >= 2) gram_tile(kNo(), kYes(), 8 + (pw & 1), n);
-                    else gram_tile(kYes(), kNo(), 8 + (pw & 1), n);
-                }
+                // (M) and the readout (P) of chunk n: they run here on producer
+                // waves 0..3 and 6, 7, one matrix product each (beta G_K into M,
+                // G_V into G3, P), so that no wave carries two; producer waves
+                // pw and pw + 4 share a SIMD, so the G_K waves (with the decay
+                // factors) have theirs alone
+                if (pw < 2) gram_tile(kGK(), 8 + pw, n);
+                else if (pw < 4) gram_tile(kGV(), 8 + (pw & 1), n);
+                else if (pw >= 6) gram_tile(kP(), 8 + (pw & 1), n);
                 if (sm.fbany[n & 1] != 0u) {   // every tile of chunk n is done: exact pass
                     lds_barrier();
                     if ((pw & 1) == 0) diag_exact(pw >> 1, n);
@@ -826,7 +855,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
             load_k(npf);
-            if (prod_on) gram_tile(kYes(), kYes(), pw, nn);   // tiles 0..7
+            if (prod_on) gram_tile(kMP(), pw, nn);   // tiles 0..7
             load_v(npf);
             load_f(npf);
             KD_PHASE_MARK(n, 5);
