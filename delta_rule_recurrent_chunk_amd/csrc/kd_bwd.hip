@@ -1036,24 +1036,30 @@ __device__ __forceinline__ void bwd_chunk_body(
             }
         };
         float gc2 = 0.f;
+        // every K-step's column fragments first (their selection products are
+        // independent), then the contractions, so no K-step waits on its own
+        Frag bs0[KD_], bds[KD_];
 #pragma unroll
         for (int ks = 0; ks < KD_; ++ks) {
             floatx4 ts[2], td[2];
-            const Frag b_s0t = col_of(S0n, ks, ts, cs0[ks]);   // B[i][j] = S0[i][j]
-            const Frag b_dst = col_of(dSn, ks, td, cds[ks]);   // B[i][j] = dS[i][j]
+            bs0[ks] = col_of(S0n, ks, ts, cs0[ks]);   // B[i][j] = S0[i][j]
+            bds[ks] = col_of(dSn, ks, td, cds[ks]);   // B[i][j] = dS[i][j]
             if (std::is_same<TR, Bf16T>::value) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) gc2 += ts[hh][r] * td[hh][r];
             }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KD_; ++ks) {
 #pragma unroll
             for (int tt = 0; tt < NSB; ++tt) {
                 const int tr = SB * tt + cl;
                 const Frag a_v = TR::ld_colmatch(&Vs[tr * LD], ks, g);
-                aQ[tt] = TR::mma(TR::ld_colmatch(&Do[tr * LD], ks, g), b_s0t, aQ[tt]);   // dO S0
-                aK[tt] = TR::mma(a_v, b_s0t, aK[tt]);                                      // V S0
-                aT[tt] = TR::mma(a_v, b_dst, aT[tt]);                                      // V dS
+                aQ[tt] = TR::mma(TR::ld_colmatch(&Do[tr * LD], ks, g), bs0[ks], aQ[tt]);   // dO S0
+                aK[tt] = TR::mma(a_v, bs0[ks], aK[tt]);                                      // V S0
+                aT[tt] = TR::mma(a_v, bds[ks], aT[tt]);                                      // V dS
             }
         }
         if (std::is_same<TR, Bf16T>::value) {
