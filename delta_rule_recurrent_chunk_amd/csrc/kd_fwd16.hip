@@ -717,6 +717,12 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             lds_barrier();
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
+            // the producers' work bounds stages B and C, where the consumers
+            // other than the substitution's wave have slack: their instructions
+            // issue first (the substitution itself runs at a higher level).  With
+            // the gates, the consumers' row writes carry the gated norm in stage
+            // B, so there the boost starts in stage C.
+            if (!GATES) __builtin_amdgcn_s_setprio(2);
             if (prod_on) {   // operands of chunk nn into LDS
                 // Decay products from the 8-row blocks of the producer waves
                 // (bprod[p]; sub-block I2 = blocks 2 I2 and 2 I2 + 1), per wave:
@@ -854,11 +860,13 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
+            if (GATES) __builtin_amdgcn_s_setprio(2);
             load_k(npf);
             if (prod_on) gram_tile(kMP(), pw, nn);   // tiles 0..7
             load_v(npf);
             load_f(npf);
             KD_PHASE_MARK(n, 5);
+            __builtin_amdgcn_s_setprio(0);
             lds_barrier();
         }
         lds_barrier();   // the consumers stage the last chunk's o
