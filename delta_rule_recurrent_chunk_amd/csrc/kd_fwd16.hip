@@ -662,6 +662,9 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
             const int oz = opaque_zero();     // per-lane LDS addresses stay inside the loop
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
+            // the producer waves with a Gram product in this stage (beta G_K and
+            // P) would finish last: they issue before the others
+            if (pw < 2 || pw >= 6) __builtin_amdgcn_s_setprio(1);
             if (n >= 0) {   // transposed K-tilde of chunk n and its last two Gram tiles
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
@@ -714,6 +717,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
             }
             KD_PHASE_MARK(n, 3);
+            __builtin_amdgcn_s_setprio(0);
             lds_barrier();
             // ======================================================= stage B
             KD_PHASE_MARK(n, 1);
