@@ -21,13 +21,15 @@
 //   1. every wave prepares 8 rows of the chunk (two key channels per lane):
 //      decay products, the operands above into LDS (the next chunk's rows are
 //      loaded during phases 2 and 3);
-//   2. Gram tiles of T and P; each wave forms Ebar S0 and Qbar S0 for its 16
-//      value columns (the state lives in its MFMA accumulators, keys as rows);
-//      the wave of each diagonal Gram tile inverts that 16 x 16 block of I + T;
+//   2. Gram tiles of T and P (waves 4..7 take the four diagonal tiles and
+//      invert that 16 x 16 block of I + T, four lanes per column); each wave
+//      forms Ebar S0 and Qbar S0 for its 16 value columns (the state lives in
+//      its MFMA accumulators, keys as rows).  The off-diagonal T blocks and
+//      the block inverses go to LDS once, as bf16 hi + lo operand fragments;
 //   3. each wave solves (I + T) U = Z - Ebar S0 for its value columns block by
-//      block with 16 x 16 x 16 MFMAs on bf16 hi + lo splits (fp32-like
-//      products), then the readout O = Qbar S0 + P U and the update
-//      S <- diag(gamma_C) S + Ktil^T U (Ktil and U also split hi + lo).
+//      block with 16x16x32 products of the hi + lo parts (fp32-like), then
+//      the readout O = Qbar S0 + P U and the update S <- diag(gamma_C) S +
+//      Ktil^T U, whose operands go in fp16 with exact power-of-two scales.
 #include "kd_device.h"
 
 // Phase markers: no-ops here; a profiling build may define them to record
@@ -45,24 +47,28 @@ constexpr int NW = 8;             // waves
 constexpr int RB = CH / NW;       // rows per wave in phase 1
 constexpr int LD = D + 16;        // row-major [CH][D] operands (key columns in pcol order)
 constexpr int LDT = CH + 8;       // transposed [D][CH] operands
-constexpr int LDM = CH + 4;       // fp32 T (and the fallback scratch)
+constexpr int LDM = CH + 4;       // fp32 exact-term scratch
+constexpr int LDO = 2 * LDM;      // bf16 o staging rows over the same bytes
 constexpr int LDP = CH + 8;       // P (token columns in pcol order)
-constexpr int LDX = 16 + 4;       // fp32 inverses of the diagonal blocks
 }  // namespace g2w
 
 struct Gdn2Smem {
     alignas(16) __bf16 Qb[CH * g2w::LD];       // q * gamma
     alignas(16) __bf16 Eb[CH * g2w::LD];       // b * k * gamma
     alignas(16) __bf16 Kc[CH * g2w::LD];       // k / gamma (0 for fallback channels)
-    alignas(16) __bf16 KtH[g2w::D * g2w::LDT]; // Ktil^T, high bf16 part (token columns in pcol order)
-    alignas(16) __bf16 KtL[g2w::D * g2w::LDT]; // Ktil^T, low part
+    alignas(16) _Float16 Kt[2][g2w::D * g2w::LDT]; // (Ktil 2^-ek)^T in fp16 (token columns in pcol order), by chunk parity
     alignas(16) __bf16 ZT[g2w::D * g2w::LDT];  // (w * v)^T, natural token order
-    alignas(16) float Tm[CH * g2w::LDM];       // T; fallback scratch
+    alignas(16) float Tm[CH * g2w::LDM];       // exact terms of the fallback channels; o staging in phase 3
     alignas(16) __bf16 P[CH * g2w::LDP];
-    alignas(16) float X[4][16 * g2w::LDX];     // (I + T_II)^{-1}
+    alignas(16) float X[4][16 * 16];           // scratch of the block inverses
+    // A operands of the block solve, ready for 16x16x32 products: per lane,
+    // the bf16 hi and lo parts of four adjacent entries of one row
+    alignas(16) __bf16 TF[6][64 * 8];          // -T_IJ (I > J)
+    alignas(16) __bf16 XF[4][64 * 8];          // (I + T_II)^{-1}
     alignas(16) float bprod[g2w::NW][g2w::D];  // product of alpha over each 8-row block
-    alignas(16) float gam[g2w::D];             // gamma_C
-    unsigned unsafe;
+    alignas(16) float gam[2][g2w::D];          // gamma_C, by chunk parity
+    float kmx[g2w::NW];                        // largest |k| of each wave's rows
+    unsigned unsafe[2];                        // a fallback channel in the chunk, by parity
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -77,26 +83,23 @@ __device__ __forceinline__ void split_hl(floatx4 x, s16x4& hi, s16x4& lo) {
         lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)hh));
     }
 }
-__device__ __forceinline__ floatx4 mma16(s16x4 a, s16x4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+// Entry (i, k) of a 16 x 16 block into the x32 A-operand layout: lane
+// 16 (k / 4) + i holds row i, columns 4 (k / 4) .. + 3, hi parts first.
+__device__ __forceinline__ void put_frag(__bf16* f, int i, int k, float x) {
+    const __bf16 hh = (__bf16)x;
+    __bf16* p = f + (16 * (k >> 2) + i) * 8 + (k & 3);
+    p[0] = hh;
+    p[4] = (__bf16)(x - (float)hh);
 }
-__device__ __forceinline__ floatx4 mma16_3(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, floatx4 c) {
-    c = mma16(ah, bh, c);
-    c = mma16(ah, bl, c);
-    return mma16(al, bh, c);
-}
-// low bf16 parts of Bf16T::state_frag(acc, ks)
-__device__ __forceinline__ Bf16T::Frag state_frag_lo(const floatx4* acc, int ks, Bf16T::Frag hi) {
-    const floatx4 a = acc[2 * ks], b = acc[2 * ks + 1];
-    Bf16T::Frag r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = (__bf16)(a[e] - (float)hi[e]);
-        r[4 + e] = (__bf16)(b[e] - (float)hi[4 + e]);
+// x of lane k of each quad, to all four lanes of the quad
+__device__ __forceinline__ float quad_bcast(float x, int k) {
+    switch (k) {
+    case 0: return dpp_quad<0x00>(x);
+    case 1: return dpp_quad<0x55>(x);
+    case 2: return dpp_quad<0xAA>(x);
+    default: return dpp_quad<0xFF>(x);
     }
-    return r;
 }
-
 __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ al, const __bf16* __restrict__ bg, const __bf16* __restrict__ wg,
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
     // one-time init: the upper triangles of T and P are never written
     for (int x = tid; x < CH * LDM; x += NT) sm.Tm[x] = 0.f;
     for (int x = tid; x < CH * LDP; x += NT) sm.P[x] = (E)0.f;
-    if (tid == 0) sm.unsafe = 0u;
+    if (tid < 2) sm.unsafe[tid] = 0u;
 
     // state: this wave's value columns i0 .. i0 + 15, S[16mj + 4g + r][i0 + cl] in S[mj][r]
     const int i0 = 16 * w;
@@ -169,17 +172,17 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
         rbb.load(bgb, off, rs, last);
         rw.load(wgb, off, rs, last);
     };
-    load_rows_a(0);
-    load_rows_b(0);
-    lds_barrier();
-
-    for (int n = 0; n < NC; ++n) {
-        KD_PHASE_MARK(n, 0);
-        // =========================================== phase 1: operands of chunk n
-        if (n * CH + CH > T) {   // ragged last chunk: rows past the end contribute nothing
+    // Chunk m's operands are prepared one phase ahead: its block products at
+    // the end of phase 2 of chunk m - 1, the rest during phase 3 of chunk m - 1.
+    // In phase 3 the waves of one SIMD (w and w + 4) take the two jobs in
+    // opposite orders, so the preparation's vector arithmetic runs beside the
+    // other wave's products.
+    // chunk m's decay products over each wave's 8 rows and its largest |k|
+    auto prep_a = [&](int m) __attribute__((always_inline)) {
+        if (m * CH + CH > T) {   // ragged last chunk: rows past the end contribute nothing
 #pragma unroll
             for (int e = 0; e < RB; ++e)
-                if (n * CH + rb + e >= T) {
+                if (m * CH + rb + e >= T) {
                     rq.clear(e, 0.f); rk.clear(e, 0.f); rv.clear(e, 0.f);
                     ra.clear(e, 1.f); rbb.clear(e, 0.f); rw.clear(e, 0.f);
                 }
@@ -193,9 +196,30 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 tot[c2] = (x0 * x1) * (x2 * x3);
             }
             st2(&sm.bprod[w][ch0], tot[0], tot[1]);
+            float km = 0.f;
+#pragma unroll
+            for (int e = 0; e < RB; ++e)
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) km = fmaxf(km, fabsf(rk.get(e, c2)));
+            km = wave_max_nonneg(km);
+            if (lane == 0) sm.kmx[w] = km;
         }
-        lds_barrier();
-        unsigned pmask = 0;   // fallback channels (bit c: ch0 + c)
+    };
+    // chunk m's operands into LDS: Qbar, Ebar, Kbar, Z^T and the K~ and gamma_C
+    // buffers of its parity; ek_out is its K~ scale exponent and pmask_out the
+    // lane's fallback channels
+    auto prep_b = [&](int m, int& ek_out, unsigned& pmask_out) __attribute__((always_inline)) {
+        // Ktil = k gamma_C / gamma is at most |k| in size: with the chunk's
+        // largest |k| = x 2^ek (1/2 <= x < 1), Ktil 2^-ek lies in (-1, 1) and
+        // goes to the update in fp16
+        {
+            float kmax = 0.f;
+#pragma unroll
+            for (int p = 0; p < NW; ++p) kmax = fmaxf(kmax, sm.kmx[p]);
+            ek_out = pow2_exp(kmax);
+        }
+        const float ksc = ldexpf(1.f, -ek_out);
+        pmask_out = 0u;   // fallback channels (bit c: ch0 + c)
         {
             // gamma before this block (plt), after it (pgt) and over the chunk
             // (gC, multiplied in one fixed order so every wave agrees on it)
@@ -210,11 +234,11 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const bool un = !(gC[c2] >= kSafeFloor);
-                if (un) pmask |= 1u << c2;
+                if (un) pmask_out |= 1u << c2;
                 rgC[c2] = un ? 0.f : 1.f / gC[c2];
             }
-            if (w == 0) st2(&sm.gam[ch0], gC[0], gC[1]);
-            if (pmask) atomicOr(&sm.unsafe, 1u);
+            if (w == 0) st2(&sm.gam[m & 1][2 * (lane + opaque_zero())], gC[0], gC[1]);   // address formed here, not held
+            if (pmask_out) atomicOr(&sm.unsafe[m & 1], 1u);
             // gamma_C / gamma at each row: suffix products within the block
             float om[RB][2];
 #pragma unroll
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 for (int e = RB - 2; e >= 0; --e) om[e][c2] = om[e + 1][c2] * ra.get(e + 1, c2);
             }
             float ga[2] = {plt[0], plt[1]};
-            uint32_t kth[2][RB / 2], ktl[2][RB / 2], zt[2][RB / 2];   // transposed pairs of tokens
+            uint32_t kth[2][RB / 2], zt[2][RB / 2];   // transposed pairs of tokens
 #pragma unroll
             for (int e = 0; e < RB; ++e) {
                 float qo[2], eo[2], co[2], kt[2], zo[2];
@@ -244,17 +268,13 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 // (token e, token e + 1) pairs per channel for the transposed stores
 #pragma unroll
                 for (int c2 = 0; c2 < 2; ++c2) {
-                    const __bf16 hh = (__bf16)kt[c2];
-                    const uint32_t hb = (uint32_t)__builtin_bit_cast(unsigned short, hh);
-                    const uint32_t lb = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)(kt[c2] - (float)hh));
+                    const uint32_t hb = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)(kt[c2] * ksc));
                     const uint32_t zb = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)zo[c2]);
                     if (e & 1) {
                         kth[c2][e >> 1] |= hb << 16;
-                        ktl[c2][e >> 1] |= lb << 16;
                         zt[c2][e >> 1] |= zb << 16;
                     } else {
                         kth[c2][e >> 1] = hb;
-                        ktl[c2][e >> 1] = lb;
                         zt[c2][e >> 1] = zb;
                     }
                 }
@@ -265,17 +285,26 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int row = (ch0 + c2) * LDT;
-                *reinterpret_cast<uint2*>(&sm.KtH[row + TR::pcol(rb)]) = make_uint2(kth[c2][0], kth[c2][1]);
-                *reinterpret_cast<uint2*>(&sm.KtH[row + TR::pcol(rb + 4)]) = make_uint2(kth[c2][2], kth[c2][3]);
-                *reinterpret_cast<uint2*>(&sm.KtL[row + TR::pcol(rb)]) = make_uint2(ktl[c2][0], ktl[c2][1]);
-                *reinterpret_cast<uint2*>(&sm.KtL[row + TR::pcol(rb + 4)]) = make_uint2(ktl[c2][2], ktl[c2][3]);
+                *reinterpret_cast<uint2*>(&sm.Kt[m & 1][row + TR::pcol(rb)]) = make_uint2(kth[c2][0], kth[c2][1]);
+                *reinterpret_cast<uint2*>(&sm.Kt[m & 1][row + TR::pcol(rb + 4)]) = make_uint2(kth[c2][2], kth[c2][3]);
                 *reinterpret_cast<uint4*>(&sm.ZT[row + rb]) = make_uint4(zt[c2][0], zt[c2][1], zt[c2][2], zt[c2][3]);
             }
         }
-        lds_barrier();
+    };
+    load_rows_a(0);
+    load_rows_b(0);
+    lds_barrier();
+    prep_a(0);
+    lds_barrier();
+    int ek_cur, ek_next = 0;
+    unsigned pmask, pmask_next = 0u;
+    prep_b(0, ek_cur, pmask);
+    lds_barrier();
 
+    for (int n = 0; n < NC; ++n) {
+        KD_PHASE_MARK(n, 0);
         // =========================================== exact fallback terms (rare)
-        const bool fbk = sm.unsafe != 0u;
+        const bool fbk = sm.unsafe[n & 1] != 0u;
         if (fbk) {
             // Exact T and P terms of the key channels whose decay over the chunk
             // falls below the floor: T[t,s] (s<t) accumulates at Tm[t][s], P[t,s]
@@ -309,73 +338,103 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
 
         KD_PHASE_MARK(n, 1);
         // =========================================== phase 2: Grams, state products
-        // next chunk's rows, in flight through the rest of this chunk (the raw
-        // rows of this chunk were last read in phase 1)
-        if (n + 1 < NC) load_rows_a(n + 1);
-        // Gram tile (I_ >= J_) of T and P: waves 0..7 take tiles 0..7, waves 0, 1
-        // also tiles 8, 9.  The wave of a diagonal tile (I_ == J_) then inverts
-        // that 16 x 16 block of I + T: it alone wrote the block, and a wave's LDS
-        // accesses complete in order.
-        auto gram_tile = [&](int tile) {
+        // the next chunk's rows (this chunk's rows were last read in its
+        // preparation), in flight through the rest of the phase: waves 0..3
+        // issue them first, waves 4..7 after their inverses, which the solve
+        // waits for
+        auto load_next = [&]() {
+            if (n + 1 < NC) {
+                load_rows_a(n + 1);
+                load_rows_b(n + 1);
+            }
+        };
+        if (w < 4) load_next();
+        // Gram tile (I_ >= J_) of T and P.  The diagonal tiles 0, 2, 5, 9 go to
+        // waves 4..7, which then invert that 16 x 16 block of I + T; waves 0..3
+        // take the six off-diagonal tiles (waves 0 and 1 two each).
+        auto gram_tile = [&](int tile) __attribute__((always_inline)) {
             const int I_ = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J_ = tile - (I_ * (I_ + 1)) / 2;
             const E* aE = &sm.Eb[(SB * I_ + cl) * LD];
             const E* aQ = &sm.Qb[(SB * I_ + cl) * LD];
             const E* bK = &sm.Kc[(SB * J_ + cl) * LD];
+            // all twelve fragments are read before the first product, so the
+            // LDS latency is paid once
+            Frag fk[KD_], fe[KD_], fq[KD_];
+#pragma unroll
+            for (int ks = 0; ks < KD_; ++ks) {
+                fk[ks] = TR::ld_nat(bK, ks, g);
+                fe[ks] = TR::ld_nat(aE, ks, g);
+                fq[ks] = TR::ld_nat(aQ, ks, g);
+            }
             floatx4 gt = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KD_; ++ks) {
-                const Frag kk = TR::ld_nat(bK, ks, g);
-                gt = TR::mma(TR::ld_nat(aE, ks, g), kk, gt);
-                pp = TR::mma(TR::ld_nat(aQ, ks, g), kk, pp);
+                gt = TR::mma(fe[ks], fk[ks], gt);
+                pp = TR::mma(fq[ks], fk[ks], pp);
             }
             const int s_ = SB * J_ + cl;
+            if (fbk) {   // the exact terms of this tile (every entry is read by one tile)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t_ = SB * I_ + 4 * g + r;
-                if (fbk) {
+                for (int r = 0; r < 4; ++r) {
+                    const int t_ = SB * I_ + 4 * g + r;
                     if (s_ < t_) gt[r] += sm.Tm[t_ * LDM + s_];
-                    if (s_ <= t_) {
-                        pp[r] += sm.Tm[s_ * LDM + t_];
-                        if (s_ < t_) sm.Tm[s_ * LDM + t_] = 0.f;
-                    }
+                    if (s_ <= t_) pp[r] += sm.Tm[s_ * LDM + t_];
                 }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t_ = SB * I_ + 4 * g + r;
-                if (s_ < t_) sm.Tm[t_ * LDM + s_] = gt[r];
-                else if (s_ == t_) sm.Tm[t_ * LDM + s_] = 0.f;   // clears the P diagonal scratch
                 sm.P[t_ * LDP + TR::pcol(s_)] = (E)((s_ <= t_) ? pp[r] : 0.f);
             }
+            if (I_ > J_) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) put_frag(sm.TF[tile - I_], 4 * g + r, cl, -gt[r]);
+            }
             if (I_ == J_) {
-                // (I + T_II)^{-1}: lane c < 16 runs forward substitution down column c
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (lane < 16) {
-                    const int c = lane;
-                    const float* Tb = &sm.Tm[(16 * I_) * LDM + 16 * I_];
-                    float x[16];
+                // (I + T_II)^{-1} by forward substitution down the 16 columns,
+                // right-looking: lane 4c + q holds column c of the rows t = q
+                // (mod 4).  Once row r is final, its owner's value goes to the
+                // other lanes of the quad (a DPP broadcast) and every lane takes
+                // T[t][r] x_r off its later rows, so each row adds one broadcast
+                // and one multiply-add to the chain.  The strict lower triangle
+                // goes through X[I_] with T[4j + q][s] at (16 q + s) 4 + j.
+                float* Tq = sm.X[I_];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        // the row of T as four 16-byte reads, the sum over s < r in
-                        // four independent chains
-                        floatx4 tr[4];
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            if (4 * q4 < r) tr[q4] = *reinterpret_cast<const floatx4*>(&Tb[r * LDM + 4 * q4]);
-                        float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s = 0; s < r; ++s) a4[s & 3] = fmaf(tr[s >> 2][s & 3], x[s], a4[s & 3]);
-                        const float acc = ((r == c) ? 1.f : 0.f) - ((a4[0] + a4[1]) + (a4[2] + a4[3]));
-                        x[r] = (r < c) ? 0.f : acc;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sm.X[I_][r * LDX + c] = x[r];
+                for (int r = 0; r < 4; ++r) {
+                    const int t16 = 4 * g + r;
+                    Tq[(16 * r + cl) * 4 + g] = (cl < t16) ? gt[r] : 0.f;
                 }
+                const int c = lane >> 2, q = lane & 3;
+                float tq[16][4];   // tq[r][j] = T[4j + q][r], needed for 4j + 3 > r
+#pragma unroll
+                for (int r = 0; r < 15; ++r)
+#pragma unroll
+                    for (int j = r >> 2; j < 4; ++j) tq[r][j] = Tq[(16 * q + r) * 4 + j];
+                float xs[4];   // x[4j + q]
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xs[j] = (4 * j + q == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int r = 0; r < 15; ++r) {
+                    const float xr = quad_bcast(xs[r >> 2], r & 3);
+#pragma unroll
+                    for (int j = r >> 2; j < 4; ++j) xs[j] = fmaf(-tq[r][j], xr, xs[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put_frag(sm.XF[I_], 4 * j + q, c, xs[j]);
             }
         };
-        gram_tile(w);
-        if (w < 2) gram_tile(8 + w);
+        if (w >= 4) {
+            // the diagonal tiles and their inverses feed the whole solve: these
+            // waves issue first until the inverses are out
+            __builtin_amdgcn_s_setprio(2);
+            gram_tile(w == 4 ? 0 : w == 5 ? 2 : w == 6 ? 5 : 9);
+            __builtin_amdgcn_s_setprio(0);
+            load_next();
+        } else {
+            gram_tile(w == 0 ? 1 : w == 1 ? 3 : w == 2 ? 4 : 8);
+            if (w < 2) gram_tile(w == 0 ? 6 : 7);
+        }
 
         // X = Op S0 for this wave's value columns (Op rows = tokens 16tt + cl;
         // K = keys in the state order of the accumulators)
@@ -401,74 +460,129 @@ __global__ __launch_bounds__(g2w::NT) void kd_gdn2_kernel(
                 for (int r = 0; r < 4; ++r) R[tt][r] = (float)zz[r] - R[tt][r];
             }
         }
+        if (n + 1 < NC) prep_a(n + 1);
         lds_barrier();
 
         KD_PHASE_MARK(n, 2);
         // =========================================== phase 3: solve, readout, update
-        if (n + 1 < NC) load_rows_b(n + 1);
-        floatx4 U[NSB];
+        auto phase3 = [&]() __attribute__((always_inline)) {
+            // the solve is a chain of dependent products: it issues ahead of
+            // the next chunk's preparation on the same SIMD
+            __builtin_amdgcn_s_setprio(1);
+            // U = (I + T)^{-1} R by 16-row blocks, right-looking: as soon as U_J is
+            // known, its terms -T_IJ U_J go into every later R_I, so the chain runs
+            // through one product per block step.  Products carry about 16 bits:
+            // (hi + lo) x (hi + lo) bf16 splits as two 16x16x32 products,
+            // [hi | lo] [hi ; hi] and [hi | lo] [lo ; lo].
+            floatx4 U[NSB];
+            {
+                auto prod = [&](Frag a2, s16x4 bh, s16x4 bl, floatx4 c) {
+                    const Frag bh2 = __builtin_bit_cast(Frag, __builtin_shufflevector(bh, bh, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const Frag bl2 = __builtin_bit_cast(Frag, __builtin_shufflevector(bl, bl, 0, 1, 2, 3, 4, 5, 6, 7));
+                    c = TR::mma(a2, bh2, c);
+                    return TR::mma(a2, bl2, c);
+                };
 #pragma unroll
-        for (int I_ = 0; I_ < NSB; ++I_) {
-            floatx4 acc = R[I_];
+                for (int J_ = 0; J_ < NSB; ++J_) {
+                    s16x4 bh, bl;
+                    split_hl(R[J_], bh, bl);
+                    U[J_] = prod(*reinterpret_cast<const Frag*>(&sm.XF[J_][8 * lane]), bh, bl,
+                                 floatx4{0.f, 0.f, 0.f, 0.f});
+                    if (J_ + 1 < NSB) {
+                        split_hl(U[J_], bh, bl);
 #pragma unroll
-            for (int J_ = 0; J_ < I_; ++J_) {   // acc -= T_IJ U_J
-                const floatx4 tv = -*reinterpret_cast<const floatx4*>(&sm.Tm[(16 * I_ + cl) * LDM + 16 * J_ + 4 * g]);
-                s16x4 th, tl, uh, ul;
-                split_hl(tv, th, tl);
-                split_hl(U[J_], uh, ul);
-                acc = mma16_3(th, tl, uh, ul, acc);
+                        for (int I_ = J_ + 1; I_ < NSB; ++I_) {
+                            const int ij = I_ * (I_ - 1) / 2 + J_;
+                            R[I_] = prod(*reinterpret_cast<const Frag*>(&sm.TF[ij][8 * lane]), bh, bl, R[I_]);
+                        }
+                    }
+                }
             }
-            const floatx4 xv = *reinterpret_cast<const floatx4*>(&sm.X[I_][cl * LDX + 4 * g]);
-            s16x4 xh, xl, ah, alo;
-            split_hl(xv, xh, xl);
-            split_hl(acc, ah, alo);
-            U[I_] = mma16_3(xh, xl, ah, alo, floatx4{0.f, 0.f, 0.f, 0.f});
-        }
-        // O = Qbar S0 + P U
+            // O = Qbar S0 + P U
 #pragma unroll
-        for (int ks = 0; ks < KC_; ++ks) {
-            const Frag uf = TR::state_frag(U, ks);
+            for (int ks = 0; ks < KC_; ++ks) {
+                const Frag uf = TR::state_frag(U, ks);
 #pragma unroll
-            for (int tt = 0; tt < NSB; ++tt)
-                OQ[tt] = TR::mma(TR::ld_state_p(&sm.P[(SB * tt + cl) * LDP], ks, g), uf, OQ[tt]);
-        }
-        if (o) {
-            // O goes out through LDS (the wave's own 16 columns of the Qbar
-            // tile, last read in phase 2): each lane then stores 16 bytes,
-            // eight adjacent columns of one token, instead of sixteen 2-byte
-            // values; no other wave reads these columns, so no barrier
-            E* ost = sm.Qb;
-#pragma unroll
-            for (int tt = 0; tt < NSB; ++tt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ost[(SB * tt + 4 * g + r) * LD + i0 + cl] = (E)OQ[tt][r];
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes before its reads
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int pce = 64 * it + lane, tk = pce >> 1, half = pce & 1;
-                const int t = n * CH + tk;
-                const uint4 val = *reinterpret_cast<const uint4*>(&ost[tk * LD + i0 + 8 * half]);
-                if (t < T) cp16_nt(o + bbase + (size_t)t * rs + hoff + i0 + 8 * half, &val);
+                for (int tt = 0; tt < NSB; ++tt)
+                    OQ[tt] = TR::mma(TR::ld_state_p(&sm.P[(SB * tt + cl) * LDP], ks, g), uf, OQ[tt]);
             }
-        }
-        // S <- diag(gamma_C) S + Ktil^T U
+            if (o) {
+                // O goes out through LDS (the wave's own 16 columns of a bf16 tile
+                // over Tm, which holds nothing in this phase): each lane then
+                // stores 16 bytes, eight adjacent columns of one token, instead of
+                // sixteen 2-byte values; no other wave reads these columns, so no
+                // barrier
+                E* ost = reinterpret_cast<E*>(sm.Tm);
 #pragma unroll
-        for (int mj = 0; mj < D / 16; ++mj)
-            S[mj] = S[mj] * *reinterpret_cast<const floatx4*>(&sm.gam[16 * mj + 4 * g]);
+                for (int tt = 0; tt < NSB; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < KC_; ++ks) {
-            const Frag uh = TR::state_frag(U, ks);
-            const Frag ul = state_frag_lo(U, ks, uh);
+                    for (int r = 0; r < 4; ++r) ost[(SB * tt + 4 * g + r) * LDO + i0 + cl] = (E)OQ[tt][r];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes before its reads
 #pragma unroll
-            for (int mj = 0; mj < D / 16; ++mj) {
-                const Frag kh = TR::ld_state_p(&sm.KtH[(16 * mj + cl) * LDT], ks, g);
-                const Frag kl = TR::ld_state_p(&sm.KtL[(16 * mj + cl) * LDT], ks, g);
-                S[mj] = TR::mma(kh, uh, S[mj]);
-                S[mj] = TR::mma(kh, ul, S[mj]);
-                S[mj] = TR::mma(kl, uh, S[mj]);
+                for (int it = 0; it < 2; ++it) {
+                    const int pce = 64 * it + lane, tk = pce >> 1, half = pce & 1;
+                    const int t = n * CH + tk;
+                    const uint4 val = *reinterpret_cast<const uint4*>(&ost[tk * LDO + i0 + 8 * half]);
+                    if (t < T) cp16_nt(o + bbase + (size_t)t * rs + hoff + i0 + 8 * half, &val);
+                }
             }
+            // S <- diag(gamma_C) S + Ktil^T U: Ktil 2^-ek and U 2^-eu (eu from this
+            // wave's largest |U|) in fp16, their product in fresh accumulators,
+            // scaled back by 2^(ek + eu) and added to the decayed state
+            {
+                float um = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < NSB; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) um = fmaxf(um, fabsf(U[tt][r]));
+                const int eu = pow2_exp(wave_max_nonneg(um));
+                const float usc = ldexpf(1.f, -eu);
+                const int es = ek_cur + eu;
+                TR::FragH uf[KC_];
+#pragma unroll
+                for (int ks = 0; ks < KC_; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uf[ks][e] = (_Float16)(U[2 * ks][e] * usc);
+                        uf[ks][4 + e] = (_Float16)(U[2 * ks + 1][e] * usc);
+                    }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    floatx4 dS[D / 32];
+#pragma unroll
+                    for (int m = 0; m < D / 32; ++m) dS[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KC_; ++ks)
+#pragma unroll
+                        for (int m = 0; m < D / 32; ++m) {
+                            const int mj = (D / 32) * half + m;
+                            dS[m] = TR::mma_h(*reinterpret_cast<const TR::FragH*>(
+                                                  &sm.Kt[n & 1][(16 * mj + cl) * LDT + TR::KS * ks + 8 * g]),
+                                              uf[ks], dS[m]);
+                        }
+#pragma unroll
+                    for (int m = 0; m < D / 32; ++m) {
+                        const int mj = (D / 32) * half + m;
+                        const floatx4 gm = *reinterpret_cast<const floatx4*>(&sm.gam[n & 1][16 * mj + 4 * g]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[mj][r] = fmaf(S[mj][r], gm[r], ldexpf(dS[m][r], es));
+                    }
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+        if (w < 4) {
+            phase3();
+            if (n + 1 < NC) prep_b(n + 1, ek_next, pmask_next);
+        } else {
+            if (n + 1 < NC) prep_b(n + 1, ek_next, pmask_next);
+            phase3();
         }
-        if (tid == 0) sm.unsafe = 0u;
+        // chunk n's fallback flag was read before the phase-2 barrier; chunk
+        // n + 2 sets it during the next phase 3
+        if (tid == 0) sm.unsafe[n & 1] = 0u;
+        ek_cur = ek_next;
+        pmask = pmask_next;
         KD_PHASE_MARK(n, 3);
         lds_barrier();
     }
