@@ -297,8 +297,8 @@ kd_status bwd_impl(const kd_desc* d, const void* q, const void* k, const void* v
                    size_t ws_bytes, void* stream, int recompute) {
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
-    // the chunk-local backward kernel holds its fp32 operands in LDS only up to d = 32
-    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;
+    // the chunk-local backward kernel holds its fp32 operands in LDS only up to d = 64
+    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
     const size_t gb = ntok * sizeof(float);
@@ -360,7 +360,7 @@ kd_status kron_delta_bwd_noalloc(const kd_desc* d, const void* q, const void* k,
 kd_status kron_delta_bwd_status(const kd_desc* d, const void* ws, size_t ws_bytes, void* stream) {
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
-    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;
+    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;
     const size_t need = kron_delta_workspace_bytes(d, 1);
     if (ws == nullptr) {   // the fixed scratch of kron_delta_bwd_noalloc on the current device
         if (need > kScratchBytes) return KD_ERR_SCRATCH;
@@ -394,7 +394,7 @@ kd_status kron_delta_fwd_train(const kd_desc* d, const void* q, const void* k, c
                                void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
     kd_status st = check_desc(d);
     if (st != KD_OK) return st;
-    if (d->dtype == KD_F32 && d->dk != 32) return KD_ERR_DTYPE;   // as kron_delta_bwd
+    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;   // as kron_delta_bwd
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
     const size_t gb = ntok * sizeof(float);

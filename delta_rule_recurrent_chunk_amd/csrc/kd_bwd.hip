@@ -565,12 +565,15 @@ template <class TR, int D>
 struct BwdChunkSmem {
     typedef typename TR::E E;
     static constexpr int LD = D + TR::PAD;     // [CH][D] operands
-    static constexpr int LDP = CH + TR::PAD;   // [CH][CH] matrices
+    // [CH][CH] matrices; fp32 at d = 64 drops their padding to fit the LDS
+    // (its column reads then meet bank conflicts)
+    static constexpr int LDP = CH + ((TR::SPLIT || D < 64) ? TR::PAD : 0);
     static constexpr int LDF = D + 4;          // fp32 staging of the results
     static constexpr int NFW = (D + 31) / 32;  // words of a per-channel bit set
     static constexpr size_t ROWB = (size_t)CH * LD * sizeof(E);
     static constexpr size_t SQB = (size_t)CH * LDP * sizeof(E);
-    static constexpr size_t OPB = 5 * ROWB + 6 * SQB;
+    static constexpr int NSQ = TR::SPLIT ? 6 : 4;   // square matrices (no lo parts without the split)
+    static constexpr size_t OPB = 5 * ROWB + NSQ * SQB;
     static constexpr size_t STB = 4 * (size_t)CH * LDF * sizeof(float);
     // operands (Qloc, Kloc, Kr, V, dO, then P, dGK hi/lo, dP hi/lo, Gsym); later the staging
     alignas(16) unsigned char big[OPB > STB ? OPB : STB];
@@ -652,10 +655,10 @@ __device__ __forceinline__ void bwd_chunk_body(
     E* Vs = Kc + CH * LD;
     E* Do = Vs + CH * LD;
     E* P = Do + CH * LD;
-    E* dGK = P + CH * LDP;     // hi part (bf16) ...
-    E* dGKl = dGK + CH * LDP;  // ... and the rest
+    E* dGK = P + CH * LDP;                                // hi part (bf16) ...
+    E* dGKl = dGK + (TR::SPLIT ? CH * LDP : 0);           // ... and the rest (fp32: none)
     E* dP = dGKl + CH * LDP;
-    E* dPl = dP + CH * LDP;
+    E* dPl = dP + (TR::SPLIT ? CH * LDP : 0);
     E* Gs = dPl + CH * LDP;
     float* stQ = reinterpret_cast<float*>(sm.big);
     float* stK = stQ + CH * LDF;
@@ -728,7 +731,7 @@ __device__ __forceinline__ void bwd_chunk_body(
             if (n * CH + row0 + e >= T) { rv.clear(e, 0.f); ro.clear(e, 0.f); }
     }
     // the upper triangles of P, dGK, dP (hi and lo) are never written
-    for (int x = tid; x < 5 * CH * LDP * (int)sizeof(E) / 16; x += NT)
+    for (int x = tid; x < (TR::SPLIT ? 5 : 3) * CH * LDP * (int)sizeof(E) / 16; x += NT)
         reinterpret_cast<uint4*>(P)[x] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < NSB * NFW) { (&sm.fbm[0][0])[tid] = 0u; (&sm.xset[0][0])[tid] = 0u; }
     if (tid == 0) sm.stale = stale;
@@ -902,9 +905,11 @@ __device__ __forceinline__ void bwd_chunk_body(
             const float dpv = inc ? dp[r] : 0.f, dgkv = bt * dM * gv[r];
             const E dph = TR::cvt(dpv), dgkh = TR::cvt(dgkv);
             dP[t_ * LDP + s_] = dph;
-            dPl[t_ * LDP + s_] = TR::lo_part(dpv, dph);
             dGK[t_ * LDP + s_] = dgkh;
-            dGKl[t_ * LDP + s_] = TR::lo_part(dgkv, dgkh);
+            if constexpr (TR::SPLIT) {
+                dPl[t_ * LDP + s_] = TR::lo_part(dpv, dph);
+                dGKl[t_ * LDP + s_] = TR::lo_part(dgkv, dgkh);
+            }
             if (low) {
                 Gs[t_ * LDP + s_] = TR::cvt(dgv);
                 Gs[s_ * LDP + t_] = TR::cvt(dgv);
@@ -1686,6 +1691,8 @@ hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void*
         }
     } else if (d == 32) {
         return launch_bwd_t<F32T, 32>(KD_BWD_ARGS);
+    } else if (d == 64) {
+        return launch_bwd_t<F32T, 64>(KD_BWD_ARGS);
     }
 #undef KD_BWD_ARGS
     return hipErrorInvalidValue;

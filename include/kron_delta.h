@@ -173,8 +173,8 @@ KD_API kd_status kron_delta_decode(const kd_desc *desc,
  * + 776 bytes, e the element size); its contents on entry are ignored and on
  * exit are unspecified; two calls that overlap on the device must not share
  * it.
- * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv = 32
- * (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
+ * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv in
+ * {32, 64} (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
  * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2
  * summary, section "핵심 기여" (gate-aware backward pass), applied to the rule
  * of the onedev.kr KronLSTM summary, section "어떻게 동작하나".
@@ -234,7 +234,7 @@ KD_API kd_status kron_delta_bwd_noalloc(const kd_desc *desc,
  * entering each chunk, u and r0, and the chunk's M and P.  ws must hold at
  * least kron_delta_workspace_bytes(desc, 1) bytes (KD_ERR_WORKSPACE) and
  * overlap no tensor.  Shapes and dtypes as kron_delta_bwd (fp32 only at
- * d = 32).
+ * d in {32, 64}).
  *
  * kron_delta_bwd_saved: kron_delta_bwd without its recording forward.  It reads
  * the records that the last kron_delta_fwd_train left in ws, so the caller

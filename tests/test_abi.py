@@ -232,7 +232,7 @@ def test_training_pair_argument_checks(L):
     assert ftrain(d, ws_bytes=need - 1) == WORKSPACE
     assert ftrain(d, ws=P(2)) == ALIAS                     # workspace == v
     assert ftrain(d, o=P(40)) == ALIAS                     # o == workspace
-    assert ftrain(_desc(dk=64, dv=64, dtype=kd.KD_F32)) == DTYPE
+    assert ftrain(_desc(dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE   # fp32 only up to d = 64
     assert ftrain(d, f=None) == NULL
     # the saved backward takes the same checks as kron_delta_bwd
     bn = ["q", "k", "v", "f", "beta", "c", "S0", "dO", "dST", "dq", "dk", "dv", "df",
