@@ -197,7 +197,7 @@ size_t kron_delta_workspace_bytes(const kd_desc* d, int which) {
 kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const void* v,
                          const void* f, const float* beta, const float* c, const float* S0,
                          void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
-    kd_status st = check_desc(d);
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
@@ -215,6 +215,14 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
             if (overlap(a, b)) return KD_ERR_ALIAS;
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
+    if (d->dtype == KD_F32 && d->dk == 128) {
+        // fp32 at d = 128: the chunk kernels' fp32 operands do not fit the LDS,
+        // so the tokens go through the per-token recurrence (the decode kernel,
+        // state in registers across all T tokens): exact in fp32, sequential in t
+        hipError_t e = kd::launch_decode(0, 128, q, k, v, f, beta, c, S0, o, ST, d->B, d->T, d->H,
+                                         (hipStream_t)stream);
+        return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+    }
     const size_t need = fwd_ws_bytes(d);
     if (need > 0 && ws && ws_bytes >= need) {   // few heads: preparation, then the state pass
         if (misaligned(ws)) return KD_ERR_ALIGN;

@@ -98,8 +98,10 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
         }
         __syncthreads();   // the token vectors and partials are reused
     }
+    if (S_out) {   // NULL when a caller does not want the final state
 #pragma unroll
-    for (int x = 0; x < NV; ++x) st4_nt(S_out + sbase + 4 * (size_t)NT * x, S[x]);
+        for (int x = 0; x < NV; ++x) st4_nt(S_out + sbase + 4 * (size_t)NT * x, S[x]);
+    }
 }
 
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,

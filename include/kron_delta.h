@@ -32,7 +32,8 @@
  *  * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs.
  *  * Supported shapes: B, H >= 1, T >= 0 (any length; a ragged last chunk is
  *    handled), dk == dv == d with d in {32, 64, 128} for KD_BF16 and
- *    d in {32, 64} for KD_F32.  B*H <= 2^31-1, and one batch element's
+ *    d in {32, 64} for KD_F32 (kron_delta_fwd and kron_delta_decode also
+ *    take KD_F32 at d = 128).  B*H <= 2^31-1, and one batch element's
  *    [T, H, d] tensor must span at most 2^31-1 bytes (T*H*d*elemsize).
  *  * The state is always fp32.  Inputs f must lie in [0, 1].
  *  * Argument checks run before any launch.  A failed check returns a
@@ -116,7 +117,11 @@ KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int which);
  * A = (I + M)^{-1}, aitrends.kr Gated DeltaNet-2 summary, "방법론" step 3)
  * in parallel, then one pass per head over the chunks, u = A (c - beta r0).
  * Without it, or for other shapes, one launch (the substitution form).  Both
- * hold the same tolerance against the definition.
+ * hold the same tolerance against the definition.  fp32 at d = 128 (a
+ * diagnostic precision: its chunk operands do not fit the LDS) runs the
+ * per-token recurrence of kron_delta_decode over all T tokens from S0, one
+ * workgroup per (b, h) with the state in registers: exact in fp32 and
+ * sequential in time (onedev.kr KronLSTM summary, "어떻게 동작하나").
  */
 #define KRON_DELTA_FWD_SPLIT_MAX_HEADS 64
 KD_API kd_status kron_delta_fwd(const kd_desc *desc,

@@ -87,7 +87,9 @@ def test_fwd_argument_checks(L):
     assert fwd(L, _desc(T=-1)) == SHAPE
     assert fwd(L, _desc(dk=64, dv=32)) == SHAPE
     assert fwd(L, _desc(dk=48, dv=48)) == SHAPE
-    assert fwd(L, _desc(dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE
+    # fp32 at d = 128 is accepted (the per-token path); its checks still run first
+    assert fwd(L, _desc(dk=128, dv=128, dtype=kd.KD_F32), q=None) == NULL
+    assert fwd(L, _desc(dk=96, dv=96, dtype=kd.KD_F32)) == SHAPE
     assert fwd(L, _desc(T=1 << 20, H=16, dk=128, dv=128)) == SHAPE   # > 2^31 bytes per batch element
     assert fwd(L, _desc(), q=None) == NULL
     assert fwd(L, _desc(), o=None) == NULL

@@ -72,8 +72,25 @@ def test_workload_full_size(name):
     check(x, w.dtype)
 
 
+def test_long_context_fp32_diagnostic():
+    """fp32 inputs at the long-context shape (B=1, T=32768, H=16, d=128, near-1
+    decay, beta in (0, 2)): the whole launch on the GPU (the per-token path
+    of fp32 at d = 128), two heads against the oracle run on those heads."""
+    torch = _torch()
+    w = sy.WORKLOADS["long_ctx"]
+    xr = sy.rounded(sy.draw_workload(w, with_dO=False), "fp32")
+    o, ST = run_fwd(xr, "fp32")
+    for h in (0, 9):
+        sl = {n: (xr[n][:, :, h:h + 1] if xr[n] is not None else None) for n in ("q", "k", "v", "f", "beta", "c")}
+        o_ref, ST_ref, _ = oracle.fwd(sl["q"], sl["k"], sl["v"], sl["f"], sl["beta"], sl["c"], None)
+        e_o, e_s = rel(o[:, :, h:h + 1], o_ref), rel(ST[:, h:h + 1], ST_ref)
+        print("  head %d: err o=%.3e  S_T=%.3e" % (h, e_o, e_s), flush=True)
+        assert e_o <= TOL["fp32"] and e_s <= TOL["fp32"], (h, e_o, e_s)
+
+
 # ------------------------------------------------------------ shapes and tails
-@pytest.mark.parametrize("dtype,d", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp32", 32), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp32", 32), ("fp32", 64),
+                                     ("fp32", 128)])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 384])
 def test_shapes_ragged_tails_nonzero_state(dtype, d, T):
     x = sy.draw(2, T, 3, d, d, seed=100 + T + d, beta_scale=2.0, s0_std=0.1)
@@ -113,7 +130,7 @@ def test_clustered_repeated_keys_beta_near_two(T):
     check(x, "bf16")
 
 
-FAST = [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp32", 32), ("fp32", 64)]
+FAST = [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp32", 32), ("fp32", 64), ("fp32", 128)]
 
 
 @pytest.mark.parametrize("dtype,d", FAST)
