@@ -38,9 +38,29 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KronDeltaError(RuntimeError):
-    def __init__(self, status: int, what: str):
+    def __init__(self, status: int, what: str, detail: str = ""):
         self.status = status
-        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+        super().__init__("%s failed: %s (status %d)%s" % (what, status_string(status), status, detail))
+
+
+KD_ERR_LAUNCH = -6
+SYNC_CHECK_ENV = "KRON_DELTA_SYNC_CHECK"
+
+
+def _done(st: int, what: str, device=None):
+    """Raise for a failed call.  With KRON_DELTA_SYNC_CHECK=1 in the
+    environment, also wait for the enqueued work and report a device error
+    (a fault in a kernel of this call) against this entry point; skipped while
+    the current stream is being captured into a graph."""
+    if st != 0:
+        raise KronDeltaError(st, what)
+    if os.environ.get(SYNC_CHECK_ENV) == "1":
+        import torch
+        if torch.cuda.is_available() and not torch.cuda.is_current_stream_capturing():
+            try:
+                torch.cuda.synchronize(device)
+            except RuntimeError as e:   # the device reported an error for the enqueued work
+                raise KronDeltaError(KD_ERR_LAUNCH, what, " after the launch: %s" % e) from e
 
 
 class KdDesc(ctypes.Structure):
@@ -168,8 +188,7 @@ def fwd(q, k, v, f, beta, c, S0=None, *, return_state=True, workspace=None):
     wsb = workspace.numel() if workspace is not None else 0
     st = L.kron_delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
                           _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), wsp, wsb, ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_fwd")
+    _done(st, "kron_delta_fwd")
     return o, ST
 
 
@@ -203,8 +222,7 @@ def fwd_varlen(q, k, v, f, beta, c, cu_seqlens, S0=None, *, return_state=True):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = L.kron_delta_fwd_varlen(ctypes.byref(desc), _ptr(cu), _ptr(q4), _ptr(k4), _ptr(v4), _ptr(f4),
                                  _ptr(b4), _ptr(c4), _ptr(S0b), _ptr(o), _ptr(ST), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_fwd_varlen")
+    _done(st, "kron_delta_fwd_varlen")
     return o, ST
 
 
@@ -225,8 +243,7 @@ def decode(q, k, v, f, beta, c, S, *, S_out=None):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = L.kron_delta_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
                              _ptr(c), _ptr(S), _ptr(o), _ptr(out), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_decode")
+    _done(st, "kron_delta_decode")
     return o
 
 
@@ -252,8 +269,7 @@ def fwd_train(q, k, v, f, beta, c, S0=None, *, return_state=True, workspace=None
     st = L.kron_delta_fwd_train(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta),
                                 _ptr(c), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_fwd_train")
+    _done(st, "kron_delta_fwd_train")
     return o, ST, workspace
 
 
@@ -288,8 +304,7 @@ def bwd(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, workspace=None,
             _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
             _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
             _ptr(out["dS0"]), _ptr(workspace), need, ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_bwd_saved" if saved else "kron_delta_bwd")
+    _done(st, "kron_delta_bwd_saved" if saved else "kron_delta_bwd")
     return out
 
 
@@ -338,8 +353,7 @@ def bwd_noalloc(q, k, v, f, beta, c, S0, dO, dST=None, *, want_dS0=True, out=Non
                                   _ptr(c), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
                                   _ptr(out["dv"]), _ptr(out["df"]), _ptr(out["dbeta"]), _ptr(out["dc"]),
                                   _ptr(out["dS0"]), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_bwd_noalloc")
+    _done(st, "kron_delta_bwd_noalloc")
     return out
 
 
@@ -372,8 +386,7 @@ def gdn2_fwd(q, k, v, alpha, b, w, S0=None, *, return_state=True):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = L.kron_delta_gdn2_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
                                _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_gdn2_fwd")
+    _done(st, "kron_delta_gdn2_fwd")
     return o, ST
 
 
@@ -427,8 +440,7 @@ def mixer_pre(q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, conv_q, conv_k, conv_
     stream = torch.cuda.current_stream(q_raw.device).cuda_stream
     st = L.kron_delta_mixer_pre(ctypes.byref(desc), ctypes.byref(p), *[_ptr(t) for t in ins],
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(beta), _ptr(c), ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_mixer_pre")
+    _done(st, "kron_delta_mixer_pre")
     return q, k, v, f, beta, c
 
 
@@ -446,8 +458,7 @@ def mixer_post(o, g, norm_w, *, norm_eps=1e-5):
     stream = torch.cuda.current_stream(o.device).cuda_stream
     st = L.kron_delta_mixer_post(ctypes.byref(desc), ctypes.byref(p), _ptr(o), _ptr(g), _ptr(y),
                                  ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_mixer_post")
+    _done(st, "kron_delta_mixer_post")
     return y
 
 
@@ -476,7 +487,6 @@ def mixer_fwd(q_raw, k_raw, v_raw, f_raw, beta_raw, c_raw, g, conv_q, conv_k, co
     st = L.kron_delta_mixer_fwd(ctypes.byref(desc), ctypes.byref(p), *[_ptr(t) for t in ins], _ptr(S0), _ptr(y),
                                 _ptr(ST), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 ctypes.c_void_p(stream))
-    if st != 0:
-        raise KronDeltaError(st, "kron_delta_mixer_fwd")
+    _done(st, "kron_delta_mixer_fwd")
     return y, ST
 

@@ -324,3 +324,15 @@ def test_few_heads_workspace_query():
     unit = ws(1, 64, 1)
     assert unit > 0 and ws(1, 65, 1) == 2 * unit and ws(4, 130, 16) == 64 * 3 * unit
     assert ws(5, 130, 13) == 0 and ws(1, 64, 1, d=64) == 0 and ws(1, 64, 1, dt=0) == 0
+
+
+def test_status_check_and_sync_switch(monkeypatch):
+    """The binding raises KronDeltaError for a failed call; with
+    KRON_DELTA_SYNC_CHECK=1 and no device it has nothing to wait for."""
+    with pytest.raises(kd.KronDeltaError) as e:
+        kd._done(-3, "kron_delta_fwd")
+    assert e.value.status == -3 and "kron_delta_fwd" in str(e.value)
+    monkeypatch.setenv(kd.SYNC_CHECK_ENV, "1")
+    import torch
+    if not torch.cuda.is_available():
+        assert kd._done(0, "kron_delta_fwd") is None

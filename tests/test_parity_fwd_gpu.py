@@ -191,6 +191,25 @@ def run_fwd_path(x, dtype, split):
     return o.double().cpu().numpy(), ST.double().cpu().numpy()
 
 
+# workgroup shapes of the bf16 forward: waves per workgroup for each path
+WAVE_FORMS = [(32, False, 2), (64, False, 4), (128, True, 8), (128, False, 16)]
+
+
+@pytest.mark.parametrize("d,split,waves", WAVE_FORMS)
+def test_lds_barriers_across_wave_counts(d, split, waves):
+    """One ragged problem (three chunks and a tail, a non-zero state) through
+    every workgroup shape of the bf16 forward (2, 4, 8 and 16 waves): a
+    missing barrier or a stage that reads another wave's LDS early shows up
+    as a mismatch with the oracle in the shape where it happens."""
+    xr = sy.rounded(sy.draw(2, 200, 3, d, d, seed=330 + d, beta_scale=2.0, s0_std=0.1), "bf16")
+    print("waves per workgroup:", waves, flush=True)
+    o, ST = run_fwd_path(xr, "bf16", split)
+    o_ref, ST_ref, _ = oracle.fwd(xr["q"], xr["k"], xr["v"], xr["f"], xr["beta"], xr["c"], xr["S0"])
+    e_o, e_s = rel(o, o_ref), rel(ST, ST_ref)
+    print("  err o=%.3e  S_T=%.3e" % (e_o, e_s), flush=True)
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (waves, e_o, e_s)
+
+
 def _clustered(B, T, H, d, seed):
     rng = np.random.default_rng(seed)
     x = sy.draw(B, T, H, d, d, seed=seed, mu=5.0, beta_scale=2.0)
