@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkrondelta.so")
-SOURCES = ["kd_api.hip", "kd_fwd.hip", "kd_fwd16.hip", "kd_fwd16s.hip", "kd_bwd.hip", "kd_decode.hip", "kd_gdn2.hip",
+SOURCES = ["kd_api.hip", "kd_fwd.hip", "kd_fwd16.hip", "kd_fwd16s.hip", "kd_bwd.hip", "kd_bwd_token.hip", "kd_decode.hip", "kd_gdn2.hip",
            "kd_mixer.hip"]
 
 HIPCC_FLAGS = [

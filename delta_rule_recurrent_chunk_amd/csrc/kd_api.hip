@@ -161,7 +161,7 @@ const char* kron_delta_status_string(int s) {
     case KD_OK: return "ok";
     case KD_ERR_NULL: return "a required pointer is NULL";
     case KD_ERR_SHAPE: return "unsupported shape (need B,H>=1, T>=0, dk==dv in {32,64,128})";
-    case KD_ERR_DTYPE: return "unsupported dtype (bf16: d in {32,64,128}; fp32: d in {32,64})";
+    case KD_ERR_DTYPE: return "unsupported dtype for this call (bf16: d in {32,64,128}; fp32: d in {32,64}, and 128 in the forward, decode, backward and training pair)";
     case KD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KD_ERR_WORKSPACE: return "workspace missing or too small";
     case KD_ERR_LAUNCH: return "kernel launch failed";
@@ -185,7 +185,7 @@ static size_t fwd_ws_bytes(const kd_desc* d) {
 }
 
 size_t kron_delta_workspace_bytes(const kd_desc* d, int which) {
-    if (check_desc(d) != KD_OK) return 0;
+    if (check_desc(d, true) != KD_OK) return 0;
     switch (which) {
     case KD_WS_FWD: return fwd_ws_bytes(d);
     case KD_WS_BWD: return kd::bwd_workspace_bytes(d->dtype == KD_BF16, d->dk, d->B, d->T, d->H);
@@ -303,10 +303,10 @@ kd_status bwd_impl(const kd_desc* d, const void* q, const void* k, const void* v
                    const void* dO, const float* dST, void* dq, void* dk, void* dv,
                    void* df, float* dbeta, float* dc, float* dS0, void* ws,
                    size_t ws_bytes, void* stream, int recompute) {
-    kd_status st = check_desc(d);
+    // fp32 at d = 128 takes the per-token backward (the chunk kernels hold their
+    // fp32 operands in LDS only up to d = 64)
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
-    // the chunk-local backward kernel holds its fp32 operands in LDS only up to d = 64
-    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
     const size_t gb = ntok * sizeof(float);
@@ -352,7 +352,7 @@ kd_status kron_delta_bwd_noalloc(const kd_desc* d, const void* q, const void* k,
                                  const void* f, const float* beta, const float* c, const float* S0,
                                  const void* dO, const float* dST, void* dq, void* dk, void* dv,
                                  void* df, float* dbeta, float* dc, float* dS0, void* stream) {
-    kd_status st = check_desc(d);
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
     const size_t need = kron_delta_workspace_bytes(d, 1);
     if (need > kScratchBytes) return KD_ERR_SCRATCH;
@@ -366,9 +366,8 @@ kd_status kron_delta_bwd_noalloc(const kd_desc* d, const void* q, const void* k,
 }
 
 kd_status kron_delta_bwd_status(const kd_desc* d, const void* ws, size_t ws_bytes, void* stream) {
-    kd_status st = check_desc(d);
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
-    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;
     const size_t need = kron_delta_workspace_bytes(d, 1);
     if (ws == nullptr) {   // the fixed scratch of kron_delta_bwd_noalloc on the current device
         if (need > kScratchBytes) return KD_ERR_SCRATCH;
@@ -400,9 +399,8 @@ kd_status kron_delta_bwd_saved(const kd_desc* d, const void* q, const void* k, c
 kd_status kron_delta_fwd_train(const kd_desc* d, const void* q, const void* k, const void* v,
                                const void* f, const float* beta, const float* c, const float* S0,
                                void* o, float* ST, void* ws, size_t ws_bytes, void* stream) {
-    kd_status st = check_desc(d);
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
-    if (d->dtype == KD_F32 && d->dk > 64) return KD_ERR_DTYPE;   // as kron_delta_bwd
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = ntok * d->dk * esize(d);
     const size_t gb = ntok * sizeof(float);

@@ -54,6 +54,14 @@ namespace kd {
 hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                       const float* beta, const float* c, const float* S0, void* o, float* ST,
                       const FwdCkpt* ck, const int* cu, int B, int T, int H, hipStream_t st);
+hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
+                         const float* beta, const float* c, const float* S_in, void* o, float* S_out,
+                         int B, int T, int H, hipStream_t st);
+size_t bwd_token_ws_states(int d, int B, int T, int H, size_t* tb_off);
+hipError_t launch_bwd_token(int d, const void* q, const void* k, const void* v, const void* f,
+                            const float* beta, const float* c, const float* S0, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, void* df, float* dbeta,
+                            float* dc, float* dS0, void* ws, int B, int T, int H, hipStream_t st);
 
 // Workspace: [S0 | u, r0 | dS | drho | M | P] per (b, h, chunk) unit,
 // 256-byte aligned parts (per unit: d*d*e, 2*CH*4, d*d*e, CH*4, CH*CH*4,
@@ -104,6 +112,13 @@ static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     const size_t units = (size_t)B * H * nc;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     BwdWs w;
+    if (esz == 4 && d == 128) {   // the per-token backward (kd_bwd_token.hip): its states, then the status word
+        size_t tb_off = 0;
+        w.s0 = 0;
+        w.ur = w.ds = w.rho = w.mm = w.pp = w.fl = up(bwd_token_ws_states(d, B, T, H, &tb_off));
+        w.total = w.fl + 256;
+        return w;
+    }
     w.s0 = 0;
     w.ur = up(units * d * d * esz);
     w.ds = w.ur + up(units * 2 * CH * sizeof(float));
@@ -1618,6 +1633,9 @@ hipError_t launch_fwd_train(int bf16, int d, const void* q, const void* k, const
                             const float* beta, const float* c, const float* S0, void* o, float* ST,
                             void* ws, int B, int T, int H, hipStream_t st)
 {
+    // fp32 at d = 128: the per-token forward of kron_delta_fwd; the backward
+    // there recomputes what it needs and reads no records
+    if (!bf16 && d == 128) return launch_decode(0, d, q, k, v, f, beta, c, S0, o, ST, B, T, H, st);
     const FwdCkpt ck = ckpt_in(ws, bf16 ? 2 : 4, d, B, T, H);
     return launch_fwd(bf16, d, q, k, v, f, beta, c, S0, o, ST, &ck, nullptr, B, T, H, st);
 }
@@ -1693,6 +1711,17 @@ hipError_t launch_bwd(int bf16, int d, const void* q, const void* k, const void*
         return launch_bwd_t<F32T, 32>(KD_BWD_ARGS);
     } else if (d == 64) {
         return launch_bwd_t<F32T, 64>(KD_BWD_ARGS);
+    } else if (d == 128) {
+        // fp32 at d = 128: the per-token form, which recomputes its states itself
+        // (also after kron_delta_fwd_train) and never waits: its status word reads 0
+        const BwdWs L = bwd_ws_layout(4, d, B, T, H);
+        hipLaunchKernelGGL(kd_bwd_clear_kernel, dim3(1), dim3(64), 0, st,
+                           reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + L.fl),
+                           (unsigned long long*)nullptr, 0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_bwd_token(d, q, k, v, f, beta, c, S0, dO, dST, dq, dk, dv, df, dbeta, dc, dS0, ws, B, T,
+                                H, st);
     }
 #undef KD_BWD_ARGS
     return hipErrorInvalidValue;

@@ -32,8 +32,9 @@
  *  * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs.
  *  * Supported shapes: B, H >= 1, T >= 0 (any length; a ragged last chunk is
  *    handled), dk == dv == d with d in {32, 64, 128} for KD_BF16 and
- *    d in {32, 64} for KD_F32 (kron_delta_fwd and kron_delta_decode also
- *    take KD_F32 at d = 128).  B*H <= 2^31-1, and one batch element's
+ *    d in {32, 64} for KD_F32 (kron_delta_fwd, kron_delta_decode, the
+ *    backward entry points and the training pair also take KD_F32 at
+ *    d = 128).  B*H <= 2^31-1, and one batch element's
  *    [T, H, d] tensor must span at most 2^31-1 bytes (T*H*d*elemsize).
  *  * The state is always fp32.  Inputs f must lie in [0, 1].
  *  * Argument checks run before any launch.  A failed check returns a
@@ -178,8 +179,13 @@ KD_API kd_status kron_delta_decode(const kd_desc *desc,
  * + 776 bytes, e the element size); its contents on entry are ignored and on
  * exit are unspecified; two calls that overlap on the device must not share
  * it.
- * Supported: bf16 with dk = dv in {32, 64, 128}; fp32 with dk = dv in
- * {32, 64} (KD_ERR_DTYPE otherwise).  The method (reverse mode of the chunked WY form
+ * Supported: bf16 and fp32 with dk = dv in {32, 64, 128}.  fp32 at d = 128
+ * (a diagnostic precision: the chunk kernels' fp32 operands do not fit the
+ * LDS) takes the reverse mode of the per-token recurrence instead, one
+ * workgroup per (b, h) with the state and its adjoint in registers,
+ * sequential in t; its workspace holds the state entering every 64-token
+ * chunk and the states entering one chunk's tokens, per head
+ * ((ceil(T/64) + 64) * d*d*4 bytes per head, plus 256).  The method (reverse mode of the chunked WY form
  * of the delta rule, gate-aware) follows the aitrends.kr Gated DeltaNet-2
  * summary, section "핵심 기여" (gate-aware backward pass), applied to the rule
  * of the onedev.kr KronLSTM summary, section "어떻게 동작하나".
@@ -238,8 +244,9 @@ KD_API kd_status kron_delta_bwd_noalloc(const kd_desc *desc,
  * per-chunk records kron_delta_bwd otherwise recomputes first: the state
  * entering each chunk, u and r0, and the chunk's M and P.  ws must hold at
  * least kron_delta_workspace_bytes(desc, 1) bytes (KD_ERR_WORKSPACE) and
- * overlap no tensor.  Shapes and dtypes as kron_delta_bwd (fp32 only at
- * d in {32, 64}).
+ * overlap no tensor.  Shapes and dtypes as kron_delta_bwd (fp32 at d = 128:
+ * the per-token forward of kron_delta_fwd, which writes no records; the
+ * backward there recomputes its states).
  *
  * kron_delta_bwd_saved: kron_delta_bwd without its recording forward.  It reads
  * the records that the last kron_delta_fwd_train left in ws, so the caller

@@ -234,7 +234,8 @@ def test_training_pair_argument_checks(L):
     assert ftrain(d, ws_bytes=need - 1) == WORKSPACE
     assert ftrain(d, ws=P(2)) == ALIAS                     # workspace == v
     assert ftrain(d, o=P(40)) == ALIAS                     # o == workspace
-    assert ftrain(_desc(dk=128, dv=128, dtype=kd.KD_F32)) == DTYPE   # fp32 only up to d = 64
+    # fp32 at d = 128 is accepted (the per-token forward); its checks still run first
+    assert ftrain(_desc(dk=128, dv=128, dtype=kd.KD_F32), f=None) == NULL
     assert ftrain(d, f=None) == NULL
     # the saved backward takes the same checks as kron_delta_bwd
     bn = ["q", "k", "v", "f", "beta", "c", "S0", "dO", "dST", "dq", "dk", "dv", "df",
@@ -324,6 +325,23 @@ def test_few_heads_workspace_query():
     unit = ws(1, 64, 1)
     assert unit > 0 and ws(1, 65, 1) == 2 * unit and ws(4, 130, 16) == 64 * 3 * unit
     assert ws(5, 130, 13) == 0 and ws(1, 64, 1, d=64) == 0 and ws(1, 64, 1, dt=0) == 0
+
+
+def test_fp32_d128_backward_workspace():
+    """fp32 at d = 128 (the per-token backward): the state entering every
+    64-token chunk and the states entering one chunk's tokens, per head, plus
+    the status block; the 64 MiB fixed scratch of the allocation-free backward
+    covers one head of 2048 tokens."""
+    import ctypes
+    L = kd.lib()
+
+    def ws(B, T, H):
+        return int(L.kron_delta_workspace_bytes(ctypes.byref(kd.KdDesc(B, T, H, 128, 128, 0)), 1))
+    st = 128 * 128 * 4
+    assert ws(1, 64, 1) == st * (1 + 64) + 256
+    assert ws(2, 130, 3) == 6 * st * (3 + 64) + 256
+    assert ws(1, 0, 1) == 256
+    assert ws(1, 2048, 1) <= 64 << 20
 
 
 def test_status_check_and_sync_switch(monkeypatch):

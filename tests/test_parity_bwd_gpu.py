@@ -99,7 +99,8 @@ def test_tiny_fp32_with_state_gradients():
 
 
 # ------------------------------------------------------------ shapes and tails
-@pytest.mark.parametrize("dtype,d", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp32", 32), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp32", 32), ("fp32", 64),
+                                     ("fp32", 128)])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
 def test_shapes_ragged_tails_nonzero_states(dtype, d, T):
     x = sy.draw(2, T, 3, d, d, seed=300 + T + d, beta_scale=2.0, with_dO=True,
@@ -154,7 +155,7 @@ def test_no_decay_no_erase():
     check(x, "bf16")
 
 
-FAST = [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp32", 32), ("fp32", 64)]
+FAST = [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp32", 32), ("fp32", 64), ("fp32", 128)]
 
 
 @pytest.mark.parametrize("dtype,d", FAST)
@@ -201,17 +202,16 @@ def test_backward_deterministic_bitwise():
         assert torch.equal(g1[n], g2[n]), n
 
 
-def test_backward_rejects_fp32_d128():
-    """fp32 operands at d = 128 do not fit the chunk kernels' LDS: refused."""
-    torch = _torch()
-    import delta_rule_recurrent_chunk_amd as kd
-    x = sy.rounded(sy.draw(1, 64, 1, 128, 128, seed=316, with_dO=True), "fp32")
-    t = to_dev(torch, x, "fp32")
-    with pytest.raises(kd.KronDeltaError):
-        kd.bwd(t["q"], t["k"], t["v"], t["f"], t["beta"], t["c"], None, t["dO"])
+def test_fp32_d128_fwd_bwd_shape():
+    """fp32 inputs at the fwd_bwd shape (B=4, T=2048, H=16, d=128), S0 and
+    dS_T non-zero: the per-token backward against the oracle at the 1e-5 bar
+    on every gradient (the fp32 diagnostic of the training pair)."""
+    x = sy.draw(4, 2048, 16, 128, 128, seed=1017, with_dO=True, s0_std=0.1, dST_std=0.1)
+    check(x, "fp32")
 
 
-@pytest.mark.parametrize("dtype,d,T", [("bf16", 128, 150), ("bf16", 64, 200), ("fp32", 32, 130), ("fp32", 64, 130)])
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 128, 150), ("bf16", 64, 200), ("fp32", 32, 130), ("fp32", 64, 130),
+                                       ("fp32", 128, 130)])
 def test_training_pair_equals_forward_and_backward_bitwise(dtype, d, T):
     """kron_delta_fwd_train gives the one-launch kron_delta_fwd's o and S_T,
     and kron_delta_bwd_saved from its records gives kron_delta_bwd's
