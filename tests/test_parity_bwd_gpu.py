@@ -114,6 +114,15 @@ def test_long_context_shape_near_one_decay():
     check(x, "bf16")
 
 
+def test_long_context_workload_backward_full_size():
+    """The backward at the long_ctx workload's full shape and distributions
+    (B=1, T=32768, H=16, d=128, bf16, beta = 2 sigmoid(N(0,1)) in (0, 2),
+    f = sigmoid(N(5,1))^e): 512 chunks of state gradient carried in fp32,
+    all seven gradients against the oracle at the bf16 bar."""
+    w = sy.WORKLOADS["long_ctx"]
+    check(sy.draw_workload(w, with_dO=True), w.dtype)
+
+
 def test_empty_sequence_passes_state_gradient_through():
     torch = _torch()
     import delta_rule_recurrent_chunk_amd as kd
