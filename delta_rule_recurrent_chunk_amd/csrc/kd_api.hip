@@ -28,7 +28,7 @@ hipError_t launch_gdn2(const void* q, const void* k, const void* v, const void* 
                        hipStream_t st);
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
-                         int B, int T, int H, hipStream_t st);
+                         int B, int T, int H, hipStream_t st, const int* cu = nullptr);
 bool mixer_grid_ok(int B, int T, int H);
 hipError_t launch_mixer_pre(int bf16, int d, const void* const raw[4], void* const out[4],
                             const float* const conv[3], int K, const float* a_log, const float* beta_raw,
@@ -242,7 +242,7 @@ kd_status kron_delta_fwd(const kd_desc* d, const void* q, const void* k, const v
 kd_status kron_delta_fwd_varlen(const kd_desc* d, const int32_t* cu_seqlens, const void* q,
                                 const void* k, const void* v, const void* f, const float* beta,
                                 const float* c, const float* S0, void* o, float* ST, void* stream) {
-    kd_status st = check_desc(d);
+    kd_status st = check_desc(d, true);
     if (st != KD_OK) return st;
     if (!cu_seqlens) return KD_ERR_NULL;
     if (((uintptr_t)cu_seqlens & 3u) != 0) return KD_ERR_ALIGN;
@@ -263,8 +263,12 @@ kd_status kron_delta_fwd_varlen(const kd_desc* d, const int32_t* cu_seqlens, con
             if (overlap(a, b)) return KD_ERR_ALIAS;
     if (overlap(outs[0], outs[1])) return KD_ERR_ALIAS;
     if (ntok == 0 && !ST) return KD_OK;
-    hipError_t e = kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
-                                  nullptr, cu_seqlens, d->B, d->T, d->H, (hipStream_t)stream);
+    // fp32 at d = 128: the per-token recurrence over each sequence (as kron_delta_fwd)
+    hipError_t e = d->dtype == KD_F32 && d->dk == 128
+                       ? kd::launch_decode(0, 128, q, k, v, f, beta, c, S0, o, ST, d->B, d->T, d->H,
+                                           (hipStream_t)stream, cu_seqlens)
+                       : kd::launch_fwd(d->dtype == KD_BF16, d->dk, q, k, v, f, beta, c, S0, o, ST,
+                                        nullptr, cu_seqlens, d->B, d->T, d->H, (hipStream_t)stream);
     return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

@@ -56,7 +56,7 @@ hipError_t launch_fwd(int bf16, int d, const void* q, const void* k, const void*
                       const FwdCkpt* ck, const int* cu, int B, int T, int H, hipStream_t st);
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
-                         int B, int T, int H, hipStream_t st);
+                         int B, int T, int H, hipStream_t st, const int* cu = nullptr);
 size_t bwd_token_ws_states(int d, int B, int T, int H, size_t* tb_off);
 hipError_t launch_bwd_token(int d, const void* q, const void* k, const void* v, const void* f,
                             const float* beta, const float* c, const float* S0, const void* dO,

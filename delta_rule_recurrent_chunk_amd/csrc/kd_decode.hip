@@ -23,7 +23,7 @@ template <class E, int D>
 __global__ __launch_bounds__(256) void kd_decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ f,
     const float* __restrict__ beta, const float* __restrict__ cc, const float* S_in,
-    E* __restrict__ o, float* S_out, int T, int H)
+    E* __restrict__ o, float* S_out, const int* __restrict__ cu, int T_, int H)
 {
     constexpr int NT = 256;
     constexpr int RL = D / 4;             // lanes per state row
@@ -36,6 +36,14 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     const int i0 = tid / RL, j0 = 4 * (tid % RL);   // first row, first column
+    // (b, h) walks tokens tok0 .. tok0 + T - 1: T_ tokens each, or, for packed
+    // sequences, those between the offsets cu[b] and cu[b + 1] (clamped to
+    // [0, T_], so bad offsets cannot reach outside the tensors)
+    int tok0 = b * T_, T = T_;
+    if (cu) {
+        tok0 = min(max(cu[b], 0), T_);
+        T = min(max(cu[b + 1], tok0), T_) - tok0;
+    }
     const bool lead = tid % RL == 0;                  // counts its rows once
 
     floatx4 S[NV];   // S[x] = S[i0 + RPX x][j0 .. j0 + 3]
@@ -45,7 +53,7 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
         S[x] = S_in ? *reinterpret_cast<const floatx4*>(S_in + sbase + 4 * (size_t)NT * x) : floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int t = 0; t < T; ++t) {
-        const size_t row = ((size_t)b * T + t) * H + h;   // token (b, t, h)
+        const size_t row = ((size_t)tok0 + t) * H + h;   // token (b, t, h)
         if (tid < D) {
             sq[tid] = (float)q[row * D + tid];
             sk[tid] = (float)k[row * D + tid];
@@ -104,13 +112,14 @@ __global__ __launch_bounds__(256) void kd_decode_kernel(
     }
 }
 
+// cu: NULL, or the B + 1 offsets of packed sequences (device memory)
 hipError_t launch_decode(int bf16, int d, const void* q, const void* k, const void* v, const void* f,
                          const float* beta, const float* c, const float* S_in, void* o, float* S_out,
-                         int B, int T, int H, hipStream_t st)
+                         int B, int T, int H, hipStream_t st, const int* cu)
 {
 #define KD_DEC(E, D)                                                                                     \
     hipLaunchKernelGGL((kd_decode_kernel<E, D>), dim3((unsigned)(B * H)), dim3(256), 0, st, (const E*)q,  \
-                       (const E*)k, (const E*)v, (const E*)f, beta, c, S_in, (E*)o, S_out, T, H)
+                       (const E*)k, (const E*)v, (const E*)f, beta, c, S_in, (E*)o, S_out, cu, T, H)
     if (bf16) {
         switch (d) {
         case 32: KD_DEC(__bf16, 32); break;

@@ -32,9 +32,9 @@
  *  * Every pointer must be 16-byte aligned.  Outputs must not overlap inputs.
  *  * Supported shapes: B, H >= 1, T >= 0 (any length; a ragged last chunk is
  *    handled), dk == dv == d with d in {32, 64, 128} for KD_BF16 and
- *    d in {32, 64} for KD_F32 (kron_delta_fwd, kron_delta_decode, the
- *    backward entry points and the training pair also take KD_F32 at
- *    d = 128).  B*H <= 2^31-1, and one batch element's
+ *    d in {32, 64} for KD_F32 (kron_delta_fwd, kron_delta_fwd_varlen,
+ *    kron_delta_decode, the backward entry points and the training pair
+ *    also take KD_F32 at d = 128).  B*H <= 2^31-1, and one batch element's
  *    [T, H, d] tensor must span at most 2^31-1 bytes (T*H*d*elemsize).
  *  * The state is always fp32.  Inputs f must lie in [0, 1].
  *  * Argument checks run before any launch.  A failed check returns a

@@ -51,7 +51,7 @@ def run(x, S0, cu, dtype):
     return o.double().cpu().numpy(), ST.double().cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 32)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 32), ("fp32", 128)])
 def test_mixed_lengths_match_each_sequence_alone(dtype, d):
     lengths = [130, 0, 1, 64, 63, 65, 200]
     x, S0, cu = packed(lengths, 3, d, dtype, seed=500 + d)
