@@ -270,6 +270,10 @@ def main():
              ("q", "k", "v", "alpha", "b", "w") if w.gdn2 else ("q", "k", "v", "f", "beta", "c"))
     t = {n: torch.tensor(x[n], dtype=tdt if n in per_token else torch.float32, device=dev) for n in names}
     esize = 2 if w.dtype == "bf16" else 4
+    # the forward takes the few-heads form (preparation workers beside the
+    # per-head passes) when the library asks for a workspace for it
+    few_heads = (not (w.mixer or w.gdn2 or w.decode or w.backward) and
+                 kd.workspace_bytes(w.B, w.T, w.H, w.dk, 1 if w.dtype == "bf16" else 0, with_backward=False) > 0)
 
     if w.mixer:      # a step is one mixer forward from the projections
         desc = kd.KdDesc(w.B, w.T, w.H, w.dk, w.dv, 1 if w.dtype == "bf16" else 0)
@@ -378,12 +382,13 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "d": w.dk, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kd_mixer_conv_kernel + kd_fwd16_kernel<false, true> + kd_mixer_post_kernel"
+                     "kernel": "kd_mixer_conv_kernel + kd_fwd16_kernel<false, true>"
                      if w.mixer else
                      "kd_gdn2_kernel" if w.gdn2 else
                      "kd_decode_kernel<bf16,128>" if w.decode else
-                     "kd_fwd16_kernel<false, false>" if not w.backward else
-                     "kd_fwd16_kernel(ckpt) + kd_bwd_fused_kernel",
+                     "kd_fwd16_kernel(ckpt) + kd_bwd_clear_kernel + kd_bwd_fused_kernel" if w.backward else
+                     "kd_fwd16_split_clear_kernel + kd_fwd16_split_fused_kernel" if few_heads else
+                     "kd_fwd16_kernel<false, false>",
                      "kernel_ms": kernel_ms,
                      "launch_ms": {"mean": kernel_ms, "median": float(np.median(per_launch)),
                                    "p10": float(np.percentile(per_launch, 10)),

@@ -88,25 +88,6 @@ struct BwdPub {
 // ctr[BWD_STATUS]: nonzero when some worker's bounded wait ran out (its units
 // were then written as NaN); cleared before every backward launch
 constexpr int BWD_STATUS = 8;
-constexpr unsigned long long PUB_FLUSHED = 2ull;
-
-__device__ __forceinline__ unsigned xcc_id() {
-    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));   // HW_REG_XCC_ID[3:0]
-}
-__device__ __forceinline__ unsigned long long pub_word(unsigned epoch, unsigned xcc) {
-    return ((unsigned long long)epoch << 32) | ((unsigned long long)(xcc & 0xffu) << 24) | 1ull;
-}
-// bounded wait of one thread for a flag of this launch that has the bits
-// `need`; false when the bound ran out (then nothing may be read)
-__device__ __forceinline__ bool pub_wait(const unsigned long long* fp, unsigned epoch, unsigned long long need,
-                                         unsigned long long& w, unsigned spin) {
-    for (unsigned s = 0; s < spin; ++s) {
-        w = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((unsigned)(w >> 32) == epoch && (w & need) == need) return true;
-        __builtin_amdgcn_s_sleep(2);
-    }
-    return false;
-}
 static BwdWs bwd_ws_layout(size_t esz, int d, int B, int T, int H) {
     const size_t nc = (size_t)(T + CH - 1) / CH;
     const size_t units = (size_t)B * H * nc;
@@ -1578,7 +1559,7 @@ __global__ void kd_bwd_clear_kernel(unsigned long long* __restrict__ ctr, unsign
 // --------------------------------------------------------------- launchers
 // compute units of the current device (the fused backward sizes its worker
 // pool to the CUs the sweep leaves free)
-static int compute_units() {
+int compute_units() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -1594,7 +1575,7 @@ static int compute_units() {
 // the waits take microseconds), or a smaller test value
 static std::atomic<unsigned> g_bwd_wait_polls{0u};
 void set_bwd_wait_polls(unsigned polls) { g_bwd_wait_polls.store(polls); }
-static unsigned bwd_wait_polls() {
+unsigned bwd_wait_polls() {
     const unsigned p = g_bwd_wait_polls.load();
     return p ? p : (1u << 23);
 }

@@ -30,6 +30,8 @@
 //      whole chunk earlier.  Per chunk: A: state reads (MFMA), r0 partials;
 //      B: u = A b on one wave (64 broadcasts), the loaders write the previous
 //      chunk's o rows; C: readout and update (MFMA).
+#include <atomic>
+#include <ctime>
 #include <type_traits>
 
 #include "kd_device.h"
@@ -81,9 +83,12 @@ constexpr int N = 7;
 }  // namespace frow
 }  // namespace f16s
 
+// Workspace of the few-heads forward: one image per (b, h, chunk), then the
+// hand-off words of the fused launch: hdr [B*H], flags [B*H*NC].
 size_t fwd16_split_ws_bytes(int B, int T, int H) {
     const size_t nc = (size_t)((T + CH - 1) / CH);
-    return (size_t)B * H * nc * f16s::UNIT_BYTES;
+    const size_t units = (size_t)B * H * nc;
+    return units * f16s::UNIT_BYTES + 8 * ((size_t)B * H + units);
 }
 
 struct PrepSmem {
@@ -101,22 +106,22 @@ struct PrepSmem {
     unsigned fbany;
 };
 
-__global__ __launch_bounds__(f16s::PNT) void kd_fwd16_prep_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+// One preparation unit (b, h, chunk n) with the block's LDS sm: the image of
+// chunk n of head bh into img.  Every thread of the block calls it.
+__device__ __forceinline__ void prep_unit(
+    PrepSmem& sm, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
-    unsigned char* __restrict__ img, int T, int H)
+    unsigned char* __restrict__ img, int n, int bh, int T, int H)
 {
     using namespace f16s;
     typedef Bf16T TR;
     typedef __bf16 E;
     typedef TR::Frag Frag;
     constexpr int KD_ = D / TR::KS;
-    __shared__ PrepSmem sm;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
     const int pw = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int b = bh / H, h = bh % H;
     const int NC = (T + CH - 1) / CH;
     const uint32_t rs = (uint32_t)H * D;
     const size_t bbase = (size_t)b * T * H * D;
@@ -484,6 +489,15 @@ __global__ __launch_bounds__(f16s::PNT) void kd_fwd16_prep_kernel(
     }
 }
 
+__global__ __launch_bounds__(f16s::PNT) void kd_fwd16_prep_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
+    unsigned char* __restrict__ img, int T, int H)
+{
+    __shared__ PrepSmem sm;
+    prep_unit(sm, q, k, v, f, beta, cc, img, blockIdx.x, blockIdx.y, T, H);
+}
+
 struct StateSmem {
     alignas(16) unsigned char g1[f16s::G1_BYTES];
     alignas(16) unsigned char g2[f16s::G2_BYTES];
@@ -496,9 +510,25 @@ struct StateSmem {
     float oinv, sinv;
 };
 
-__global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
-    const unsigned char* __restrict__ img, const float* __restrict__ S0, __bf16* __restrict__ o,
-    float* __restrict__ ST, int T, int H)
+// Hand-off of the preparation images to the state pass when both run in one
+// launch (kd_fwd16_split_fused_kernel): flags[bh * NC + n] is published once
+// unit (bh, n)'s image is in memory, hdr[bh] carries the XCD of the state
+// block of head bh (both words as pub_word; cleared before the launch).
+struct SplitPub {
+    unsigned long long* flags;   // [B*H*NC]
+    unsigned long long* hdr;     // [B*H]
+    unsigned epoch;
+    unsigned spin;               // polls of a bounded wait before it gives up
+};
+
+// The state pass of head bh with the block's LDS sm.  FUSED: the images come
+// from preparation units running in the same launch; the loader waves wait
+// for each unit's flag before reading its image (a wait that runs out of its
+// bound makes that chunk's images, and all later ones, NaN).
+template <bool FUSED>
+__device__ __forceinline__ void state_pass(
+    StateSmem& sm, const unsigned char* __restrict__ img, const float* __restrict__ S0, __bf16* __restrict__ o,
+    float* __restrict__ ST, int T, int H, int bh, const SplitPub& pub)
 {
     using namespace f16s;
     typedef Bf16T TR;
@@ -507,12 +537,10 @@ __global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
     typedef TR::FragH FragH;
     constexpr int KD_ = D / TR::KS;
     constexpr int KC_ = CH / TR::KS;
-    __shared__ StateSmem sm;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int b = bh / H, h = bh % H;
     const int NC = (T + CH - 1) / CH;
     const uint32_t rs = (uint32_t)H * D;
     E* ob = o + (size_t)b * T * H * D;
@@ -758,15 +786,41 @@ __global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
         u32x4 r1[G1_SLOTS], r2[G2_SLOTS];
         u32x4* d1 = reinterpret_cast<u32x4*>(sm.g1);
         u32x4* d2 = reinterpret_cast<u32x4*>(sm.g2);
+        // FUSED: chunk nc's flag before its first read (group 1 of a chunk is
+        // always loaded before its group 2); dead: a wait ran out
+        bool dead = false;
+        const unsigned me = FUSED ? xcc_id() : 0u;
+        auto wait_unit = [&](int nc) {
+            if (!FUSED || dead) return;
+            unsigned long long wd = 0;
+            bool ok = pub_wait(&pub.flags[(size_t)bh * NC + nc], pub.epoch, 1ull, wd, pub.spin);
+            // a writer on another XCD wrote its L2 back before publishing: drop
+            // this XCD's copies before reading
+            if (ok && ((unsigned)(wd >> 24) & 0xffu) != me) {
+                ok = (wd & PUB_FLUSHED) != 0ull;
+                if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no image read moves above the wait
+            dead = !ok;
+        };
 #define KD_LOAD1(nc)                                                                              \
     {                                                                                             \
+        wait_unit(nc);                                                                            \
         const u32x4* src_ = reinterpret_cast<const u32x4*>(himg + (size_t)(nc) * UNIT_BYTES);     \
-        _Pragma("unroll") for (int s = 0; s < G1_SLOTS; ++s) if (li + LS * s < G1N) r1[s] = src_[li + LS * s]; \
+        if (FUSED && dead) {                                                                      \
+            _Pragma("unroll") for (int s = 0; s < G1_SLOTS; ++s) r1[s] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; \
+        } else {                                                                                  \
+            _Pragma("unroll") for (int s = 0; s < G1_SLOTS; ++s) if (li + LS * s < G1N) r1[s] = src_[li + LS * s]; \
+        }                                                                                         \
     }
 #define KD_LOAD2(nc)                                                                              \
     {                                                                                             \
         const u32x4* src_ = reinterpret_cast<const u32x4*>(himg + (size_t)(nc) * UNIT_BYTES + G1_BYTES); \
-        _Pragma("unroll") for (int s = 0; s < G2_SLOTS; ++s) if (li + LS * s < G2N) r2[s] = src_[li + LS * s]; \
+        if (FUSED && dead) {                                                                      \
+            _Pragma("unroll") for (int s = 0; s < G2_SLOTS; ++s) r2[s] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}; \
+        } else {                                                                                  \
+            _Pragma("unroll") for (int s = 0; s < G2_SLOTS; ++s) if (li + LS * s < G2N) r2[s] = src_[li + LS * s]; \
+        }                                                                                         \
     }
 #define KD_PUT1() _Pragma("unroll") for (int s = 0; s < G1_SLOTS; ++s) if (li + LS * s < G1N) d1[li + LS * s] = r1[s];
 #define KD_PUT2() _Pragma("unroll") for (int s = 0; s < G2_SLOTS; ++s) if (li + LS * s < G2N) d2[li + LS * s] = r2[s];
@@ -807,12 +861,131 @@ __global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
     }
 }
 
+__global__ __launch_bounds__(f16s::SNT) void kd_fwd16_state_kernel(
+    const unsigned char* __restrict__ img, const float* __restrict__ S0, __bf16* __restrict__ o,
+    float* __restrict__ ST, int T, int H)
+{
+    __shared__ StateSmem sm;
+    state_pass<false>(sm, img, S0, o, ST, T, H, blockIdx.x, SplitPub{});
+}
+
+static_assert(f16s::PNT == f16s::SNT, "the fused launch runs both roles with one block size");
+
+// Both launches of the few-heads forward in one, so the state passes start as
+// soon as their first chunk is prepared instead of after every chunk is.
+// Blocks 0 .. BHpad - 1 run the state passes (one per (b, h); blocks past B*H
+// have no head and leave).  The others are persistent workers that prepare
+// units: under round-robin placement blocks x and x + 8 share an XCD, so the
+// workers with x = c (mod 8) take the units of the heads bh = c (mod 8), in
+// chunk order, r, r + R, ... for the r-th of the R workers of XCD c, and the
+// state block of head bh reads them through the XCD's L2.  Dispatch is in
+// block order, so every state block is resident before any worker, and the
+// workers never wait: the state blocks' waits end.  A worker that finds the
+// state block of a unit's head on another XCD (or not yet known) writes its
+// L2 back to memory before publishing (PUB_FLUSHED).
+__global__ __launch_bounds__(f16s::SNT) void kd_fwd16_split_fused_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
+    unsigned char* __restrict__ img, const float* __restrict__ S0, __bf16* __restrict__ o,
+    float* __restrict__ ST, SplitPub pub, int BH, int BHpad, int nwork, int T, int H)
+{
+    union Smem {
+        PrepSmem p;
+        StateSmem s;
+    };
+    __shared__ Smem sm;
+    const int x = blockIdx.x;
+    if (x < BHpad) {
+        if (x < BH) {
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&pub.hdr[x], pub_word(pub.epoch, xcc_id()), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            state_pass<true>(sm.s, img, S0, o, ST, T, H, x, pub);
+        }
+        return;
+    }
+    const int NC = (T + CH - 1) / CH;
+    const int c = x & 7, r = (x - BHpad) >> 3, R = nwork >> 3;
+    const int nh = c < BH ? (BH - c + 7) / 8 : 0;   // heads c, c + 8, ... on this XCD
+    const int total = nh * NC;
+    const unsigned me = xcc_id();
+#pragma unroll 1
+    for (int u = r; u < total; u += R) {
+        const int n = u / nh, bh = c + 8 * (u % nh);
+        prep_unit(sm.p, q, k, v, f, beta, cc, img, n, bh, T, H);
+        // every thread's image stores have reached L2; the flag goes out after
+        // the barrier (which also frees the LDS for the next unit)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (threadIdx.x == 0) {
+            const unsigned long long hw =
+                __hip_atomic_load(&pub.hdr[bh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned long long extra = 0ull;
+            if ((unsigned)(hw >> 32) != pub.epoch || ((unsigned)(hw >> 24) & 0xffu) != me) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                extra = PUB_FLUSHED;
+            }
+            __hip_atomic_store(&pub.flags[(size_t)bh * NC + n], pub_word(pub.epoch, me) | extra, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Zeroes the hand-off words of a fused launch (a kernel rather than a memset,
+// so that a captured graph replays it correctly).
+__global__ void kd_fwd16_split_clear_kernel(unsigned long long* __restrict__ w, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) w[i] = 0ull;
+}
+
+int compute_units();
+unsigned bwd_wait_polls();
+
+// preparation workers of the fused launch (at most one per compute unit the
+// state passes leave free)
+#ifndef KD_FWD16S_MAXWORK
+#define KD_FWD16S_MAXWORK 1024
+#endif
+
+// launch epochs of the fused few-heads forward (see SplitPub)
+static unsigned next_split_epoch() {
+    static std::atomic<unsigned> e{0u};
+    unsigned v = e.fetch_add(1u) + 1u;
+    if (v == 1u) {   // first launch of the process: start from the clock
+        const unsigned t = (unsigned)time(nullptr) * 2246822519u;
+        e.fetch_add(t);
+        v += t;
+    }
+    return v;
+}
+
 hipError_t launch_fwd16_split(const void* q, const void* k, const void* v, const void* f, const float* beta,
                               const float* c, const float* S0, void* o, float* ST, void* ws, int B, int T,
                               int H, hipStream_t st)
 {
     typedef __bf16 E;
     const int NC = (T + CH - 1) / CH;
+    const int BH = B * H, BHpad = (BH + 7) & ~7;
+    // about four workers per head keep ahead of the state passes; more only
+    // crowd the memory system the state passes read from
+    const int nwork = min(min(((compute_units() - BHpad) / 8) * 8, KD_FWD16S_MAXWORK),
+                          max(64, ((4 * BH + 7) / 8) * 8));
+    if (NC > 0 && nwork >= 64) {   // one launch: the state passes beside the preparation workers
+        unsigned char* wb = static_cast<unsigned char*>(ws);
+        SplitPub pub;
+        pub.hdr = reinterpret_cast<unsigned long long*>(wb + (size_t)BH * NC * f16s::UNIT_BYTES);
+        pub.flags = pub.hdr + BH;
+        pub.epoch = next_split_epoch();
+        pub.spin = bwd_wait_polls();
+        const int nw = BH + BH * NC;
+        hipLaunchKernelGGL(kd_fwd16_split_clear_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st,
+                           pub.hdr, nw);
+        hipLaunchKernelGGL(kd_fwd16_split_fused_kernel, dim3((unsigned)(BHpad + nwork)), dim3(f16s::SNT), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, wb, S0, (E*)o, ST, pub,
+                           BH, BHpad, nwork, T, H);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(kd_fwd16_prep_kernel, dim3((unsigned)NC, (unsigned)(B * H)), dim3(f16s::PNT), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c,
                        static_cast<unsigned char*>(ws), T, H);

@@ -112,19 +112,25 @@ KD_API size_t kron_delta_workspace_bytes(const kd_desc *desc, int which);
  * ws / ws_bytes may be NULL / 0.  Few heads (bf16, dk = dv = 128, B*H at
  * most KRON_DELTA_FWD_SPLIT_MAX_HEADS): given a workspace of at least
  * kron_delta_workspace_bytes(desc, KD_WS_FWD) bytes (16-byte aligned, not
- * overlapping any argument; about 99 KiB per head and 64-token chunk), the
- * forward runs as two launches on the stream: every chunk's state-free part
- * (decay products, operands, the Gram matrices M and P and the inverse
- * A = (I + M)^{-1}, aitrends.kr Gated DeltaNet-2 summary, "방법론" step 3)
- * in parallel, then one pass per head over the chunks, u = A (c - beta r0).
- * Without it, or for other shapes, one launch (the substitution form).  Both
+ * overlapping any argument; about 99 KiB per head and 64-token chunk; its
+ * contents on entry are ignored), the forward splits each chunk's
+ * state-free part (decay products, operands, the Gram matrices M and P and
+ * the inverse A = (I + M)^{-1}, aitrends.kr Gated DeltaNet-2 summary,
+ * "방법론" step 3) from the pass over the chunks, u = A (c - beta r0): one
+ * launch (after a kernel that clears its hand-off words) in which workers on
+ * the compute units the passes leave free prepare the chunks in order while
+ * one workgroup per head runs its pass as they arrive (a chunk whose hand-off
+ * does not arrive within a bound of seconds, which should never happen, gets
+ * NaN outputs from there on), or, on a device with too few compute units,
+ * the preparation and then the passes as two launches.  Without the
+ * workspace, or for other shapes, one launch (the substitution form).  All
  * hold the same tolerance against the definition.  fp32 at d = 128 (a
  * diagnostic precision: its chunk operands do not fit the LDS) runs the
  * per-token recurrence of kron_delta_decode over all T tokens from S0, one
  * workgroup per (b, h) with the state in registers: exact in fp32 and
  * sequential in time (onedev.kr KronLSTM summary, "어떻게 동작하나").
  */
-#define KRON_DELTA_FWD_SPLIT_MAX_HEADS 64
+#define KRON_DELTA_FWD_SPLIT_MAX_HEADS 48
 KD_API kd_status kron_delta_fwd(const kd_desc *desc,
                          const void *q, const void *k, const void *v, const void *f,
                          const float *beta, const float *c, const float *S0,

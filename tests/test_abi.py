@@ -315,15 +315,20 @@ def test_mixer_argument_checks(L):
 
 def test_few_heads_workspace_query():
     """The workspace that selects the few-heads path: one image per (b, h,
-    64-token chunk) up to the head limit, none past it or for other shapes."""
+    64-token chunk) and the hand-off words, up to the head limit; none past it
+    or for other shapes."""
     import ctypes
     import delta_rule_recurrent_chunk_amd as kd
     L = kd.lib()
 
     def ws(B, T, H, d=128, dt=1):
         return int(L.kron_delta_workspace_bytes(ctypes.byref(kd.KdDesc(B, T, H, d, d, dt)), 0))
-    unit = ws(1, 64, 1)
-    assert unit > 0 and ws(1, 65, 1) == 2 * unit and ws(4, 130, 16) == 64 * 3 * unit
+    # per head and chunk an image, plus one 8-byte hand-off word per head and
+    # per (head, chunk) for the fused launch
+    img = ws(1, 64, 1) - 16
+    assert img > 0 and img % 256 == 0
+    assert ws(1, 65, 1) == 2 * img + 8 * (1 + 2) and ws(3, 130, 16) == 48 * 3 * img + 8 * (48 + 48 * 3)
+    assert kd.lib() and ws(4, 130, 16) == 0   # 64 heads: past KRON_DELTA_FWD_SPLIT_MAX_HEADS (48)
     assert ws(5, 130, 13) == 0 and ws(1, 64, 1, d=64) == 0 and ws(1, 64, 1, dt=0) == 0
 
 
