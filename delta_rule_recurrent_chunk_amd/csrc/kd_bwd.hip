@@ -39,6 +39,7 @@
 #include <atomic>
 
 #include "kd_device.h"
+#include "kd_handoff.h"
 
 // Stage markers of the chunk gradients: no-ops here; a profiling build may
 // define them to record timestamps at the stage boundaries.

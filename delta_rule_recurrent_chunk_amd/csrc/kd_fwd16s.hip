@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "kd_device.h"
+#include "kd_handoff.h"
 
 // Phase markers: no-ops here; a profiling build may define them to record
 // timestamps at the stage boundaries of the state pass.
