@@ -41,6 +41,12 @@ hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const
 hipError_t launch_mixer_post(int bf16, int d, const void* o, const void* g, const float* w, float eps, void* y,
                              int B, int T, int H, hipStream_t st);
 size_t fwd16_split_ws_bytes(int B, int T, int H);
+int fwd16_feed_workers(int BH);
+hipError_t launch_fwd16_mixer_fed(const void* const raw[3], void* const out[3], const float* const conv[3],
+                                  const void* f_raw, const float* beta_raw, const float* c_raw,
+                                  const float* a_log, float beta_scale, const void* og, const float* norm_w,
+                                  float norm_eps, const float* S0, void* o, float* ST, void* hw, int nwork,
+                                  int B, int T, int H, hipStream_t st);
 void set_bwd_wait_polls(unsigned polls);
 size_t bwd_status_offset(int bf16, int d, int B, int T, int H);
 hipError_t launch_fwd16_split(const void* q, const void* k, const void* v, const void* f, const float* beta,
@@ -87,20 +93,23 @@ size_t esize(const kd_desc* d) { return d->dtype == KD_BF16 ? 2 : 4; }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The mixer forward's workspace: q, k, v, f (desc dtype), beta, c (fp32) and
-// the read-out o, each part 256-byte aligned.
+// The mixer forward's workspace: q, k, v, f (desc dtype), beta, c (fp32), the
+// read-out o, and the hand-off words of the one-launch form (8 bytes per
+// head and per (head, 64-token chunk)), each part 256-byte aligned.
 struct MixWs {
-    size_t x[4], beta, c, o, total;
+    size_t x[4], beta, c, o, hw, total;
 };
 MixWs mixer_ws(const kd_desc* d) {
     const size_t ntok = (size_t)d->B * d->T * d->H;
     const size_t xb = up256(ntok * d->dk * esize(d)), gb = up256(ntok * sizeof(float));
+    const size_t bh = (size_t)d->B * d->H, nc = ((size_t)d->T + 63) / 64;
     MixWs w;
     for (int i = 0; i < 4; ++i) w.x[i] = i * xb;
     w.beta = 4 * xb;
     w.c = w.beta + gb;
     w.o = w.c + gb;
-    w.total = w.o + xb;
+    w.hw = w.o + xb;
+    w.total = w.hw + up256(8 * (bh + bh * nc));
     return w;
 }
 
@@ -566,6 +575,16 @@ kd_status kron_delta_mixer_fwd(const kd_desc* d, const kd_mixer_params* p, const
     // y through the gated norm as it stores each chunk's rows (the
     // post-processing kernel's arithmetic)
     const bool fused_gates = bf && d->dk == 128;
+    // and with conv_size 4, when the compute units the forward blocks leave
+    // free hold enough workers, the convolution runs on them inside the same
+    // launch, each chunk published to the forward as soon as it is done
+    const int nwork = fused_gates && p->conv_size == 4 ? kd::fwd16_feed_workers(d->B * d->H) : 0;
+    if (nwork > 0) {
+        hipError_t e = kd::launch_fwd16_mixer_fed(raw, x, conv, f_raw, beta_raw, c_raw, p->a_log, p->beta_scale, g,
+                                                  p->norm_w, p->norm_eps, S0, y, ST, wb + L.hw, nwork, d->B, d->T,
+                                                  d->H, sm);
+        return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+    }
     hipError_t e = kd::launch_mixer_pre(bf, d->dk, raw, x, conv, p->conv_size, p->a_log, beta_raw, c_raw,
                                         p->beta_scale, beta, c, d->B, d->T, d->H, fused_gates ? 0 : 1, sm);
     if (e == hipSuccess)

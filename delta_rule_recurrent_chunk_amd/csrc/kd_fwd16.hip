@@ -43,9 +43,13 @@
 //          prefetch of n+2.
 // Stage C: readout and update of n | Gram tiles 0-7 of n+1, rest of the
 //          prefetch.
+#include <atomic>
+#include <ctime>
 #include <type_traits>
 
 #include "kd_device.h"
+#include "kd_handoff.h"
+#include "kd_mixer_conv.h"
 
 // Phase markers: no-ops here; a profiling build may define them to record
 // timestamps at the stage boundaries of the chunk loop.
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ f, const float* __restrict__ beta, const float* __restrict__ cc,
     const float* __restrict__ S0, __bf16* __restrict__ o, float* __restrict__ ST,
-    FwdCkpt ck, FwdGates gt, const int* __restrict__ cu, int T_, int H)
+    FwdCkpt ck, FwdGates gt, ConvFeed cf, const int* __restrict__ cu, int T_, int H)
 {
     using namespace f16w;
     typedef Bf16T TR;
@@ -130,6 +134,22 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
     constexpr int KC_ = CH / TR::KS;   // K-steps over a chunk
 
     __shared__ Fwd16Smem sm;
+
+    // GATES with a convolution feed: blocks BHpad and up convolve q, k, v for
+    // the forward blocks 0 .. BH - 1 (conv_feed_worker), which publish their XCD
+    const bool feed = GATES && cf.nwork > 0;
+    if constexpr (GATES) {
+        if (feed) {
+            if ((int)blockIdx.x >= cf.BHpad) {
+                conv_feed_worker(cf, &sm, T_, H);
+                return;
+            }
+            if ((int)blockIdx.x >= cf.BH) return;
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&cf.hdr[blockIdx.x], pub_word(cf.epoch, xcc_id()), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, cl = lane & 15;
@@ -523,10 +543,42 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         auto load_k = [&](int n) { int last; const uint32_t off = row_off(n, last); rk.load(kb, off, rs, last); };
         auto load_v = [&](int n) { int last; const uint32_t off = row_off(n, last); rv.load(vb, off, rs, last); };
         auto load_f = [&](int n) { int last; const uint32_t off = row_off(n, last); rf.load(fb, off, rs, last); };
+        // the convolution feed: a chunk's q, k, v rows are read only after its
+        // unit is published (its flag read a stage early: a unit that is ready
+        // costs no poll); a wait that runs out makes the rows NaN from there on
+        bool feed_dead = false;
+        unsigned long long feed_pk = 0ull;
+        const unsigned feed_me = feed ? xcc_id() : 0u;
+        auto feed_peek = [&](int nc) {
+            if (feed && !feed_dead)
+                feed_pk = __hip_atomic_load(&cf.flags[(size_t)bh * NC + nc], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto feed_wait = [&](int nc) {
+            if (!feed || feed_dead) return;
+            unsigned long long wd = feed_pk;
+            bool ok = ((unsigned)(wd >> 32) == cf.epoch && (wd & 1ull) != 0ull) ||
+                      pub_wait(&cf.flags[(size_t)bh * NC + nc], cf.epoch, 1ull, wd, cf.spin);
+            if (ok && ((unsigned)(wd >> 24) & 0xffu) != feed_me) {   // written back by a writer elsewhere
+                ok = (wd & PUB_FLUSHED) != 0ull;
+                if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no row read moves above the wait
+            feed_dead = !ok;
+        };
+        auto feed_poison = [&](Raw8x2& r) {
+            if (feed && feed_dead)
+#pragma unroll
+                for (int e = 0; e < RB; ++e) r.clear(e, __builtin_nanf(""));
+        };
+        feed_wait(0);
         load_q(0);
         load_k(0);
         load_v(0);
         load_f(0);
+        feed_poison(rq);
+        feed_poison(rk);
+        feed_poison(rv);
         // Exact terms of the diagonal tile I_ of chunk ch for the key channels
         // whose decay over that sub-block is below the floor (left out of the
         // tile's matrix product), added to M and P in LDS: lane (g, cl) takes
@@ -659,6 +711,7 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
         for (int n = -1; n < NC; ++n) {
             const int nn = n + 1;             // chunk the producers prepare
             const bool prod_on = nn < NC;
+            feed_peek(min(nn + 1, NC - 1));   // the chunk whose rows this iteration loads
             const int oz = opaque_zero();     // per-lane LDS addresses stay inside the loop
             // ======================================================= stage A
             KD_PHASE_MARK(n, 0);
@@ -859,15 +912,19 @@ __global__ __launch_bounds__(f16w::NT) void kd_fwd16_kernel(
                 }
             }
             const int npf = min(nn + 1, NC - 1);   // prefetch of chunk nn + 1
+            feed_wait(npf);
             load_q(npf);
+            feed_poison(rq);
             KD_PHASE_MARK(n, 4);
             lds_barrier();
             // ======================================================= stage C
             KD_PHASE_MARK(n, 2);
             if (GATES) __builtin_amdgcn_s_setprio(2);
             load_k(npf);
+            feed_poison(rk);
             if (prod_on) gram_tile(kMP(), pw, nn);   // tiles 0..7
             load_v(npf);
+            feed_poison(rv);
             load_f(npf);
             KD_PHASE_MARK(n, 5);
             __builtin_amdgcn_s_setprio(0);
@@ -885,11 +942,11 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void*
     if (ck)
         hipLaunchKernelGGL((kd_fwd16_kernel<true, false>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           *ck, FwdGates{}, (const int*)nullptr, T, H);
+                           *ck, FwdGates{}, ConvFeed{}, (const int*)nullptr, T, H);
     else
         hipLaunchKernelGGL((kd_fwd16_kernel<false, false>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)f, beta, c, S0, (E*)o, ST,
-                           FwdCkpt{}, FwdGates{}, cu, T, H);
+                           FwdCkpt{}, FwdGates{}, ConvFeed{}, cu, T, H);
     return hipGetLastError();
 }
 
@@ -910,7 +967,76 @@ hipError_t launch_fwd16_gates(const void* q, const void* k, const void* v, const
     gt.norm_eps = norm_eps;
     hipLaunchKernelGGL((kd_fwd16_kernel<false, true>), dim3((unsigned)(B * H)), dim3(f16w::NT), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)f_raw, beta_raw, c_raw, S0, (E*)o, ST,
-                       FwdCkpt{}, gt, (const int*)nullptr, T, H);
+                       FwdCkpt{}, gt, ConvFeed{}, (const int*)nullptr, T, H);
+    return hipGetLastError();
+}
+
+int compute_units();
+unsigned bwd_wait_polls();
+
+// launch epochs of the fused mixer forward (see ConvFeed)
+static unsigned next_feed_epoch() {
+    static std::atomic<unsigned> e{0u};
+    unsigned v = e.fetch_add(1u) + 1u;
+    if (v == 1u) {   // first launch of the process: start from the clock
+        const unsigned t = (unsigned)time(nullptr) * 3266489917u;
+        e.fetch_add(t);
+        v += t;
+    }
+    return v;
+}
+
+// Zeroes the hand-off words of a fused mixer launch (a kernel rather than a
+// memset, so that a captured graph replays it correctly).
+__global__ void kd_fwd16_feed_clear_kernel(unsigned long long* __restrict__ w, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) w[i] = 0ull;
+}
+
+// Convolution workers a forward block can take beside the B*H forward blocks
+// (0: the feed does not fit; then the convolution runs as its own kernel
+// first): one per free compute unit, in multiples of 8, at least 64.
+int fwd16_feed_workers(int BH) {
+    const int BHpad = (BH + 7) & ~7;
+    const int nwork = ((compute_units() - BHpad) / 8) * 8;
+    return nwork >= 64 ? nwork : 0;
+}
+
+// The mixer forward in one launch: the convolution of q, k, v (conv_size 4,
+// into q, k, v) by workers beside the forward with the gates from their
+// logits (launch_fwd16_gates); hw: 8 * (B*H + B*H*NC) bytes of hand-off words.
+hipError_t launch_fwd16_mixer_fed(const void* const raw[3], void* const out[3], const float* const conv[3],
+                                  const void* f_raw, const float* beta_raw, const float* c_raw,
+                                  const float* a_log, float beta_scale, const void* og, const float* norm_w,
+                                  float norm_eps, const float* S0, void* o, float* ST, void* hw, int nwork,
+                                  int B, int T, int H, hipStream_t st)
+{
+    typedef __bf16 E;
+    MixPreArgs mx{};
+    for (int i = 0; i < 3; ++i) { mx.raw[i] = raw[i]; mx.out[i] = out[i]; mx.conv[i] = conv[i]; }
+    mx.K = 4;
+    FwdGates gt;
+    gt.a_log = a_log;
+    gt.beta_scale = beta_scale;
+    gt.og = static_cast<const E*>(og);
+    gt.norm_w = norm_w;
+    gt.norm_eps = norm_eps;
+    const int NC = (T + CH - 1) / CH;
+    ConvFeed cf;
+    cf.mx = mx;
+    cf.BH = B * H;
+    cf.BHpad = (cf.BH + 7) & ~7;
+    cf.nwork = nwork;
+    cf.hdr = static_cast<unsigned long long*>(hw);
+    cf.flags = cf.hdr + cf.BH;
+    cf.epoch = next_feed_epoch();
+    cf.spin = bwd_wait_polls();
+    const int nw = cf.BH + cf.BH * NC;
+    hipLaunchKernelGGL(kd_fwd16_feed_clear_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st, cf.hdr, nw);
+    hipLaunchKernelGGL((kd_fwd16_kernel<false, true>), dim3((unsigned)(cf.BHpad + nwork)), dim3(f16w::NT), 0, st,
+                       (const E*)mx.out[0], (const E*)mx.out[1], (const E*)mx.out[2], (const E*)f_raw, beta_raw,
+                       c_raw, S0, (E*)o, ST, FwdCkpt{}, gt, cf, (const int*)nullptr, T, H);
     return hipGetLastError();
 }
 

@@ -10,107 +10,21 @@
 #include <hip/hip_runtime.h>
 
 #include "kd_device.h"
+#include "kd_mixer_conv.h"
 
 namespace kd {
 
-constexpr int MIX_TT = 32;     // tokens walked by one thread (gates, post-processing)
-constexpr int MIX_TB = 8;      // tokens whose loads are in flight together
-constexpr int MIX_CT = 64;     // tokens of one convolution block
-constexpr int MIX_NT = 256;    // threads per block
-constexpr int MIX_KMAX = 4;    // widest convolution
-constexpr float MIX_EPS_L2 = 1e-6f;
-
-struct MixPreArgs {
-    const void* raw[4];        // q, k, v, f projections [B, T, H, d]
-    void* out[4];              // q, k, v, f
-    const float* conv[3];      // [H, d, K] taps of q, k, v (tap K-1 on the current token)
-    const float* a_log;        // [H]
-    const float* beta_raw;     // [B, T, H]
-    const float* c_raw;        // [B, T, H]
-    float* beta;
-    float* c;
-    float beta_scale;
-    int K;
-};
-
-// q, k, v: one block per (b, h, tensor) and MIX_CT consecutive tokens.  The
-// block stages the raw rows of its tokens and the K - 1 before them, and the
-// head's taps, in LDS (one coalesced pass), then each row of D/8 lanes makes
-// one output token from K staged rows: convolution, SiLU, the row's sum of
-// squares on DPP lane moves, the scale, one 16-byte store per lane.
+// q, k, v: one block per (b, h, tensor) and MIX_CT consecutive tokens
+// (conv_fetch, conv_stage, conv_rows).
 template <class E, int D, int K>
 __global__ __launch_bounds__(MIX_NT) void kd_mixer_conv_kernel(MixPreArgs a, int T, int H) {
-    constexpr int LPR = D / 8;                  // lanes per row
-    constexpr int TPP = MIX_NT / LPR;           // tokens per pass
-    static_assert(MIX_CT % TPP == 0, "a block's tokens are whole passes");
-    constexpr int ROWS = MIX_CT + K - 1;
-    constexpr int PPR = D * (int)sizeof(E) / 16; // 16-byte pieces per row
-    static_assert(D * K <= 4 * MIX_NT, "one float4 of taps per thread");
-    __shared__ __align__(16) E st[ROWS * D];
-    __shared__ __align__(16) float sw[D * K];   // taps of (h, channel i) at i*K
-    const int z = blockIdx.z % 3, b = blockIdx.z / 3, h = blockIdx.y;
-    const int t0 = blockIdx.x * MIX_CT;
-    const uint32_t rs = (uint32_t)H * D;   // token stride (elements); one batch element fits 2^31 bytes
-    const size_t base = (size_t)b * T * rs + (size_t)h * D;
-    const E* __restrict__ src = static_cast<const E*>(a.raw[z]) + base;
-    E* __restrict__ dst = static_cast<E*>(a.out[z]) + base;
-    const int tid = threadIdx.x;
-    // stage rows t0 - (K-1) .. t0 + MIX_CT - 1 (zero before the first token;
-    // rows past the last token are never read) and the taps: every load is
-    // issued before the first LDS store
-    constexpr int NPC = (ROWS * PPR + MIX_NT - 1) / MIX_NT;
-    uint4 pcs[NPC];
-    floatx4 tw = {0.f, 0.f, 0.f, 0.f};
-    if (tid < D * K / 4) tw = reinterpret_cast<const floatx4*>(a.conv[z] + (size_t)h * D * K)[tid];
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-        const int x = tid + i * MIX_NT;
-        const int r = x / PPR, pc = x % PPR;
-        const int t = t0 - (K - 1) + r;
-        pcs[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (x < ROWS * PPR && t >= 0 && t < T)
-            pcs[i] = *reinterpret_cast<const uint4*>(src + (uint32_t)t * rs + pc * (16 / sizeof(E)));
-    }
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-        const int x = tid + i * MIX_NT;
-        if (x < ROWS * PPR)
-            *reinterpret_cast<uint4*>(&st[(x / PPR) * D + (x % PPR) * (16 / sizeof(E))]) = pcs[i];
-    }
-    if (tid < D * K / 4) reinterpret_cast<floatx4*>(sw)[tid] = tw;
+    __shared__ ConvLds<E, D, K> L;
+    const int b = blockIdx.z / 3, h = blockIdx.y, z = blockIdx.z % 3, t0 = blockIdx.x * MIX_CT;
+    ConvRegs<E, D, K> R;
+    conv_fetch<E, D, K>(a, T, H, b, h, z, t0, threadIdx.x, R);
+    conv_stage<E, D, K>(L, R, threadIdx.x);
     __syncthreads();
-    // taps of this lane's eight channels: wt[e][j] multiplies the token t - (K-1) + j
-    const int o8 = tid % LPR, slot = tid / LPR;
-    float wt[8][K];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int j = 0; j < K; ++j) wt[e][j] = sw[(8 * o8 + e) * K + j];
-#pragma unroll
-    for (int ps = 0; ps < MIX_CT / TPP; ++ps) {
-        const int r = ps * TPP + slot;   // output token t0 + r, staged rows r .. r + 3
-        const int t = t0 + r;
-        if (t >= T) break;               // the row's lanes leave together
-        float y[8], ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = 0.f;
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            float x[8];
-            ld8f(&st[(r + j) * D + 8 * o8], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = fmaf(wt[e][j], x[e], y[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            y[e] = y[e] * gate_sigmoid(y[e]);   // SiLU
-            ss = fmaf(y[e], y[e], ss);
-        }
-        const float sc = rsqrtf(row_sum<LPR>(ss) + MIX_EPS_L2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] *= sc;
-        st8v_nt(dst + (uint32_t)t * rs + 8 * o8, y);
-    }
+    conv_rows<E, D, K, true>(a, T, H, b, h, z, t0, L, threadIdx.x);
 }
 
 // f, beta, c: elementwise over the B*T token rows.  A lane owns eight

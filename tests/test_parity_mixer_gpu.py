@@ -215,3 +215,41 @@ def test_mixer_step_workload_sampled():
         ey, es = rel(yh[b:b + 1, :, h:h + 1], ry), rel(sh[b:b + 1, h:h + 1], rST)
         print("  (b,h)=(%d,%d) y=%.2e ST=%.2e" % (b, h, ey, es), flush=True)
         assert ey <= FWD_TOL["bf16"] and es <= FWD_TOL["bf16"]
+
+
+def test_mixer_fwd_replays_under_graph_capture():
+    """The mixer forward with its convolution on workers beside the rule
+    (one launch, hand-off words cleared by a kernel ahead of it) captured in
+    a graph and replayed with new inputs: every replay equals an eager call
+    on the same inputs, bit for bit, with eager work between the replays."""
+    torch = _torch()
+    import delta_rule_recurrent_chunk_amd as kd
+    xs = [draw(2, 200, 3, 128, 4, "bf16", seed=995 + i, s0_std=0.05) for i in range(2)]
+    t = to_dev(torch, xs[0], "bf16")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    ws_eager = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+
+    def call(w):
+        return kd.mixer_fwd(t["q_raw"], t["k_raw"], t["v_raw"], t["f_raw"], t["beta_raw"], t["c_raw"], t["g"],
+                            t["conv_q"], t["conv_k"], t["conv_v"], t["a_log"], t["norm_w"], t["S0"],
+                            norm_eps=1e-5, workspace=w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            call(ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y, ST = call(ws)
+    for rep, i in enumerate((1, 0, 1, 1, 0)):
+        src = to_dev(torch, xs[i], "bf16")
+        for n in t:
+            if t[n] is not None and n in src and src[n] is not None:
+                t[n].copy_(src[n])
+        graph.replay()
+        torch.cuda.synchronize()
+        y_ref, ST_ref = call(ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(ST, ST_ref), rep
