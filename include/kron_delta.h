@@ -376,10 +376,18 @@ KD_API kd_status kron_delta_mixer_post(const kd_desc *desc, const kd_mixer_param
 /*
  * The mixer forward from the projections: kron_delta_mixer_pre, then
  * kron_delta_fwd (S0 NULL = zero; S_T returned when ST is non-NULL), then
- * kron_delta_mixer_post, enqueued on `stream`.  ws must hold
- * kron_delta_workspace_bytes(desc, KD_WS_MIXER) bytes (the rule's inputs
- * and read-out between the steps) and overlap no tensor.  Shapes and
- * dtypes as kron_delta_fwd (bf16 d in {32, 64, 128}, fp32 d in {32, 64}).
+ * kron_delta_mixer_post, enqueued on `stream`, with the same results bit
+ * for bit.  ws must hold kron_delta_workspace_bytes(desc, KD_WS_MIXER) bytes
+ * (the rule's inputs and read-out between the steps, and hand-off words;
+ * contents on entry ignored) and overlap no tensor.  Shapes and dtypes as
+ * kron_delta_fwd (bf16 d in {32, 64, 128}, fp32 d in {32, 64}).  With bf16,
+ * d = 128 and conv_size 4 the gates and the gated norm run inside the
+ * forward, and, when at least 64 compute units are left free beside its
+ * B*H workgroups, the convolution runs on them in the same launch (after a
+ * kernel that clears the hand-off words), each chunk handed to the forward
+ * as soon as it is done (a chunk whose hand-off does not arrive within a
+ * bound of seconds, which should never happen, gets NaN outputs from there
+ * on).
  */
 KD_API kd_status kron_delta_mixer_fwd(const kd_desc *desc, const kd_mixer_params *p,
                          const void *q_raw, const void *k_raw, const void *v_raw,
