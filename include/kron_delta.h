@@ -288,10 +288,11 @@ KD_API kd_status kron_delta_bwd_saved(const kd_desc *desc,
 KD_API kd_status kron_delta_bwd_status(const kd_desc *desc, const void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Number of polls a bounded wait of the backward makes before it gives up
- * (0 restores the default, 2^23 polls with a short sleep each: seconds).  For
- * tests of the timeout path, which set a small value so that the workers give
- * up at once; process-wide, read at each backward launch.
+ * Number of polls a bounded wait makes before it gives up (0 restores the
+ * default, 2^23 polls with a short sleep each: seconds): the backward's chunk
+ * workers, and the hand-offs of the one-launch few-heads forward and mixer
+ * forward.  For tests of the timeout path, which set a small value so that
+ * the waits give up at once; process-wide, read at each launch.
  */
 KD_API void kron_delta_bwd_set_wait_limit(uint32_t polls);
 
